@@ -1,0 +1,270 @@
+"""Plain fp64 CPU oracle for one step of cached masked-diffusion decoding.
+
+TEST INFRASTRUCTURE ONLY.  The tests, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` are the only callers.  The product path
+(``cached_denoising_amd``) never imports this package, and this package never
+imports the product; the two meet only at the seeded input generators in
+``workloads``.
+
+The arithmetic lives in ``oracle.c`` (C11, IEEE binary64, no FMA contraction,
+no fast-math).  This module only marshals numpy arrays into it.  Storage
+formats: float32 arrays as ``np.float32``, bfloat16 as raw ``np.uint16`` bits,
+OCP e4m3fn codes as ``np.uint8`` with float32 per-128-group scales.
+
+Citations name the page and its section:
+  [SWD]     Stable Window Decoding blog page (wmrh.cn/news/51151)
+  [LaCache] "LaCache: Exact Caching and Precision-Adaptive Inference for
+            Diffusion Large Language Models" (gist.science explainer)
+  [Sinks]   attention-sinks / rolling K/V cache blog page (wmrh.cn/news/159578)
+  [Flash]   Flash-dLLM page: I/O-aware KV cache and self-verifying parallel
+            decoding (bjdmk.com.cn/news/5926815)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+F32, BF16, E4M3 = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SOURCES = [os.path.join(_HERE, "oracle.c")]
+GCC_FLAGS = ["-std=c11", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+             "-fno-unsafe-math-optimizations", "-shared", "-fPIC", "-Wall", "-Wextra"]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile ``liboracle.so`` with gcc (always recompiles)."""
+    cmd = ["gcc", *GCC_FLAGS, "-o", LIB_PATH + ".tmp", *SOURCES, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    global _lib
+    _lib = None
+    return LIB_PATH
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        i32, i64, dbl = ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        L.oracle_set_threads.argtypes = [i32]
+        L.oracle_set_threads.restype = i32
+        L.oracle_get_threads.restype = i32
+        L.oracle_bf16_value.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_value.restype = dbl
+        L.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_value.restype = dbl
+        L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        L.oracle_e4m3_encode.restype = ctypes.c_uint8
+        L.oracle_e4m3_quantize_group.argtypes = [P, i32, P, P]
+        L.oracle_scatter_kv.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, i32, P, P, P, i32]
+        L.oracle_scatter_kv.restype = i32
+        L.oracle_sink_rolling_keys.argtypes = [i32, i32, i32, P]
+        L.oracle_sink_rolling_keys.restype = i32
+        L.oracle_block_attention.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, i32, P, i32, i32,
+                                             P, i32, dbl, P, P, P, i32]
+        L.oracle_block_attention.restype = i32
+        L.oracle_vocab_stats.argtypes = [i32, P, i64, i64, i64, P, P, P, P, i64]
+        L.oracle_vocab_stats.restype = i32
+        L.oracle_stability_step.argtypes = [i32, i32, i32, P, i32, P, P, P, P, P, P, P, P, P,
+                                            i32, dbl, i32, i32, dbl, dbl, dbl, dbl, i64,
+                                            P, P, P, P, P]
+        L.oracle_stability_step.restype = i32
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what}: bad argument (rc={rc})")
+
+
+def set_threads(n: int) -> int:
+    return lib().oracle_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return lib().oracle_get_threads()
+
+
+# ---- number formats ---------------------------------------------------------
+
+def bf16_value(bits: np.ndarray) -> np.ndarray:
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    return np.array([lib().oracle_bf16_value(int(b)) for b in bits.ravel()]).reshape(bits.shape)
+
+
+def e4m3_value(codes) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    return np.array([lib().oracle_e4m3_value(int(c)) for c in codes.ravel()]).reshape(codes.shape)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    f = lib().oracle_e4m3_encode
+    return np.array([f(float(v)) for v in x.ravel()], dtype=np.uint8).reshape(x.shape)
+
+
+def e4m3_quantize_group(x):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    codes = np.zeros(x.shape, dtype=np.uint8)
+    scale = np.zeros(1, dtype=np.float32)
+    lib().oracle_e4m3_quantize_group(_ptr(x), x.size, _ptr(codes), _ptr(scale))
+    return codes, float(scale[0])
+
+
+# ---- A1 ---------------------------------------------------------------------
+
+def scatter_kv(cache_k, cache_v, k_scale, v_scale, cache_dtype, k_new, v_new, src_dtype, pos):
+    """In-place: cache[b, h, pos[b, j], :] = new[b, j, h, :] (quantized for e4m3)."""
+    B, Hkv, L, d = cache_k.shape
+    n = pos.shape[1]
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    rc = lib().oracle_scatter_kv(cache_dtype, B, L, Hkv, d, _ptr(cache_k), _ptr(cache_v),
+                                 _ptr(k_scale), _ptr(v_scale), src_dtype,
+                                 _ptr(np.ascontiguousarray(k_new)), _ptr(np.ascontiguousarray(v_new)),
+                                 _ptr(pos), n)
+    _check(rc, "scatter_kv")
+
+
+# ---- A2 ---------------------------------------------------------------------
+
+def sink_rolling_keys(S: int, R: int, end: int) -> np.ndarray:
+    out = np.zeros(S + R, dtype=np.int32)
+    k = lib().oracle_sink_rolling_keys(S, R, end, _ptr(out))
+    if k < 0:
+        raise ValueError("oracle sink_rolling_keys: bad argument")
+    return out[:k].copy()
+
+
+# ---- A3 ---------------------------------------------------------------------
+
+def block_attention(cache_k, cache_v, k_scale, v_scale, cache_dtype, q, q_dtype,
+                    key_idx=None, scale=0.0, heads=None):
+    """softmax(q K^T * scale) V over the selected keys, fp64.
+
+    Returns (out [B, Hq, b, d], lse [B, Hq, b]) or, with ``heads`` (an
+    [n, 2] array of (batch, query-head) pairs), ([n, b, d], [n, b]).
+    """
+    B, Hkv, L, d = cache_k.shape
+    _, Hq, b, _ = q.shape
+    q = np.ascontiguousarray(q)
+    if key_idx is not None:
+        key_idx = np.ascontiguousarray(key_idx, dtype=np.int32)
+        n_keys = key_idx.shape[1]
+    else:
+        n_keys = L
+    if heads is not None:
+        heads = np.ascontiguousarray(heads, dtype=np.int32).reshape(-1, 2)
+        out = np.zeros((heads.shape[0], b, d))
+        lse = np.zeros((heads.shape[0], b))
+        nh = heads.shape[0]
+    else:
+        out = np.zeros((B, Hq, b, d))
+        lse = np.zeros((B, Hq, b))
+        nh = 0
+    rc = lib().oracle_block_attention(cache_dtype, B, L, Hkv, d, _ptr(cache_k), _ptr(cache_v),
+                                      _ptr(k_scale), _ptr(v_scale), q_dtype, _ptr(q), Hq, b,
+                                      _ptr(key_idx), n_keys, float(scale), _ptr(out), _ptr(lse),
+                                      _ptr(heads), nh)
+    _check(rc, "block_attention")
+    return out, lse
+
+
+# ---- A4 ---------------------------------------------------------------------
+
+def vocab_stats(logits, dtype, V=None, rows=None):
+    """argmax (lowest index of the max), maxprob, entropy per row, fp64.
+
+    ``logits`` is [N, stride] (f32, or uint16 bf16 bits); V <= stride is the
+    vocabulary size (default: the full row).
+    """
+    logits = np.ascontiguousarray(logits)
+    N, stride = logits.shape
+    V = stride if V is None else V
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        n_out = rows.shape[0]
+    else:
+        n_out = N
+    am = np.zeros(n_out, dtype=np.int32)
+    mp = np.zeros(n_out)
+    en = np.zeros(n_out)
+    rc = lib().oracle_vocab_stats(dtype, _ptr(logits), N, V, stride, _ptr(am), _ptr(mp), _ptr(en),
+                                  _ptr(rows), 0 if rows is None else n_out)
+    _check(rc, "vocab_stats")
+    return am, mp, en
+
+
+# ---- A5-A7 ------------------------------------------------------------------
+
+class StabilityState:
+    """Per-sequence decode state: step-history ring plus sticky stable flags."""
+
+    def __init__(self, B: int, L: int, D: int):
+        self.B, self.L, self.D = B, L, D
+        self.ring_argmax = np.zeros((D, B, L), dtype=np.int32)
+        self.ring_maxprob = np.zeros((D, B, L), dtype=np.float32)
+        self.ring_step = np.full((D, B, L), -1, dtype=np.int32)
+        self.entropy_latest = np.zeros((B, L), dtype=np.float32)
+        self.t_write = np.zeros((B, L), dtype=np.int32)
+        self.stable = np.zeros((B, L), dtype=np.uint8)
+
+    def copy(self):
+        c = StabilityState.__new__(StabilityState)
+        c.B, c.L, c.D = self.B, self.L, self.D
+        for k in ("ring_argmax", "ring_maxprob", "ring_step", "entropy_latest", "t_write", "stable"):
+            setattr(c, k, getattr(self, k).copy())
+        return c
+
+
+def stability_step(state: StabilityState, step, pos, argmax, maxprob, entropy, *, K, tau, R,
+                   alpha=0.0, beta=0.0, lam=0.0, conf_thresh=0.0, V=2):
+    """One step of history update, stability test, confidence and window mask.
+
+    pos: [B, n] recomputed positions or None (all L).  argmax/maxprob/entropy
+    are [B, n] (float32 maxprob/entropy).  Returns dict with mask, conf,
+    next_pos, count, all_stable.  ``state`` is updated in place.
+    """
+    B, L, D = state.B, state.L, state.D
+    if pos is not None:
+        pos = np.ascontiguousarray(pos, dtype=np.int32)
+        n = pos.shape[1]
+    else:
+        n = L
+    argmax = np.ascontiguousarray(argmax, dtype=np.int32).reshape(B, n)
+    maxprob = np.ascontiguousarray(maxprob, dtype=np.float32).reshape(B, n)
+    entropy = np.ascontiguousarray(entropy, dtype=np.float32).reshape(B, n)
+    mask = np.zeros((B, L), dtype=np.uint8)
+    conf = np.zeros((B, L))
+    next_pos = np.zeros((B, L), dtype=np.int32)
+    count = np.zeros(B, dtype=np.int32)
+    all_stable = np.zeros(B, dtype=np.uint8)
+    rc = lib().oracle_stability_step(B, L, int(step), _ptr(pos), n, _ptr(argmax), _ptr(maxprob),
+                                     _ptr(entropy), _ptr(state.ring_argmax), _ptr(state.ring_maxprob),
+                                     _ptr(state.ring_step), _ptr(state.entropy_latest),
+                                     _ptr(state.t_write), _ptr(state.stable), int(K), float(tau), D,
+                                     int(R), float(alpha), float(beta), float(lam),
+                                     float(conf_thresh), int(V), _ptr(mask), _ptr(conf),
+                                     _ptr(next_pos), _ptr(count), _ptr(all_stable))
+    _check(rc, "stability_step")
+    return dict(mask=mask, conf=conf, next_pos=next_pos, count=count, all_stable=all_stable)

@@ -1,0 +1,442 @@
+/*
+ * oracle.c -- plain fp64 CPU reference for one step of cached
+ * masked-diffusion decoding.  TEST INFRASTRUCTURE ONLY (see oracle.h).
+ *
+ * Build: gcc -std=c11 -O2 -fopenmp -ffp-contract=off -fno-fast-math
+ *        -shared -fPIC oracle.c -lm
+ * Parallel loops run over independent rows or heads only, so results do not
+ * depend on the thread count.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
+
+int oracle_get_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------------ */
+/* number formats                                                            */
+/* ------------------------------------------------------------------------ */
+
+double oracle_bf16_value(uint16_t bits)
+{
+    /* a bfloat16 is the upper half of a float32 */
+    uint32_t w = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return (double)f;
+}
+
+/* OCP e4m3fn: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits.
+ * Exponent field 0 is subnormal (value m * 2^-9); exponent 15 with mantissa
+ * 7 is NaN; there are no infinities.  Largest finite value 1.75 * 2^8 = 448. */
+double oracle_e4m3_value(uint8_t code)
+{
+    int sign = (code >> 7) & 1;
+    int e = (code >> 3) & 0xF;
+    int m = code & 0x7;
+    double v;
+    if (e == 0xF && m == 0x7) return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);                 /* m/8 * 2^(1-7) */
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+/* Round |x| to the e4m3 grid by direct construction: find the spacing of
+ * the grid in x's binade, divide (exact: power of two), round half to even
+ * with rint (the default rounding mode), multiply back, then read the code
+ * off the rounded value. */
+uint8_t oracle_e4m3_encode(float xf)
+{
+    double x = (double)xf;
+    uint8_t sign = 0;
+    double a, spacing, r, v;
+    int e, E, M;
+
+    if (isnan(x)) return 0x7F;
+    if (signbit(x)) { sign = 0x80; a = -x; } else { a = x; }
+    if (a > 448.0) return (uint8_t)(sign | 0x7E);   /* saturate: 0x7E = 448 */
+    if (a == 0.0) return sign;
+
+    frexp(a, &e);              /* a = f * 2^e with f in [0.5, 1): binade 2^(e-1) */
+    e -= 1;                    /* a in [2^e, 2^(e+1)) */
+    if (e < -6)
+        spacing = ldexp(1.0, -9);            /* subnormal spacing */
+    else
+        spacing = ldexp(1.0, e - 3);          /* 3 mantissa bits */
+    r = rint(a / spacing);                    /* ties to even */
+    v = r * spacing;
+    if (v == 0.0) return sign;
+    if (v < ldexp(1.0, -6)) {                 /* subnormal result */
+        E = 0;
+        M = (int)(v / ldexp(1.0, -9));
+    } else {
+        frexp(v, &e);
+        e -= 1;
+        E = e + 7;
+        M = (int)((v / ldexp(1.0, e) - 1.0) * 8.0);
+    }
+    return (uint8_t)(sign | (E << 3) | M);
+}
+
+void oracle_e4m3_quantize_group(const float *x, int n, uint8_t *codes, float *scale)
+{
+    float amax = 0.0f, s;
+    int i;
+    for (i = 0; i < n; ++i) {
+        float a = fabsf(x[i]);
+        if (a > amax) amax = a;
+    }
+    if (amax == 0.0f) {
+        *scale = 0.0f;
+        for (i = 0; i < n; ++i) codes[i] = 0;
+        return;
+    }
+    s = amax / 448.0f;                        /* float32 divide */
+    *scale = s;
+    for (i = 0; i < n; ++i) {
+        float q = x[i] / s;                   /* float32 divide */
+        codes[i] = oracle_e4m3_encode(q);
+    }
+}
+
+/* element -> double for the two float source formats */
+static double load_src(int dtype, const void *p, int64_t i)
+{
+    if (dtype == ORC_F32) return (double)((const float *)p)[i];
+    return oracle_bf16_value(((const uint16_t *)p)[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* A1: scatter                                                               */
+/* ------------------------------------------------------------------------ */
+
+int oracle_scatter_kv(int cache_dtype, int B, int L, int Hkv, int d,
+                      void *cache_k, void *cache_v, float *k_scale, float *v_scale,
+                      int src_dtype, const void *k_new, const void *v_new,
+                      const int32_t *pos, int n)
+{
+    int b, j, h, c, g;
+    if (B < 0 || L <= 0 || Hkv <= 0 || d <= 0 || n < 0) return -1;
+    if (cache_dtype == ORC_E4M3) {
+        if (d % 128 != 0 || !k_scale || !v_scale) return -1;
+        if (src_dtype != ORC_F32 && src_dtype != ORC_BF16) return -1;
+    } else if (cache_dtype == ORC_F32 || cache_dtype == ORC_BF16) {
+        if (src_dtype != cache_dtype) return -1;
+    } else {
+        return -1;
+    }
+    for (b = 0; b < B; ++b)
+        for (j = 0; j < n; ++j) {
+            int p = pos[(int64_t)b * n + j];
+            if (p < 0 || p >= L) return -1;
+        }
+
+    for (b = 0; b < B; ++b) {
+        for (j = 0; j < n; ++j) {
+            int p = pos[(int64_t)b * n + j];
+            for (h = 0; h < Hkv; ++h) {
+                int64_t src_row = (((int64_t)b * n + j) * Hkv + h) * d;
+                int64_t dst_row = (((int64_t)b * Hkv + h) * L + p) * d;
+                if (cache_dtype == ORC_F32) {
+                    memcpy((float *)cache_k + dst_row, (const float *)k_new + src_row, (size_t)d * 4);
+                    memcpy((float *)cache_v + dst_row, (const float *)v_new + src_row, (size_t)d * 4);
+                } else if (cache_dtype == ORC_BF16) {
+                    memcpy((uint16_t *)cache_k + dst_row, (const uint16_t *)k_new + src_row, (size_t)d * 2);
+                    memcpy((uint16_t *)cache_v + dst_row, (const uint16_t *)v_new + src_row, (size_t)d * 2);
+                } else {
+                    /* per-group FP8: one float32 scale per 128 consecutive
+                     * elements of a row [LaCache, Methodology 2: 1x128 groups] */
+                    float xk[128], xv[128];
+                    int ng = d / 128;
+                    for (g = 0; g < ng; ++g) {
+                        int64_t sidx = (((int64_t)b * Hkv + h) * L + p) * ng + g;
+                        for (c = 0; c < 128; ++c) {
+                            xk[c] = (float)load_src(src_dtype, k_new, src_row + g * 128 + c);
+                            xv[c] = (float)load_src(src_dtype, v_new, src_row + g * 128 + c);
+                        }
+                        oracle_e4m3_quantize_group(xk, 128, (uint8_t *)cache_k + dst_row + g * 128, &k_scale[sidx]);
+                        oracle_e4m3_quantize_group(xv, 128, (uint8_t *)cache_v + dst_row + g * 128, &v_scale[sidx]);
+                    }
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* A2: sink + rolling key index map                                          */
+/* ------------------------------------------------------------------------ */
+
+int oracle_sink_rolling_keys(int S, int R, int end, int32_t *key_idx)
+{
+    /* sinks keep their original positions; the rolling part keeps the R
+     * newest keys, oldest first [Sinks, 2.3 and 3.2] */
+    int k = 0, i, start;
+    if (S < 0 || R < 0 || end < 0) return -1;
+    for (i = 0; i < S && i < end; ++i) key_idx[k++] = i;
+    start = end - R;
+    if (start < S) start = S;
+    for (i = start; i < end; ++i) key_idx[k++] = i;
+    return k;
+}
+
+/* ------------------------------------------------------------------------ */
+/* A3: block attention                                                       */
+/* ------------------------------------------------------------------------ */
+
+/* value of element c of cached row (bh, key) */
+static double cache_value(int dtype, const void *cache, const float *scale,
+                          int64_t row, int d, int c)
+{
+    int64_t i = row * d + c;
+    if (dtype == ORC_F32) return (double)((const float *)cache)[i];
+    if (dtype == ORC_BF16) return oracle_bf16_value(((const uint16_t *)cache)[i]);
+    /* e4m3: code times its group's float32 scale, exact in double */
+    return oracle_e4m3_value(((const uint8_t *)cache)[i]) *
+           (double)scale[row * (d / 128) + c / 128];
+}
+
+int oracle_block_attention(int cache_dtype, int B, int L, int Hkv, int d,
+                           const void *cache_k, const void *cache_v,
+                           const float *k_scale, const float *v_scale,
+                           int q_dtype, const void *q, int Hq, int b,
+                           const int32_t *key_idx, int n_keys, double scale,
+                           double *out, double *lse,
+                           const int32_t *heads, int n_heads)
+{
+    int64_t task, n_tasks;
+    int group, err = 0;
+    if (B <= 0 || L <= 0 || Hkv <= 0 || d <= 0 || Hq <= 0 || b <= 0) return -1;
+    if (Hq % Hkv != 0) return -1;
+    if (cache_dtype == ORC_E4M3 && (d % 128 != 0 || !k_scale || !v_scale)) return -1;
+    if (!key_idx) n_keys = L;
+    if (n_keys <= 0) return -1;
+    if (key_idx) {
+        int64_t i;
+        for (i = 0; i < (int64_t)B * n_keys; ++i)
+            if (key_idx[i] < 0 || key_idx[i] >= L) return -1;
+    }
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
+    group = Hq / Hkv;
+    n_tasks = heads ? (int64_t)n_heads : (int64_t)B * Hq;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (task = 0; task < n_tasks; ++task) {
+        int bi, h, kvh, i, j, c;
+        double *s = (double *)malloc(sizeof(double) * (size_t)n_keys);
+        if (!s) { err = 1; continue; }
+        if (heads) { bi = heads[2 * task]; h = heads[2 * task + 1]; }
+        else { bi = (int)(task / Hq); h = (int)(task % Hq); }
+        kvh = h / group;
+        for (i = 0; i < b; ++i) {
+            int64_t qrow = (((int64_t)bi * Hq + h) * b + i) * d;
+            int64_t orow = (task * b + i) * d;
+            double m = -INFINITY, z = 0.0;
+            /* scores s_j = scale * q . k_j */
+            for (j = 0; j < n_keys; ++j) {
+                int key = key_idx ? key_idx[(int64_t)bi * n_keys + j] : j;
+                int64_t krow = ((int64_t)bi * Hkv + kvh) * L + key;
+                double dot = 0.0;
+                for (c = 0; c < d; ++c)
+                    dot += load_src(q_dtype, q, qrow + c) *
+                           cache_value(cache_dtype, cache_k, k_scale, krow, d, c);
+                s[j] = scale * dot;
+                if (s[j] > m) m = s[j];
+            }
+            /* softmax weights and the weighted sum of values */
+            for (j = 0; j < n_keys; ++j) {
+                s[j] = exp(s[j] - m);
+                z += s[j];
+            }
+            for (c = 0; c < d; ++c) out[orow + c] = 0.0;
+            for (j = 0; j < n_keys; ++j) {
+                int key = key_idx ? key_idx[(int64_t)bi * n_keys + j] : j;
+                int64_t vrow = ((int64_t)bi * Hkv + kvh) * L + key;
+                double p = s[j] / z;
+                for (c = 0; c < d; ++c)
+                    out[orow + c] += p * cache_value(cache_dtype, cache_v, v_scale, vrow, d, c);
+            }
+            if (lse) lse[task * b + i] = m + log(z);
+        }
+        free(s);
+    }
+    return err ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* A4: vocab statistics                                                      */
+/* ------------------------------------------------------------------------ */
+
+int oracle_vocab_stats(int dtype, const void *logits, int64_t N, int64_t V,
+                       int64_t row_stride, int32_t *argmax, double *maxprob,
+                       double *entropy, const int64_t *rows, int64_t n_rows)
+{
+    int64_t t, n_out;
+    if (N < 0 || V <= 0 || row_stride < V) return -1;
+    if (dtype != ORC_F32 && dtype != ORC_BF16) return -1;
+    n_out = rows ? n_rows : N;
+    if (rows) {
+        for (t = 0; t < n_rows; ++t)
+            if (rows[t] < 0 || rows[t] >= N) return -1;
+    }
+
+#pragma omp parallel for schedule(dynamic, 4)
+    for (t = 0; t < n_out; ++t) {
+        int64_t r = rows ? rows[t] : t;
+        int64_t base = r * row_stride, j, best = 0;
+        double m = -INFINITY, z = 0.0, h = 0.0;
+        /* the largest logit, lowest index first */
+        for (j = 0; j < V; ++j) {
+            double x = load_src(dtype, logits, base + j);
+            if (x > m) { m = x; best = j; }
+        }
+        /* normaliser of the softmax */
+        for (j = 0; j < V; ++j)
+            z += exp(load_src(dtype, logits, base + j) - m);
+        /* entropy -sum p ln p; a zero probability adds nothing */
+        for (j = 0; j < V; ++j) {
+            double p = exp(load_src(dtype, logits, base + j) - m) / z;
+            if (p > 0.0) h -= p * log(p);
+        }
+        argmax[t] = (int32_t)best;
+        maxprob[t] = exp(load_src(dtype, logits, base + best) - m) / z;
+        entropy[t] = h;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* A5-A7: history ring, stability test, confidence, window mask             */
+/* ------------------------------------------------------------------------ */
+
+int oracle_stability_step(int B, int L, int step, const int32_t *pos, int n,
+                          const int32_t *argmax, const float *maxprob,
+                          const float *entropy,
+                          int32_t *ring_argmax, float *ring_maxprob, int32_t *ring_step,
+                          float *entropy_latest, int32_t *t_write, uint8_t *stable,
+                          int K, double tau, int D, int R,
+                          double alpha, double beta, double lambda,
+                          double conf_thresh, int64_t V,
+                          uint8_t *mask, double *conf, int32_t *next_pos,
+                          int32_t *count, uint8_t *all_stable)
+{
+    int b;
+    double hmax;
+    if (B <= 0 || L <= 0 || step < 0 || K < 1 || D < K || R < 0 || V < 2) return -1;
+    if (!pos) n = L;
+    if (n < 0 || n > L) return -1;
+    if (pos) {
+        int64_t i;
+        for (i = 0; i < (int64_t)B * n; ++i)
+            if (pos[i] < 0 || pos[i] >= L) return -1;
+    }
+    hmax = log((double)V);                    /* entropy of the uniform row */
+
+    for (b = 0; b < B; ++b) {
+        int j, i, k, c;
+        int64_t row = (int64_t)b * L;
+        int slot = step % D;
+        uint8_t *seed = (uint8_t *)calloc((size_t)L, 1);
+        int any_seed = 0;
+        if (!seed) return -1;
+
+        /* (c) record this step's prediction for every recomputed position
+         * [SWD, 3.3 step c]; the position's K/V were written at this step */
+        for (j = 0; j < n; ++j) {
+            int p = pos ? pos[(int64_t)b * n + j] : j;
+            int64_t ri = (int64_t)slot * B * L + row + p;
+            ring_argmax[ri] = argmax[(int64_t)b * n + j];
+            ring_maxprob[ri] = maxprob[(int64_t)b * n + j];
+            ring_step[ri] = step;
+            entropy_latest[row + p] = entropy[(int64_t)b * n + j];
+            t_write[row + p] = step;
+        }
+
+        /* (d) a position not yet stable becomes stable when its last K
+         * records are the steps s, s-1, ..., s-K+1, all with the same token,
+         * and the mean of their max-probabilities exceeds tau
+         * [SWD, 3.1 criterion; 4.2 update_stability]; stable is sticky */
+        for (j = 0; j < n; ++j) {
+            int p = pos ? pos[(int64_t)b * n + j] : j;
+            int ok = 1, tok;
+            double sum = 0.0, mean;
+            if (stable[row + p]) continue;
+            if (step + 1 < K) continue;              /* fewer than K steps so far */
+            tok = ring_argmax[(int64_t)slot * B * L + row + p];
+            for (k = K - 1; k >= 0; --k) {           /* oldest record first */
+                int sk = (step - k) % D;
+                int64_t ri = (int64_t)sk * B * L + row + p;
+                if (ring_step[ri] != step - k || ring_argmax[ri] != tok) { ok = 0; break; }
+                sum += (double)ring_maxprob[ri];
+            }
+            if (!ok) continue;
+            mean = sum / (double)K;
+            if (mean > tau) stable[row + p] = 1;
+        }
+
+        /* cache confidence alpha(1 - H/Hmax) + beta exp(-lambda (s - t_write))
+         * for every position; below the threshold its cache is refreshed
+         * [Flash, 3.1] */
+        for (i = 0; i < L; ++i) {
+            double h = (double)entropy_latest[row + i];
+            double dt = (double)(step - t_write[row + i]);
+            double cf = alpha * (1.0 - h / hmax) + beta * exp(-lambda * dt);
+            int low = cf < conf_thresh;
+            conf[row + i] = cf;
+            seed[i] = (uint8_t)(!stable[row + i] || low);
+            if (seed[i]) any_seed = 1;
+        }
+
+        /* window: each seed position u covers [max(0, u-R), min(L-1, u+R)];
+         * nothing to recompute -> full mask and the all-stable flag
+         * [SWD, 3.2; 4.2 get_computation_mask] */
+        for (i = 0; i < L; ++i) mask[row + i] = 0;
+        if (!any_seed) {
+            for (i = 0; i < L; ++i) mask[row + i] = 1;
+        } else {
+            for (i = 0; i < L; ++i) {
+                int lo, hi, u;
+                if (!seed[i]) continue;
+                lo = i - R < 0 ? 0 : i - R;
+                hi = i + R > L - 1 ? L - 1 : i + R;
+                for (u = lo; u <= hi; ++u) mask[row + u] = 1;
+            }
+        }
+        all_stable[b] = (uint8_t)(!any_seed);
+
+        /* positions to recompute next step, ascending */
+        c = 0;
+        for (i = 0; i < L; ++i)
+            if (mask[row + i]) next_pos[row + c++] = i;
+        count[b] = c;
+        for (i = c; i < L; ++i) next_pos[row + i] = -1;
+        free(seed);
+    }
+    return 0;
+}

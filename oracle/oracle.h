@@ -1,0 +1,130 @@
+/*
+ * oracle.h -- plain, slow, obviously-correct CPU reference for one step of
+ * cached masked-diffusion decoding.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link
+ * or call this code: only the tests, the smoke check and the CPU-baseline
+ * leg of the benchmark use it.  It shares no code, header, table or helper
+ * with the HIP library; the two meet only at the seeded input generators.
+ *
+ * Everything is computed in IEEE binary64 (double), scalar, in the order the
+ * pages state, with no FMA contraction and no fast-math.  Inputs are the
+ * exact bytes the GPU reads: float32 as float, bfloat16 as raw uint16 bits,
+ * OCP e4m3fn codes as uint8 with one float32 scale per 128-element group.
+ *
+ * Page titles used in citations:
+ *   [SWD]     "Stable Window Decoding (SWD)" blog page on temporal stability
+ *             in diffusion-LM decoding (wmrh.cn/news/51151)
+ *   [LaCache] "LaCache: Exact Caching and Precision-Adaptive Inference for
+ *             Diffusion Large Language Models" (gist.science explainer)
+ *   [Sinks]   "Attention sinks and the rolling K/V cache" blog page on GPT-2
+ *             (wmrh.cn/news/159578)
+ *   [Flash]   "Diffusion-LM inference acceleration: I/O-aware KV cache and
+ *             self-verifying parallel decoding" (Flash-dLLM, bjdmk.com.cn)
+ *
+ * Where the pages leave a step open, the plainest reading is taken and is
+ * stated next to the function that takes it.
+ */
+#ifndef DLLM_ORACLE_H
+#define DLLM_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* storage codes, numerically equal to the library's but defined here anew */
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_E4M3 = 2 };
+
+/* number of OpenMP threads used by the parallel loops; returns the count */
+int oracle_set_threads(int n);
+int oracle_get_threads(void);
+
+/* ---- number formats --------------------------------------------------- */
+/* bfloat16 bits -> exact value */
+double oracle_bf16_value(uint16_t bits);
+/* OCP e4m3fn code -> exact value (0x7f / 0xff are NaN) */
+double oracle_e4m3_value(uint8_t code);
+/* float32 -> OCP e4m3fn code, round to nearest, ties to even mantissa,
+ * finite overflow saturates to +-448 [LaCache, Methodology 2: per-group FP8;
+ * the pages give only the group shapes, so format and rounding are a reading] */
+uint8_t oracle_e4m3_encode(float x);
+/* quantize one group of n values: scale = amax/448 (float32 divide),
+ * code_i = encode(x_i / scale) (float32 divide); amax == 0 -> scale 0, codes 0 */
+void oracle_e4m3_quantize_group(const float *x, int n, uint8_t *codes, float *scale);
+
+/* ---- A1: scatter fresh K/V rows into the persistent cache ---------------
+ * [LaCache, Methodology 1 (RoPECache) and 3 (workflow)]; [SWD, 4.1/4.3
+ * write-back of masked positions]; [Sinks, 3.2 fixed-size cache].
+ * cache_k/cache_v: [B, Hkv, L, d] in cache_dtype; k_scale/v_scale:
+ * [B, Hkv, L, d/128] float (e4m3 only).  k_new/v_new: [B, n, Hkv, d] in
+ * src_dtype (== cache dtype for f32/bf16; f32 or bf16 for e4m3).
+ * pos: [B, n] int32, unique per sequence, each in [0, L).  Returns 0, or -1
+ * on a bad argument (nothing written). */
+int oracle_scatter_kv(int cache_dtype, int B, int L, int Hkv, int d,
+                      void *cache_k, void *cache_v, float *k_scale, float *v_scale,
+                      int src_dtype, const void *k_new, const void *v_new,
+                      const int32_t *pos, int n);
+
+/* ---- A2: sink + rolling key map [Sinks, 2.3 and 3.2] --------------------
+ * keys = {0..S-1} followed by the newest R keys before `end`, i.e.
+ * [max(S, end-R), end).  Writes at most S+R indices, returns the count. */
+int oracle_sink_rolling_keys(int S, int R, int end, int32_t *key_idx);
+
+/* ---- A3: block attention over the cache ---------------------------------
+ * softmax(q . K^T * scale) V per query, bidirectional, over the selected
+ * keys [Sinks, 2.1]; [LaCache, problem statement: bidirectional attention].
+ * q: [B, Hq, b, d] in q_dtype (f32 or bf16); cache as in A1; key_idx:
+ * [B, n_keys] or NULL (= 0..L-1, n_keys = L); query head h reads KV head
+ * h / (Hq/Hkv).  scale <= 0 -> 1/sqrt(d).  out: [B, Hq, b, d] double;
+ * lse: [B, Hq, b] double (natural-log log-sum-exp of the scaled scores) or
+ * NULL.  Optional head subset: when heads != NULL, only the n_heads listed
+ * (b_idx, h) pairs are computed, packed in order into out/lse. */
+int oracle_block_attention(int cache_dtype, int B, int L, int Hkv, int d,
+                           const void *cache_k, const void *cache_v,
+                           const float *k_scale, const float *v_scale,
+                           int q_dtype, const void *q, int Hq, int b,
+                           const int32_t *key_idx, int n_keys, double scale,
+                           double *out, double *lse,
+                           const int32_t *heads, int n_heads);
+
+/* ---- A4: vocab statistics per row ---------------------------------------
+ * p = softmax(x); argmax = lowest index of the largest logit; maxprob =
+ * max_j p_j; entropy = -sum p_j ln p_j (terms with p_j = 0 add nothing).
+ * [SWD, 3.1 and 4.2: max probability token]; [Flash, 3.1: entropy].
+ * logits: rows of length V at stride row_stride elements, f32 or bf16.
+ * rows != NULL selects n_rows row indices (outputs packed in that order). */
+int oracle_vocab_stats(int dtype, const void *logits, int64_t N, int64_t V,
+                       int64_t row_stride, int32_t *argmax, double *maxprob,
+                       double *entropy, const int64_t *rows, int64_t n_rows);
+
+/* ---- A5-A7: history, stability, confidence, window mask -----------------
+ * One decode step s for B sequences of length L.
+ * pos [B, n] lists the positions recomputed this step (NULL: all L, n = L);
+ * argmax/maxprob/entropy are this step's statistics for those rows,
+ * laid out [B, n].  State (in/out): ring_argmax/ring_maxprob/ring_step
+ * [D, B, L] (slot s mod D holds step s; ring_step = -1 marks empty),
+ * entropy_latest/t_write [B, L], stable [B, L] (0/1, sticky).
+ * Params: K steps, tau (strict >), D ring depth >= K, R radius >= 0,
+ * alpha, beta, lambda, conf_thresh (<= 0 disables the gate), vocab V
+ * (Hmax = ln V).  Outputs: mask [B, L] (0/1), conf [B, L] double,
+ * next_pos [B, L] (ascending masked positions, rest -1), count [B],
+ * all_stable [B].
+ * [SWD, 3.1 stability test; 3.2 window; 3.3 steps c-d; 4.2 scheduler];
+ * [Flash, 3.1 cache confidence]. */
+int oracle_stability_step(int B, int L, int step, const int32_t *pos, int n,
+                          const int32_t *argmax, const float *maxprob,
+                          const float *entropy,
+                          int32_t *ring_argmax, float *ring_maxprob, int32_t *ring_step,
+                          float *entropy_latest, int32_t *t_write, uint8_t *stable,
+                          int K, double tau, int D, int R,
+                          double alpha, double beta, double lambda,
+                          double conf_thresh, int64_t V,
+                          uint8_t *mask, double *conf, int32_t *next_pos,
+                          int32_t *count, uint8_t *all_stable);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
