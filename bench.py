@@ -1,0 +1,292 @@
+"""Benchmark of one decode step of the cached masked-diffusion hot path.
+
+A step is one pass over the four kernels of the GPT-2-small-shaped workload
+(B=8 sequences of L=1024, 12 heads x 64, bf16 K/V cache, active block of 32
+at a per-sequence offset, vocab 50257 bf16 logits for every position):
+    dllm_scatter_kv -> dllm_block_attention -> dllm_vocab_stats -> dllm_stability_mask
+all on one stream with inputs resident in HBM.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config gpt2]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "denoise steps/sec (block attn + vocab stats); achieved HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+VOCAB_SRC = os.path.join(ROOT, "cached_denoising_amd", "csrc", "vocab_stats.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="gpt2", choices=["gpt2", "llada", "vocab", "longctx"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(config):
+    """HBM bytes per launch of the vocab kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source"""
+    path = os.path.join(PROFILES, f"vocab_stats_{config}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_tb = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_tb or m_sha.group(1) != kernel_sha(VOCAB_SRC):
+        return None
+    return float(m_tb.group(1))
+
+
+class Step:
+    """All device buffers of one workload and the kernels of one step."""
+
+    def __init__(self, D, W, cfg, dev):
+        import torch
+        self.D, self.W, self.cfg, self.dev = D, W, cfg, dev
+        B, L, H, d = cfg.B, cfg.L, cfg.Hkv, cfg.d
+        kvt = {W.BF16: torch.bfloat16, W.E4M3: torch.uint8, W.F32: torch.float32}[cfg.kv_dtype]
+        self.has_attn = cfg.b > 0 and d > 0 and cfg.name != "vocab"
+        self.has_vocab = cfg.V > 0
+        self.has_stab = cfg.name in ("gpt2", "vocab", "tiny")
+        if self.has_attn:
+            k = torch.empty((B, H, L, d), dtype=kvt, device=dev)
+            v = torch.empty_like(k)
+            ks = vs = None
+            if cfg.kv_dtype == W.E4M3:
+                ks = torch.empty((B, H, L, d // 128), dtype=torch.float32, device=dev)
+                vs = torch.empty_like(ks)
+            self.cache = D.dllm_cache_init(k, v, cfg.kv_dtype, ks, vs)
+            kc, vc = W.kv_rows(cfg, device=dev)
+            D.dllm_scatter_kv(self.cache, kc, vc, torch.arange(L, dtype=torch.int32, device=dev).repeat(B, 1))
+            del kc, vc
+            self.kn, self.vn = W.kv_rows(cfg, device=dev, which="fresh")
+            self.pos = W.block_positions(cfg, dev)
+            self.q = W.queries(cfg, device=dev)
+            self.key_idx = None
+            if cfg.sinks:
+                end = (self.pos[:, -1] + 1).contiguous()
+                self.key_idx = torch.empty((B, cfg.sinks + cfg.rolling), dtype=torch.int32, device=dev)
+                D.dllm_sink_rolling_map(L, cfg.sinks, cfg.rolling, end, self.key_idx)
+            n_keys = L if self.key_idx is None else self.key_idx.shape[1]
+            self.n_keys = n_keys
+            self.out = torch.empty((B, cfg.Hq, cfg.b, d), dtype=torch.bfloat16, device=dev)
+            wsb = D.dllm_block_attention_workspace(self.cache, W.BF16, cfg.Hq, cfg.b, n_keys)
+            self.attn_ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+        if self.has_vocab:
+            self.logits = W.logits(cfg, device=dev)
+            N = self.logits.shape[0]
+            self.N = N
+            self.am = torch.empty(N, dtype=torch.int32, device=dev)
+            self.mp = torch.empty(N, dtype=torch.float32, device=dev)
+            self.en = torch.empty(N, dtype=torch.float32, device=dev)
+            wsb = D.dllm_vocab_stats_workspace(N, cfg.V)
+            self.vocab_ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+        if self.has_stab:
+            self.st = D.StabilityState(B, L, cfg.D, device=dev)
+            self.kw = dict(K=cfg.K, tau=cfg.tau, R=cfg.R, alpha=cfg.alpha, beta=cfg.beta,
+                           lam=cfg.lam, conf_thresh=cfg.conf_thresh, V=cfg.V)
+        self.step_no = 0
+
+    def kernels(self):
+        ks = []
+        if self.has_attn:
+            ks += ["scatter", "attention"]
+        if self.has_vocab:
+            ks.append("vocab_stats")
+        if self.has_stab:
+            ks.append("stability")
+        return ks
+
+    def run(self, events=None):
+        D, cfg = self.D, self.cfg
+
+        def mark(name, i):
+            if events is not None:
+                events[name][i].record()
+
+        if self.has_attn:
+            mark("scatter", 0)
+            D.dllm_scatter_kv(self.cache, self.kn, self.vn, self.pos)
+            mark("scatter", 1)
+            mark("attention", 0)
+            D.dllm_block_attention(self.cache, self.q, key_idx=self.key_idx, out=self.out,
+                                   workspace=self.attn_ws)
+            mark("attention", 1)
+        if self.has_vocab:
+            mark("vocab_stats", 0)
+            D.dllm_vocab_stats(self.logits, V=cfg.V, argmax=self.am, maxprob=self.mp,
+                               entropy=self.en, workspace=self.vocab_ws)
+            mark("vocab_stats", 1)
+        if self.has_stab:
+            mark("stability", 0)
+            B, L = cfg.B, cfg.L
+            D.dllm_stability_mask(self.st, self.step_no, None, self.am.view(B, L), self.mp.view(B, L),
+                                  self.en.view(B, L), **self.kw)
+            mark("stability", 1)
+        self.step_no += 1
+
+    def algorithmic_bytes(self):
+        """bytes each kernel must move (reads + writes), per launch"""
+        cfg = self.cfg
+        out = {}
+        if self.has_attn:
+            esz = 1 if cfg.kv_dtype == self.W.E4M3 else 2
+            rows = cfg.B * cfg.b * cfg.Hkv
+            scale_b = 4 * 2 if cfg.kv_dtype == self.W.E4M3 else 0
+            out["scatter"] = rows * cfg.d * (2 * 2 + 2 * esz) + rows * scale_b + cfg.B * cfg.b * 4
+            kv = cfg.B * cfg.Hkv * self.n_keys * (cfg.d * esz * 2 + scale_b)
+            qo = cfg.B * cfg.Hq * cfg.b * cfg.d * 2 * 2
+            out["attention"] = kv + qo
+        if self.has_vocab:
+            out["vocab_stats"] = self.N * cfg.V * 2 + self.N * 12
+        if self.has_stab:
+            BL = cfg.B * cfg.L
+            # stats in (12) + ring slot write (12) + K-1 ring reads (12 each) +
+            # state read/write (entropy 4, t_write 4, stable 1: twice) + outputs
+            # (mask 1, conf 4, next_pos 4)
+            out["stability"] = BL * (12 + 12 + 12 * (cfg.K - 1) + 2 * 9 + 9)
+        return out
+
+
+def cpu_baseline(step, D, W, cfg):
+    """The oracle as it stands, on a bounded sample of the same step, on the
+    host's cores; scaled to steps/s."""
+    import numpy as np
+    import torch
+
+    import oracle
+    threads = oracle.set_threads(int(os.environ.get("OMP_NUM_THREADS", min(16, os.cpu_count() or 1))))
+    t_total = 0.0
+    parts = []
+    if step.has_vocab:
+        n = min(step.N, 1024)
+        host = W.as_numpy_bits(step.logits[:n])
+        t0 = time.perf_counter()
+        oracle.vocab_stats(host, W.BF16 if step.logits.dtype == torch.bfloat16 else W.F32, V=cfg.V)
+        dt = (time.perf_counter() - t0) * step.N / n
+        t_total += dt
+        parts.append(f"vocab stats on {n} of {step.N} rows")
+    if step.has_attn:
+        ck, cv = W.as_numpy_bits(step.cache.k), W.as_numpy_bits(step.cache.v)
+        ks = step.cache.k_scale.cpu().numpy() if step.cache.k_scale is not None else None
+        vs = step.cache.v_scale.cpu().numpy() if step.cache.v_scale is not None else None
+        n_heads = cfg.B * cfg.Hq
+        ns = min(n_heads, 24)
+        heads = np.stack([np.arange(ns) % cfg.B, np.arange(ns) % cfg.Hq], 1).astype(np.int32)
+        kid = step.key_idx.cpu().numpy() if step.key_idx is not None else None
+        t0 = time.perf_counter()
+        oracle.block_attention(ck, cv, ks, vs, cfg.kv_dtype, W.as_numpy_bits(step.q), W.BF16,
+                               key_idx=kid, heads=heads)
+        t_total += (time.perf_counter() - t0) * n_heads / ns
+        t0 = time.perf_counter()
+        oracle.scatter_kv(ck, cv, ks, vs, cfg.kv_dtype, W.as_numpy_bits(step.kn), W.as_numpy_bits(step.vn),
+                          W.BF16, step.pos.cpu().numpy())
+        t_total += time.perf_counter() - t0
+        parts.append(f"attention on {ns} of {n_heads} (sequence, head) pairs; full scatter")
+    if step.has_stab:
+        ost = oracle.StabilityState(cfg.B, cfg.L, cfg.D)
+        am = step.am.cpu().numpy().reshape(cfg.B, cfg.L)
+        mp = step.mp.cpu().numpy().reshape(cfg.B, cfg.L)
+        en = step.en.cpu().numpy().reshape(cfg.B, cfg.L)
+        t0 = time.perf_counter()
+        for s in range(3):
+            oracle.stability_step(ost, s, None, am, mp, en, **step.kw)
+        t_total += (time.perf_counter() - t0) / 3
+        parts.append("full stability step")
+    return {"value": 1.0 / t_total, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": "; ".join(parts) + "; times scaled linearly to the whole step"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); there is no "
+              f"multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import cached_denoising_amd as D
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    cfg = W.CONFIGS[args.config]
+    step = Step(D, W, cfg, dev)
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    names = step.kernels()
+    events = {n: [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+              for n in names}
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step.run({n: events[n][i] for n in names})
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = start.elapsed_time(end) / args.steps
+    per_kernel_us = {n: 1000.0 * sum(e[0].elapsed_time(e[1]) for e in events[n]) / args.steps
+                     for n in names}
+    alg = step.algorithmic_bytes()
+    dom = "vocab_stats" if step.has_vocab else "attention"
+    dom_us = per_kernel_us[dom]
+    achieved = alg[dom] / (dom_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(args.config) if dom == "vocab_stats" else None,
+                "kernel": dom, "algorithmic_bytes_per_launch": alg[dom],
+                "avg_launch_us": round(dom_us, 2)}
+    cpu = None if args.no_cpu_baseline else cpu_baseline(step, D, W, cfg)
+    desc = {
+        "gpt2": "GPT-2-small-shaped decode step: B=8, L=1024, 12 heads x d64, bf16 K/V cache, "
+                "block b=32 at a random offset, vocab 50257 bf16 logits for all 8192 positions, "
+                "K=3 tau=0.95 R=2",
+        "llada": "LLaDA-8B-shaped SAR step: B=16, L=2048, 32 heads x d128, bf16 K/V, block 32, "
+                 "vocab 126464 bf16 logits for the 512 block rows",
+        "vocab": "vocab-stats sweep: 32768 rows x 126464 bf16 logits, 64-step ring, K=3 tau=0.9 R=3",
+        "longctx": "long-context step: B=4, L=32768, 32/8 GQA heads x d128, e4m3 K/V with "
+                   "per-128 scales, block 64, 4 sinks + 8188 rolling keys",
+    }[args.config]
+    line = {
+        "metric": METRIC, "value": round(1000.0 / ms, 2), "unit": "steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": desc, "name": cfg.name, "B": cfg.B, "L": cfg.L, "heads": cfg.Hq,
+                   "kv_heads": cfg.Hkv, "d_head": cfg.d, "block": cfg.b, "vocab": cfg.V},
+        "kernels_us": {n: round(v, 2) for n, v in per_kernel_us.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "wall_s": round(t_wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,287 @@
+"""Python binding of libdllm, the MI355X (gfx950) hot path of cached
+masked-diffusion decoding.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C
+ABI declared in ``include/dllm.h``.  PyTorch supplies device memory and the
+current stream.  The functions keep the C names.  There is no fallback: if
+``libdllm.so`` is missing or a tensor is not on a GPU, a call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "F32", "BF16", "E4M3", "DllmError", "lib", "Cache", "StabilityState", "dllm_status_str",
+    "dllm_version", "dllm_cache_init", "dllm_scatter_kv", "dllm_sink_rolling_map",
+    "dllm_block_attention", "dllm_block_attention_workspace", "dllm_vocab_stats",
+    "dllm_vocab_stats_workspace", "dllm_stability_reset", "dllm_stability_mask",
+]
+
+F32, BF16, E4M3 = 0, 1, 2
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdllm.so")
+
+
+class DllmError(RuntimeError):
+    pass
+
+
+class _KVCache(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("L", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("d_head", ctypes.c_int32), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p)]
+
+
+class _StabParams(ctypes.Structure):
+    _fields_ = [("K", ctypes.c_int32), ("D", ctypes.c_int32), ("R", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("tau", ctypes.c_double), ("alpha", ctypes.c_double),
+                ("beta", ctypes.c_double), ("lam", ctypes.c_double),
+                ("conf_thresh", ctypes.c_double), ("vocab", ctypes.c_int64)]
+
+
+EXPORTS = {
+    # name: (restype, argtypes)
+    "dllm_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "dllm_version": (ctypes.c_int, []),
+    "dllm_cache_init": (ctypes.c_int, [ctypes.POINTER(_KVCache), ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p]),
+    "dllm_scatter_kv": (ctypes.c_int, [ctypes.POINTER(_KVCache), ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p]),
+    "dllm_sink_rolling_map": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                             ctypes.c_void_p]),
+    "dllm_block_attention": (ctypes.c_int, [ctypes.POINTER(_KVCache), ctypes.c_void_p, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                            ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
+                                            ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_size_t, ctypes.c_void_p]),
+    "dllm_block_attention_workspace": (ctypes.c_size_t, [ctypes.POINTER(_KVCache), ctypes.c_int,
+                                                         ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+    "dllm_vocab_stats": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_size_t, ctypes.c_void_p]),
+    "dllm_vocab_stats_workspace": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64]),
+    "dllm_stability_reset": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p]),
+    "dllm_stability_mask": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.POINTER(_StabParams), ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p]),
+}
+
+_lib = None
+
+
+def lib():
+    """Load libdllm.so (built in-tree by ``build()``); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise DllmError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def dllm_status_str(status: int) -> str:
+    return lib().dllm_status_str(status).decode()
+
+
+def dllm_version() -> int:
+    return lib().dllm_version()
+
+
+def _check(rc: int, fn: str):
+    if rc != 0:
+        raise DllmError(f"{fn}: {dllm_status_str(rc)} ({rc})")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return E4M3
+    raise DllmError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _dev(t: Optional[torch.Tensor], name: str, contiguous: bool = True):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise DllmError(f"{name} must be a GPU tensor")
+    if contiguous and not t.is_contiguous():
+        raise DllmError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+class Cache:
+    """One layer's persistent K/V cache: the C descriptor plus the tensors it
+    points to (kept alive here)."""
+
+    def __init__(self, desc: _KVCache, k, v, k_scale, v_scale):
+        self.desc, self.k, self.v, self.k_scale, self.v_scale = desc, k, v, k_scale, v_scale
+
+    @property
+    def dtype(self) -> int:
+        return self.desc.dtype
+
+
+def dllm_cache_init(k: torch.Tensor, v: torch.Tensor, dtype: Optional[int] = None,
+                    k_scale: Optional[torch.Tensor] = None,
+                    v_scale: Optional[torch.Tensor] = None) -> Cache:
+    """k, v: [B, Hkv, L, d] GPU tensors (float32, bfloat16, or uint8 e4m3 codes
+    with float32 scales [B, Hkv, L, d/128]).  Zero-fills them."""
+    dtype = _dtype_code(k) if dtype is None else dtype
+    B, H, L, d = k.shape
+    desc = _KVCache()
+    rc = lib().dllm_cache_init(ctypes.byref(desc), B, L, H, d, dtype, _dev(k, "k"), _dev(v, "v"),
+                               _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"), _stream())
+    _check(rc, "dllm_cache_init")
+    return Cache(desc, k, v, k_scale, v_scale)
+
+
+def dllm_scatter_kv(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, pos: torch.Tensor,
+                    bad_count: Optional[torch.Tensor] = None):
+    """k_new, v_new: [B, n, Hkv, d]; pos: [B, n] int32 (-1 = padding)."""
+    n = pos.shape[1]
+    rc = lib().dllm_scatter_kv(ctypes.byref(cache.desc), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                               _dtype_code(k_new), _dev(pos, "pos"), n, _dev(bad_count, "bad_count"),
+                               _stream())
+    _check(rc, "dllm_scatter_kv")
+
+
+def dllm_sink_rolling_map(L: int, S: int, R: int, end: torch.Tensor, key_idx: torch.Tensor):
+    """key_idx[b] = sinks [0, min(S, e)) then [max(S, e-R), e), -1 padded."""
+    B, n_keys = key_idx.shape
+    rc = lib().dllm_sink_rolling_map(B, L, S, R, _dev(end, "end"), _dev(key_idx, "key_idx"), n_keys,
+                                     _stream())
+    _check(rc, "dllm_sink_rolling_map")
+    return key_idx
+
+
+def dllm_block_attention_workspace(cache: Cache, q_dtype: int, Hq: int, b: int, n_keys: int) -> int:
+    return lib().dllm_block_attention_workspace(ctypes.byref(cache.desc), q_dtype, Hq, b, n_keys)
+
+
+def dllm_block_attention(cache: Cache, q: torch.Tensor, key_idx: Optional[torch.Tensor] = None,
+                         scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                         out_dtype: Optional[torch.dtype] = None, lse: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None):
+    """q: [B, Hq, b, d]; returns out [B, Hq, b, d] (and fills lse if given)."""
+    B, Hq, b, d = q.shape
+    n_keys = key_idx.shape[1] if key_idx is not None else cache.desc.L
+    if out is None:
+        out = torch.empty((B, Hq, b, d), dtype=out_dtype or q.dtype, device=q.device)
+    ws_need = dllm_block_attention_workspace(cache, _dtype_code(q), Hq, b, n_keys)
+    if workspace is None and ws_need:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().dllm_block_attention(ctypes.byref(cache.desc), _dev(q, "q"), _dtype_code(q), Hq, b,
+                                    _dev(key_idx, "key_idx"), n_keys, float(scale), _dev(out, "out"),
+                                    _dtype_code(out), _dev(lse, "lse"), _dev(workspace, "workspace"),
+                                    ws_bytes, _stream())
+    _check(rc, "dllm_block_attention")
+    return out
+
+
+def dllm_vocab_stats_workspace(N: int, V: int) -> int:
+    return lib().dllm_vocab_stats_workspace(N, V)
+
+
+def dllm_vocab_stats(logits: torch.Tensor, V: Optional[int] = None,
+                     argmax: Optional[torch.Tensor] = None, maxprob: Optional[torch.Tensor] = None,
+                     entropy: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None):
+    """logits: [N, >= V] (rows may be a strided view); returns (argmax, maxprob, entropy)."""
+    N = logits.shape[0]
+    V = logits.shape[1] if V is None else V
+    if logits.stride(1) != 1:
+        raise DllmError("logits rows must be contiguous")
+    dev = logits.device
+    argmax = torch.empty(N, dtype=torch.int32, device=dev) if argmax is None else argmax
+    maxprob = torch.empty(N, dtype=torch.float32, device=dev) if maxprob is None else maxprob
+    entropy = torch.empty(N, dtype=torch.float32, device=dev) if entropy is None else entropy
+    ws_need = dllm_vocab_stats_workspace(N, V)
+    if workspace is None and ws_need:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().dllm_vocab_stats(_dev(logits, "logits", contiguous=False), _dtype_code(logits), N, V,
+                                logits.stride(0), _dev(argmax, "argmax"), _dev(maxprob, "maxprob"),
+                                _dev(entropy, "entropy"), _dev(workspace, "workspace"), ws_bytes,
+                                _stream())
+    _check(rc, "dllm_vocab_stats")
+    return argmax, maxprob, entropy
+
+
+class StabilityState:
+    """Device decode state of B sequences of length L with ring depth D."""
+
+    def __init__(self, B: int, L: int, D: int, device="cuda"):
+        self.B, self.L, self.D = B, L, D
+        self.ring_argmax = torch.empty((D, B, L), dtype=torch.int32, device=device)
+        self.ring_maxprob = torch.empty((D, B, L), dtype=torch.float32, device=device)
+        self.ring_step = torch.empty((D, B, L), dtype=torch.int32, device=device)
+        self.entropy_latest = torch.empty((B, L), dtype=torch.float32, device=device)
+        self.t_write = torch.empty((B, L), dtype=torch.int32, device=device)
+        self.stable = torch.empty((B, L), dtype=torch.uint8, device=device)
+        self.mask = torch.empty((B, L), dtype=torch.uint8, device=device)
+        self.conf = torch.empty((B, L), dtype=torch.float32, device=device)
+        self.next_pos = torch.empty((B, L), dtype=torch.int32, device=device)
+        self.count = torch.empty((B,), dtype=torch.int32, device=device)
+        self.all_stable = torch.empty((B,), dtype=torch.uint8, device=device)
+        dllm_stability_reset(self)
+
+
+def dllm_stability_reset(st: StabilityState):
+    rc = lib().dllm_stability_reset(st.B, st.L, st.D, _dev(st.ring_argmax, "ring_argmax"),
+                                    _dev(st.ring_maxprob, "ring_maxprob"), _dev(st.ring_step, "ring_step"),
+                                    _dev(st.entropy_latest, "entropy_latest"), _dev(st.t_write, "t_write"),
+                                    _dev(st.stable, "stable"), _stream())
+    _check(rc, "dllm_stability_reset")
+
+
+def dllm_stability_mask(st: StabilityState, step: int, pos: Optional[torch.Tensor],
+                        argmax: torch.Tensor, maxprob: torch.Tensor, entropy: torch.Tensor, *,
+                        K: int, tau: float, R: int, alpha: float = 0.0, beta: float = 0.0,
+                        lam: float = 0.0, conf_thresh: float = 0.0, V: int = 2,
+                        with_conf: bool = True):
+    """One step of history, stability, confidence and window mask; outputs
+    land in st.mask, st.conf, st.next_pos, st.count, st.all_stable."""
+    n = pos.shape[1] if pos is not None else st.L
+    prm = _StabParams(K=K, D=st.D, R=R, reserved=0, tau=tau, alpha=alpha, beta=beta, lam=lam,
+                      conf_thresh=conf_thresh, vocab=V)
+    rc = lib().dllm_stability_mask(st.B, st.L, int(step), _dev(pos, "pos"), n, _dev(argmax, "argmax"),
+                                   _dev(maxprob, "maxprob"), _dev(entropy, "entropy"),
+                                   _dev(st.ring_argmax, "ring_argmax"), _dev(st.ring_maxprob, "ring_maxprob"),
+                                   _dev(st.ring_step, "ring_step"), _dev(st.entropy_latest, "entropy_latest"),
+                                   _dev(st.t_write, "t_write"), _dev(st.stable, "stable"),
+                                   ctypes.byref(prm), _dev(st.mask, "mask"),
+                                   _dev(st.conf, "conf") if with_conf else None,
+                                   _dev(st.next_pos, "next_pos"), _dev(st.count, "count"),
+                                   _dev(st.all_stable, "all_stable"), _stream())
+    _check(rc, "dllm_stability_mask")
+    return st

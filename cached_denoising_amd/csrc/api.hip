@@ -1,0 +1,205 @@
+// C ABI of libdllm: host-side argument checks, then the launches.  The
+// contract of every entry point is documented in include/dllm.h.
+#include "common.hpp"
+
+#include <cmath>
+
+using namespace dllm;
+
+namespace {
+
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+inline int dtype_size(int dt) {
+    switch (dt) {
+    case DLLM_F32: return 4;
+    case DLLM_BF16: return 2;
+    case DLLM_E4M3: return 1;
+    default: return 0;
+    }
+}
+
+int check_cache(const dllm_kv_cache *c) {
+    if (!c || !c->k || !c->v) return DLLM_EINVAL;
+    if (c->B < 1 || c->L < 1 || c->n_kv_heads < 1) return DLLM_ESHAPE;
+    if (c->d_head < 16 || c->d_head > 256) return DLLM_ESHAPE;
+    const int esz = dtype_size(c->dtype);
+    if (!esz) return DLLM_EDTYPE;
+    if ((c->d_head * esz) % 16 != 0) return DLLM_EALIGN;
+    if (!aligned16(c->k) || !aligned16(c->v)) return DLLM_EALIGN;
+    if (c->dtype == DLLM_E4M3) {
+        if (c->d_head % 128 != 0) return DLLM_ESHAPE;
+        if (!c->k_scale || !c->v_scale) return DLLM_EINVAL;
+    }
+    return DLLM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dllm_status_str(int status) {
+    switch (status) {
+    case DLLM_OK: return "ok";
+    case DLLM_EINVAL: return "invalid argument";
+    case DLLM_EDTYPE: return "unsupported dtype";
+    case DLLM_ESHAPE: return "unsupported or inconsistent shape";
+    case DLLM_EALIGN: return "pointer or row not 16-byte aligned";
+    case DLLM_ERANGE: return "size beyond the supported maximum";
+    case DLLM_EHIP: return "HIP runtime or launch failure";
+    case DLLM_EWORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+    }
+}
+
+int dllm_version(void) { return 100; }
+
+int dllm_cache_init(dllm_kv_cache *cache, int B, int L, int n_kv_heads, int d_head, int dtype,
+                    void *k, void *v, float *k_scale, float *v_scale, void *stream) {
+    if (!cache) return DLLM_EINVAL;
+    dllm_kv_cache c{};
+    c.B = B;
+    c.L = L;
+    c.n_kv_heads = n_kv_heads;
+    c.d_head = d_head;
+    c.dtype = dtype;
+    c.k = k;
+    c.v = v;
+    c.k_scale = dtype == DLLM_E4M3 ? k_scale : nullptr;
+    c.v_scale = dtype == DLLM_E4M3 ? v_scale : nullptr;
+    int rc = check_cache(&c);
+    if (rc != DLLM_OK) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t rows = (size_t)B * n_kv_heads * L;
+    const size_t bytes = rows * d_head * dtype_size(dtype);
+    if ((rc = launch_fill_zero(k, bytes, s)) != DLLM_OK) return rc;
+    if ((rc = launch_fill_zero(v, bytes, s)) != DLLM_OK) return rc;
+    if (dtype == DLLM_E4M3) {
+        const size_t sbytes = rows * (d_head / 128) * sizeof(float);
+        if ((rc = launch_fill_zero(k_scale, sbytes, s)) != DLLM_OK) return rc;
+        if ((rc = launch_fill_zero(v_scale, sbytes, s)) != DLLM_OK) return rc;
+    }
+    *cache = c;
+    return DLLM_OK;
+}
+
+int dllm_scatter_kv(const dllm_kv_cache *cache, const void *k_new, const void *v_new,
+                    int src_dtype, const int32_t *pos, int n, int32_t *bad_count, void *stream) {
+    int rc = check_cache(cache);
+    if (rc != DLLM_OK) return rc;
+    if (n < 0) return DLLM_EINVAL;
+    if (n == 0) return DLLM_OK;
+    if (!k_new || !v_new || !pos) return DLLM_EINVAL;
+    if (cache->dtype == DLLM_E4M3) {
+        if (src_dtype != DLLM_F32 && src_dtype != DLLM_BF16) return DLLM_EDTYPE;
+    } else if (src_dtype != cache->dtype) {
+        return DLLM_EDTYPE;
+    }
+    if (!aligned16(k_new) || !aligned16(v_new)) return DLLM_EALIGN;
+    return launch_scatter(*cache, k_new, v_new, src_dtype, pos, n, bad_count,
+                          static_cast<hipStream_t>(stream));
+}
+
+int dllm_sink_rolling_map(int B, int L, int S, int R, const int32_t *end, int32_t *key_idx,
+                          int n_keys, void *stream) {
+    if (B < 1 || L < 1 || S < 0 || R < 0) return DLLM_EINVAL;
+    if (!end || !key_idx) return DLLM_EINVAL;
+    if ((int64_t)n_keys < (int64_t)S + R || n_keys < 1) return DLLM_ESHAPE;
+    if (B > 65535) return DLLM_ERANGE;
+    return launch_sink_rolling(B, L, S, R, end, key_idx, n_keys, static_cast<hipStream_t>(stream));
+}
+
+size_t dllm_block_attention_workspace(const dllm_kv_cache *cache, int q_dtype, int Hq, int b,
+                                      int n_keys) {
+    if (check_cache(cache) != DLLM_OK || Hq < 1 || b < 1 || n_keys < 1) return 0;
+    if (Hq % cache->n_kv_heads != 0) return 0;
+    AttnPlan p;
+    if (plan_attention(*cache, q_dtype, Hq, b, n_keys, &p) != DLLM_OK) return 0;
+    return p.ws_bytes;
+}
+
+int dllm_block_attention(const dllm_kv_cache *cache, const void *q, int q_dtype, int Hq, int b,
+                         const int32_t *key_idx, int n_keys, float scale, void *out,
+                         int out_dtype, float *lse, void *workspace, size_t ws_bytes,
+                         void *stream) {
+    int rc = check_cache(cache);
+    if (rc != DLLM_OK) return rc;
+    if (!q || !out) return DLLM_EINVAL;
+    if (Hq < 1 || b < 1) return DLLM_ESHAPE;
+    if (Hq % cache->n_kv_heads != 0) return DLLM_ESHAPE;
+    if (!key_idx) n_keys = cache->L;
+    if (n_keys < 1) return DLLM_ESHAPE;
+    if (q_dtype != DLLM_F32 && q_dtype != DLLM_BF16) return DLLM_EDTYPE;
+    if (out_dtype != DLLM_F32 && out_dtype != DLLM_BF16) return DLLM_EDTYPE;
+    if (!(scale >= 0.f) || std::isinf(scale)) return DLLM_EINVAL;
+    if (scale == 0.f) scale = 1.0f / std::sqrt((float)cache->d_head);
+    if ((int64_t)cache->B * Hq * b > INT32_MAX / 4) return DLLM_ERANGE;
+    AttnPlan p;
+    if ((rc = plan_attention(*cache, q_dtype, Hq, b, n_keys, &p)) != DLLM_OK) return rc;
+    if (p.path == 1 && (!aligned16(q) || !aligned16(out))) return DLLM_EALIGN;
+    if (p.ws_bytes > 0 && (!workspace || ws_bytes < p.ws_bytes || !aligned16(workspace)))
+        return DLLM_EWORKSPACE;
+    return launch_attention(*cache, p, q, q_dtype, Hq, b, key_idx, n_keys, scale, out, out_dtype,
+                            lse, workspace, static_cast<hipStream_t>(stream));
+}
+
+size_t dllm_vocab_stats_workspace(int64_t N, int64_t V) {
+    if (N < 0 || V < 1) return 0;
+    return plan_vocab(N, V).ws_bytes;
+}
+
+int dllm_vocab_stats(const void *logits, int dtype, int64_t N, int64_t V, int64_t row_stride,
+                     int32_t *argmax, float *maxprob, float *entropy, void *workspace,
+                     size_t ws_bytes, void *stream) {
+    if (N < 0 || V < 1 || row_stride < V) return DLLM_ESHAPE;
+    if (V > INT32_MAX) return DLLM_ERANGE;
+    if (dtype != DLLM_F32 && dtype != DLLM_BF16) return DLLM_EDTYPE;
+    if (N == 0) return DLLM_OK;
+    if (!logits || !argmax || !maxprob || !entropy) return DLLM_EINVAL;
+    if (((uintptr_t)logits & (uintptr_t)(dtype_size(dtype) - 1)) != 0) return DLLM_EALIGN;
+    const VocabPlan p = plan_vocab(N, V);
+    if (p.ws_bytes > 0 && (!workspace || ws_bytes < p.ws_bytes || !aligned16(workspace)))
+        return DLLM_EWORKSPACE;
+    return launch_vocab(logits, dtype, N, V, row_stride, argmax, maxprob, entropy, p, workspace,
+                        static_cast<hipStream_t>(stream));
+}
+
+int dllm_stability_reset(int B, int L, int D, int32_t *ring_argmax, float *ring_maxprob,
+                         int32_t *ring_step, float *entropy_latest, int32_t *t_write,
+                         uint8_t *stable, void *stream) {
+    if (B < 1 || L < 1 || D < 1) return DLLM_ESHAPE;
+    if (!ring_argmax || !ring_maxprob || !ring_step || !entropy_latest || !t_write || !stable)
+        return DLLM_EINVAL;
+    return launch_stability_reset(B, L, D, ring_argmax, ring_maxprob, ring_step, entropy_latest,
+                                  t_write, stable, static_cast<hipStream_t>(stream));
+}
+
+int dllm_stability_mask(int B, int L, int step, const int32_t *pos, int n,
+                        const int32_t *argmax, const float *maxprob, const float *entropy,
+                        int32_t *ring_argmax, float *ring_maxprob, int32_t *ring_step,
+                        float *entropy_latest, int32_t *t_write, uint8_t *stable,
+                        const dllm_stab_params *params, uint8_t *mask, float *conf,
+                        int32_t *next_pos, int32_t *count, uint8_t *all_stable, void *stream) {
+    if (!params) return DLLM_EINVAL;
+    if (B < 1 || L < 1 || step < 0) return DLLM_ESHAPE;
+    if (B > 65535) return DLLM_ERANGE;
+    if (!pos && n != L) return DLLM_ESHAPE;
+    if (n < 0 || n > L) return DLLM_ESHAPE;
+    const dllm_stab_params &p = *params;
+    if (p.K < 1 || p.D < p.K || p.R < 0 || p.vocab < 2) return DLLM_EINVAL;
+    if (!(p.tau == p.tau) || !(p.alpha == p.alpha) || !(p.beta == p.beta) ||
+        !(p.lambda == p.lambda) || !(p.conf_thresh == p.conf_thresh))
+        return DLLM_EINVAL;
+    if ((n > 0 && (!argmax || !maxprob || !entropy)) || !ring_argmax || !ring_maxprob ||
+        !ring_step || !entropy_latest || !t_write || !stable || !mask || !next_pos || !count ||
+        !all_stable)
+        return DLLM_EINVAL;
+    // maximum entropy of a vocab-V distribution, computed once on the host
+    const double hmax = std::log((double)p.vocab);
+    return launch_stability(B, L, step, pos, n, argmax, maxprob, entropy, ring_argmax,
+                            ring_maxprob, ring_step, entropy_latest, t_write, stable, p, hmax,
+                            mask, conf, next_pos, count, all_stable,
+                            static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,579 @@
+// Block attention: the queries of the active block attend to the selected
+// cached keys with no causal mask, out = softmax(q K^T * scale) V.
+// [LaCache explainer, problem statement (bidirectional attention over the
+// whole context within a SAR block) and Methodology 1 (FlashAttention's
+// online-softmax state m, l, O~); attention-sinks page, 2.1 (the score
+// matrix Q K^T / sqrt(d_k), softmax, times V) and 2.3 (fixed key set).]
+//
+// MFMA path (bf16 queries; bf16 or e4m3 cache; d = 64 or 128):
+//   A workgroup of 4 waves owns one (sequence, KV head, row group, key
+//   split).  The rows are the G query heads sharing the KV head times the
+//   block's queries.  Each wave walks its own run of 32-key tiles:
+//     S^T (keys x rows) = K . Q^T     on v_mfma_f32_16x16x32_bf16, K straight
+//                                      from HBM into the A operand
+//     online softmax in base 2        per row, state (m, l) in registers
+//     O^T (dims x rows) += V^T . P^T  V staged through a per-wave LDS tile in
+//                                      transposed (dim-major) order
+//   The two key tiles of a 32-key step are loaded in an interleaved order so
+//   that the S^T accumulator of a lane holds 8 consecutive keys of one row:
+//   exactly the P^T operand the second product needs, with no shuffles.
+//   e4m3 codes widen to bf16 exactly (e4m3 is a subset of bf16) with
+//   v_cvt_scalef32_pk_bf16_fp8; the per-key float32 scales multiply the
+//   scores (K) and the probabilities (V) in float32.
+//   The 4 waves merge through LDS in a fixed order; key splits across
+//   workgroups write (m, l, O~) partials merged by a second kernel.
+// VALU path (float32 queries and cache, any d <= 256): one wave per query.
+#include "common.hpp"
+
+#include <climits>
+
+namespace dllm {
+namespace {
+
+constexpr int kNW = 4;                 // waves per MFMA workgroup
+constexpr int kVtStride = 80;          // bytes per dim row of the V^T tile (32 keys + pad)
+constexpr float kNegInf = -__builtin_inff();
+
+union Frag {
+    uint4 u;
+    bf16x8_t v;
+};
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    // one v_cvt_pk_bf16_f32: round to nearest even
+    const bf16x2_t p = __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, p);
+}
+
+// 8 e4m3 codes (two words) -> 8 bf16 (exact)
+__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+    uint4 r;
+    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+    r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+    r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+    return r;
+}
+
+// key index of tile-local key k (or -1): NULL map means identity over [0, n_keys)
+__device__ __forceinline__ int key_at(const int32_t *kmap, int n_keys, int L, int j) {
+    if (j >= n_keys) return -1;
+    const int k = kmap ? kmap[j] : j;
+    return (k >= 0 && k < L) ? k : -1;
+}
+
+// Logical block order that keeps the row groups of one (sequence, KV head,
+// split) on one XCD: workgroups are dealt to the 8 XCDs round robin.
+__device__ __forceinline__ int xcd_remap(int pid, int nblk) {
+    if ((nblk & 7) != 0) return pid;
+    const int per = nblk >> 3;
+    return (pid & 7) * per + (pid >> 3);
+}
+
+template <int D, int KVDT, int RT>
+__global__ __launch_bounds__(kNW * kWave, RT == 2 ? 2 : 1) void attn_mfma_kernel(
+    const void *__restrict__ ck, const void *__restrict__ cv, const float *__restrict__ ksc,
+    const float *__restrict__ vsc, const uint16_t *__restrict__ q, int Hq, int Hkv, int L, int b,
+    int G, const int32_t *__restrict__ key_idx, int n_keys, float scale_log2, int row_groups,
+    int splits, int tiles_per_wave, int64_t rows_total, void *__restrict__ out, int out_dtype,
+    float *__restrict__ lse, float *__restrict__ part_o, float *__restrict__ part_ml) {
+    constexpr int NC = D / 32;           // k-chunks of the first product
+    constexpr int NDT = D / 16;          // dim tiles of the second product
+    constexpr int DPG = D / 4;           // dims per lane group in the first product
+    constexpr int ROWS = 16 * RT;        // rows per workgroup
+    constexpr int VBLK = D / 64;         // 4-key x 8-dim V blocks per lane per tile
+    constexpr int ESZ = KVDT == DLLM_E4M3 ? 1 : 2;
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kNW * D * kVtStride];
+    __shared__ float sm_ml[kNW][ROWS][2];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int l16 = lane & 15;
+    const int g = lane >> 4;
+
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int rg = lid % row_groups;
+    int rest = lid / row_groups;
+    const int split = rest % splits;
+    rest /= splits;
+    const int kvh = rest % Hkv;
+    const int bi = rest / Hkv;
+    const int M = G * b;                 // rows of this (sequence, KV head)
+
+    const int64_t kv_base = ((int64_t)bi * Hkv + kvh) * L;
+    const int32_t *kmap = key_idx ? key_idx + (int64_t)bi * n_keys : nullptr;
+
+    // ---- queries: B operand of S^T = K Q^T, kept for the whole kernel ----
+    Frag qf[RT][NC];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int r = rg * ROWS + rt * 16 + l16;
+        if (r < M) {
+            const int gq = r / b, i = r - gq * b;
+            const uint16_t *qp = q + (((int64_t)bi * Hq + kvh * G + gq) * b + i) * D + g * DPG;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) qf[rt][c].u = *reinterpret_cast<const uint4 *>(qp + c * 8);
+        } else {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) qf[rt][c].u = make_uint4(0, 0, 0, 0);
+        }
+    }
+
+    f32x4_t o[NDT][RT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) o[dt][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m[RT], l[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) { m[rt] = kNegInf; l[rt] = 0.f; }
+
+    unsigned char *vt = smem + wave * D * kVtStride;
+    const int n_tiles = (n_keys + 31) / 32;
+    const int t_begin = (split * kNW + wave) * tiles_per_wave;
+    const int t_end = min(n_tiles, t_begin + tiles_per_wave);
+
+    for (int kt = t_begin; kt < t_end; ++kt) {
+        const int key0 = kt * 32;
+        // ---- K into the A operand: slot l16 of tile t is key 8(l16/4) + 4t + l16%4
+        Frag kf[2][NC];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int kk = key_at(kmap, n_keys, L, key0 + 8 * (l16 >> 2) + 4 * t + (l16 & 3));
+            const int64_t krow = kv_base + (kk < 0 ? 0 : kk);
+            if (KVDT == DLLM_E4M3) {
+                const uint8_t *kp = static_cast<const uint8_t *>(ck) + krow * D + g * DPG;
+#pragma unroll
+                for (int c = 0; c < NC; c += 2) {
+                    const uint4 w = *reinterpret_cast<const uint4 *>(kp + c * 8);
+                    kf[t][c].u = e4m3x8_to_bf16(w.x, w.y);
+                    kf[t][c + 1].u = e4m3x8_to_bf16(w.z, w.w);
+                }
+            } else {
+                const uint16_t *kp = static_cast<const uint16_t *>(ck) + krow * D + g * DPG;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) kf[t][c].u = *reinterpret_cast<const uint4 *>(kp + c * 8);
+            }
+        }
+        // ---- V: 4-key x 8-dim blocks, transposed into the wave's V^T tile
+        uint4 vr[VBLK][4];
+#pragma unroll
+        for (int u = 0; u < VBLK; ++u) {
+            const int blk = lane + 64 * u;
+            const int oct = blk % (D / 8), q4 = blk / (D / 8);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int kk = key_at(kmap, n_keys, L, key0 + 4 * q4 + k);
+                const int64_t vrow = kv_base + (kk < 0 ? 0 : kk);
+                uint4 w;
+                if (KVDT == DLLM_E4M3) {
+                    const uint2 c2 = *reinterpret_cast<const uint2 *>(
+                        static_cast<const uint8_t *>(cv) + vrow * D + oct * 8);
+                    w = e4m3x8_to_bf16(c2.x, c2.y);
+                } else {
+                    w = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(cv) +
+                                                         vrow * D + oct * 8);
+                }
+                if (kk < 0) w = make_uint4(0, 0, 0, 0);
+                vr[u][k] = w;
+            }
+        }
+        // keys held by this lane in the S^T accumulator: 8g .. 8g+7
+        int kkd[8];
+        float kscale[8], vscale[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            kkd[e] = key_at(kmap, n_keys, L, key0 + 8 * g + e);
+            if (KVDT == DLLM_E4M3) {
+                const int64_t rr = kv_base + (kkd[e] < 0 ? 0 : kkd[e]);
+                kscale[e] = ksc[rr];
+                vscale[e] = vsc[rr];
+            }
+        }
+
+        // ---- S^T = K Q^T
+        f32x4_t s[2][RT];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][c].v, qf[rt][c].v, acc, 0, 0, 0);
+                s[t][rt] = acc;
+            }
+
+        // ---- stage V^T (dim-major) in LDS: rows 8*oct + e, keys 4*q4 .. 4*q4+3
+#pragma unroll
+        for (int u = 0; u < VBLK; ++u) {
+            const int blk = lane + 64 * u;
+            const int oct = blk % (D / 8), q4 = blk / (D / 8);
+            const uint32_t a[4][4] = {{vr[u][0].x, vr[u][0].y, vr[u][0].z, vr[u][0].w},
+                                      {vr[u][1].x, vr[u][1].y, vr[u][1].z, vr[u][1].w},
+                                      {vr[u][2].x, vr[u][2].y, vr[u][2].z, vr[u][2].w},
+                                      {vr[u][3].x, vr[u][3].y, vr[u][3].z, vr[u][3].w}};
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                // dims 2w (low halves) and 2w+1 (high halves) of the 4 keys
+                const uint2 lo = make_uint2(__builtin_amdgcn_perm(a[1][w], a[0][w], 0x05040100u),
+                                            __builtin_amdgcn_perm(a[3][w], a[2][w], 0x05040100u));
+                const uint2 hi = make_uint2(__builtin_amdgcn_perm(a[1][w], a[0][w], 0x07060302u),
+                                            __builtin_amdgcn_perm(a[3][w], a[2][w], 0x07060302u));
+                *reinterpret_cast<uint2 *>(vt + (oct * 8 + 2 * w) * kVtStride + q4 * 8) = lo;
+                *reinterpret_cast<uint2 *>(vt + (oct * 8 + 2 * w + 1) * kVtStride + q4 * 8) = hi;
+            }
+        }
+
+        // ---- online softmax per row (row = rt*16 + l16), keys 8g..8g+7 of this lane
+        Frag pf[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float v = s[e >> 2][rt][e & 3] * scale_log2;
+                if (KVDT == DLLM_E4M3) v *= kscale[e];
+                x[e] = kkd[e] < 0 ? kNegInf : v;
+            }
+            float mx = x[0];
+#pragma unroll
+            for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+            mx = fmaxf(mx, shfl_xor_f(mx, 16));
+            mx = fmaxf(mx, shfl_xor_f(mx, 32));
+            const float mn = fmaxf(m[rt], mx);
+            float p[8], ps = 0.f;
+            if (mn == kNegInf) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) p[e] = 0.f;
+            } else {
+                const float corr = __builtin_amdgcn_exp2f(m[rt] - mn);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    p[e] = __builtin_amdgcn_exp2f(x[e] - mn);
+                    ps += p[e];
+                }
+                l[rt] = l[rt] * corr + ps;
+                if (corr != 1.0f) {
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) o[dt][rt] *= corr;
+                }
+                m[rt] = mn;
+            }
+            if (KVDT == DLLM_E4M3) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) p[e] *= vscale[e];
+            }
+            pf[rt].u = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                  pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+        }
+
+        // ---- O^T += V^T P^T
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            Frag vf;
+            vf.u = *reinterpret_cast<const uint4 *>(vt + (dt * 16 + l16) * kVtStride + g * 16);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.v, pf[rt].v, o[dt][rt], 0, 0, 0);
+        }
+    }
+
+    // ---- row sums over the 4 lane groups
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        l[rt] += shfl_xor_f(l[rt], 16);
+        l[rt] += shfl_xor_f(l[rt], 32);
+    }
+
+    // ---- merge the 4 waves in a fixed order through LDS
+    if (g == 0) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            sm_ml[wave][rt * 16 + l16][0] = m[rt];
+            sm_ml[wave][rt * 16 + l16][1] = l[rt];
+        }
+    }
+    __syncthreads();
+    float fown[RT], Mrow[RT], Ltot[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int r = rt * 16 + l16;
+        float mm = kNegInf;
+#pragma unroll
+        for (int w = 0; w < kNW; ++w) mm = fmaxf(mm, sm_ml[w][r][0]);
+        float lt = 0.f;
+#pragma unroll
+        for (int w = 0; w < kNW; ++w) {
+            const float mw = sm_ml[w][r][0];
+            if (mw != kNegInf) lt += sm_ml[w][r][1] * __builtin_amdgcn_exp2f(mw - mm);
+        }
+        Mrow[rt] = mm;
+        Ltot[rt] = lt;
+        fown[rt] = m[rt] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m[rt] - mm);
+    }
+    float *buf = reinterpret_cast<float *>(smem);       // [ROWS][D + 4] floats
+    constexpr int BST = D + 4;
+    for (int w = 0; w < kNW; ++w) {
+        if (wave == w) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    float4 *bp = reinterpret_cast<float4 *>(buf + (rt * 16 + l16) * BST + dt * 16 + 4 * g);
+                    const f32x4_t v = o[dt][rt] * fown[rt];
+                    float4 acc = w == 0 ? make_float4(0.f, 0.f, 0.f, 0.f) : *bp;
+                    acc.x += v[0]; acc.y += v[1]; acc.z += v[2]; acc.w += v[3];
+                    if (w < kNW - 1) *bp = acc;
+                    else o[dt][rt] = f32x4_t{acc.x, acc.y, acc.z, acc.w};
+                }
+        }
+        if (w < kNW - 1) __syncthreads();
+    }
+    if (wave != kNW - 1) return;
+
+    // ---- the last wave writes the result (or this split's partial)
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int r = rg * ROWS + rt * 16 + l16;
+        if (r >= M) continue;
+        const int gq = r / b, i = r - gq * b;
+        const int64_t orow = ((int64_t)bi * Hq + kvh * G + gq) * b + i;
+        if (splits == 1) {
+            const float inv = Ltot[rt] > 0.f ? 1.0f / Ltot[rt] : 0.f;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const f32x4_t v = o[dt][rt] * inv;
+                const int64_t off = orow * D + dt * 16 + 4 * g;
+                if (out_dtype == DLLM_F32) {
+                    *reinterpret_cast<float4 *>(static_cast<float *>(out) + off) =
+                        make_float4(v[0], v[1], v[2], v[3]);
+                } else {
+                    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + off) =
+                        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                }
+            }
+            if (lse && g == 0)
+                lse[orow] = Ltot[rt] > 0.f ? Mrow[rt] * kLn2 + logf(Ltot[rt]) : kNegInf;
+        } else {
+            // partial of this split: unnormalised O~, running max (base 2), sum
+            const int64_t prow = (int64_t)split * rows_total + orow;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const f32x4_t v = o[dt][rt];
+                *reinterpret_cast<float4 *>(part_o + prow * D + dt * 16 + 4 * g) =
+                    make_float4(v[0], v[1], v[2], v[3]);
+            }
+            if (g == 0) {
+                part_ml[prow * 2 + 0] = Mrow[rt];
+                part_ml[prow * 2 + 1] = Ltot[rt];
+            }
+        }
+    }
+}
+
+// Merge of the key splits: one thread per (row, 4 dims), splits in order.
+__global__ __launch_bounds__(256) void attn_merge_kernel(
+    const float *__restrict__ part_o, const float *__restrict__ part_ml, int64_t rows_total, int D,
+    int splits, void *__restrict__ out, int out_dtype, float *__restrict__ lse) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int q4 = D / 4;
+    if (t >= rows_total * q4) return;
+    const int64_t row = t / q4;
+    const int c = (int)(t - row * q4) * 4;
+    float mm = kNegInf;
+    for (int s = 0; s < splits; ++s) mm = fmaxf(mm, part_ml[((int64_t)s * rows_total + row) * 2]);
+    float lt = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (mm != kNegInf) {
+        for (int s = 0; s < splits; ++s) {
+            const int64_t pr = (int64_t)s * rows_total + row;
+            const float ms = part_ml[pr * 2];
+            if (ms == kNegInf) continue;
+            const float f = __builtin_amdgcn_exp2f(ms - mm);
+            lt += part_ml[pr * 2 + 1] * f;
+            const float4 v = *reinterpret_cast<const float4 *>(part_o + pr * D + c);
+            acc.x += v.x * f; acc.y += v.y * f; acc.z += v.z * f; acc.w += v.w * f;
+        }
+    }
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    const int64_t off = row * D + c;
+    if (out_dtype == DLLM_F32) {
+        *reinterpret_cast<float4 *>(static_cast<float *>(out) + off) =
+            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    } else {
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + off) =
+            make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
+    }
+    if (lse && c == 0) lse[row] = lt > 0.f ? mm * kLn2 + logf(lt) : kNegInf;
+}
+
+// ---- float32 VALU path: one wave per query row ----------------------------
+// Keys go 64 at a time: lane j scores key j of the tile, the tile's
+// probabilities go through LDS, and lane c accumulates output dims c, c+64,
+// c+128, c+192.
+__device__ __forceinline__ float load_elem(const void *p, int dtype, int64_t i, const float *sc,
+                                           int64_t srow, int c) {
+    if (dtype == DLLM_F32) return static_cast<const float *>(p)[i];
+    if (dtype == DLLM_BF16) return bf16_to_f32(static_cast<const uint16_t *>(p)[i]);
+    const uint32_t code = static_cast<const uint8_t *>(p)[i];
+    const f32x2_t v = __builtin_amdgcn_cvt_pk_f32_fp8(code, false);
+    return v[0] * sc[srow + (c >> 7)];
+}
+
+__global__ __launch_bounds__(256) void attn_valu_kernel(
+    const void *__restrict__ ck, const void *__restrict__ cv, const float *__restrict__ ksc,
+    const float *__restrict__ vsc, int kv_dtype, const void *__restrict__ q, int q_dtype, int B,
+    int Hq, int Hkv, int L, int D, int b, const int32_t *__restrict__ key_idx, int n_keys,
+    float scale, void *__restrict__ out, int out_dtype, float *__restrict__ lse) {
+    __shared__ float sq[4][256];
+    __shared__ float sp[4][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t row = (int64_t)blockIdx.x * 4 + wave;     // (bi, hq, i)
+    const int64_t rows_total = (int64_t)B * Hq * b;
+    const bool live = row < rows_total;
+    const int64_t rr = live ? row : 0;
+    const int bi = (int)(rr / ((int64_t)Hq * b));
+    const int hq = (int)((rr / b) % Hq);
+    const int kvh = hq / (Hq / Hkv);
+    const int64_t kv_base = ((int64_t)bi * Hkv + kvh) * L;
+    const int ng = D >> 7;
+    for (int c = lane; c < D; c += 64)
+        sq[wave][c] = q_dtype == DLLM_F32 ? static_cast<const float *>(q)[rr * D + c]
+                                          : bf16_to_f32(static_cast<const uint16_t *>(q)[rr * D + c]);
+    __syncthreads();
+    const int32_t *kmap = key_idx ? key_idx + (int64_t)bi * n_keys : nullptr;
+    float mrun = kNegInf, lrun = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < n_keys; j0 += 64) {
+        const int kk = key_at(kmap, n_keys, L, j0 + lane);
+        float sc = kNegInf;
+        if (kk >= 0) {
+            const int64_t krow = kv_base + kk;
+            float dot = 0.f;
+            for (int c = 0; c < D; ++c)
+                dot = fmaf(sq[wave][c], load_elem(ck, kv_dtype, krow * D + c, ksc, krow * ng, c), dot);
+            sc = dot * scale;
+        }
+        float mx = sc;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, o));
+        const float mn = fmaxf(mrun, mx);
+        if (mn == kNegInf) continue;                         // wave-uniform
+        const float corr = expf(mrun - mn);
+        const float p = expf(sc - mn);
+        float ps = p;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) ps += shfl_xor_f(ps, o);
+        lrun = lrun * corr + ps;
+        mrun = mn;
+        sp[wave][lane] = p;
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] *= corr;
+        const int nk = min(64, n_keys - j0);
+        for (int j = 0; j < nk; ++j) {
+            const float pj = sp[wave][j];
+            const int kj = key_at(kmap, n_keys, L, j0 + j);
+            if (pj == 0.f || kj < 0) continue;
+            const int64_t vrow = kv_base + kj;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int c = lane + 64 * r;
+                if (c < D) acc[r] = fmaf(pj, load_elem(cv, kv_dtype, vrow * D + c, vsc, vrow * ng, c), acc[r]);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    }
+    if (!live) return;
+    const float inv = lrun > 0.f ? 1.0f / lrun : 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int c = lane + 64 * r;
+        if (c >= D) break;
+        const float v = acc[r] * inv;
+        if (out_dtype == DLLM_F32) static_cast<float *>(out)[rr * D + c] = v;
+        else static_cast<uint16_t *>(out)[rr * D + c] = f32_to_bf16(v);
+    }
+    if (lse && lane == 0) lse[rr] = lrun > 0.f ? mrun + logf(lrun) : kNegInf;
+}
+
+template <int D, int KVDT, int RT>
+int launch_mfma(const dllm_kv_cache &c, const AttnPlan &p, const void *q, int Hq, int b,
+                const int32_t *key_idx, int n_keys, float scale, void *out, int out_dtype,
+                float *lse, void *ws, hipStream_t s) {
+    const int G = Hq / c.n_kv_heads;
+    const int64_t rows_total = (int64_t)c.B * Hq * b;
+    const int64_t blocks = (int64_t)c.B * c.n_kv_heads * p.row_groups * p.splits;
+    float *part_o = nullptr, *part_ml = nullptr;
+    if (p.splits > 1) {
+        part_o = static_cast<float *>(ws);
+        part_ml = part_o + (int64_t)p.splits * rows_total * D;
+    }
+    const float scale_log2 = scale * kLog2e;
+    attn_mfma_kernel<D, KVDT, RT><<<dim3((unsigned)blocks), dim3(kNW * kWave), 0, s>>>(
+        c.k, c.v, c.k_scale, c.v_scale, static_cast<const uint16_t *>(q), Hq, c.n_kv_heads, c.L,
+        b, G, key_idx, n_keys, scale_log2, p.row_groups, p.splits, p.tiles_per_wave, rows_total,
+        out, out_dtype, lse, part_o, part_ml);
+    int rc = launch_status();
+    if (rc != DLLM_OK || p.splits == 1) return rc;
+    const int64_t threads = rows_total * (D / 4);
+    attn_merge_kernel<<<dim3((unsigned)cdiv64(threads, 256)), dim3(256), 0, s>>>(
+        part_o, part_ml, rows_total, D, p.splits, out, out_dtype, lse);
+    return launch_status();
+}
+
+}  // namespace
+
+int plan_attention(const dllm_kv_cache &c, int q_dtype, int Hq, int b, int n_keys, AttnPlan *p) {
+    const int G = Hq / c.n_kv_heads;
+    const int M = G * b;
+    const bool mfma = q_dtype == DLLM_BF16 && (c.dtype == DLLM_BF16 || c.dtype == DLLM_E4M3) &&
+                      (c.d_head == 64 || c.d_head == 128);
+    *p = AttnPlan{};
+    p->rows = M;
+    if (!mfma) {
+        p->path = 0;
+        return DLLM_OK;
+    }
+    p->path = 1;
+    p->waves = kNW;
+    p->row_tiles = M > 32 ? 4 : 2;
+    p->row_groups = cdiv(M, 16 * p->row_tiles);
+    const int64_t units = (int64_t)c.B * c.n_kv_heads * p->row_groups;
+    const int n_tiles = cdiv(n_keys, 32);
+    // enough workgroups for 2 per CU, but at least 4 key tiles per wave
+    int splits = (int)std::max<int64_t>(1, cdiv64(512, units));
+    splits = std::min(splits, std::max(1, n_tiles / (4 * kNW)));
+    p->splits = splits;
+    p->tiles_per_wave = cdiv(n_tiles, splits * kNW);
+    p->ws_bytes = splits > 1 ? (size_t)splits * c.B * Hq * b * (c.d_head + 2) * sizeof(float) : 0;
+    return DLLM_OK;
+}
+
+int launch_attention(const dllm_kv_cache &c, const AttnPlan &p, const void *q, int q_dtype, int Hq,
+                     int b, const int32_t *key_idx, int n_keys, float scale, void *out,
+                     int out_dtype, float *lse, void *ws, hipStream_t s) {
+    if (p.path == 0) {
+        const int64_t rows_total = (int64_t)c.B * Hq * b;
+        attn_valu_kernel<<<dim3((unsigned)cdiv64(rows_total, 4)), dim3(256), 0, s>>>(
+            c.k, c.v, c.k_scale, c.v_scale, c.dtype, q, q_dtype, c.B, Hq, c.n_kv_heads, c.L,
+            c.d_head, b, key_idx, n_keys, scale, out, out_dtype, lse);
+        return launch_status();
+    }
+    const bool e4 = c.dtype == DLLM_E4M3;
+    const bool rt4 = p.row_tiles == 4;
+    if (c.d_head == 128) {
+        if (e4) return rt4 ? launch_mfma<128, DLLM_E4M3, 4>(c, p, q, Hq, b, key_idx, n_keys, scale, out, out_dtype, lse, ws, s)
+                           : launch_mfma<128, DLLM_E4M3, 2>(c, p, q, Hq, b, key_idx, n_keys, scale, out, out_dtype, lse, ws, s);
+        return rt4 ? launch_mfma<128, DLLM_BF16, 4>(c, p, q, Hq, b, key_idx, n_keys, scale, out, out_dtype, lse, ws, s)
+                   : launch_mfma<128, DLLM_BF16, 2>(c, p, q, Hq, b, key_idx, n_keys, scale, out, out_dtype, lse, ws, s);
+    }
+    if (e4) return DLLM_ESHAPE;                 // e4m3 needs d % 128 == 0
+    return rt4 ? launch_mfma<64, DLLM_BF16, 4>(c, p, q, Hq, b, key_idx, n_keys, scale, out, out_dtype, lse, ws, s)
+               : launch_mfma<64, DLLM_BF16, 2>(c, p, q, Hq, b, key_idx, n_keys, scale, out, out_dtype, lse, ws, s);
+}
+
+}  // namespace dllm

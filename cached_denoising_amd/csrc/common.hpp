@@ -1,0 +1,91 @@
+// Internal helpers shared by the HIP kernels of libdllm (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "dllm.h"
+
+namespace dllm {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kWave = 64;
+
+// bfloat16 bits <-> float (exact widening; the low half of the float is zero)
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// float -> bfloat16 bits, round to nearest even (NaN stays NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// cross-lane helpers on a 64-wide wavefront
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
+__device__ __forceinline__ int shfl_xor_i(int v, int m) { return __shfl_xor(v, m, kWave); }
+
+__host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ constexpr int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// status of the last launch on this thread
+inline int launch_status() {
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? DLLM_OK : DLLM_EHIP;
+}
+
+// ---- launchers (one translation unit each) ---------------------------------
+int launch_fill_zero(void *p, size_t bytes, hipStream_t s);
+
+int launch_scatter(const dllm_kv_cache &c, const void *k_new, const void *v_new, int src_dtype,
+                   const int32_t *pos, int n, int32_t *bad_count, hipStream_t s);
+
+int launch_sink_rolling(int B, int L, int S, int R, const int32_t *end, int32_t *key_idx,
+                        int n_keys, hipStream_t s);
+
+struct AttnPlan {
+    int path;          // 0: float32 VALU path, 1: MFMA path
+    int rows;          // query rows per (batch, kv-head): G * b
+    int row_tiles;     // 16-row tiles per wave (MFMA path)
+    int row_groups;    // workgroups along the rows of one (batch, kv-head)
+    int splits;        // key splits across workgroups
+    int waves;         // waves per workgroup (MFMA path)
+    int tiles_per_wave;// 32-key tiles per wave
+    size_t ws_bytes;   // partial-result workspace
+};
+int plan_attention(const dllm_kv_cache &c, int q_dtype, int Hq, int b, int n_keys, AttnPlan *p);
+int launch_attention(const dllm_kv_cache &c, const AttnPlan &p, const void *q, int q_dtype, int Hq,
+                     int b, const int32_t *key_idx, int n_keys, float scale, void *out,
+                     int out_dtype, float *lse, void *ws, hipStream_t s);
+
+struct VocabPlan {
+    int splits;        // workgroups per row
+    int64_t chunk;     // elements per split
+    size_t ws_bytes;
+};
+VocabPlan plan_vocab(int64_t N, int64_t V);
+int launch_vocab(const void *logits, int dtype, int64_t N, int64_t V, int64_t stride,
+                 int32_t *argmax, float *maxprob, float *entropy, const VocabPlan &p, void *ws,
+                 hipStream_t s);
+
+int launch_stability_reset(int B, int L, int D, int32_t *ring_argmax, float *ring_maxprob,
+                           int32_t *ring_step, float *entropy_latest, int32_t *t_write,
+                           uint8_t *stable, hipStream_t s);
+int launch_stability(int B, int L, int step, const int32_t *pos, int n, const int32_t *argmax,
+                     const float *maxprob, const float *entropy, int32_t *ring_argmax,
+                     float *ring_maxprob, int32_t *ring_step, float *entropy_latest,
+                     int32_t *t_write, uint8_t *stable, const dllm_stab_params &prm, double hmax,
+                     uint8_t *mask, float *conf, int32_t *next_pos, int32_t *count,
+                     uint8_t *all_stable, hipStream_t s);
+
+}  // namespace dllm

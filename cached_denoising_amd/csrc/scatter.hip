@@ -1,0 +1,219 @@
+// K/V scatter: the recomputed block's fresh rows go to their positions in
+// the persistent cache; every other cached row is untouched, so the cache
+// afterwards holds what a full recompute would have produced.  [LaCache
+// explainer, Methodology 1 (RoPECache) and 3 (inference workflow); SWD
+// page, 4.1 and 4.3 (write results back at the masked positions); sinks
+// page, 5.1 (index writes instead of concatenation).]
+//
+// Also the small fill and key-map kernels of the cache set-up.
+#include "common.hpp"
+
+namespace dllm {
+namespace {
+
+// ---- float32 -> OCP e4m3fn, round to nearest even, saturate to +-448 -----
+// Works on the float's bits: the e4m3 value is the float's significand
+// shifted right so that 3 fraction bits remain (more for results below the
+// e4m3 normal range), rounded half to even on the dropped bits.
+__device__ __forceinline__ uint32_t e4m3_rne(float q) {
+    const uint32_t u = __float_as_uint(q);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return 0x7fu;                  // NaN
+    if (a > 0x43e00000u) return sign | 0x7eu;            // |q| > 448 (incl. inf)
+    const int E = (int)(a >> 23) - 127;                  // unbiased exponent
+    uint32_t r;
+    if (E < -6) {
+        // below 2^-6: count units of 2^-9 (the e4m3 subnormal spacing)
+        const uint32_t mant = (a >> 23) ? ((a & 0x7fffffu) | 0x800000u) : (a & 0x7fffffu);
+        const int sh = (a >> 23) ? (14 - E) : 140;       // q * 2^9 = mant >> sh
+        if (sh >= 32) {
+            r = 0;
+        } else {
+            r = mant >> sh;
+            const uint32_t rem = mant & ((1u << sh) - 1u);
+            const uint32_t half = 1u << (sh - 1);
+            if (rem > half || (rem == half && (r & 1u))) ++r;   // r = 8 is 2^-6: code 0x08
+        }
+    } else {
+        // exponent field E + 7 and the top 3 fraction bits, rounded on the other 20
+        r = ((uint32_t)(E + 7) << 3) | ((a >> 20) & 7u);
+        const uint32_t rem = a & 0xfffffu;
+        if (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ++r;
+    }
+    return sign | r;
+}
+
+// ---- plain copy: one 16-byte chunk per thread ------------------------------
+__global__ __launch_bounds__(256) void scatter_copy_kernel(
+    const uint4 *__restrict__ k_new, const uint4 *__restrict__ v_new, uint4 *__restrict__ ck,
+    uint4 *__restrict__ cv, const int32_t *__restrict__ pos, int n, int Hkv, int L,
+    int chunks_per_row, int64_t total, int32_t *__restrict__ bad) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= total) return;
+    const int64_t row = t / chunks_per_row;            // (b, j, h) of the fresh rows
+    const int c = (int)(t - row * chunks_per_row);
+    const int h = (int)(row % Hkv);
+    const int64_t bj = row / Hkv;
+    const int b = (int)(bj / n);
+    const int p = pos[bj];
+    if (p < 0 || p >= L) {
+        if (p != -1 && bad && c == 0 && h == 0) atomicAdd(bad, 1);
+        return;
+    }
+    const int64_t dst = (((int64_t)b * Hkv + h) * L + p) * chunks_per_row + c;
+    ck[dst] = k_new[t];
+    cv[dst] = v_new[t];
+}
+
+// ---- e4m3 quantise: 16 lanes per 128-element group, 8 elements per lane ----
+template <int SRC>
+__global__ __launch_bounds__(256) void scatter_e4m3_kernel(
+    const void *__restrict__ k_new, const void *__restrict__ v_new, uint8_t *__restrict__ ck,
+    uint8_t *__restrict__ cv, float *__restrict__ ks, float *__restrict__ vs,
+    const int32_t *__restrict__ pos, int n, int Hkv, int L, int d, int64_t n_groups,
+    int32_t *__restrict__ bad) {
+    const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t grp = gt >> 4;                       // global group id over (b, j, h, g)
+    const int lane16 = threadIdx.x & 15;
+    const bool live = grp < n_groups;
+    const int ng = d >> 7;
+    const int64_t row = live ? grp / ng : 0;           // (b, j, h)
+    const int g = live ? (int)(grp - row * ng) : 0;
+    const int h = (int)(row % Hkv);
+    const int64_t bj = row / Hkv;
+    const int b = (int)(bj / n);
+    const int p = live ? pos[bj] : -1;
+    const bool ok = live && p >= 0 && p < L;
+    if (live && !ok && p != -1 && bad && lane16 == 0 && h == 0 && g == 0) atomicAdd(bad, 1);
+
+    // every lane takes part in the shuffles below; dead lanes contribute 0
+    const int64_t src = row * d + g * 128 + lane16 * 8;
+    float xk[8], xv[8];
+    if (ok) {
+        if (SRC == DLLM_BF16) {
+            const uint4 wk = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(k_new) + src);
+            const uint4 wv = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(v_new) + src);
+            const uint32_t a[4] = {wk.x, wk.y, wk.z, wk.w}, c[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                xk[2 * i] = bf16lo(a[i]); xk[2 * i + 1] = bf16hi(a[i]);
+                xv[2 * i] = bf16lo(c[i]); xv[2 * i + 1] = bf16hi(c[i]);
+            }
+        } else {
+            const float4 *pk = reinterpret_cast<const float4 *>(static_cast<const float *>(k_new) + src);
+            const float4 *pv = reinterpret_cast<const float4 *>(static_cast<const float *>(v_new) + src);
+            const float4 k0 = pk[0], k1 = pk[1], v0 = pv[0], v1 = pv[1];
+            xk[0] = k0.x; xk[1] = k0.y; xk[2] = k0.z; xk[3] = k0.w;
+            xk[4] = k1.x; xk[5] = k1.y; xk[6] = k1.z; xk[7] = k1.w;
+            xv[0] = v0.x; xv[1] = v0.y; xv[2] = v0.z; xv[3] = v0.w;
+            xv[4] = v1.x; xv[5] = v1.y; xv[6] = v1.z; xv[7] = v1.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xk[i] = xv[i] = 0.f;
+    }
+    float ak = 0.f, av = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        ak = fmaxf(ak, fabsf(xk[i]));
+        av = fmaxf(av, fabsf(xv[i]));
+    }
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) {                 // max over the 16 lanes of the group
+        ak = fmaxf(ak, __shfl_xor(ak, o, kWave));
+        av = fmaxf(av, __shfl_xor(av, o, kWave));
+    }
+    if (!ok) return;
+    const float sk = ak / 448.0f;                      // IEEE float32 divides
+    const float sv = av / 448.0f;
+    uint32_t lok = 0, hik = 0, lov = 0, hiv = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t ek = ak == 0.f ? 0u : e4m3_rne(xk[i] / sk);
+        const uint32_t ev = av == 0.f ? 0u : e4m3_rne(xv[i] / sv);
+        if (i < 4) { lok |= ek << (8 * i); lov |= ev << (8 * i); }
+        else { hik |= ek << (8 * (i - 4)); hiv |= ev << (8 * (i - 4)); }
+    }
+    const int64_t drow = ((int64_t)b * Hkv + h) * L + p;
+    const int64_t dst = drow * d + g * 128 + lane16 * 8;
+    *reinterpret_cast<uint2 *>(ck + dst) = make_uint2(lok, hik);
+    *reinterpret_cast<uint2 *>(cv + dst) = make_uint2(lov, hiv);
+    if (lane16 == 0) {
+        ks[drow * ng + g] = ak == 0.f ? 0.f : sk;
+        vs[drow * ng + g] = av == 0.f ? 0.f : sv;
+    }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint4 *__restrict__ p, int64_t n16,
+                                                        uint8_t *__restrict__ tail, int ntail) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t j = i; j < n16; j += stride) p[j] = make_uint4(0, 0, 0, 0);
+    if (i < ntail) tail[i] = 0;
+}
+
+// sinks [0, min(S, e)) then the newest keys [max(S, e-R), e), then -1
+__global__ __launch_bounds__(256) void sink_rolling_kernel(int L, int S, int R,
+                                                           const int32_t *__restrict__ end,
+                                                           int32_t *__restrict__ key_idx,
+                                                           int n_keys) {
+    const int b = blockIdx.y;
+    int e = end[b];
+    e = e < 0 ? 0 : (e > L ? L : e);
+    const int ns = S < e ? S : e;
+    const int start = (e - R) > S ? (e - R) : S;
+    const int nr = e > start ? e - start : 0;
+    int32_t *out = key_idx + (int64_t)b * n_keys;
+    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < n_keys; j += gridDim.x * blockDim.x)
+        out[j] = j < ns ? j : (j < ns + nr ? start + (j - ns) : -1);
+}
+
+}  // namespace
+
+int launch_fill_zero(void *p, size_t bytes, hipStream_t s) {
+    if (bytes == 0) return DLLM_OK;
+    const int64_t n16 = (int64_t)(bytes / 16);
+    const int ntail = (int)(bytes % 16);
+    const int64_t blocks = std::min<int64_t>(std::max<int64_t>(cdiv64(n16, 256), 1), 8192);
+    fill_zero_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
+        static_cast<uint4 *>(p), n16, static_cast<uint8_t *>(p) + n16 * 16, ntail);
+    return launch_status();
+}
+
+int launch_scatter(const dllm_kv_cache &c, const void *k_new, const void *v_new, int src_dtype,
+                   const int32_t *pos, int n, int32_t *bad, hipStream_t s) {
+    if (n == 0) return DLLM_OK;
+    const int Hkv = c.n_kv_heads, d = c.d_head, L = c.L;
+    const int64_t rows = (int64_t)c.B * n * Hkv;
+    if (c.dtype == DLLM_E4M3) {
+        const int64_t groups = rows * (d / 128);
+        const int64_t threads = groups * 16;
+        const unsigned blocks = (unsigned)cdiv64(threads, 256);
+        if (src_dtype == DLLM_BF16)
+            scatter_e4m3_kernel<DLLM_BF16><<<blocks, 256, 0, s>>>(
+                k_new, v_new, static_cast<uint8_t *>(c.k), static_cast<uint8_t *>(c.v), c.k_scale,
+                c.v_scale, pos, n, Hkv, L, d, groups, bad);
+        else
+            scatter_e4m3_kernel<DLLM_F32><<<blocks, 256, 0, s>>>(
+                k_new, v_new, static_cast<uint8_t *>(c.k), static_cast<uint8_t *>(c.v), c.k_scale,
+                c.v_scale, pos, n, Hkv, L, d, groups, bad);
+        return launch_status();
+    }
+    const int esz = c.dtype == DLLM_F32 ? 4 : 2;
+    const int cpr = d * esz / 16;
+    const int64_t total = rows * cpr;
+    scatter_copy_kernel<<<(unsigned)cdiv64(total, 256), 256, 0, s>>>(
+        static_cast<const uint4 *>(k_new), static_cast<const uint4 *>(v_new),
+        static_cast<uint4 *>(c.k), static_cast<uint4 *>(c.v), pos, n, Hkv, L, cpr, total, bad);
+    return launch_status();
+}
+
+int launch_sink_rolling(int B, int L, int S, int R, const int32_t *end, int32_t *key_idx,
+                        int n_keys, hipStream_t s) {
+    const unsigned gx = (unsigned)std::min(cdiv(n_keys, 256), 64);
+    sink_rolling_kernel<<<dim3(gx, (unsigned)B), dim3(256), 0, s>>>(L, S, R, end, key_idx, n_keys);
+    return launch_status();
+}
+
+}  // namespace dllm

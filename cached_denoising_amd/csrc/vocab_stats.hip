@@ -1,0 +1,274 @@
+// Vocab statistics: for every row of logits, the argmax token (lowest index
+// wins ties), the largest softmax probability and the entropy, in one pass
+// over the row.  [SWD page, 3.1 and 4.2: per-position max probability and
+// its token; Flash-dLLM page, 3.1: entropy of the step's distribution.]
+//
+// One workgroup of 256 threads streams one row (or one contiguous split of
+// a row) with 16-byte loads; the few elements before the first 16-byte
+// boundary and after the last are peeled off.  Each thread keeps an online
+// state over base-2 exponents a_j = (x_j - m) log2(e):
+//     m = running max,  s = sum 2^a_j,  t = sum 2^a_j a_j,  idx = argmax
+// so that  maxprob = 1/s  and  entropy = ln s - ln2 * t / s.  States merge in
+// a fixed order (wave butterfly, then waves 0..3, then splits 0..n-1), so
+// the result is bitwise reproducible.  The probabilities never touch memory.
+#include "common.hpp"
+
+#include <climits>
+
+namespace dllm {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+constexpr float kNegInf = -__builtin_inff();
+
+struct Acc {
+    float m, s, t;
+    int idx;
+};
+
+__device__ __forceinline__ Acc acc_empty() { return Acc{kNegInf, 0.f, 0.f, INT_MAX}; }
+
+// merge b into a; a tie in the max keeps the lower index
+__device__ __forceinline__ void acc_merge(Acc &a, const Acc &b) {
+    const float m = fmaxf(a.m, b.m);
+    int idx;
+    if (a.m > b.m) idx = a.idx;
+    else if (b.m > a.m) idx = b.idx;
+    else idx = min(a.idx, b.idx);
+    float s = 0.f, t = 0.f;
+    if (a.s > 0.f) {
+        const float d = (a.m - m) * kLog2e;
+        const float f = exp2f(d);
+        s += a.s * f;
+        t += f * (a.t + a.s * d);
+    }
+    if (b.s > 0.f) {
+        const float d = (b.m - m) * kLog2e;
+        const float f = exp2f(d);
+        s += b.s * f;
+        t += f * (b.t + b.s * d);
+    }
+    a = Acc{m, s, t, idx};
+}
+
+// Fold NE consecutive-in-thread-order elements into the state.  gidx(e)
+// gives element e's column; columns increase with e.
+template <int NE, typename IdxFn>
+__device__ __forceinline__ void consume(Acc &st, const float (&x)[NE], IdxFn gidx) {
+    float cm = x[0];
+#pragma unroll
+    for (int e = 1; e < NE; ++e) cm = fmaxf(cm, x[e]);
+    if (cm >= st.m && cm != kNegInf) {
+        int first = NE - 1;
+#pragma unroll
+        for (int e = NE - 1; e >= 0; --e)
+            if (x[e] == cm) first = e;
+        const int gi = gidx(first);
+        if (cm > st.m) {
+            if (st.s > 0.f) {                    // rescale to the new max
+                const float d = (st.m - cm) * kLog2e;
+                const float f = __builtin_amdgcn_exp2f(d);
+                st.t = f * (st.t + st.s * d);
+                st.s *= f;
+            }
+            st.m = cm;
+            st.idx = gi;
+        } else if (gi < st.idx) {
+            st.idx = gi;
+        }
+    }
+    if (st.m == kNegInf) return;                 // nothing finite seen yet
+    const float mL = st.m * kLog2e;
+    float s0 = 0.f, s1 = 0.f, t0 = 0.f, t1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < NE; e += 2) {
+        const float a0 = fmaf(x[e], kLog2e, -mL);
+        const float p0 = __builtin_amdgcn_exp2f(a0);
+        s0 += p0;
+        t0 = fmaf(p0, a0, t0);
+        if (e + 1 < NE) {
+            const float a1 = fmaf(x[e + 1], kLog2e, -mL);
+            const float p1 = __builtin_amdgcn_exp2f(a1);
+            s1 += p1;
+            t1 = fmaf(p1, a1, t1);
+        }
+    }
+    float cs = s0 + s1, ct = t0 + t1;
+    if (ct != ct) {
+        // a -inf logit gave 0 * -inf; such terms add nothing, drop them
+        cs = 0.f;
+        ct = 0.f;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            if (x[e] != kNegInf) {
+                const float a = fmaf(x[e], kLog2e, -mL);
+                const float p = __builtin_amdgcn_exp2f(a);
+                cs += p;
+                ct = fmaf(p, a, ct);
+            }
+        }
+    }
+    st.s += cs;
+    st.t += ct;
+}
+
+template <int DT> struct Elem;
+template <> struct Elem<DLLM_F32> {
+    typedef float T;
+    static constexpr int kVec = 4;
+    __device__ static void unpack(const uint4 &w, float *x) {
+        x[0] = __uint_as_float(w.x);
+        x[1] = __uint_as_float(w.y);
+        x[2] = __uint_as_float(w.z);
+        x[3] = __uint_as_float(w.w);
+    }
+    __device__ static float scalar(const T *p) { return *p; }
+};
+template <> struct Elem<DLLM_BF16> {
+    typedef uint16_t T;
+    static constexpr int kVec = 8;
+    __device__ static void unpack(const uint4 &w, float *x) {
+        x[0] = bf16lo(w.x); x[1] = bf16hi(w.x);
+        x[2] = bf16lo(w.y); x[3] = bf16hi(w.y);
+        x[4] = bf16lo(w.z); x[5] = bf16hi(w.z);
+        x[6] = bf16lo(w.w); x[7] = bf16hi(w.w);
+    }
+    __device__ static float scalar(const T *p) { return bf16_to_f32(*p); }
+};
+
+__device__ __forceinline__ void write_stats(const Acc &a, int64_t row, int32_t *argmax,
+                                            float *maxprob, float *entropy) {
+    argmax[row] = a.idx == INT_MAX ? 0 : a.idx;
+    maxprob[row] = 1.0f / a.s;
+    entropy[row] = logf(a.s) - kLn2 * a.t / a.s;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void vocab_stats_kernel(
+    const typename Elem<DT>::T *__restrict__ logits, int64_t V, int64_t stride, int64_t chunk,
+    int splits, int32_t *__restrict__ argmax, float *__restrict__ maxprob,
+    float *__restrict__ entropy, float4 *__restrict__ partial) {
+    typedef Elem<DT> E;
+    constexpr int kVec = E::kVec;
+    const int tid = threadIdx.x;
+    const int64_t row = blockIdx.x / splits;
+    const int split = blockIdx.x - (int)(row * splits);
+    const int64_t j0 = (int64_t)split * chunk;
+    const int64_t j1 = min(V, j0 + chunk);
+    const typename E::T *rp = logits + row * stride;
+
+    Acc st = acc_empty();
+    if (j0 < j1) {
+        // aligned body [a0, a1) of whole 16-byte vectors
+        const uintptr_t addr = (uintptr_t)(rp + j0);
+        const int64_t mis = (int64_t)(((16u - (unsigned)(addr & 15u)) & 15u) / sizeof(typename E::T));
+        const int64_t a0 = min(j1, j0 + mis);
+        const int64_t nvec = (j1 - a0) / kVec;
+        const int64_t a1 = a0 + nvec * kVec;
+        // peeled elements: [j0, a0) and [a1, j1), fewer than 2*kVec
+        const int64_t nhead = a0 - j0, ntail = j1 - a1;
+        if (tid < nhead + ntail) {
+            const int64_t j = tid < nhead ? j0 + tid : a1 + (tid - nhead);
+            float x1[1] = {E::scalar(rp + j)};
+            consume<1>(st, x1, [&](int) { return (int)j; });
+        }
+        const uint4 *vp = reinterpret_cast<const uint4 *>(rp + a0);
+        int64_t v = tid;
+        for (; v + (kUnroll - 1) * kThreads < nvec; v += kUnroll * kThreads) {
+            uint4 w[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) w[u] = vp[v + u * kThreads];
+            float x[kUnroll * kVec];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) E::unpack(w[u], x + u * kVec);
+            consume<kUnroll * kVec>(st, x, [&](int e) {
+                return (int)(a0 + (v + (e / kVec) * kThreads) * kVec + (e % kVec));
+            });
+        }
+        for (; v < nvec; v += kThreads) {
+            const uint4 w = vp[v];
+            float x[kVec];
+            E::unpack(w, x);
+            consume<kVec>(st, x, [&](int e) { return (int)(a0 + v * kVec + e); });
+        }
+    }
+
+    // wave butterfly, then the four waves in order
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        Acc other{shfl_xor_f(st.m, o), shfl_xor_f(st.s, o), shfl_xor_f(st.t, o),
+                  shfl_xor_i(st.idx, o)};
+        acc_merge(st, other);
+    }
+    __shared__ Acc waves[kThreads / kWave];
+    if ((tid & (kWave - 1)) == 0) waves[tid / kWave] = st;
+    __syncthreads();
+    if (tid == 0) {
+        Acc r = waves[0];
+#pragma unroll
+        for (int w = 1; w < kThreads / kWave; ++w) acc_merge(r, waves[w]);
+        if (splits == 1)
+            write_stats(r, row, argmax, maxprob, entropy);
+        else
+            partial[blockIdx.x] = make_float4(r.m, r.s, r.t, __int_as_float(r.idx));
+    }
+}
+
+__global__ __launch_bounds__(256) void vocab_merge_kernel(const float4 *__restrict__ partial,
+                                                          int64_t N, int splits,
+                                                          int32_t *__restrict__ argmax,
+                                                          float *__restrict__ maxprob,
+                                                          float *__restrict__ entropy) {
+    const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (row >= N) return;
+    const float4 *p = partial + row * splits;
+    Acc r = acc_empty();
+    for (int i = 0; i < splits; ++i) {
+        const float4 q = p[i];
+        acc_merge(r, Acc{q.x, q.y, q.z, __float_as_int(q.w)});
+    }
+    write_stats(r, row, argmax, maxprob, entropy);
+}
+
+}  // namespace
+
+VocabPlan plan_vocab(int64_t N, int64_t V) {
+    VocabPlan p;
+    const int64_t target_blocks = 2048;     // 8 workgroups per CU
+    const int64_t min_chunk = 16384;        // elements per split, at least
+    int64_t splits = N > 0 ? cdiv64(target_blocks, N) : 1;
+    splits = std::max<int64_t>(1, std::min<int64_t>(splits, cdiv64(V, min_chunk)));
+    int64_t chunk = cdiv64(V, splits);
+    chunk = cdiv64(chunk, 8) * 8;
+    splits = cdiv64(V, chunk);
+    p.splits = (int)splits;
+    p.chunk = chunk;
+    p.ws_bytes = splits > 1 ? (size_t)(N * splits) * sizeof(float4) : 0;
+    return p;
+}
+
+int launch_vocab(const void *logits, int dtype, int64_t N, int64_t V, int64_t stride,
+                 int32_t *argmax, float *maxprob, float *entropy, const VocabPlan &p, void *ws,
+                 hipStream_t s) {
+    if (N == 0) return DLLM_OK;
+    const int64_t blocks = N * p.splits;
+    if (blocks > INT_MAX) return DLLM_ERANGE;
+    float4 *partial = static_cast<float4 *>(ws);
+    if (dtype == DLLM_BF16)
+        vocab_stats_kernel<DLLM_BF16><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
+            static_cast<const uint16_t *>(logits), V, stride, p.chunk, p.splits, argmax, maxprob,
+            entropy, partial);
+    else
+        vocab_stats_kernel<DLLM_F32><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
+            static_cast<const float *>(logits), V, stride, p.chunk, p.splits, argmax, maxprob,
+            entropy, partial);
+    int rc = launch_status();
+    if (rc != DLLM_OK || p.splits == 1) return rc;
+    vocab_merge_kernel<<<dim3((unsigned)cdiv64(N, 256)), dim3(256), 0, s>>>(partial, N, p.splits,
+                                                                            argmax, maxprob,
+                                                                            entropy);
+    return launch_status();
+}
+
+}  // namespace dllm

@@ -1,0 +1,252 @@
+/*
+ * dllm.h -- C ABI of the per-step hot path of cached masked-diffusion
+ * language-model decoding on AMD Instinct MI355X (gfx950).
+ *
+ * One decoding step of a diffusion LM recomputes only the positions of the
+ * active block.  This library covers what happens around that recompute:
+ *
+ *   dllm_cache_init        describe and clear a persistent per-layer K/V cache
+ *   dllm_scatter_kv        write the block's fresh K/V rows into the cache
+ *   dllm_sink_rolling_map  build a sink + rolling-window key index map
+ *   dllm_block_attention   block queries vs. the cached keys, bidirectional
+ *   dllm_vocab_stats       argmax token, max-probability, entropy per row
+ *   dllm_stability_reset   clear the per-position decode state
+ *   dllm_stability_mask    history ring, stability test, confidence score and
+ *                          window expansion -> next step's compute mask
+ *
+ * Page titles cited below (section numbers are the pages' own):
+ *   [SWD]     Stable Window Decoding blog page on temporal stability in
+ *             diffusion-LM decoding (wmrh.cn/news/51151)
+ *   [LaCache] "LaCache: Exact Caching and Precision-Adaptive Inference for
+ *             Diffusion Large Language Models" (gist.science explainer;
+ *             sections of its technical summary)
+ *   [Sinks]   attention-sinks and rolling K/V cache blog page for GPT-2
+ *             (wmrh.cn/news/159578)
+ *   [Flash]   Flash-dLLM page: I/O-aware KV cache and self-verifying
+ *             parallel decoding (bjdmk.com.cn/news/5926815)
+ *
+ * Conventions shared by every call
+ *   - Every array argument is a DEVICE pointer to memory the caller owns
+ *     (the library allocates no device memory and keeps no state between
+ *     calls).  Scalars and parameter structs are host values.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls enqueue work on it and return without synchronising.
+ *   - Shapes are row-major (C order), innermost dimension last.
+ *   - Host-side validation returns a negative dllm_status and enqueues
+ *     nothing; a HIP launch error returns DLLM_EHIP.
+ *   - An index of -1 in a position list or key map is padding and is
+ *     skipped; any other index outside [0, L) is skipped too and counted in
+ *     the optional `bad_count` where a call has one.  Duplicate positions
+ *     within one sequence in a single call are a caller error (racing writes).
+ *   - Results are bitwise reproducible run to run: reductions merge in a
+ *     fixed order and use no floating-point atomics.
+ */
+#ifndef DLLM_H
+#define DLLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DLLM_OK = 0,
+    DLLM_EINVAL = -1,      /* null pointer or out-of-range scalar argument   */
+    DLLM_EDTYPE = -2,      /* unsupported dtype or dtype combination         */
+    DLLM_ESHAPE = -3,      /* inconsistent or unsupported shape              */
+    DLLM_EALIGN = -4,      /* pointer or row size not 16-byte aligned        */
+    DLLM_ERANGE = -5,      /* size beyond a supported maximum                */
+    DLLM_EHIP = -6,        /* a HIP runtime call or kernel launch failed     */
+    DLLM_EWORKSPACE = -7   /* workspace missing or smaller than required     */
+} dllm_status;
+
+typedef enum {
+    DLLM_F32 = 0,          /* IEEE binary32                                  */
+    DLLM_BF16 = 1,         /* bfloat16                                       */
+    DLLM_E4M3 = 2          /* OCP e4m3fn, one float32 scale per 128 elements */
+} dllm_dtype;
+
+/* Descriptor of one layer's persistent K/V cache, filled by dllm_cache_init.
+ * Plain data; the caller owns the memory it points to.
+ *   k, v       [B, n_kv_heads, L, d_head] elements of `dtype`
+ *   k_scale,   [B, n_kv_heads, L, d_head/128] float32, E4M3 only (else NULL):
+ *   v_scale    element c of a row decodes to code * scale[c / 128]        */
+typedef struct {
+    int32_t B, L, n_kv_heads, d_head;
+    int32_t dtype;
+    int32_t reserved;
+    void *k, *v;
+    float *k_scale, *v_scale;
+} dllm_kv_cache;
+
+/* Parameters of the stability / confidence / window step.
+ *   K            steps a position's argmax must persist [SWD, 3.1]
+ *   D            depth of the step-history ring, D >= K
+ *   R            window radius around each position to recompute [SWD, 3.2]
+ *   tau          stability threshold: mean max-prob over the K steps must
+ *                exceed it (strictly) [SWD, 3.1]
+ *   alpha, beta, lambda
+ *                cache confidence alpha*(1 - H/ln V) + beta*exp(-lambda*dt)
+ *                [Flash, 3.1]
+ *   conf_thresh  positions whose confidence is below it are recomputed
+ *                [Flash, 3.1]; <= 0 turns the gate off
+ *   vocab        V of the vocab pass (max entropy ln V)                    */
+typedef struct {
+    int32_t K, D, R, reserved;
+    double tau, alpha, beta, lambda, conf_thresh;
+    int64_t vocab;
+} dllm_stab_params;
+
+/* Human-readable name of a status code (static string). */
+const char *dllm_status_str(int status);
+
+/* Library version, as major*10000 + minor*100 + patch. */
+int dllm_version(void);
+
+/* ---------------------------------------------------------------------------
+ * dllm_cache_init -- validate and fill `cache`, and zero the K/V (and scale)
+ * storage on `stream`.  The persistent per-layer cache of the states of the
+ * unchanged tokens [LaCache, Methodology 1: RoPECache], fixed in size for
+ * its lifetime [Sinks, 3.1].
+ *   dtype     DLLM_F32, DLLM_BF16 or DLLM_E4M3 (E4M3 needs d % 128 == 0 and
+ *             non-NULL scale arrays)
+ *   k, v      device, 16-byte aligned, B*n_kv_heads*L*d elements each
+ * Limits: B, L, n_kv_heads >= 1; d in 16..256 with d*size(dtype) % 16 == 0.
+ * Returns DLLM_OK or a negative dllm_status.
+ * ------------------------------------------------------------------------- */
+int dllm_cache_init(dllm_kv_cache *cache, int B, int L, int n_kv_heads, int d_head,
+                    int dtype, void *k, void *v, float *k_scale, float *v_scale,
+                    void *stream);
+
+/* ---------------------------------------------------------------------------
+ * dllm_scatter_kv -- write the recomputed block's fresh K/V rows into the
+ * cache: cache[b, h, pos[b, j], :] = new[b, j, h, :].  Every other row is
+ * left bit-for-bit unchanged, so the cache then holds exactly what a full
+ * recompute would assemble [LaCache, Methodology 1 and 3; SWD, 4.1 and 4.3
+ * write-back of masked positions; Sinks, 3.2 and 5.1 index writes].
+ *   k_new, v_new  [B, n, n_kv_heads, d] in src_dtype.  For F32/BF16 caches
+ *                 src_dtype must equal the cache dtype (plain copy).  For
+ *                 E4M3 caches src_dtype is F32 or BF16 and each 128-element
+ *                 group is quantised: scale = amax/448 (float32 divide),
+ *                 code = round-to-nearest-even(x/scale) on the e4m3 grid,
+ *                 saturating at +-448; an all-zero group gets scale 0
+ *                 [LaCache, Methodology 2: per-group 1x128 FP8].
+ *   pos           [B, n] int32 device; -1 = padding.
+ *   bad_count     optional device int32; out-of-range positions (other than
+ *                 -1) are skipped and atomically added here.  May be NULL.
+ * n == 0 is a no-op.
+ * ------------------------------------------------------------------------- */
+int dllm_scatter_kv(const dllm_kv_cache *cache, const void *k_new, const void *v_new,
+                    int src_dtype, const int32_t *pos, int n, int32_t *bad_count,
+                    void *stream);
+
+/* ---------------------------------------------------------------------------
+ * dllm_sink_rolling_map -- key index map of S attention sinks plus a rolling
+ * window of the R newest keys [Sinks, 2.3 and 3.2]: for sequence b with
+ * block end e = end[b] (one past its last position),
+ *   key_idx[b, :] = {0, ..., min(S, e)-1} then [max(S, e-R), e), ascending,
+ * padded with -1 up to n_keys.  The sinks keep their original positions and
+ * the map never holds more than S + R keys.
+ *   end      [B] int32 device, values in [0, L]; values outside are clamped
+ *   key_idx  [B, n_keys] int32 device; n_keys >= S + R
+ * ------------------------------------------------------------------------- */
+int dllm_sink_rolling_map(int B, int L, int S, int R, const int32_t *end,
+                          int32_t *key_idx, int n_keys, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * dllm_block_attention -- for every query of the active block,
+ *   out = softmax(q . K^T * scale) . V
+ * over the selected cached keys, with no causal mask (the block attends
+ * bidirectionally to the whole context) [LaCache, problem statement and
+ * Methodology 1 (FACache's online-softmax statistics m, l, O~); Sinks, 2.1].
+ * Query head h reads KV head h / (Hq / n_kv_heads).
+ *   q        [B, Hq, b, d] in q_dtype.  BF16 queries run on bf16 MFMA with
+ *            float32 accumulation (BF16 or E4M3 caches, d in {64, 128});
+ *            F32 queries with an F32 cache run a float32 VALU path.
+ *   key_idx  [B, n_keys] int32 device, or NULL for all L keys (n_keys = L);
+ *            -1 entries are padding.  A row with no key gets out = 0 and
+ *            lse = -inf.
+ *   scale    > 0, or 0 for 1/sqrt(d)
+ *   out      [B, Hq, b, d] in out_dtype (F32 or BF16)
+ *   lse      optional [B, Hq, b] float32: natural-log log-sum-exp of the
+ *            scaled scores (the softmax normaliser).  May be NULL.
+ *   workspace / ws_bytes: device scratch of at least
+ *            dllm_block_attention_workspace(...) bytes (may be 0 bytes).
+ * ------------------------------------------------------------------------- */
+int dllm_block_attention(const dllm_kv_cache *cache, const void *q, int q_dtype, int Hq,
+                         int b, const int32_t *key_idx, int n_keys, float scale,
+                         void *out, int out_dtype, float *lse,
+                         void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes dllm_block_attention needs for these shapes (0 if none). */
+size_t dllm_block_attention_workspace(const dllm_kv_cache *cache, int q_dtype, int Hq,
+                                      int b, int n_keys);
+
+/* ---------------------------------------------------------------------------
+ * dllm_vocab_stats -- one pass over each row of logits:
+ *   argmax[r]  lowest index of the largest logit
+ *   maxprob[r] largest softmax probability, 1 / sum_j exp(x_j - max)
+ *   entropy[r] -sum_j p_j ln p_j (natural log)
+ * [SWD, 3.1 and 4.2: per-position max probability and its token;
+ *  Flash, 3.1: the entropy of the step's distribution].  The probabilities
+ * are never written out.
+ *   logits     [N, row_stride] of dtype F32 or BF16; columns >= V are ignored
+ *   V          1 <= V <= row_stride, V < 2^31
+ *   Logits are finite or -inf with at least one finite value per row (other
+ *   rows give unspecified results).
+ *   workspace / ws_bytes: at least dllm_vocab_stats_workspace(N, V) bytes.
+ * ------------------------------------------------------------------------- */
+int dllm_vocab_stats(const void *logits, int dtype, int64_t N, int64_t V, int64_t row_stride,
+                     int32_t *argmax, float *maxprob, float *entropy,
+                     void *workspace, size_t ws_bytes, void *stream);
+
+size_t dllm_vocab_stats_workspace(int64_t N, int64_t V);
+
+/* ---------------------------------------------------------------------------
+ * dllm_stability_reset -- empty the history ring (ring_step = -1) and clear
+ * entropy_latest, t_write and stable for B sequences of length L with ring
+ * depth D: the scheduler reset of [SWD, 4.2].
+ * ------------------------------------------------------------------------- */
+int dllm_stability_reset(int B, int L, int D, int32_t *ring_argmax, float *ring_maxprob,
+                         int32_t *ring_step, float *entropy_latest, int32_t *t_write,
+                         uint8_t *stable, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * dllm_stability_mask -- after the forward of step s (s >= 0), for each
+ * sequence:
+ *  1. record (argmax, maxprob, s) of every recomputed position in ring slot
+ *     s mod D, set entropy_latest and t_write = s [SWD, 3.3 step c];
+ *  2. a recomputed position that is not yet stable becomes stable when its
+ *     ring holds the steps s, s-1, ..., s-K+1, all with one argmax, and the
+ *     mean of their max-probs (float64, oldest first) exceeds tau; stable
+ *     is never cleared [SWD, 3.1 and 4.2];
+ *  3. conf = alpha(1 - H/ln V) + beta exp(-lambda (s - t_write)) in float64
+ *     for every position, H = entropy_latest [Flash, 3.1];
+ *  4. seed = not stable, or conf < conf_thresh; mask[j] = 1 when a seed lies
+ *     within R of j (clamped to the sequence); with no seed at all the mask
+ *     is all ones and all_stable = 1 [SWD, 3.2 and 4.2];
+ *  5. next_pos lists the mask's positions ascending, padded with -1, and
+ *     count holds their number: the positions to recompute at step s+1.
+ *   pos        [B, n] recomputed positions of step s, or NULL for all L
+ *              (then n must be L); -1 entries are padding
+ *   argmax, maxprob, entropy  [B, n] statistics of those rows (as written
+ *              by dllm_vocab_stats)
+ *   ring_*     [D, B, L] state; entropy_latest, t_write, stable [B, L] state
+ *   mask [B, L] u8, conf [B, L] f32, next_pos [B, L] i32, count [B] i32,
+ *   all_stable [B] u8: outputs (conf may be NULL)
+ * Limits: L <= 131072, 1 <= K <= D, R >= 0, vocab >= 2.
+ * ------------------------------------------------------------------------- */
+int dllm_stability_mask(int B, int L, int step, const int32_t *pos, int n,
+                        const int32_t *argmax, const float *maxprob, const float *entropy,
+                        int32_t *ring_argmax, float *ring_maxprob, int32_t *ring_step,
+                        float *entropy_latest, int32_t *t_write, uint8_t *stable,
+                        const dllm_stab_params *params,
+                        uint8_t *mask, float *conf, int32_t *next_pos, int32_t *count,
+                        uint8_t *all_stable, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DLLM_H */

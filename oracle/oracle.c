@@ -153,12 +153,13 @@ int oracle_scatter_kv(int cache_dtype, int B, int L, int Hkv, int d,
     for (b = 0; b < B; ++b)
         for (j = 0; j < n; ++j) {
             int p = pos[(int64_t)b * n + j];
-            if (p < 0 || p >= L) return -1;
+            if (p < -1 || p >= L) return -1;     /* -1 is padding */
         }
 
     for (b = 0; b < B; ++b) {
         for (j = 0; j < n; ++j) {
             int p = pos[(int64_t)b * n + j];
+            if (p == -1) continue;
             for (h = 0; h < Hkv; ++h) {
                 int64_t src_row = (((int64_t)b * n + j) * Hkv + h) * d;
                 int64_t dst_row = (((int64_t)b * Hkv + h) * L + p) * d;
@@ -240,7 +241,7 @@ int oracle_block_attention(int cache_dtype, int B, int L, int Hkv, int d,
     if (key_idx) {
         int64_t i;
         for (i = 0; i < (int64_t)B * n_keys; ++i)
-            if (key_idx[i] < 0 || key_idx[i] >= L) return -1;
+            if (key_idx[i] < -1 || key_idx[i] >= L) return -1;   /* -1 is padding */
     }
     if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
     group = Hq / Hkv;
@@ -258,27 +259,33 @@ int oracle_block_attention(int cache_dtype, int B, int L, int Hkv, int d,
             int64_t qrow = (((int64_t)bi * Hq + h) * b + i) * d;
             int64_t orow = (task * b + i) * d;
             double m = -INFINITY, z = 0.0;
-            /* scores s_j = scale * q . k_j */
+            /* scores s_j = scale * q . k_j; a padding key has no score */
             for (j = 0; j < n_keys; ++j) {
                 int key = key_idx ? key_idx[(int64_t)bi * n_keys + j] : j;
                 int64_t krow = ((int64_t)bi * Hkv + kvh) * L + key;
                 double dot = 0.0;
+                if (key < 0) { s[j] = -INFINITY; continue; }
                 for (c = 0; c < d; ++c)
                     dot += load_src(q_dtype, q, qrow + c) *
                            cache_value(cache_dtype, cache_k, k_scale, krow, d, c);
                 s[j] = scale * dot;
                 if (s[j] > m) m = s[j];
             }
+            for (c = 0; c < d; ++c) out[orow + c] = 0.0;
+            if (m == -INFINITY) {                /* only padding: no keys at all */
+                if (lse) lse[task * b + i] = -INFINITY;
+                continue;
+            }
             /* softmax weights and the weighted sum of values */
             for (j = 0; j < n_keys; ++j) {
                 s[j] = exp(s[j] - m);
                 z += s[j];
             }
-            for (c = 0; c < d; ++c) out[orow + c] = 0.0;
             for (j = 0; j < n_keys; ++j) {
                 int key = key_idx ? key_idx[(int64_t)bi * n_keys + j] : j;
                 int64_t vrow = ((int64_t)bi * Hkv + kvh) * L + key;
                 double p = s[j] / z;
+                if (key < 0) continue;
                 for (c = 0; c < d; ++c)
                     out[orow + c] += p * cache_value(cache_dtype, cache_v, v_scale, vrow, d, c);
             }
@@ -354,7 +361,7 @@ int oracle_stability_step(int B, int L, int step, const int32_t *pos, int n,
     if (pos) {
         int64_t i;
         for (i = 0; i < (int64_t)B * n; ++i)
-            if (pos[i] < 0 || pos[i] >= L) return -1;
+            if (pos[i] < -1 || pos[i] >= L) return -1;     /* -1 is padding */
     }
     hmax = log((double)V);                    /* entropy of the uniform row */
 
@@ -371,6 +378,7 @@ int oracle_stability_step(int B, int L, int step, const int32_t *pos, int n,
         for (j = 0; j < n; ++j) {
             int p = pos ? pos[(int64_t)b * n + j] : j;
             int64_t ri = (int64_t)slot * B * L + row + p;
+            if (p < 0) continue;
             ring_argmax[ri] = argmax[(int64_t)b * n + j];
             ring_maxprob[ri] = maxprob[(int64_t)b * n + j];
             ring_step[ri] = step;
@@ -386,7 +394,7 @@ int oracle_stability_step(int B, int L, int step, const int32_t *pos, int n,
             int p = pos ? pos[(int64_t)b * n + j] : j;
             int ok = 1, tok;
             double sum = 0.0, mean;
-            if (stable[row + p]) continue;
+            if (p < 0 || stable[row + p]) continue;
             if (step + 1 < K) continue;              /* fewer than K steps so far */
             tok = ring_argmax[(int64_t)slot * B * L + row + p];
             for (k = K - 1; k >= 0; --k) {           /* oldest record first */

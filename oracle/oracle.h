@@ -60,8 +60,8 @@ void oracle_e4m3_quantize_group(const float *x, int n, uint8_t *codes, float *sc
  * cache_k/cache_v: [B, Hkv, L, d] in cache_dtype; k_scale/v_scale:
  * [B, Hkv, L, d/128] float (e4m3 only).  k_new/v_new: [B, n, Hkv, d] in
  * src_dtype (== cache dtype for f32/bf16; f32 or bf16 for e4m3).
- * pos: [B, n] int32, unique per sequence, each in [0, L).  Returns 0, or -1
- * on a bad argument (nothing written). */
+ * pos: [B, n] int32, unique per sequence, each in [0, L) or -1 (padding,
+ * skipped).  Returns 0, or -1 on a bad argument (nothing written). */
 int oracle_scatter_kv(int cache_dtype, int B, int L, int Hkv, int d,
                       void *cache_k, void *cache_v, float *k_scale, float *v_scale,
                       int src_dtype, const void *k_new, const void *v_new,
@@ -76,7 +76,8 @@ int oracle_sink_rolling_keys(int S, int R, int end, int32_t *key_idx);
  * softmax(q . K^T * scale) V per query, bidirectional, over the selected
  * keys [Sinks, 2.1]; [LaCache, problem statement: bidirectional attention].
  * q: [B, Hq, b, d] in q_dtype (f32 or bf16); cache as in A1; key_idx:
- * [B, n_keys] or NULL (= 0..L-1, n_keys = L); query head h reads KV head
+ * [B, n_keys] or NULL (= 0..L-1, n_keys = L), an entry of -1 is padding
+ * (no key; a row with only padding gets out = 0, lse = -inf); query head h reads KV head
  * h / (Hq/Hkv).  scale <= 0 -> 1/sqrt(d).  out: [B, Hq, b, d] double;
  * lse: [B, Hq, b] double (natural-log log-sum-exp of the scaled scores) or
  * NULL.  Optional head subset: when heads != NULL, only the n_heads listed
@@ -101,7 +102,8 @@ int oracle_vocab_stats(int dtype, const void *logits, int64_t N, int64_t V,
 
 /* ---- A5-A7: history, stability, confidence, window mask -----------------
  * One decode step s for B sequences of length L.
- * pos [B, n] lists the positions recomputed this step (NULL: all L, n = L);
+ * pos [B, n] lists the positions recomputed this step (NULL: all L, n = L;
+ * -1 entries are padding);
  * argmax/maxprob/entropy are this step's statistics for those rows,
  * laid out [B, n].  State (in/out): ring_argmax/ring_maxprob/ring_step
  * [D, B, L] (slot s mod D holds step s; ring_step = -1 marks empty),

@@ -1,0 +1,70 @@
+"""The C-ABI library loads, exports every entry point include/dllm.h declares,
+and its host-side argument checks answer without a GPU (no compute call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dllm.h")
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dllm_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def dl():
+    import cached_denoising_amd as D
+    return D
+
+
+def test_header_declares_the_boundary():
+    names = declared()
+    for n in ["dllm_cache_init", "dllm_scatter_kv", "dllm_block_attention", "dllm_vocab_stats",
+              "dllm_stability_mask", "dllm_sink_rolling_map", "dllm_stability_reset",
+              "dllm_block_attention_workspace", "dllm_vocab_stats_workspace", "dllm_status_str"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(dl):
+    lib = ctypes.CDLL(dl.LIB_PATH)
+    missing = [n for n in declared() if not hasattr(lib, n)]
+    assert not missing
+    # the binding wraps exactly these
+    assert sorted(dl.EXPORTS) == declared()
+
+
+def test_status_strings_and_version(dl):
+    assert dl.dllm_status_str(0) == "ok"
+    assert "workspace" in dl.dllm_status_str(-7)
+    assert dl.dllm_version() >= 100
+
+
+def test_host_validation_without_gpu(dl):
+    L = dl.lib()
+    desc = dl._KVCache()
+    # null storage, bad dtype, misaligned row size: rejected before any HIP call
+    assert L.dllm_cache_init(ctypes.byref(desc), 1, 8, 1, 16, 1, None, None, None, None, None) == -1
+    assert L.dllm_cache_init(ctypes.byref(desc), 1, 8, 1, 16, 7, 16, 16, None, None, None) == -2
+    assert L.dllm_cache_init(ctypes.byref(desc), 1, 8, 1, 24, 2, 16, 16, 16, 16, None) in (-3, -4)
+    assert L.dllm_cache_init(None, 1, 8, 1, 16, 0, 16, 16, None, None, None) == -1
+    assert L.dllm_vocab_stats(None, 1, 4, 10, 5, None, None, None, None, 0, None) == -3   # stride < V
+    assert L.dllm_vocab_stats(None, 5, 4, 10, 10, None, None, None, None, 0, None) == -2  # dtype
+    assert L.dllm_vocab_stats(None, 1, 0, 10, 10, None, None, None, None, 0, None) == 0   # N = 0: no-op
+    prm = dl._StabParams(K=3, D=2, R=1, tau=0.9, vocab=10)                                  # D < K
+    assert L.dllm_stability_mask(1, 4, 0, None, 4, 16, 16, 16, 16, 16, 16, 16, 16, 16,
+                                 ctypes.byref(prm), 16, 16, 16, 16, 16, None) == -1
+    assert L.dllm_sink_rolling_map(1, 10, 4, 8, 16, 16, 11, None) == -3                     # n_keys < S+R
+
+
+def test_workspace_sizes(dl):
+    L = dl.lib()
+    assert L.dllm_vocab_stats_workspace(32768, 126464) == 0          # one workgroup per row
+    assert L.dllm_vocab_stats_workspace(512, 126464) > 0             # rows split across workgroups
+    desc = dl._KVCache(B=4, L=32768, n_kv_heads=8, d_head=128, dtype=2, k=16, v=16, k_scale=16,
+                       v_scale=16)
+    assert L.dllm_block_attention_workspace(ctypes.byref(desc), 1, 32, 64, 8192) > 0

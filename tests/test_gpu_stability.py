@@ -1,0 +1,162 @@
+"""GPU parity of dllm_stability_reset / dllm_stability_mask against the
+oracle on shared step statistics: stable flags, masks, next positions,
+counts and all-stable flags bit-exact; confidence within float32 rounding;
+the ring state bit-exact.  A decision the two sides take in float64 could
+only differ if a value sat within an ulp of its threshold; any mismatch is
+reported with its margin."""
+import dataclasses
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_util import need_gpu, say
+
+pytestmark = pytest.mark.gpu
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _state_equal(gst, ost, label):
+    for name in ("ring_argmax", "ring_maxprob", "ring_step", "entropy_latest", "t_write", "stable"):
+        a = getattr(gst, name).cpu().numpy()
+        b = getattr(ost, name)
+        assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                              b.view(np.uint32) if b.dtype == np.float32 else b), (label, name)
+
+
+def _step(orc, D, gst, ost, step, pos, am, mp, en, kw, label):
+    say("stability", label, "step", step)
+    D.dllm_stability_mask(gst, step, None if pos is None else pos.cuda(), am.cuda(), mp.cuda(), en.cuda(), **kw)
+    torch.cuda.synchronize()
+    r = orc.stability_step(ost, step, None if pos is None else pos.numpy(), am.numpy(), mp.numpy(),
+                           en.numpy(), **kw)
+    _state_equal(gst, ost, (label, step))
+    mask = gst.mask.cpu().numpy()
+    if not np.array_equal(mask, r["mask"]):
+        conf = r["conf"]
+        margin = np.abs(conf - kw.get("conf_thresh", 0.0)).min()
+        raise AssertionError(f"{label} step {step}: mask differs; closest confidence margin {margin:.3e}")
+    assert np.array_equal(gst.next_pos.cpu().numpy(), r["next_pos"]), (label, step)
+    assert np.array_equal(gst.count.cpu().numpy(), r["count"]), (label, step)
+    assert np.array_equal(gst.all_stable.cpu().numpy(), r["all_stable"]), (label, step)
+    assert np.allclose(gst.conf.cpu().numpy(), r["conf"], rtol=1e-6, atol=1e-7), (label, step)
+    return r
+
+
+def _kw(cfg):
+    return dict(K=cfg.K, tau=cfg.tau, R=cfg.R, alpha=cfg.alpha, beta=cfg.beta, lam=cfg.lam,
+                conf_thresh=cfg.conf_thresh, V=max(cfg.V, 2))
+
+
+def test_swd_page_example_gpu(orc):
+    D = need_gpu()
+    g = json.load(open(os.path.join(GOLD, "swd_window_example.json")))
+    L = g["L"]
+    gst = D.StabilityState(1, L, 3)
+    st = torch.zeros((1, L), dtype=torch.uint8)
+    st[0, torch.tensor(g["stable_1based"]) - 1] = 1
+    gst.stable.copy_(st)
+    e = torch.zeros((1, 0))
+    say("swd example")
+    D.dllm_stability_mask(gst, 5, torch.zeros((1, 0), dtype=torch.int32, device="cuda"),
+                          e.int().cuda(), e.cuda(), e.cuda(), K=3, tau=0.95, R=g["R"], V=100)
+    torch.cuda.synchronize()
+    assert (torch.nonzero(gst.mask[0]).flatten().cpu() + 1).tolist() == g["mask_1based"]
+
+
+def test_tiny_trajectory_shared_stats(orc):
+    """16 steps of the tiny workload: GPU vocab stats of each step's logits feed
+    both the GPU kernel and the oracle, with the confidence gate on and off"""
+    D = need_gpu()
+    cfg = W.CONFIGS["tiny"]
+    for thresh in (cfg.conf_thresh, 0.0):
+        kw = dict(_kw(cfg), conf_thresh=thresh)
+        gst = D.StabilityState(cfg.B, cfg.L, cfg.D)
+        ost = orc.StabilityState(cfg.B, cfg.L, cfg.D)
+        n_stable = []
+        for s in range(cfg.T):
+            x = W.logits(cfg, device="cuda", step=s)
+            am, mp, en = (t.cpu() for t in D.dllm_vocab_stats(x))
+            _step(orc, D, gst, ost, s, None, am.view(1, -1), mp.view(1, -1), en.view(1, -1), kw,
+                  f"tiny thresh {thresh}")
+            n_stable.append(int(ost.stable.sum()))
+        assert n_stable[-1] > 0                       # the planted peaks settle
+
+
+def _structured(cfg, B, L, T, seed):
+    """per-position settle steps; after settling the argmax is the planted
+    token and the max-prob is U(0.85, 1): many means near tau"""
+    rng = np.random.default_rng(seed)
+    settle = rng.integers(0, T, (B, L))
+    tok = rng.integers(0, 50, (B, L))
+    ams, mps, ens = [], [], []
+    for s in range(T):
+        noise_tok = rng.integers(0, 50, (B, L))
+        settled = s >= settle
+        am = np.where(settled, tok, noise_tok).astype(np.int32)
+        mp = np.where(settled, rng.uniform(0.85, 1.0, (B, L)), rng.uniform(0.0, 0.9, (B, L))).astype(np.float32)
+        en = np.where(settled, rng.uniform(0, 0.5, (B, L)), rng.uniform(1, 11, (B, L))).astype(np.float32)
+        ams.append(am); mps.append(mp); ens.append(en)
+    return ams, mps, ens
+
+
+@pytest.mark.parametrize("thresh", [0.8, 0.0])
+def test_sweep_structured_history(orc, thresh):
+    D = need_gpu()
+    cfg = W.CONFIGS["vocab"]
+    B, L, T = cfg.B, cfg.L, 24
+    kw = dict(_kw(cfg), conf_thresh=thresh)
+    ams, mps, ens = _structured(cfg, B, L, T, seed=7)
+    gst = D.StabilityState(B, L, cfg.D)
+    ost = orc.StabilityState(B, L, cfg.D)
+    total_stable = 0
+    for s in range(T):
+        r = _step(orc, D, gst, ost, s, None, torch.from_numpy(ams[s]), torch.from_numpy(mps[s]),
+                  torch.from_numpy(ens[s]), kw, f"sweep thresh {thresh}")
+        total_stable = int(ost.stable.sum())
+    assert 0 < total_stable < B * L
+
+
+def test_masked_positions_and_padding(orc):
+    """recompute only the previous mask's positions (next_pos, -1 padded), as
+    a decode loop would"""
+    D = need_gpu()
+    cfg = dataclasses.replace(W.CONFIGS["gpt2"], K=2, tau=0.9, R=2)
+    B, L, T = 4, 300, 12
+    kw = dict(K=2, tau=0.9, R=2, alpha=0.7, beta=0.3, lam=0.25, conf_thresh=0.5, V=50257)
+    ams, mps, ens = _structured(cfg, B, L, T, seed=11)
+    gst = D.StabilityState(B, L, 4)
+    ost = orc.StabilityState(B, L, 4)
+    pos = None
+    for s in range(T):
+        if pos is None:
+            am, mp, en = ams[s], mps[s], ens[s]
+        else:
+            p = pos.numpy()
+            safe = np.where(p < 0, 0, p)
+            am = np.take_along_axis(ams[s], safe, 1)
+            mp = np.take_along_axis(mps[s], safe, 1)
+            en = np.take_along_axis(ens[s], safe, 1)
+        r = _step(orc, D, gst, ost, s, pos, torch.from_numpy(np.ascontiguousarray(am)),
+                  torch.from_numpy(np.ascontiguousarray(mp)), torch.from_numpy(np.ascontiguousarray(en)),
+                  kw, "masked")
+        pos = torch.from_numpy(r["next_pos"].copy())
+    assert int(ost.stable.sum()) > 0
+
+
+def test_large_L_and_radius(orc):
+    D = need_gpu()
+    B, L, T = 2, 40000, 4
+    kw = dict(K=1, tau=0.5, R=700, alpha=0.7, beta=0.3, lam=0.1, conf_thresh=0.75, V=1000)
+    rng = np.random.default_rng(3)
+    gst = D.StabilityState(B, L, 2)
+    ost = orc.StabilityState(B, L, 2)
+    for s in range(T):
+        am = rng.integers(0, 3, (B, L)).astype(np.int32)
+        mp = (rng.uniform(0, 1, (B, L)) ** 0.05).astype(np.float32)
+        en = rng.uniform(0, 0.3, (B, L)).astype(np.float32)
+        _step(orc, D, gst, ost, s, None, torch.from_numpy(am), torch.from_numpy(mp), torch.from_numpy(en),
+              kw, "large L")

@@ -236,3 +236,24 @@ def test_attention_head_subset(orc):
     sub, ls = orc.block_attention(ck, cv, None, None, orc.F32, q, orc.F32, heads=heads)
     for i, (bb, hh) in enumerate(heads):
         assert np.array_equal(sub[i], full[bb, hh]) and np.array_equal(ls[i], lf[bb, hh])
+
+
+def test_padding_entries(orc):
+    """-1 in a position list or key map is padding: it is skipped"""
+    B, L, H, d = 2, 30, 2, 16
+    ck, cv, _, _, _, _ = _cache(orc, B, L, H, d, orc.F32, seed=18)
+    q = np.random.default_rng(19).standard_normal((B, H, 3, d)).astype(np.float32)
+    kid = np.array([[3, 4, 5, 9, 10], [0, 1, 2, 28, 29]], dtype=np.int32)
+    padded = np.array([[3, -1, 4, 5, 9, -1, 10], [-1, 0, 1, 2, 28, 29, -1]], dtype=np.int32)
+    a, la = orc.block_attention(ck, cv, None, None, orc.F32, q, orc.F32, key_idx=kid)
+    b1, lb = orc.block_attention(ck, cv, None, None, orc.F32, q, orc.F32, key_idx=padded)
+    assert np.allclose(a, b1, rtol=1e-14, atol=1e-15) and np.allclose(la, lb, rtol=1e-14)
+    empty = np.full((B, 4), -1, dtype=np.int32)
+    e, le = orc.block_attention(ck, cv, None, None, orc.F32, q, orc.F32, key_idx=empty)
+    assert np.all(e == 0) and np.all(np.isneginf(le))
+    # scatter: a -1 row writes nothing
+    before = ck.copy()
+    kn = np.ones((B, 2, H, d), np.float32)
+    orc.scatter_kv(ck, cv, None, None, orc.F32, kn, kn, orc.F32, np.array([[-1, 7], [-1, -1]], np.int32))
+    changed = np.argwhere(np.any(ck != before, axis=-1))
+    assert changed.tolist() == [[0, 0, 7], [0, 1, 7]]

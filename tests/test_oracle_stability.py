@@ -226,3 +226,15 @@ def test_checkpoint_resume(orc):
     rest = [orc.stability_step(saved, s, None, tok[s], pr[s], ent[s], **kw)["mask"] for s in range(4, T)]
     for a, b in zip(full[4:], rest):
         assert np.array_equal(a, b)
+
+
+def test_padding_positions_skipped(orc):
+    B, L = 1, 6
+    st = _state(orc, B, L, 3)
+    pos = np.array([[2, -1, 4]], np.int32)
+    am = np.array([[7, 9, 7]], np.int32)
+    mp = np.ones((1, 3), np.float32)
+    for s in range(3):
+        orc.stability_step(st, s, pos, am, mp, mp * 0, K=3, tau=0.5, R=0, V=10)
+    assert st.stable[0].tolist() == [0, 0, 1, 0, 1, 0]
+    assert st.ring_step[:, 0, 1].tolist() == [-1, -1, -1]
