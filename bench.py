@@ -34,7 +34,22 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="gpt2", choices=["gpt2", "llada", "vocab", "longctx"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 5 times (HBM counter calibration)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters give
+    the factor from counter units to bytes for the kernels measured alike."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 5}), flush=True)
 
 
 def kernel_sha(path):
@@ -231,6 +246,9 @@ def main():
         sys.exit(1)
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     cfg = W.CONFIGS[args.config]
     step = Step(D, W, cfg, dev)
     for _ in range(args.warmup):

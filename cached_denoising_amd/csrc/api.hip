@@ -183,7 +183,7 @@ int dllm_stability_mask(int B, int L, int step, const int32_t *pos, int n,
     if (!params) return DLLM_EINVAL;
     if (B < 1 || L < 1 || step < 0) return DLLM_ESHAPE;
     if (B > 65535) return DLLM_ERANGE;
-    if (!pos && n != L) return DLLM_ESHAPE;
+    if (!pos && n != L && n != 0) return DLLM_ESHAPE;   // NULL list: all L, or none
     if (n < 0 || n > L) return DLLM_ESHAPE;
     const dllm_stab_params &p = *params;
     if (p.K < 1 || p.D < p.K || p.R < 0 || p.vocab < 2) return DLLM_EINVAL;

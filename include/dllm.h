@@ -230,7 +230,7 @@ int dllm_stability_reset(int B, int L, int D, int32_t *ring_argmax, float *ring_
  *  5. next_pos lists the mask's positions ascending, padded with -1, and
  *     count holds their number: the positions to recompute at step s+1.
  *   pos        [B, n] recomputed positions of step s, or NULL for all L
- *              (then n must be L); -1 entries are padding
+ *              (then n must be L, or 0 for none); -1 entries are padding
  *   argmax, maxprob, entropy  [B, n] statistics of those rows (as written
  *              by dllm_vocab_stats)
  *   ring_*     [D, B, L] state; entropy_latest, t_write, stable [B, L] state
