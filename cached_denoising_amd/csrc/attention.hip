@@ -12,8 +12,9 @@
 //     S^T (keys x rows) = K . Q^T     on v_mfma_f32_16x16x32_bf16, K straight
 //                                      from HBM into the A operand
 //     online softmax in base 2        per row, state (m, l) in registers
-//     O^T (dims x rows) += V^T . P^T  V staged through a per-wave LDS tile in
-//                                      transposed (dim-major) order
+//     O^T (dims x rows) += V^T . P^T  V rows staged as stored in a per-wave
+//                                      LDS tile, read back transposed with
+//                                      ds_read_b64_tr_b16 / _tr_b8
 //   The two key tiles of a 32-key step are loaded in an interleaved order so
 //   that the S^T accumulator of a lane holds 8 consecutive keys of one row:
 //   exactly the P^T operand the second product needs, with no shuffles.
@@ -31,7 +32,6 @@ namespace dllm {
 namespace {
 
 constexpr int kNW = 4;                 // waves per MFMA workgroup
-constexpr int kVtStride = 80;          // bytes per dim row of the V^T tile (32 keys + pad)
 constexpr float kNegInf = -__builtin_inff();
 
 union Frag {
@@ -55,11 +55,51 @@ __device__ __forceinline__ uint4 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
     return r;
 }
 
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef int v2i32_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i%4
+// of the 8 bytes addressed by lane 4r + i/4, for r = 0..3
+__device__ __forceinline__ uint2 lds_tr16(const unsigned char *p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef __attribute__((address_space(3))) v4i16_t lds_v4i16;
+    const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u8 *)p);
+    return __builtin_bit_cast(uint2, r);
+#else
+    (void)p;
+    return make_uint2(0, 0);
+#endif
+}
+
+// ds_read_b64_tr_b8: within each 16-lane group, lane i receives byte i%8 of
+// the 8 bytes addressed by lane 2r + i/8, for r = 0..7
+__device__ __forceinline__ uint2 lds_tr8(const unsigned char *p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef __attribute__((address_space(3))) v2i32_t lds_v2i32;
+    const v2i32_t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32 *)(lds_u8 *)p);
+    return __builtin_bit_cast(uint2, r);
+#else
+    (void)p;
+    return make_uint2(0, 0);
+#endif
+}
+
 // key index of tile-local key k (or -1): NULL map means identity over [0, n_keys)
 __device__ __forceinline__ int key_at(const int32_t *kmap, int n_keys, int L, int j) {
     if (j >= n_keys) return -1;
     const int k = kmap ? kmap[j] : j;
     return (k >= 0 && k < L) ? k : -1;
+}
+
+// First dim of k-chunk c (8 dims) held by lane group g in the first product.
+// Any assignment works as long as Q and K agree; this one makes the four lane
+// groups of one key row read 64 contiguous bytes per load instruction.  e4m3
+// rows load two chunks (16 codes) at once, bf16 rows one chunk (8 values).
+template <int KVDT>
+__device__ __forceinline__ int chunk_dim(int c, int g) {
+    if (KVDT == DLLM_E4M3) return ((c >> 1) * 4 + g) * 16 + (c & 1) * 8;
+    return (c * 4 + g) * 8;
 }
 
 // Logical block order that keeps the row groups of one (sequence, KV head,
@@ -79,12 +119,17 @@ __global__ __launch_bounds__(kNW * kWave, RT == 2 ? 2 : 1) void attn_mfma_kernel
     float *__restrict__ lse, float *__restrict__ part_o, float *__restrict__ part_ml) {
     constexpr int NC = D / 32;           // k-chunks of the first product
     constexpr int NDT = D / 16;          // dim tiles of the second product
-    constexpr int DPG = D / 4;           // dims per lane group in the first product
     constexpr int ROWS = 16 * RT;        // rows per workgroup
-    constexpr int VBLK = D / 64;         // 4-key x 8-dim V blocks per lane per tile
     constexpr int ESZ = KVDT == DLLM_E4M3 ? 1 : 2;
+    constexpr int ROWB = D * ESZ;        // bytes of one cached row
+    constexpr int VSTR = ROWB + 32;      // LDS row stride: the transpose reads hit distinct banks
+    constexpr int CPR = ROWB / 16;       // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;        // rows per wave-wide 16-byte load
+    constexpr int VIT = 32 / RPI;        // loads per 32-key V tile
+    constexpr int SMEM = kNW * 32 * VSTR;
+    static_assert(SMEM >= 16 * RT * (D + 4) * 4, "merge buffer must fit in the V tiles");
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kNW * D * kVtStride];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
     __shared__ float sm_ml[kNW][ROWS][2];
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -111,9 +156,10 @@ __global__ __launch_bounds__(kNW * kWave, RT == 2 ? 2 : 1) void attn_mfma_kernel
         const int r = rg * ROWS + rt * 16 + l16;
         if (r < M) {
             const int gq = r / b, i = r - gq * b;
-            const uint16_t *qp = q + (((int64_t)bi * Hq + kvh * G + gq) * b + i) * D + g * DPG;
+            const uint16_t *qp = q + (((int64_t)bi * Hq + kvh * G + gq) * b + i) * D;
 #pragma unroll
-            for (int c = 0; c < NC; ++c) qf[rt][c].u = *reinterpret_cast<const uint4 *>(qp + c * 8);
+            for (int c = 0; c < NC; ++c)
+                qf[rt][c].u = *reinterpret_cast<const uint4 *>(qp + chunk_dim<KVDT>(c, g));
         } else {
 #pragma unroll
             for (int c = 0; c < NC; ++c) qf[rt][c].u = make_uint4(0, 0, 0, 0);
@@ -129,67 +175,67 @@ __global__ __launch_bounds__(kNW * kWave, RT == 2 ? 2 : 1) void attn_mfma_kernel
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) { m[rt] = kNegInf; l[rt] = 0.f; }
 
-    unsigned char *vt = smem + wave * D * kVtStride;
+    unsigned char *vt = smem + wave * 32 * VSTR;
     const int n_tiles = (n_keys + 31) / 32;
     const int t_begin = (split * kNW + wave) * tiles_per_wave;
     const int t_end = min(n_tiles, t_begin + tiles_per_wave);
 
     for (int kt = t_begin; kt < t_end; ++kt) {
         const int key0 = kt * 32;
+        // one key index (and, for e4m3, its two scales) per lane; lanes share
+        // them by shuffle.  A NULL map needs neither loads nor shuffles.
+        const int kl = key_at(kmap, n_keys, L, key0 + (lane & 31));
+        auto kidx = [&](int kappa) -> int {
+            if (kmap) return __shfl(kl, kappa, kWave);
+            return key0 + kappa < n_keys ? key0 + kappa : -1;
+        };
+        float kfl = scale_log2, vsl = 1.f;
+        if (KVDT == DLLM_E4M3) {
+            const int64_t rr = kv_base + (kl < 0 ? 0 : kl);
+            kfl = scale_log2 * ksc[rr];
+            vsl = vsc[rr];
+        }
         // ---- K into the A operand: slot l16 of tile t is key 8(l16/4) + 4t + l16%4
         Frag kf[2][NC];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const int kk = key_at(kmap, n_keys, L, key0 + 8 * (l16 >> 2) + 4 * t + (l16 & 3));
+            const int kk = kidx(8 * (l16 >> 2) + 4 * t + (l16 & 3));
             const int64_t krow = kv_base + (kk < 0 ? 0 : kk);
             if (KVDT == DLLM_E4M3) {
-                const uint8_t *kp = static_cast<const uint8_t *>(ck) + krow * D + g * DPG;
+                const uint8_t *kp = static_cast<const uint8_t *>(ck) + krow * D;
 #pragma unroll
                 for (int c = 0; c < NC; c += 2) {
-                    const uint4 w = *reinterpret_cast<const uint4 *>(kp + c * 8);
+                    const uint4 w = *reinterpret_cast<const uint4 *>(kp + chunk_dim<KVDT>(c, g));
                     kf[t][c].u = e4m3x8_to_bf16(w.x, w.y);
                     kf[t][c + 1].u = e4m3x8_to_bf16(w.z, w.w);
                 }
             } else {
-                const uint16_t *kp = static_cast<const uint16_t *>(ck) + krow * D + g * DPG;
+                const uint16_t *kp = static_cast<const uint16_t *>(ck) + krow * D;
 #pragma unroll
-                for (int c = 0; c < NC; ++c) kf[t][c].u = *reinterpret_cast<const uint4 *>(kp + c * 8);
+                for (int c = 0; c < NC; ++c)
+                    kf[t][c].u = *reinterpret_cast<const uint4 *>(kp + chunk_dim<KVDT>(c, g));
             }
         }
-        // ---- V: 4-key x 8-dim blocks, transposed into the wave's V^T tile
-        uint4 vr[VBLK][4];
+        // ---- V rows, as stored, into the wave's LDS tile (16-byte chunks;
+        // lanes of one row write consecutive chunks)
+        uint4 vr[VIT];
 #pragma unroll
-        for (int u = 0; u < VBLK; ++u) {
-            const int blk = lane + 64 * u;
-            const int oct = blk % (D / 8), q4 = blk / (D / 8);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int kk = key_at(kmap, n_keys, L, key0 + 4 * q4 + k);
-                const int64_t vrow = kv_base + (kk < 0 ? 0 : kk);
-                uint4 w;
-                if (KVDT == DLLM_E4M3) {
-                    const uint2 c2 = *reinterpret_cast<const uint2 *>(
-                        static_cast<const uint8_t *>(cv) + vrow * D + oct * 8);
-                    w = e4m3x8_to_bf16(c2.x, c2.y);
-                } else {
-                    w = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(cv) +
-                                                         vrow * D + oct * 8);
-                }
-                if (kk < 0) w = make_uint4(0, 0, 0, 0);
-                vr[u][k] = w;
-            }
+        for (int u = 0; u < VIT; ++u) {
+            const int kk = kidx(RPI * u + lane / CPR);
+            const int64_t vrow = kv_base + (kk < 0 ? 0 : kk);
+            const uint4 w = *reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(cv) +
+                                                             vrow * ROWB + (lane % CPR) * 16);
+            vr[u] = kk < 0 ? make_uint4(0, 0, 0, 0) : w;
         }
-        // keys held by this lane in the S^T accumulator: 8g .. 8g+7
-        int kkd[8];
-        float kscale[8], vscale[8];
+        // score factors and validity of the keys this lane holds in S^T: 8g .. 8g+7
+        const bool full = !kmap && key0 + 32 <= n_keys;
+        float kfac[8], vfac[8];
+        bool kval[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            kkd[e] = key_at(kmap, n_keys, L, key0 + 8 * g + e);
-            if (KVDT == DLLM_E4M3) {
-                const int64_t rr = kv_base + (kkd[e] < 0 ? 0 : kkd[e]);
-                kscale[e] = ksc[rr];
-                vscale[e] = vsc[rr];
-            }
+            kval[e] = full || kidx(8 * g + e) >= 0;
+            kfac[e] = KVDT == DLLM_E4M3 ? __shfl(kfl, 8 * g + e, kWave) : scale_log2;
+            vfac[e] = KVDT == DLLM_E4M3 ? __shfl(vsl, 8 * g + e, kWave) : 1.f;
         }
 
         // ---- S^T = K Q^T
@@ -205,26 +251,9 @@ __global__ __launch_bounds__(kNW * kWave, RT == 2 ? 2 : 1) void attn_mfma_kernel
                 s[t][rt] = acc;
             }
 
-        // ---- stage V^T (dim-major) in LDS: rows 8*oct + e, keys 4*q4 .. 4*q4+3
 #pragma unroll
-        for (int u = 0; u < VBLK; ++u) {
-            const int blk = lane + 64 * u;
-            const int oct = blk % (D / 8), q4 = blk / (D / 8);
-            const uint32_t a[4][4] = {{vr[u][0].x, vr[u][0].y, vr[u][0].z, vr[u][0].w},
-                                      {vr[u][1].x, vr[u][1].y, vr[u][1].z, vr[u][1].w},
-                                      {vr[u][2].x, vr[u][2].y, vr[u][2].z, vr[u][2].w},
-                                      {vr[u][3].x, vr[u][3].y, vr[u][3].z, vr[u][3].w}};
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                // dims 2w (low halves) and 2w+1 (high halves) of the 4 keys
-                const uint2 lo = make_uint2(__builtin_amdgcn_perm(a[1][w], a[0][w], 0x05040100u),
-                                            __builtin_amdgcn_perm(a[3][w], a[2][w], 0x05040100u));
-                const uint2 hi = make_uint2(__builtin_amdgcn_perm(a[1][w], a[0][w], 0x07060302u),
-                                            __builtin_amdgcn_perm(a[3][w], a[2][w], 0x07060302u));
-                *reinterpret_cast<uint2 *>(vt + (oct * 8 + 2 * w) * kVtStride + q4 * 8) = lo;
-                *reinterpret_cast<uint2 *>(vt + (oct * 8 + 2 * w + 1) * kVtStride + q4 * 8) = hi;
-            }
-        }
+        for (int u = 0; u < VIT; ++u)
+            *reinterpret_cast<uint4 *>(vt + (RPI * u + lane / CPR) * VSTR + (lane % CPR) * 16) = vr[u];
 
         // ---- online softmax per row (row = rt*16 + l16), keys 8g..8g+7 of this lane
         Frag pf[RT];
@@ -233,9 +262,8 @@ __global__ __launch_bounds__(kNW * kWave, RT == 2 ? 2 : 1) void attn_mfma_kernel
             float x[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                float v = s[e >> 2][rt][e & 3] * scale_log2;
-                if (KVDT == DLLM_E4M3) v *= kscale[e];
-                x[e] = kkd[e] < 0 ? kNegInf : v;
+                const float v = s[e >> 2][rt][e & 3] * kfac[e];
+                x[e] = kval[e] ? v : kNegInf;
             }
             float mx = x[0];
 #pragma unroll
@@ -263,17 +291,28 @@ __global__ __launch_bounds__(kNW * kWave, RT == 2 ? 2 : 1) void attn_mfma_kernel
             }
             if (KVDT == DLLM_E4M3) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) p[e] *= vscale[e];
+                for (int e = 0; e < 8; ++e) p[e] *= vfac[e];
             }
             pf[rt].u = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                                   pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
         }
 
-        // ---- O^T += V^T P^T
+        // ---- O^T += V^T P^T, V^T read from the row-major tile by LDS transpose reads
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
             Frag vf;
-            vf.u = *reinterpret_cast<const uint4 *>(vt + (dt * 16 + l16) * kVtStride + g * 16);
+            if (KVDT == DLLM_E4M3) {
+                // local lane j reads row 8g + j/2, codes dt*16 + 8(j%2) .. +7; lane i
+                // then holds codes of keys 8g .. 8g+7 at dim dt*16 + i
+                const uint2 c8 = lds_tr8(vt + (8 * g + (l16 >> 1)) * VSTR + dt * 16 + 8 * (l16 & 1));
+                vf.u = e4m3x8_to_bf16(c8.x, c8.y);
+            } else {
+                // two reads of 4 keys each: local lane j reads row 8g + 4h + j/4,
+                // dims dt*16 + 4(j%4) .. +3; lane i then holds keys 8g+4h .. +3 at dim dt*16 + i
+                const uint2 lo = lds_tr16(vt + (8 * g + (l16 >> 2)) * VSTR + dt * 32 + 8 * (l16 & 3));
+                const uint2 hi = lds_tr16(vt + (8 * g + 4 + (l16 >> 2)) * VSTR + dt * 32 + 8 * (l16 & 3));
+                vf.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            }
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
                 o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.v, pf[rt].v, o[dt][rt], 0, 0, 0);
@@ -540,7 +579,7 @@ int plan_attention(const dllm_kv_cache &c, int q_dtype, int Hq, int b, int n_key
     }
     p->path = 1;
     p->waves = kNW;
-    p->row_tiles = M > 32 ? 4 : 2;
+    p->row_tiles = 2;                    // 32 rows per workgroup
     p->row_groups = cdiv(M, 16 * p->row_tiles);
     const int64_t units = (int64_t)c.B * c.n_kv_heads * p->row_groups;
     const int n_tiles = cdiv(n_keys, 32);
@@ -564,16 +603,12 @@ int launch_attention(const dllm_kv_cache &c, const AttnPlan &p, const void *q, i
         return launch_status();
     }
     const bool e4 = c.dtype == DLLM_E4M3;
-    const bool rt4 = p.row_tiles == 4;
     if (c.d_head == 128) {
-        if (e4) return rt4 ? launch_mfma<128, DLLM_E4M3, 4>(c, p, q, Hq, b, key_idx, n_keys, scale, out, out_dtype, lse, ws, s)
-                           : launch_mfma<128, DLLM_E4M3, 2>(c, p, q, Hq, b, key_idx, n_keys, scale, out, out_dtype, lse, ws, s);
-        return rt4 ? launch_mfma<128, DLLM_BF16, 4>(c, p, q, Hq, b, key_idx, n_keys, scale, out, out_dtype, lse, ws, s)
-                   : launch_mfma<128, DLLM_BF16, 2>(c, p, q, Hq, b, key_idx, n_keys, scale, out, out_dtype, lse, ws, s);
+        if (e4) return launch_mfma<128, DLLM_E4M3, 2>(c, p, q, Hq, b, key_idx, n_keys, scale, out, out_dtype, lse, ws, s);
+        return launch_mfma<128, DLLM_BF16, 2>(c, p, q, Hq, b, key_idx, n_keys, scale, out, out_dtype, lse, ws, s);
     }
     if (e4) return DLLM_ESHAPE;                 // e4m3 needs d % 128 == 0
-    return rt4 ? launch_mfma<64, DLLM_BF16, 4>(c, p, q, Hq, b, key_idx, n_keys, scale, out, out_dtype, lse, ws, s)
-               : launch_mfma<64, DLLM_BF16, 2>(c, p, q, Hq, b, key_idx, n_keys, scale, out, out_dtype, lse, ws, s);
+    return launch_mfma<64, DLLM_BF16, 2>(c, p, q, Hq, b, key_idx, n_keys, scale, out, out_dtype, lse, ws, s);
 }
 
 }  // namespace dllm

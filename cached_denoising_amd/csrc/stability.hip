@@ -16,8 +16,8 @@ namespace dllm {
 namespace {
 
 constexpr int kThreads = 1024;
-constexpr int kMaxL = 131072;      // seed bits + counts stay within 32 KB of LDS
-constexpr int kMaxWords = kMaxL / 32;
+constexpr int kMaxL = 131072;      // seed bits stay within 16 KB of LDS
+constexpr int kWaves = kThreads / kWave;
 
 __global__ __launch_bounds__(256) void stability_reset_kernel(
     int64_t ring_n, int64_t n, int32_t *__restrict__ ring_argmax, float *__restrict__ ring_maxprob,
@@ -47,118 +47,114 @@ __global__ __launch_bounds__(kThreads) void stability_kernel(
     double lambda, double conf_thresh, double hmax, uint8_t *__restrict__ mask,
     float *__restrict__ conf, int32_t *__restrict__ next_pos, int32_t *__restrict__ count,
     uint8_t *__restrict__ all_stable) {
-    extern __shared__ uint32_t seed_bits[];            // [words] seeds, then [words + 1] scan
+    extern __shared__ uint32_t seed_bits[];            // one bit per position
     __shared__ int any_seed;
+    __shared__ int wave_cnt[kWaves];
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
     const int64_t rowoff = (int64_t)b * L;
     const int64_t plane = (int64_t)B * L;              // one ring slot
     const int slot = step % D;
-    const int words = (L + 31) >> 5;
-    uint32_t *scan = seed_bits + words;
 
     if (tid == 0) any_seed = 0;
 
-    // 1-2: record this step and test the recomputed positions
+    // 1-2: record this step, then test the recomputed positions.  Every load
+    // of a position is independent of the others, so they are all in flight
+    // together; K is small.
     for (int j = tid; j < n; j += kThreads) {
         const int p = pos ? pos[(int64_t)b * n + j] : j;
         if (p < 0 || p >= L) continue;
         const int64_t src = (int64_t)b * n + j;
-        const int64_t ri = slot * plane + rowoff + p;
         const int tok = argmax[src];
-        ring_argmax[ri] = tok;
-        ring_maxprob[ri] = maxprob[src];
-        ring_step[ri] = step;
-        entropy_latest[rowoff + p] = entropy[src];
-        t_write[rowoff + p] = step;
-        if (stable[rowoff + p] || step + 1 < K) continue;
+        const float mp = maxprob[src];
+        const float en = entropy[src];
+        const uint8_t was_stable = stable[rowoff + p];
+        const bool test = !was_stable && step + 1 >= K;
         bool same = true;
         double sum = 0.0;
-        for (int k = K - 1; k >= 0; --k) {             // oldest record first
-            const int64_t rk = (int64_t)((step - k) % D) * plane + rowoff + p;
-            if (ring_step[rk] != step - k || ring_argmax[rk] != tok) { same = false; break; }
-            sum += (double)ring_maxprob[rk];
+        if (test) {
+            for (int k = K - 1; k >= 1; --k) {         // oldest record first
+                const int64_t rk = (int64_t)((step - k) % D) * plane + rowoff + p;
+                const int rs = ring_step[rk];
+                const int ra = ring_argmax[rk];
+                const float rp = ring_maxprob[rk];
+                same = same && rs == step - k && ra == tok;
+                sum += (double)rp;
+            }
+            sum += (double)mp;                         // this step's record last
         }
-        if (same && sum / (double)K > tau) stable[rowoff + p] = 1;
+        const int64_t ri = slot * plane + rowoff + p;
+        ring_argmax[ri] = tok;
+        ring_maxprob[ri] = mp;
+        ring_step[ri] = step;
+        entropy_latest[rowoff + p] = en;
+        t_write[rowoff + p] = step;
+        if (test && same && sum / (double)K > tau) stable[rowoff + p] = 1;
     }
     __syncthreads();
 
-    // 3-4a: confidence and the seed bit of every position, 32 per word
-    for (int w = tid; w < words; w += kThreads) {
-        uint32_t bits = 0;
-        const int i0 = w * 32;
-        const int i1 = min(L, i0 + 32);
-        for (int i = i0; i < i1; ++i) {
+    // 3-4a: confidence and the seed bit of every position (one per thread)
+    for (int i0 = 0; i0 < L; i0 += kThreads) {
+        const int i = i0 + tid;
+        bool seed = false;
+        if (i < L) {
             const double h = (double)entropy_latest[rowoff + i];
             const double dt = (double)(step - t_write[rowoff + i]);
+            const bool st = stable[rowoff + i] != 0;
             const double cf = alpha * (1.0 - h / hmax) + beta * exp(-lambda * dt);
             if (conf) conf[rowoff + i] = (float)cf;
-            if (!stable[rowoff + i] || cf < conf_thresh) bits |= 1u << (i - i0);
+            seed = !st || cf < conf_thresh;
         }
-        seed_bits[w] = bits;
-        if (bits) any_seed = 1;
+        const uint64_t bal = __ballot(seed);
+        if (lane == 0) {
+            const int w = (i0 >> 5) + wave * 2;         // two 32-bit words per wave
+            seed_bits[w] = (uint32_t)bal;
+            seed_bits[w + 1] = (uint32_t)(bal >> 32);
+            if (bal) any_seed = 1;
+        }
     }
     __syncthreads();
     const bool none = any_seed == 0;
 
-    // 4b: window expansion, and the number of mask positions per word
-    for (int w = tid; w < words; w += kThreads) {
-        const int i0 = w * 32;
-        uint32_t mbits = 0;
-        if (none) {
-            mbits = 0xffffffffu;
-        } else {
-            for (int e = 0; e < 32; ++e) {
-                const int i = i0 + e;
+    // 4b-5: window test per position, then ascending compaction, 1024 at a time
+    int base = 0;
+    for (int i0 = 0; i0 < L; i0 += kThreads) {
+        const int i = i0 + tid;
+        bool on = false;
+        if (i < L) {
+            if (none) {
+                on = true;
+            } else {
                 const int lo = max(0, i - R), hi = min(L - 1, i + R);
-                if (lo > hi) continue;
                 const int wl = lo >> 5, wh = hi >> 5;
-                bool hit = false;
-                for (int q = wl; q <= wh && !hit; ++q) {
+                for (int q = wl; q <= wh && !on; ++q) {
                     uint32_t m = seed_bits[q];
                     if (q == wl) m &= 0xffffffffu << (lo & 31);
                     if (q == wh && (hi & 31) != 31) m &= (1u << ((hi & 31) + 1)) - 1u;
-                    hit = m != 0;
+                    on = m != 0;
                 }
-                if (hit) mbits |= 1u << e;
             }
-        }
-        const int i1 = min(L, i0 + 32);
-        if (i1 - i0 < 32) mbits &= (1u << (i1 - i0)) - 1u;
-        scan[w + 1] = mbits;                           // kept until the counts are scanned
-    }
-    __syncthreads();
-
-    // 5: compaction.  Thread t owns words [t*per, (t+1)*per); an exclusive
-    // scan of the per-thread counts gives each its first output slot.
-    const int per = (words + kThreads - 1) / kThreads;
-    const int w0 = tid * per, w1 = min(words, w0 + per);
-    int local = 0;
-    for (int w = w0; w < w1; ++w) local += __popc(scan[w + 1]);
-    __shared__ int tsum[kThreads];
-    tsum[tid] = local;
-    __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {     // Hillis-Steele inclusive scan
-        const int v = tid >= off ? tsum[tid - off] : 0;
-        __syncthreads();
-        tsum[tid] += v;
-        __syncthreads();
-    }
-    int out = tsum[tid] - local;
-    for (int w = w0; w < w1; ++w) {
-        const uint32_t mbits = scan[w + 1];
-        const int i0 = w * 32;
-        const int i1 = min(L, i0 + 32);
-        for (int i = i0; i < i1; ++i) {
-            const bool on = (mbits >> (i - i0)) & 1u;
             mask[rowoff + i] = on ? 1 : 0;
-            if (on) next_pos[rowoff + out++] = i;
         }
+        const uint64_t bal = __ballot(on);
+        if (lane == 0) wave_cnt[wave] = __popcll(bal);
+        __syncthreads();
+        int off = base;
+        for (int w = 0; w < wave; ++w) off += wave_cnt[w];
+        int chunk_total = 0;
+        for (int w = 0; w < kWaves; ++w) chunk_total += wave_cnt[w];
+        if (on) {
+            const uint64_t below = lane ? (bal & ((~0ull) >> (64 - lane))) : 0ull;
+            next_pos[rowoff + off + __popcll(below)] = i;
+        }
+        base += chunk_total;
+        __syncthreads();                               // wave_cnt is reused
     }
-    const int total = tsum[kThreads - 1];
-    for (int i = total + tid; i < L; i += kThreads) next_pos[rowoff + i] = -1;
+    for (int i = base + tid; i < L; i += kThreads) next_pos[rowoff + i] = -1;
     if (tid == 0) {
-        count[b] = total;
+        count[b] = base;
         all_stable[b] = none ? 1 : 0;
     }
 }
@@ -182,8 +178,8 @@ int launch_stability(int B, int L, int step, const int32_t *pos, int n, const in
                      uint8_t *mask, float *conf, int32_t *next_pos, int32_t *count,
                      uint8_t *all_stable, hipStream_t s) {
     if (L > kMaxL) return DLLM_ERANGE;
-    const int words = (L + 31) / 32;
-    const size_t shmem = sizeof(uint32_t) * (size_t)(2 * words + 1);
+    const int words = cdiv(L, kThreads) * (kThreads / 32);   // whole 1024-position chunks
+    const size_t shmem = sizeof(uint32_t) * (size_t)words;
     stability_kernel<<<dim3((unsigned)B), dim3(kThreads), shmem, s>>>(
         B, L, step, pos, n, argmax, maxprob, entropy, ring_argmax, ring_maxprob, ring_step,
         entropy_latest, t_write, stable, prm.K, prm.D, prm.R, prm.tau, prm.alpha, prm.beta,

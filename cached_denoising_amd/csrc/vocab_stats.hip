@@ -4,7 +4,7 @@
 // its token; Flash-dLLM page, 3.1: entropy of the step's distribution.]
 //
 // One workgroup of 256 threads streams one row (or one contiguous split of
-// a row) with 16-byte loads; the few elements before the first 16-byte
+// a row) with non-temporal 16-byte loads, two in flight per thread; the few elements before the first 16-byte
 // boundary and after the last are peeled off.  Each thread keeps an online
 // state over base-2 exponents a_j = (x_j - m) log2(e):
 //     m = running max,  s = sum 2^a_j,  t = sum 2^a_j a_j,  idx = argmax
@@ -19,13 +19,21 @@ namespace dllm {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 2;      // 16-byte loads in flight per thread per step
 constexpr float kNegInf = -__builtin_inff();
 
 struct Acc {
     float m, s, t;
     int idx;
 };
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// streaming 16-byte load: the logits are read once, so keep them out of the caches' way
+__device__ __forceinline__ uint4 load_stream(const uint4 *p) {
+    const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
 
 __device__ __forceinline__ Acc acc_empty() { return Acc{kNegInf, 0.f, 0.f, INT_MAX}; }
 
@@ -178,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void vocab_stats_kernel(
         for (; v + (kUnroll - 1) * kThreads < nvec; v += kUnroll * kThreads) {
             uint4 w[kUnroll];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) w[u] = vp[v + u * kThreads];
+            for (int u = 0; u < kUnroll; ++u) w[u] = load_stream(vp + v + u * kThreads);
             float x[kUnroll * kVec];
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) E::unpack(w[u], x + u * kVec);
@@ -187,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void vocab_stats_kernel(
             });
         }
         for (; v < nvec; v += kThreads) {
-            const uint4 w = vp[v];
+            const uint4 w = load_stream(vp + v);
             float x[kVec];
             E::unpack(w, x);
             consume<kVec>(st, x, [&](int e) { return (int)(a0 + v * kVec + e); });
