@@ -34,6 +34,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="gpt2", choices=["gpt2", "llada", "vocab", "longctx"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every kernel from Python instead of replaying a captured graph")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (HBM counter calibration)")
     return ap.parse_args()
@@ -118,7 +120,9 @@ class Step:
             self.st = D.StabilityState(B, L, cfg.D, device=dev)
             self.kw = dict(K=cfg.K, tau=cfg.tau, R=cfg.R, alpha=cfg.alpha, beta=cfg.beta,
                            lam=cfg.lam, conf_thresh=cfg.conf_thresh, V=cfg.V)
-        self.step_no = 0
+        # the decode step number lives on the device, so a captured graph of
+        # several steps replays successive steps
+        self.step_t = torch.zeros(1, dtype=torch.int32, device=dev)
 
     def kernels(self):
         ks = []
@@ -153,10 +157,10 @@ class Step:
         if self.has_stab:
             mark("stability", 0)
             B, L = cfg.B, cfg.L
-            D.dllm_stability_mask(self.st, self.step_no, None, self.am.view(B, L), self.mp.view(B, L),
+            D.dllm_stability_mask(self.st, self.step_t, None, self.am.view(B, L), self.mp.view(B, L),
                                   self.en.view(B, L), **self.kw)
             mark("stability", 1)
-        self.step_no += 1
+            self.step_t.add_(1)
 
     def algorithmic_bytes(self):
         """bytes each kernel must move (reads + writes), per launch"""
@@ -260,15 +264,38 @@ def main():
               for n in names}
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    graph = None
+    if not args.eager:
+        # the K timed steps, with their per-kernel events, as one HIP graph:
+        # no launch gaps between the kernels of a step or between steps
+        # (timing events cannot be recorded inside a graph on ROCm; the kernels
+        # are timed in an eager pass of the same steps after the timed region)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                step.run()
+        torch.cuda.synchronize()
+        graph.replay()                      # one untimed replay
+        torch.cuda.synchronize()
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record()
-    for i in range(args.steps):
-        step.run({n: events[n][i] for n in names})
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step.run({n: events[n][i] for n in names})
     end.record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms = start.elapsed_time(end) / args.steps
+    if graph is None:
+        kernel_timing = "HIP events on the launch stream, in the timed region"
+    else:
+        kernel_timing = "HIP events on the launch stream, eager pass of the same steps after the timed region"
+        for i in range(args.steps):
+            step.run({n: events[n][i] for n in names})
+        torch.cuda.synchronize()
     per_kernel_us = {n: 1000.0 * sum(e[0].elapsed_time(e[1]) for e in events[n]) / args.steps
                      for n in names}
     alg = step.algorithmic_bytes()
@@ -279,7 +306,7 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(args.config) if dom == "vocab_stats" else None,
                 "kernel": dom, "algorithmic_bytes_per_launch": alg[dom],
-                "avg_launch_us": round(dom_us, 2)}
+                "avg_launch_us": round(dom_us, 2), "kernel_timing": kernel_timing}
     cpu = None if args.no_cpu_baseline else cpu_baseline(step, D, W, cfg)
     desc = {
         "gpt2": "GPT-2-small-shaped decode step: B=8, L=1024, 12 heads x d64, bf16 K/V cache, "
@@ -297,7 +324,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": desc, "name": cfg.name, "B": cfg.B, "L": cfg.L, "heads": cfg.Hq,
-                   "kv_heads": cfg.Hkv, "d_head": cfg.d, "block": cfg.b, "vocab": cfg.V},
+                   "kv_heads": cfg.Hkv, "d_head": cfg.d, "block": cfg.b, "vocab": cfg.V,
+                   "launch": "eager" if graph is None else "hip graph of the timed steps"},
         "kernels_us": {n: round(v, 2) for n, v in per_kernel_us.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -73,7 +73,7 @@ EXPORTS = {
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_void_p]),
-    "dllm_stability_mask": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+    "dllm_stability_mask": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                            ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -264,17 +264,23 @@ def dllm_stability_reset(st: StabilityState):
     _check(rc, "dllm_stability_reset")
 
 
-def dllm_stability_mask(st: StabilityState, step: int, pos: Optional[torch.Tensor],
+def dllm_stability_mask(st: StabilityState, step, pos: Optional[torch.Tensor],
                         argmax: torch.Tensor, maxprob: torch.Tensor, entropy: torch.Tensor, *,
                         K: int, tau: float, R: int, alpha: float = 0.0, beta: float = 0.0,
                         lam: float = 0.0, conf_thresh: float = 0.0, V: int = 2,
                         with_conf: bool = True):
     """One step of history, stability, confidence and window mask; outputs
-    land in st.mask, st.conf, st.next_pos, st.count, st.all_stable."""
+    land in st.mask, st.conf, st.next_pos, st.count, st.all_stable.  ``step``
+    is an int, or a one-element int32 GPU tensor read when the kernel runs
+    (for captured graphs)."""
     n = pos.shape[1] if pos is not None else st.L
     prm = _StabParams(K=K, D=st.D, R=R, reserved=0, tau=tau, alpha=alpha, beta=beta, lam=lam,
                       conf_thresh=conf_thresh, vocab=V)
-    rc = lib().dllm_stability_mask(st.B, st.L, int(step), _dev(pos, "pos"), n, _dev(argmax, "argmax"),
+    if isinstance(step, torch.Tensor):
+        step_host, step_dev = 0, _dev(step, "step")
+    else:
+        step_host, step_dev = int(step), None
+    rc = lib().dllm_stability_mask(st.B, st.L, step_host, step_dev, _dev(pos, "pos"), n, _dev(argmax, "argmax"),
                                    _dev(maxprob, "maxprob"), _dev(entropy, "entropy"),
                                    _dev(st.ring_argmax, "ring_argmax"), _dev(st.ring_maxprob, "ring_maxprob"),
                                    _dev(st.ring_step, "ring_step"), _dev(st.entropy_latest, "entropy_latest"),

@@ -114,7 +114,7 @@ size_t dllm_block_attention_workspace(const dllm_kv_cache *cache, int q_dtype, i
     if (check_cache(cache) != DLLM_OK || Hq < 1 || b < 1 || n_keys < 1) return 0;
     if (Hq % cache->n_kv_heads != 0) return 0;
     AttnPlan p;
-    if (plan_attention(*cache, q_dtype, Hq, b, n_keys, &p) != DLLM_OK) return 0;
+    if (plan_attention(*cache, q_dtype, Hq, b, n_keys, true, &p) != DLLM_OK) return 0;
     return p.ws_bytes;
 }
 
@@ -135,7 +135,8 @@ int dllm_block_attention(const dllm_kv_cache *cache, const void *q, int q_dtype,
     if (scale == 0.f) scale = 1.0f / std::sqrt((float)cache->d_head);
     if ((int64_t)cache->B * Hq * b > INT32_MAX / 4) return DLLM_ERANGE;
     AttnPlan p;
-    if ((rc = plan_attention(*cache, q_dtype, Hq, b, n_keys, &p)) != DLLM_OK) return rc;
+    if ((rc = plan_attention(*cache, q_dtype, Hq, b, n_keys, key_idx != nullptr, &p)) != DLLM_OK)
+        return rc;
     if (p.path == 1 && (!aligned16(q) || !aligned16(out))) return DLLM_EALIGN;
     if (p.ws_bytes > 0 && (!workspace || ws_bytes < p.ws_bytes || !aligned16(workspace)))
         return DLLM_EWORKSPACE;
@@ -174,7 +175,7 @@ int dllm_stability_reset(int B, int L, int D, int32_t *ring_argmax, float *ring_
                                   t_write, stable, static_cast<hipStream_t>(stream));
 }
 
-int dllm_stability_mask(int B, int L, int step, const int32_t *pos, int n,
+int dllm_stability_mask(int B, int L, int step, const int32_t *step_dev, const int32_t *pos, int n,
                         const int32_t *argmax, const float *maxprob, const float *entropy,
                         int32_t *ring_argmax, float *ring_maxprob, int32_t *ring_step,
                         float *entropy_latest, int32_t *t_write, uint8_t *stable,
@@ -196,7 +197,7 @@ int dllm_stability_mask(int B, int L, int step, const int32_t *pos, int n,
         return DLLM_EINVAL;
     // maximum entropy of a vocab-V distribution, computed once on the host
     const double hmax = std::log((double)p.vocab);
-    return launch_stability(B, L, step, pos, n, argmax, maxprob, entropy, ring_argmax,
+    return launch_stability(B, L, step, step_dev, pos, n, argmax, maxprob, entropy, ring_argmax,
                             ring_maxprob, ring_step, entropy_latest, t_write, stable, p, hmax,
                             mask, conf, next_pos, count, all_stable,
                             static_cast<hipStream_t>(stream));

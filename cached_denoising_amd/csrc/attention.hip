@@ -33,6 +33,9 @@ namespace {
 
 constexpr int kNW = 4;                 // waves per MFMA workgroup
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kLazy = 8.0f;          // log2 headroom before the running max moves
+constexpr float kMinit = -1.0e30f;     // finite start of the running max
+constexpr int kMaxMapTiles = 64;       // 32-key tiles per wave when a key map is given
 
 union Frag {
     uint4 u;
@@ -85,6 +88,36 @@ __device__ __forceinline__ uint2 lds_tr8(const unsigned char *p) {
 #endif
 }
 
+// 16 bytes from global memory straight into LDS: lane i of the wave writes
+// lds_base + 16 i (lds_base is wave-uniform).  NT marks the load
+// non-temporal: right when the rows are read once, wrong when other
+// workgroups re-read them through L2.
+template <bool NT>
+__device__ __forceinline__ void lds_dma16(const unsigned char *src, unsigned char *lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(lds_u8 *)lds_base, 16, 0,
+                                     NT ? 2 : 0);
+#else
+    (void)src;
+    (void)lds_base;
+#endif
+}
+
+// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// XOR swizzle of the 16-byte chunks of V row rho in LDS: the rows a 16-lane
+// transposed read touches land on distinct banks (bf16: 4 rows, 32-byte
+// windows; e4m3: 8 rows, 16-byte windows, two rows per 256 bytes)
+template <int KVDT>
+__device__ __forceinline__ int vswz(int rho) {
+    return KVDT == DLLM_E4M3 ? ((rho >> 1) & 3) : 2 * (rho & 3);
+}
+
 // key index of tile-local key k (or -1): NULL map means identity over [0, n_keys)
 __device__ __forceinline__ int key_at(const int32_t *kmap, int n_keys, int L, int j) {
     if (j >= n_keys) return -1;
@@ -110,8 +143,8 @@ __device__ __forceinline__ int xcd_remap(int pid, int nblk) {
     return (pid & 7) * per + (pid >> 3);
 }
 
-template <int D, int KVDT, int RT>
-__global__ __launch_bounds__(kNW * kWave, RT == 2 ? 2 : 1) void attn_mfma_kernel(
+template <int D, int KVDT, int RT, bool MAP, bool NT>
+__global__ __launch_bounds__(kNW * kWave, 2) void attn_mfma_kernel(
     const void *__restrict__ ck, const void *__restrict__ cv, const float *__restrict__ ksc,
     const float *__restrict__ vsc, const uint16_t *__restrict__ q, int Hq, int Hkv, int L, int b,
     int G, const int32_t *__restrict__ key_idx, int n_keys, float scale_log2, int row_groups,
@@ -122,12 +155,15 @@ __global__ __launch_bounds__(kNW * kWave, RT == 2 ? 2 : 1) void attn_mfma_kernel
     constexpr int ROWS = 16 * RT;        // rows per workgroup
     constexpr int ESZ = KVDT == DLLM_E4M3 ? 1 : 2;
     constexpr int ROWB = D * ESZ;        // bytes of one cached row
-    constexpr int VSTR = ROWB + 32;      // LDS row stride: the transpose reads hit distinct banks
     constexpr int CPR = ROWB / 16;       // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;        // rows per wave-wide 16-byte load
     constexpr int VIT = 32 / RPI;        // loads per 32-key V tile
-    constexpr int SMEM = kNW * 32 * VSTR;
-    static_assert(SMEM >= 16 * RT * (D + 4) * 4, "merge buffer must fit in the V tiles");
+    constexpr int QSTR = D * 2 + 16;     // LDS row stride of Q: 16 rows of one read hit distinct banks
+    constexpr int QBYTES = ROWS * QSTR;
+    constexpr int VTILE = 32 * ROWB;     // one V tile in LDS
+    constexpr int TAB = MAP ? kNW * kMaxMapTiles * 32 * 4 : 0;   // per-wave key index tables
+    constexpr int SMEM = QBYTES + kNW * 2 * VTILE + TAB;
+    static_assert(SMEM >= ROWS * (D + 4) * 4, "merge buffer must fit in the staging area");
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
     __shared__ float sm_ml[kNW][ROWS][2];
@@ -147,24 +183,22 @@ __global__ __launch_bounds__(kNW * kWave, RT == 2 ? 2 : 1) void attn_mfma_kernel
     const int M = G * b;                 // rows of this (sequence, KV head)
 
     const int64_t kv_base = ((int64_t)bi * Hkv + kvh) * L;
-    const int32_t *kmap = key_idx ? key_idx + (int64_t)bi * n_keys : nullptr;
+    const int32_t *kmap = MAP ? key_idx + (int64_t)bi * n_keys : nullptr;
 
-    // ---- queries: B operand of S^T = K Q^T, kept for the whole kernel ----
-    Frag qf[RT][NC];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const int r = rg * ROWS + rt * 16 + l16;
-        if (r < M) {
-            const int gq = r / b, i = r - gq * b;
-            const uint16_t *qp = q + (((int64_t)bi * Hq + kvh * G + gq) * b + i) * D;
-#pragma unroll
-            for (int c = 0; c < NC; ++c)
-                qf[rt][c].u = *reinterpret_cast<const uint4 *>(qp + chunk_dim<KVDT>(c, g));
-        } else {
-#pragma unroll
-            for (int c = 0; c < NC; ++c) qf[rt][c].u = make_uint4(0, 0, 0, 0);
+    // ---- queries: the B operand of S^T = K Q^T.  All waves of the workgroup
+    // use the same rows, so they are staged once in LDS; rows past M are zero.
+    unsigned char *qs = smem;
+    for (int idx = threadIdx.x; idx < ROWS * (D / 8); idx += kNW * kWave) {
+        const int r = idx / (D / 8), c8 = idx % (D / 8);
+        const int rr = rg * ROWS + r;
+        uint4 w = make_uint4(0, 0, 0, 0);
+        if (rr < M) {
+            const int gq = rr / b, i = rr - gq * b;
+            w = *reinterpret_cast<const uint4 *>(q + (((int64_t)bi * Hq + kvh * G + gq) * b + i) * D + c8 * 8);
         }
+        *reinterpret_cast<uint4 *>(qs + r * QSTR + c8 * 16) = w;
     }
+    __syncthreads();
 
     f32x4_t o[NDT][RT];
 #pragma unroll
@@ -173,122 +207,164 @@ __global__ __launch_bounds__(kNW * kWave, RT == 2 ? 2 : 1) void attn_mfma_kernel
         for (int rt = 0; rt < RT; ++rt) o[dt][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m[RT], l[RT];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) { m[rt] = kNegInf; l[rt] = 0.f; }
+    for (int rt = 0; rt < RT; ++rt) { m[rt] = kMinit; l[rt] = 0.f; }
 
-    unsigned char *vt = smem + wave * 32 * VSTR;
+    unsigned char *vbase = smem + QBYTES + wave * 2 * VTILE;
     const int n_tiles = (n_keys + 31) / 32;
     const int t_begin = (split * kNW + wave) * tiles_per_wave;
     const int t_end = min(n_tiles, t_begin + tiles_per_wave);
 
-    for (int kt = t_begin; kt < t_end; ++kt) {
-        const int key0 = kt * 32;
-        // one key index (and, for e4m3, its two scales) per lane; lanes share
-        // them by shuffle.  A NULL map needs neither loads nor shuffles.
-        const int kl = key_at(kmap, n_keys, L, key0 + (lane & 31));
-        auto kidx = [&](int kappa) -> int {
-            if (kmap) return __shfl(kl, kappa, kWave);
-            return key0 + kappa < n_keys ? key0 + kappa : -1;
-        };
-        float kfl = scale_log2, vsl = 1.f;
-        if (KVDT == DLLM_E4M3) {
-            const int64_t rr = kv_base + (kl < 0 ? 0 : kl);
-            kfl = scale_log2 * ksc[rr];
-            vsl = vsc[rr];
-        }
-        // ---- K into the A operand: slot l16 of tile t is key 8(l16/4) + 4t + l16%4
-        Frag kf[2][NC];
+    // Software pipeline, one tile deep.  While tile t is computed, tile t+1 is
+    // in flight: its K rows into the other register set, its V rows straight
+    // from HBM into the wave's other LDS buffer (global_load_lds_dwordx4, no
+    // registers).  Direct-to-LDS loads fill 1 KB per instruction in lane
+    // order, so the V rows are unpadded and their 16-byte chunks are
+    // XOR-swizzled per row instead, which keeps the transposed reads of one
+    // 16-lane group on distinct banks.
+    constexpr int KR = KVDT == DLLM_E4M3 ? NC / 2 : NC;   // 16-byte K loads per 16-key half
+    // vector-memory loads issued for one tile, in order: the map index,
+    // K rows, V rows, e4m3 scales
+    constexpr int LOADS = 2 * KR + VIT + (KVDT == DLLM_E4M3 ? 2 : 0);
+    struct Tile {
+        uint4 kr[2][KR];      // K rows as loaded (A operand of S^T = K Q^T)
+        int kl;               // key index of tile-local key lane % 32 (-1: none)
+        float kfl, vsl;       // its score factor and (e4m3) value scale
+    };
+
+    // With a key map, this wave's indices are copied once into its LDS table
+    // (tiles_per_wave <= kMaxMapTiles); without one, key j of the selection is
+    // position j.  Either way the index of tile-local key kappa is cheap.
+    int *ktab = reinterpret_cast<int *>(smem + QBYTES + kNW * 2 * VTILE) + wave * kMaxMapTiles * 32;
+    if (MAP) {
+        for (int j = lane; j < (t_end - t_begin) * 32; j += kWave)
+            ktab[j] = key_at(kmap, n_keys, L, t_begin * 32 + j);
+        __builtin_amdgcn_s_waitcnt(0);           // the table is in LDS before it is read
+        __builtin_amdgcn_wave_barrier();
+    }
+    auto key_of = [&](int kt, int kappa) -> int {
+        if (MAP) return ktab[(kt - t_begin) * 32 + kappa];
+        return kt * 32 + kappa < n_keys ? kt * 32 + kappa : -1;
+    };
+    auto issue = [&](int kt, Tile &T, unsigned char *vbuf) {
+        T.kl = key_of(kt, lane & 31);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const int kk = kidx(8 * (l16 >> 2) + 4 * t + (l16 & 3));
-            const int64_t krow = kv_base + (kk < 0 ? 0 : kk);
-            if (KVDT == DLLM_E4M3) {
-                const uint8_t *kp = static_cast<const uint8_t *>(ck) + krow * D;
+            // slot l16 of half t is key 8(l16/4) + 4t + l16%4
+            const int kk = key_of(kt, 8 * (l16 >> 2) + 4 * t + (l16 & 3));
+            const unsigned char *kp = static_cast<const unsigned char *>(ck) + (kv_base + (kk < 0 ? 0 : kk)) * ROWB;
 #pragma unroll
-                for (int c = 0; c < NC; c += 2) {
-                    const uint4 w = *reinterpret_cast<const uint4 *>(kp + chunk_dim<KVDT>(c, g));
-                    kf[t][c].u = e4m3x8_to_bf16(w.x, w.y);
-                    kf[t][c + 1].u = e4m3x8_to_bf16(w.z, w.w);
-                }
-            } else {
-                const uint16_t *kp = static_cast<const uint16_t *>(ck) + krow * D;
-#pragma unroll
-                for (int c = 0; c < NC; ++c)
-                    kf[t][c].u = *reinterpret_cast<const uint4 *>(kp + chunk_dim<KVDT>(c, g));
+            for (int cc = 0; cc < KR; ++cc) {
+                const int cd = KVDT == DLLM_E4M3 ? 2 * cc : cc;
+                T.kr[t][cc] = *reinterpret_cast<const uint4 *>(kp + chunk_dim<KVDT>(cd, g) * ESZ);
             }
         }
-        // ---- V rows, as stored, into the wave's LDS tile (16-byte chunks;
-        // lanes of one row write consecutive chunks)
-        uint4 vr[VIT];
 #pragma unroll
         for (int u = 0; u < VIT; ++u) {
-            const int kk = kidx(RPI * u + lane / CPR);
-            const int64_t vrow = kv_base + (kk < 0 ? 0 : kk);
-            const uint4 w = *reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(cv) +
-                                                             vrow * ROWB + (lane % CPR) * 16);
-            vr[u] = kk < 0 ? make_uint4(0, 0, 0, 0) : w;
+            // this lane fills chunk slot lane % CPR of row RPI*u + lane / CPR
+            const int rho = RPI * u + lane / CPR;
+            const int chunk = (lane % CPR) ^ vswz<KVDT>(rho);
+            const int kk = key_of(kt, rho);
+            const unsigned char *src = static_cast<const unsigned char *>(cv) +
+                                       (kv_base + (kk < 0 ? 0 : kk)) * ROWB + chunk * 16;
+            lds_dma16<NT>(src, vbuf + u * 1024);
         }
-        // score factors and validity of the keys this lane holds in S^T: 8g .. 8g+7
-        const bool full = !kmap && key0 + 32 <= n_keys;
+        T.kfl = scale_log2;
+        T.vsl = 1.f;
+        if (KVDT == DLLM_E4M3) {
+            const int64_t rr = kv_base + (T.kl < 0 ? 0 : T.kl);
+            T.kfl = scale_log2 * ksc[rr];
+            T.vsl = vsc[rr];
+        }
+    };
+
+    auto compute = [&](int kt, const Tile &T, const unsigned char *vt) {
+        // per-key factors of the keys this lane holds in S^T (8g .. 8g+7), and
+        // whether every key of the tile is present (then nothing is masked)
+        const bool full = MAP ? (__ballot(T.kl >= 0) == ~0ull) : (kt * 32 + 32 <= n_keys);
         float kfac[8], vfac[8];
+        if (KVDT == DLLM_E4M3) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                kfac[e] = __shfl(T.kfl, 8 * g + e, kWave);
+                vfac[e] = __shfl(T.vsl, 8 * g + e, kWave);
+            }
+        }
         bool kval[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            kval[e] = full || kidx(8 * g + e) >= 0;
-            kfac[e] = KVDT == DLLM_E4M3 ? __shfl(kfl, 8 * g + e, kWave) : scale_log2;
-            vfac[e] = KVDT == DLLM_E4M3 ? __shfl(vsl, 8 * g + e, kWave) : 1.f;
+        for (int e = 0; e < 8; ++e) kval[e] = true;
+        if (!full) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kval[e] = key_of(kt, 8 * g + e) >= 0;
         }
-
-        // ---- S^T = K Q^T
-        f32x4_t s[2][RT];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int c = 0; c < NC; ++c)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][c].v, qf[rt][c].v, acc, 0, 0, 0);
-                s[t][rt] = acc;
+        // K operand of half t, k-chunk c: the loaded bf16 rows as they are, or
+        // 8 e4m3 codes widened exactly to bf16
+        auto kop = [&](int t, int c) -> bf16x8_t {
+            if (KVDT == DLLM_E4M3) {
+                const uint4 w = T.kr[t][c >> 1];
+                return __builtin_bit_cast(bf16x8_t, (c & 1) ? e4m3x8_to_bf16(w.z, w.w) : e4m3x8_to_bf16(w.x, w.y));
             }
+            return __builtin_bit_cast(bf16x8_t, T.kr[t][c]);
+        };
 
-#pragma unroll
-        for (int u = 0; u < VIT; ++u)
-            *reinterpret_cast<uint4 *>(vt + (RPI * u + lane / CPR) * VSTR + (lane % CPR) * 16) = vr[u];
-
-        // ---- online softmax per row (row = rt*16 + l16), keys 8g..8g+7 of this lane
+        // ---- per row tile: S^T = K Q^T, then the online softmax per row
+        // (row = rt*16 + l16) over keys 8g..8g+7 of this lane, in base 2.  The
+        // reference max m moves only when a tile's max exceeds it by more than
+        // kLazy, so probabilities stay below 2^kLazy and the rescale of O is
+        // rare.  m starts at a finite sentinel, so a row without keys yet gives
+        // exp2(-inf) = 0, never NaN.
         Frag pf[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            float x[8];
+            f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float v = s[e >> 2][rt][e & 3] * kfac[e];
-                x[e] = kval[e] ? v : kNegInf;
+            for (int c = 0; c < NC; ++c) {
+                Frag qf;
+                qf.u = *reinterpret_cast<const uint4 *>(qs + (rt * 16 + l16) * QSTR + chunk_dim<KVDT>(c, g) * 2);
+                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop(0, c), qf.v, s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop(1, c), qf.v, s1, 0, 0, 0);
             }
-            float mx = x[0];
-#pragma unroll
-            for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-            mx = fmaxf(mx, shfl_xor_f(mx, 16));
-            mx = fmaxf(mx, shfl_xor_f(mx, 32));
-            const float mn = fmaxf(m[rt], mx);
-            float p[8], ps = 0.f;
-            if (mn == kNegInf) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) p[e] = 0.f;
-            } else {
-                const float corr = __builtin_amdgcn_exp2f(m[rt] - mn);
+            const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+            float x[8];
+            float mx;
+            if (KVDT == DLLM_E4M3) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    p[e] = __builtin_amdgcn_exp2f(x[e] - mn);
-                    ps += p[e];
+                    const float v = sv[e] * kfac[e];
+                    x[e] = kval[e] ? v : kNegInf;
                 }
-                l[rt] = l[rt] * corr + ps;
-                if (corr != 1.0f) {
+                mx = x[0];
+#pragma unroll
+                for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+            } else {
+                // one positive scale for every key: take the max of the raw scores
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = kval[e] ? sv[e] : kNegInf;
+                mx = x[0];
+#pragma unroll
+                for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+                mx *= scale_log2;
+            }
+            mx = fmaxf(mx, shfl_xor_f(mx, 16));
+            mx = fmaxf(mx, shfl_xor_f(mx, 32));
+            const bool grow = mx > m[rt] + kLazy;
+            if (__ballot(grow)) {
+                if (grow) {
+                    const float corr = __builtin_amdgcn_exp2f(m[rt] - mx);
+                    l[rt] *= corr;
 #pragma unroll
                     for (int dt = 0; dt < NDT; ++dt) o[dt][rt] *= corr;
+                    m[rt] = mx;
                 }
-                m[rt] = mn;
             }
+            const float mref = m[rt];
+            float p[8], ps = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float a = KVDT == DLLM_E4M3 ? x[e] - mref : fmaf(x[e], scale_log2, -mref);
+                p[e] = __builtin_amdgcn_exp2f(a);
+                ps += p[e];
+            }
+            l[rt] += ps;
             if (KVDT == DLLM_E4M3) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) p[e] *= vfac[e];
@@ -304,19 +380,45 @@ __global__ __launch_bounds__(kNW * kWave, RT == 2 ? 2 : 1) void attn_mfma_kernel
             if (KVDT == DLLM_E4M3) {
                 // local lane j reads row 8g + j/2, codes dt*16 + 8(j%2) .. +7; lane i
                 // then holds codes of keys 8g .. 8g+7 at dim dt*16 + i
-                const uint2 c8 = lds_tr8(vt + (8 * g + (l16 >> 1)) * VSTR + dt * 16 + 8 * (l16 & 1));
+                const int rho = 8 * g + (l16 >> 1);
+                const uint2 c8 = lds_tr8(vt + rho * ROWB + (dt ^ vswz<KVDT>(rho)) * 16 + 8 * (l16 & 1));
                 vf.u = e4m3x8_to_bf16(c8.x, c8.y);
             } else {
                 // two reads of 4 keys each: local lane j reads row 8g + 4h + j/4,
                 // dims dt*16 + 4(j%4) .. +3; lane i then holds keys 8g+4h .. +3 at dim dt*16 + i
-                const uint2 lo = lds_tr16(vt + (8 * g + (l16 >> 2)) * VSTR + dt * 32 + 8 * (l16 & 3));
-                const uint2 hi = lds_tr16(vt + (8 * g + 4 + (l16 >> 2)) * VSTR + dt * 32 + 8 * (l16 & 3));
+                const int r0 = 8 * g + (l16 >> 2), r1 = r0 + 4;
+                const int cl = 2 * dt + ((l16 & 3) >> 1);            // logical chunk
+                const uint2 lo = lds_tr16(vt + r0 * ROWB + (cl ^ vswz<KVDT>(r0)) * 16 + 8 * (l16 & 1));
+                const uint2 hi = lds_tr16(vt + r1 * ROWB + (cl ^ vswz<KVDT>(r1)) * 16 + 8 * (l16 & 1));
                 vf.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
             }
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
                 o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.v, pf[rt].v, o[dt][rt], 0, 0, 0);
         }
+    };
+
+    Tile A, B;
+    unsigned char *vbA = vbase, *vbB = vbase + VTILE;
+    // wait until at most n vector-memory loads are outstanding; the scheduling
+    // barriers keep every load of the next tile on the far side of the wait
+    auto wait_tile = [&](bool more) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (!more) vm_wait<0>();
+        else vm_wait<LOADS>();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    if (t_begin < t_end) issue(t_begin, A, vbA);
+    for (int kt = t_begin; kt < t_end; kt += 2) {
+        bool more = kt + 1 < t_end;
+        if (more) issue(kt + 1, B, vbB);
+        wait_tile(more);
+        compute(kt, A, vbA);
+        if (!more) break;
+        more = kt + 2 < t_end;
+        if (more) issue(kt + 2, A, vbA);
+        wait_tile(more);
+        compute(kt + 1, B, vbB);
     }
 
     // ---- row sums over the 4 lane groups
@@ -539,7 +641,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(
     if (lse && lane == 0) lse[rr] = lrun > 0.f ? mrun + logf(lrun) : kNegInf;
 }
 
-template <int D, int KVDT, int RT>
+template <int D, int KVDT, int RT, bool MAP, bool NT>
 int launch_mfma(const dllm_kv_cache &c, const AttnPlan &p, const void *q, int Hq, int b,
                 const int32_t *key_idx, int n_keys, float scale, void *out, int out_dtype,
                 float *lse, void *ws, hipStream_t s) {
@@ -552,7 +654,7 @@ int launch_mfma(const dllm_kv_cache &c, const AttnPlan &p, const void *q, int Hq
         part_ml = part_o + (int64_t)p.splits * rows_total * D;
     }
     const float scale_log2 = scale * kLog2e;
-    attn_mfma_kernel<D, KVDT, RT><<<dim3((unsigned)blocks), dim3(kNW * kWave), 0, s>>>(
+    attn_mfma_kernel<D, KVDT, RT, MAP, NT><<<dim3((unsigned)blocks), dim3(kNW * kWave), 0, s>>>(
         c.k, c.v, c.k_scale, c.v_scale, static_cast<const uint16_t *>(q), Hq, c.n_kv_heads, c.L,
         b, G, key_idx, n_keys, scale_log2, p.row_groups, p.splits, p.tiles_per_wave, rows_total,
         out, out_dtype, lse, part_o, part_ml);
@@ -566,7 +668,7 @@ int launch_mfma(const dllm_kv_cache &c, const AttnPlan &p, const void *q, int Hq
 
 }  // namespace
 
-int plan_attention(const dllm_kv_cache &c, int q_dtype, int Hq, int b, int n_keys, AttnPlan *p) {
+int plan_attention(const dllm_kv_cache &c, int q_dtype, int Hq, int b, int n_keys, bool has_map, AttnPlan *p) {
     const int G = Hq / c.n_kv_heads;
     const int M = G * b;
     const bool mfma = q_dtype == DLLM_BF16 && (c.dtype == DLLM_BF16 || c.dtype == DLLM_E4M3) &&
@@ -579,13 +681,16 @@ int plan_attention(const dllm_kv_cache &c, int q_dtype, int Hq, int b, int n_key
     }
     p->path = 1;
     p->waves = kNW;
-    p->row_tiles = 2;                    // 32 rows per workgroup
+    // 32 rows per workgroup: 64-row waves hold 128 accumulator floats per lane
+    // and drop to one wave per SIMD, which measured slower at every shape
+    p->row_tiles = 2;
     p->row_groups = cdiv(M, 16 * p->row_tiles);
     const int64_t units = (int64_t)c.B * c.n_kv_heads * p->row_groups;
     const int n_tiles = cdiv(n_keys, 32);
     // enough workgroups for 2 per CU, but at least 4 key tiles per wave
     int splits = (int)std::max<int64_t>(1, cdiv64(512, units));
     splits = std::min(splits, std::max(1, n_tiles / (4 * kNW)));
+    if (has_map) splits = std::max(splits, cdiv(n_tiles, kNW * kMaxMapTiles));
     p->splits = splits;
     p->tiles_per_wave = cdiv(n_tiles, splits * kNW);
     p->ws_bytes = splits > 1 ? (size_t)splits * c.B * Hq * b * (c.d_head + 2) * sizeof(float) : 0;
@@ -603,12 +708,20 @@ int launch_attention(const dllm_kv_cache &c, const AttnPlan &p, const void *q, i
         return launch_status();
     }
     const bool e4 = c.dtype == DLLM_E4M3;
+#define DLLM_ATTN(DD, KV, MP, NTV) \
+    launch_mfma<DD, KV, 2, MP, NTV>(c, p, q, Hq, b, key_idx, n_keys, scale, out, out_dtype, lse, ws, s)
+#define DLLM_ATTN_NT(DD, KV, MP) (nt ? DLLM_ATTN(DD, KV, MP, true) : DLLM_ATTN(DD, KV, MP, false))
+    const bool map = key_idx != nullptr;
+    // stream K/V past the caches when only one row group reads each KV head
+    const bool nt = p.row_groups == 1;
     if (c.d_head == 128) {
-        if (e4) return launch_mfma<128, DLLM_E4M3, 2>(c, p, q, Hq, b, key_idx, n_keys, scale, out, out_dtype, lse, ws, s);
-        return launch_mfma<128, DLLM_BF16, 2>(c, p, q, Hq, b, key_idx, n_keys, scale, out, out_dtype, lse, ws, s);
+        if (e4) return map ? DLLM_ATTN_NT(128, DLLM_E4M3, true) : DLLM_ATTN_NT(128, DLLM_E4M3, false);
+        return map ? DLLM_ATTN_NT(128, DLLM_BF16, true) : DLLM_ATTN_NT(128, DLLM_BF16, false);
     }
     if (e4) return DLLM_ESHAPE;                 // e4m3 needs d % 128 == 0
-    return launch_mfma<64, DLLM_BF16, 2>(c, p, q, Hq, b, key_idx, n_keys, scale, out, out_dtype, lse, ws, s);
+    return map ? DLLM_ATTN_NT(64, DLLM_BF16, true) : DLLM_ATTN_NT(64, DLLM_BF16, false);
+#undef DLLM_ATTN_NT
+#undef DLLM_ATTN
 }
 
 }  // namespace dllm

@@ -63,7 +63,8 @@ struct AttnPlan {
     int tiles_per_wave;// 32-key tiles per wave
     size_t ws_bytes;   // partial-result workspace
 };
-int plan_attention(const dllm_kv_cache &c, int q_dtype, int Hq, int b, int n_keys, AttnPlan *p);
+int plan_attention(const dllm_kv_cache &c, int q_dtype, int Hq, int b, int n_keys, bool has_map,
+                   AttnPlan *p);
 int launch_attention(const dllm_kv_cache &c, const AttnPlan &p, const void *q, int q_dtype, int Hq,
                      int b, const int32_t *key_idx, int n_keys, float scale, void *out,
                      int out_dtype, float *lse, void *ws, hipStream_t s);
@@ -81,7 +82,8 @@ int launch_vocab(const void *logits, int dtype, int64_t N, int64_t V, int64_t st
 int launch_stability_reset(int B, int L, int D, int32_t *ring_argmax, float *ring_maxprob,
                            int32_t *ring_step, float *entropy_latest, int32_t *t_write,
                            uint8_t *stable, hipStream_t s);
-int launch_stability(int B, int L, int step, const int32_t *pos, int n, const int32_t *argmax,
+int launch_stability(int B, int L, int step, const int32_t *step_dev, const int32_t *pos, int n,
+                     const int32_t *argmax,
                      const float *maxprob, const float *entropy, int32_t *ring_argmax,
                      float *ring_maxprob, int32_t *ring_step, float *entropy_latest,
                      int32_t *t_write, uint8_t *stable, const dllm_stab_params &prm, double hmax,

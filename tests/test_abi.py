@@ -56,7 +56,7 @@ def test_host_validation_without_gpu(dl):
     assert L.dllm_vocab_stats(None, 5, 4, 10, 10, None, None, None, None, 0, None) == -2  # dtype
     assert L.dllm_vocab_stats(None, 1, 0, 10, 10, None, None, None, None, 0, None) == 0   # N = 0: no-op
     prm = dl._StabParams(K=3, D=2, R=1, tau=0.9, vocab=10)                                  # D < K
-    assert L.dllm_stability_mask(1, 4, 0, None, 4, 16, 16, 16, 16, 16, 16, 16, 16, 16,
+    assert L.dllm_stability_mask(1, 4, 0, None, None, 4, 16, 16, 16, 16, 16, 16, 16, 16, 16,
                                  ctypes.byref(prm), 16, 16, 16, 16, 16, None) == -1
     assert L.dllm_sink_rolling_map(1, 10, 4, 8, 16, 16, 11, None) == -3                     # n_keys < S+R
 
