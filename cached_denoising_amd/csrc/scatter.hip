@@ -56,14 +56,17 @@ __global__ __launch_bounds__(256) void scatter_copy_kernel(
     const int h = (int)(row % Hkv);
     const int64_t bj = row / Hkv;
     const int b = (int)(bj / n);
+    // the source row does not depend on the position: issue all three loads together
+    const uint4 kw = k_new[t];
+    const uint4 vw = v_new[t];
     const int p = pos[bj];
     if (p < 0 || p >= L) {
         if (p != -1 && bad && c == 0 && h == 0) atomicAdd(bad, 1);
         return;
     }
     const int64_t dst = (((int64_t)b * Hkv + h) * L + p) * chunks_per_row + c;
-    ck[dst] = k_new[t];
-    cv[dst] = v_new[t];
+    ck[dst] = kw;
+    cv[dst] = vw;
 }
 
 // ---- e4m3 quantise: 16 lanes per 128-element group, 8 elements per lane ----
@@ -90,7 +93,7 @@ __global__ __launch_bounds__(256) void scatter_e4m3_kernel(
     // every lane takes part in the shuffles below; dead lanes contribute 0
     const int64_t src = row * d + g * 128 + lane16 * 8;
     float xk[8], xv[8];
-    if (ok) {
+    if (live) {           // not gated on the position: the loads issue together
         if (SRC == DLLM_BF16) {
             const uint4 wk = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(k_new) + src);
             const uint4 wv = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(v_new) + src);
@@ -110,6 +113,10 @@ __global__ __launch_bounds__(256) void scatter_e4m3_kernel(
             xv[4] = v1.x; xv[5] = v1.y; xv[6] = v1.z; xv[7] = v1.w;
         }
     } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xk[i] = xv[i] = 0.f;
+    }
+    if (!ok) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) xk[i] = xv[i] = 0.f;
     }

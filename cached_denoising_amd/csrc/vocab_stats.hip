@@ -3,13 +3,14 @@
 // over the row.  [SWD page, 3.1 and 4.2: per-position max probability and
 // its token; Flash-dLLM page, 3.1: entropy of the step's distribution.]
 //
-// One workgroup of 256 threads streams one row (or one contiguous split of
-// a row) with non-temporal 16-byte loads, two in flight per thread; the few elements before the first 16-byte
-// boundary and after the last are peeled off.  Each thread keeps an online
-// state over base-2 exponents a_j = (x_j - m) log2(e):
+// One workgroup of 128 threads streams one row (or one contiguous split of
+// a row) with non-temporal 16-byte loads, two in flight per thread; the few
+// elements before the first 16-byte boundary and after the last are peeled
+// off.  Each thread keeps an online state over base-2 exponents
+// a_j = (x_j - m) log2(e):
 //     m = running max,  s = sum 2^a_j,  t = sum 2^a_j a_j,  idx = argmax
 // so that  maxprob = 1/s  and  entropy = ln s - ln2 * t / s.  States merge in
-// a fixed order (wave butterfly, then waves 0..3, then splits 0..n-1), so
+// a fixed order (wave butterfly, then the waves in order, then splits), so
 // the result is bitwise reproducible.  The probabilities never touch memory.
 #include "common.hpp"
 
@@ -18,7 +19,7 @@
 namespace dllm {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 128;     // two waves: measured ahead of 256 and 512 at both row lengths
 constexpr int kUnroll = 2;      // 16-byte loads in flight per thread per step
 constexpr float kNegInf = -__builtin_inff();
 
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(256) void vocab_merge_kernel(const float4 *__restri
 
 VocabPlan plan_vocab(int64_t N, int64_t V) {
     VocabPlan p;
-    const int64_t target_blocks = 2048;     // 8 workgroups per CU
+    const int64_t target_blocks = 4096;     // 16 two-wave workgroups per CU
     const int64_t min_chunk = 16384;        // elements per split, at least
     int64_t splits = N > 0 ? cdiv64(target_blocks, N) : 1;
     splits = std::max<int64_t>(1, std::min<int64_t>(splits, cdiv64(V, min_chunk)));
