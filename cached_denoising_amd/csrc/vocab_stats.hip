@@ -3,8 +3,10 @@
 // over the row.  [SWD page, 3.1 and 4.2: per-position max probability and
 // its token; Flash-dLLM page, 3.1: entropy of the step's distribution.]
 //
-// One workgroup of 128 threads streams one row (or one contiguous split of
-// a row) with non-temporal 16-byte loads, two in flight per thread; the few
+// One workgroup of 256 threads streams one row (or one contiguous split of
+// a row) with non-temporal 16-byte loads.  The loop is software-pipelined:
+// each thread keeps the next step's two loads in flight while it folds the
+// current two, so a wave never waits on memory with nothing issued.  The few
 // elements before the first 16-byte boundary and after the last are peeled
 // off.  Each thread keeps an online state over base-2 exponents
 // a_j = (x_j - m) log2(e):
@@ -19,8 +21,8 @@
 namespace dllm {
 namespace {
 
-constexpr int kThreads = 128;     // two waves: measured ahead of 256 and 512 at both row lengths
-constexpr int kUnroll = 2;      // 16-byte loads in flight per thread per step
+constexpr int kThreads = 256;   // four waves; measured ahead of 64, 128 and 512 with the pipelined loop
+constexpr int kUnroll = 2;      // 16-byte loads per thread per step (two steps in flight)
 constexpr float kNegInf = -__builtin_inff();
 
 struct Acc {
@@ -175,31 +177,56 @@ __global__ __launch_bounds__(kThreads) void vocab_stats_kernel(
         const int64_t a0 = min(j1, j0 + mis);
         const int64_t nvec = (j1 - a0) / kVec;
         const int64_t a1 = a0 + nvec * kVec;
-        // peeled elements: [j0, a0) and [a1, j1), fewer than 2*kVec
+        // peeled elements: [j0, a0) and [a1, j1), fewer than 2*kVec; the
+        // load goes first so that it is not waited for on its own
         const int64_t nhead = a0 - j0, ntail = j1 - a1;
-        if (tid < nhead + ntail) {
-            const int64_t j = tid < nhead ? j0 + tid : a1 + (tid - nhead);
-            float x1[1] = {E::scalar(rp + j)};
-            consume<1>(st, x1, [&](int) { return (int)j; });
-        }
+        const bool peel = tid < nhead + ntail;
+        const int64_t jp = tid < nhead ? j0 + tid : a1 + (tid - nhead);
+        float xp[1] = {0.f};
+        if (peel) xp[0] = E::scalar(rp + jp);
+
         const uint4 *vp = reinterpret_cast<const uint4 *>(rp + a0);
-        int64_t v = tid;
-        for (; v + (kUnroll - 1) * kThreads < nvec; v += kUnroll * kThreads) {
-            uint4 w[kUnroll];
+        constexpr unsigned kStep = kUnroll * kThreads;       // vectors per step
+        const int steps = (int)(nvec / kStep);               // full steps, uniform
+        auto issue = [&](uint4 (&w)[kUnroll], unsigned o) {
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) w[u] = load_stream(vp + v + u * kThreads);
+            for (int u = 0; u < kUnroll; ++u) w[u] = load_stream(vp + o + u * kThreads);
+        };
+        auto fold = [&](const uint4 (&w)[kUnroll], unsigned o) {
             float x[kUnroll * kVec];
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) E::unpack(w[u], x + u * kVec);
             consume<kUnroll * kVec>(st, x, [&](int e) {
-                return (int)(a0 + (v + (e / kVec) * kThreads) * kVec + (e % kVec));
+                return (int)(a0 + (int64_t)(o + (e / kVec) * kThreads) * kVec + (e % kVec));
             });
+        };
+        // two register buffers: step i+1 is in flight while step i is folded
+        uint4 wa[kUnroll], wb[kUnroll];
+        unsigned off = tid;
+        if (steps > 0) issue(wa, off);
+        int i = 0;
+        for (; i + 2 <= steps; i += 2) {
+            issue(wb, off + kStep);
+            fold(wa, off);
+            if (i + 2 < steps) issue(wa, off + 2 * kStep);
+            fold(wb, off + kStep);
+            off += 2 * kStep;
         }
-        for (; v < nvec; v += kThreads) {
-            const uint4 w = load_stream(vp + v);
-            float x[kVec];
-            E::unpack(w, x);
-            consume<kVec>(st, x, [&](int e) { return (int)(a0 + v * kVec + e); });
+        if (i < steps) {
+            fold(wa, off);
+            off += kStep;
+        }
+        if (peel) consume<1>(st, xp, [&](int) { return (int)jp; });
+        // the rest: fewer than kStep vectors
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const unsigned v = off + u * kThreads;
+            if (v < nvec) {
+                const uint4 w = load_stream(vp + v);
+                float x[kVec];
+                E::unpack(w, x);
+                consume<kVec>(st, x, [&](int e) { return (int)(a0 + (int64_t)v * kVec + e); });
+            }
         }
     }
 
@@ -244,7 +271,7 @@ __global__ __launch_bounds__(256) void vocab_merge_kernel(const float4 *__restri
 
 VocabPlan plan_vocab(int64_t N, int64_t V) {
     VocabPlan p;
-    const int64_t target_blocks = 4096;     // 16 two-wave workgroups per CU
+    const int64_t target_blocks = 1536;     // one round of 6 four-wave workgroups per CU
     const int64_t min_chunk = 16384;        // elements per split, at least
     int64_t splits = N > 0 ? cdiv64(target_blocks, N) : 1;
     splits = std::max<int64_t>(1, std::min<int64_t>(splits, cdiv64(V, min_chunk)));
