@@ -23,8 +23,12 @@ sys.path.insert(0, ROOT)
 
 METRIC = "denoise steps/sec (block attn + vocab stats); achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0      # dense bf16 matrix peak of MI355X
 PROFILES = os.path.join(ROOT, "profiles")
-VOCAB_SRC = os.path.join(ROOT, "cached_denoising_amd", "csrc", "vocab_stats.hip")
+CSRC = os.path.join(ROOT, "cached_denoising_amd", "csrc")
+# the source file of each kernel whose counters a profile summary records
+KERNEL_SRC = {"vocab_stats": "vocab_stats.hip", "attention": "attention.hip",
+              "scatter": "scatter.hip", "stability": "stability.hip"}
 
 
 def parse():
@@ -58,16 +62,16 @@ def kernel_sha(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(config):
-    """HBM bytes per launch of the vocab kernel from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source"""
-    path = os.path.join(PROFILES, f"vocab_stats_{config}_pmc.md")
+def measured_traffic(kernel, config):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source"""
+    path = os.path.join(PROFILES, f"{kernel}_{config}_pmc.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_sha = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     m_tb = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_sha or not m_tb or m_sha.group(1) != kernel_sha(VOCAB_SRC):
+    if not m_sha or not m_tb or m_sha.group(1) != kernel_sha(os.path.join(CSRC, KERNEL_SRC[kernel])):
         return None
     return float(m_tb.group(1))
 
@@ -83,6 +87,7 @@ class Step:
         self.has_attn = cfg.b > 0 and d > 0 and cfg.name != "vocab"
         self.has_vocab = cfg.V > 0
         self.has_stab = cfg.name in ("gpt2", "vocab", "tiny")
+        self.attn_split = False
         if self.has_attn:
             k = torch.empty((B, H, L, d), dtype=kvt, device=dev)
             v = torch.empty_like(k)
@@ -107,6 +112,8 @@ class Step:
             self.out = torch.empty((B, cfg.Hq, cfg.b, d), dtype=torch.bfloat16, device=dev)
             wsb = D.dllm_block_attention_workspace(self.cache, W.BF16, cfg.Hq, cfg.b, n_keys)
             self.attn_ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+            # a workspace is needed only when the keys are split over workgroups
+            self.attn_split = wsb > 0
         if self.has_vocab:
             self.logits = W.logits(cfg, device=dev)
             N = self.logits.shape[0]
@@ -183,6 +190,14 @@ class Step:
             # (mask 1, conf 4, next_pos 4)
             out["stability"] = BL * (12 + 12 + 12 * (cfg.K - 1) + 2 * 9 + 9)
         return out
+
+    def algorithmic_flops(self):
+        """matrix flops of the attention call: QK^T and PV, 2 flops per
+        multiply-add, for every (query head, query, key, dim)"""
+        cfg = self.cfg
+        if not self.has_attn:
+            return {}
+        return {"attention": 4 * cfg.B * cfg.Hq * cfg.b * self.n_keys * cfg.d}
 
 
 def cpu_baseline(step, D, W, cfg):
@@ -299,14 +314,26 @@ def main():
     per_kernel_us = {n: 1000.0 * sum(e[0].elapsed_time(e[1]) for e in events[n]) / args.steps
                      for n in names}
     alg = step.algorithmic_bytes()
-    dom = "vocab_stats" if step.has_vocab else "attention"
+    flops = step.algorithmic_flops()
+    # the dominant kernel is the one the step spends the most time in; it is
+    # bound by the matrix cores when its flops per byte exceed the ridge
+    dom = max(per_kernel_us, key=per_kernel_us.get)
     dom_us = per_kernel_us[dom]
-    achieved = alg[dom] / (dom_us * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(args.config) if dom == "vocab_stats" else None,
-                "kernel": dom, "algorithmic_bytes_per_launch": alg[dom],
-                "avg_launch_us": round(dom_us, 2), "kernel_timing": kernel_timing}
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    traffic = measured_traffic(dom, args.config)
+    if dom in flops and flops[dom] / alg[dom] > ridge:
+        achieved = flops[dom] / (dom_us * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "traffic": traffic, "algorithmic_flops_per_launch": flops[dom]}
+    else:
+        achieved = alg[dom] / (dom_us * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+    roofline.update({"kernel": dom, "algorithmic_bytes_per_launch": alg[dom],
+                     "avg_launch_us": round(dom_us, 2), "kernel_timing": kernel_timing})
+    if dom == "attention" and step.attn_split:
+        roofline["kernel_note"] = "attention call = attn_mfma_kernel + attn_merge_kernel of the key splits"
     cpu = None if args.no_cpu_baseline else cpu_baseline(step, D, W, cfg)
     desc = {
         "gpt2": "GPT-2-small-shaped decode step: B=8, L=1024, 12 heads x d64, bf16 K/V cache, "

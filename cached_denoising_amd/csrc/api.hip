@@ -113,9 +113,11 @@ size_t dllm_block_attention_workspace(const dllm_kv_cache *cache, int q_dtype, i
                                       int n_keys) {
     if (check_cache(cache) != DLLM_OK || Hq < 1 || b < 1 || n_keys < 1) return 0;
     if (Hq % cache->n_kv_heads != 0) return 0;
-    AttnPlan p;
-    if (plan_attention(*cache, q_dtype, Hq, b, n_keys, true, &p) != DLLM_OK) return 0;
-    return p.ws_bytes;
+    // enough for the call with or without a key map
+    AttnPlan with_map, without;
+    if (plan_attention(*cache, q_dtype, Hq, b, n_keys, true, &with_map) != DLLM_OK) return 0;
+    if (plan_attention(*cache, q_dtype, Hq, b, n_keys, false, &without) != DLLM_OK) return 0;
+    return with_map.ws_bytes > without.ws_bytes ? with_map.ws_bytes : without.ws_bytes;
 }
 
 int dllm_block_attention(const dllm_kv_cache *cache, const void *q, int q_dtype, int Hq, int b,

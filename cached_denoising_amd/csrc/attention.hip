@@ -6,8 +6,10 @@
 // matrix Q K^T / sqrt(d_k), softmax, times V) and 2.3 (fixed key set).]
 //
 // MFMA path (bf16 queries; bf16 or e4m3 cache; d = 64 or 128):
-//   A workgroup of 4 waves owns one (sequence, KV head, row group, key
-//   split).  The rows are the G query heads sharing the KV head times the
+//   A workgroup of NW = 4 or 8 waves owns one (sequence, KV head, row
+//   group, key split); few (sequence, KV head) pairs get more waves per
+//   workgroup rather than more key splits, so short contexts need no merge.
+//   Each wave keeps the next key tile in flight while it computes one.  The rows are the G query heads sharing the KV head times the
 //   block's queries.  Each wave walks its own run of 32-key tiles:
 //     S^T (keys x rows) = K . Q^T     on v_mfma_f32_16x16x32_bf16, K straight
 //                                      from HBM into the A operand
@@ -21,21 +23,22 @@
 //   e4m3 codes widen to bf16 exactly (e4m3 is a subset of bf16) with
 //   v_cvt_scalef32_pk_bf16_fp8; the per-key float32 scales multiply the
 //   scores (K) and the probabilities (V) in float32.
-//   The 4 waves merge through LDS in a fixed order; key splits across
+//   The waves merge through LDS in a fixed binary tree; key splits across
 //   workgroups write (m, l, O~) partials merged by a second kernel.
 // VALU path (float32 queries and cache, any d <= 256): one wave per query.
 #include "common.hpp"
 
 #include <climits>
+#include <type_traits>
 
 namespace dllm {
 namespace {
 
-constexpr int kNW = 4;                 // waves per MFMA workgroup
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLazy = 8.0f;          // log2 headroom before the running max moves
 constexpr float kMinit = -1.0e30f;     // finite start of the running max
-constexpr int kMaxMapTiles = 64;       // 32-key tiles per wave when a key map is given
+constexpr int kMapTableTiles = 256;    // 32-key tiles of key indices a workgroup's LDS table holds
+constexpr int kStages = 2;             // key tiles per wave in the load pipeline (4 measured no faster)
 
 union Frag {
     uint4 u;
@@ -143,8 +146,15 @@ __device__ __forceinline__ int xcd_remap(int pid, int nblk) {
     return (pid & 7) * per + (pid >> 3);
 }
 
-template <int D, int KVDT, int RT, bool MAP, bool NT>
-__global__ __launch_bounds__(kNW * kWave, 2) void attn_mfma_kernel(
+// LDS of one MFMA workgroup: the staged queries, kStages V tiles per wave
+// and, with a key map, the workgroup's table of key indices
+constexpr int attn_smem_bytes(int D, int esz, int RT, int NW, bool map) {
+    return 16 * RT * (D * 2 + 16) + NW * kStages * 32 * D * esz + (map ? kMapTableTiles * 32 * 4 : 0);
+}
+constexpr int kLdsBytes = 160 * 1024;  // LDS of one gfx950 CU
+
+template <int D, int KVDT, int RT, bool MAP, bool NT, int NW>
+__global__ __launch_bounds__(NW * kWave, 2) void attn_mfma_kernel(
     const void *__restrict__ ck, const void *__restrict__ cv, const float *__restrict__ ksc,
     const float *__restrict__ vsc, const uint16_t *__restrict__ q, int Hq, int Hkv, int L, int b,
     int G, const int32_t *__restrict__ key_idx, int n_keys, float scale_log2, int row_groups,
@@ -161,12 +171,18 @@ __global__ __launch_bounds__(kNW * kWave, 2) void attn_mfma_kernel(
     constexpr int QSTR = D * 2 + 16;     // LDS row stride of Q: 16 rows of one read hit distinct banks
     constexpr int QBYTES = ROWS * QSTR;
     constexpr int VTILE = 32 * ROWB;     // one V tile in LDS
-    constexpr int TAB = MAP ? kNW * kMaxMapTiles * 32 * 4 : 0;   // per-wave key index tables
-    constexpr int SMEM = QBYTES + kNW * 2 * VTILE + TAB;
-    static_assert(SMEM >= ROWS * (D + 4) * 4, "merge buffer must fit in the staging area");
+    constexpr int MT = kMapTableTiles / NW;                      // table tiles per wave
+    constexpr int TAB = MAP ? kMapTableTiles * 32 * 4 : 0;       // per-wave key index tables
+    constexpr int S = kStages;
+    constexpr int SMEM = QBYTES + NW * S * VTILE + TAB;
+    constexpr int BST = D + 4;                                   // merge-buffer row stride (floats)
+    static_assert(S >= 2 && S <= 4, "pipeline depth");
+    static_assert(SMEM == attn_smem_bytes(D, ESZ, RT, NW, MAP), "LDS layout");
+    static_assert(SMEM <= kLdsBytes, "LDS of one workgroup");
+    static_assert(SMEM >= (NW / 2) * ROWS * BST * 4, "merge buffers must fit in the staging area");
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
-    __shared__ float sm_ml[kNW][ROWS][2];
+    __shared__ float sm_ml[NW][ROWS][2];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -188,7 +204,7 @@ __global__ __launch_bounds__(kNW * kWave, 2) void attn_mfma_kernel(
     // ---- queries: the B operand of S^T = K Q^T.  All waves of the workgroup
     // use the same rows, so they are staged once in LDS; rows past M are zero.
     unsigned char *qs = smem;
-    for (int idx = threadIdx.x; idx < ROWS * (D / 8); idx += kNW * kWave) {
+    for (int idx = threadIdx.x; idx < ROWS * (D / 8); idx += NW * kWave) {
         const int r = idx / (D / 8), c8 = idx % (D / 8);
         const int rr = rg * ROWS + r;
         uint4 w = make_uint4(0, 0, 0, 0);
@@ -209,15 +225,15 @@ __global__ __launch_bounds__(kNW * kWave, 2) void attn_mfma_kernel(
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) { m[rt] = kMinit; l[rt] = 0.f; }
 
-    unsigned char *vbase = smem + QBYTES + wave * 2 * VTILE;
+    unsigned char *vbase = smem + QBYTES + wave * S * VTILE;
     const int n_tiles = (n_keys + 31) / 32;
-    const int t_begin = (split * kNW + wave) * tiles_per_wave;
+    const int t_begin = (split * NW + wave) * tiles_per_wave;
     const int t_end = min(n_tiles, t_begin + tiles_per_wave);
 
-    // Software pipeline, one tile deep.  While tile t is computed, tile t+1 is
-    // in flight: its K rows into the other register set, its V rows straight
-    // from HBM into the wave's other LDS buffer (global_load_lds_dwordx4, no
-    // registers).  Direct-to-LDS loads fill 1 KB per instruction in lane
+    // Software pipeline, S - 1 tiles deep.  While tile t is computed, tiles
+    // t+1 .. t+S-1 are in flight: their K rows into the other register sets,
+    // their V rows straight from HBM into the wave's other LDS buffers
+    // (global_load_lds_dwordx4, no registers).  Direct-to-LDS loads fill 1 KB per instruction in lane
     // order, so the V rows are unpadded and their 16-byte chunks are
     // XOR-swizzled per row instead, which keeps the transposed reads of one
     // 16-lane group on distinct banks.
@@ -232,9 +248,9 @@ __global__ __launch_bounds__(kNW * kWave, 2) void attn_mfma_kernel(
     };
 
     // With a key map, this wave's indices are copied once into its LDS table
-    // (tiles_per_wave <= kMaxMapTiles); without one, key j of the selection is
-    // position j.  Either way the index of tile-local key kappa is cheap.
-    int *ktab = reinterpret_cast<int *>(smem + QBYTES + kNW * 2 * VTILE) + wave * kMaxMapTiles * 32;
+    // (tiles_per_wave <= MT); without one, key j of the selection is position
+    // j.  Either way the index of tile-local key kappa is cheap.
+    int *ktab = reinterpret_cast<int *>(smem + QBYTES + NW * S * VTILE) + wave * MT * 32;
     if (MAP) {
         for (int j = lane; j < (t_end - t_begin) * 32; j += kWave)
             ktab[j] = key_at(kmap, n_keys, L, t_begin * 32 + j);
@@ -398,27 +414,32 @@ __global__ __launch_bounds__(kNW * kWave, 2) void attn_mfma_kernel(
         }
     };
 
-    Tile A, B;
-    unsigned char *vbA = vbase, *vbB = vbase + VTILE;
-    // wait until at most n vector-memory loads are outstanding; the scheduling
-    // barriers keep every load of the next tile on the far side of the wait
-    auto wait_tile = [&](bool more) {
+    // wait until only the loads of the `ahead` tiles issued after this one
+    // are outstanding; the scheduling barriers keep every load of a later
+    // tile on the far side of the wait
+    auto wait_tile = [&](int ahead) {
         __builtin_amdgcn_sched_barrier(0);
-        if (!more) vm_wait<0>();
-        else vm_wait<LOADS>();
+        if (ahead <= 0) vm_wait<0>();
+        else if (S == 2 || ahead == 1) vm_wait<LOADS>();
+        else if (ahead == 2) vm_wait<(S > 2 ? 2 : 1) * LOADS>();
+        else vm_wait<(S > 2 ? 3 : 1) * LOADS>();
         __builtin_amdgcn_sched_barrier(0);
     };
-    if (t_begin < t_end) issue(t_begin, A, vbA);
-    for (int kt = t_begin; kt < t_end; kt += 2) {
-        bool more = kt + 1 < t_end;
-        if (more) issue(kt + 1, B, vbB);
-        wait_tile(more);
-        compute(kt, A, vbA);
-        if (!more) break;
-        more = kt + 2 < t_end;
-        if (more) issue(kt + 2, A, vbA);
-        wait_tile(more);
-        compute(kt + 1, B, vbB);
+    // tile t of this wave's run uses register set and V buffer (t - t_begin) % S
+    Tile T[S];
+#pragma unroll
+    for (int i = 0; i < S - 1; ++i)
+        if (t_begin + i < t_end) issue(t_begin + i, T[i], vbase + i * VTILE);
+    for (int kt = t_begin; kt < t_end; kt += S) {
+#pragma unroll
+        for (int j = 0; j < S; ++j) {
+            const int t = kt + j;
+            if (t >= t_end) break;
+            const int jn = (j + S - 1) % S;
+            if (t + S - 1 < t_end) issue(t + S - 1, T[jn], vbase + jn * VTILE);
+            wait_tile(min(S - 1, t_end - 1 - t));
+            compute(t, T[j], vbase + j * VTILE);
+        }
     }
 
     // ---- row sums over the 4 lane groups
@@ -428,7 +449,9 @@ __global__ __launch_bounds__(kNW * kWave, 2) void attn_mfma_kernel(
         l[rt] += shfl_xor_f(l[rt], 32);
     }
 
-    // ---- merge the 4 waves in a fixed order through LDS
+    // ---- merge the waves through LDS: every wave rescales its O to the
+    // workgroup's row max, then a fixed binary tree adds them up (at each
+    // level the upper half of the remaining waves hands its O to the lower)
     if (g == 0) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -437,44 +460,56 @@ __global__ __launch_bounds__(kNW * kWave, 2) void attn_mfma_kernel(
         }
     }
     __syncthreads();
-    float fown[RT], Mrow[RT], Ltot[RT];
+    float Mrow[RT], Ltot[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const int r = rt * 16 + l16;
         float mm = kNegInf;
 #pragma unroll
-        for (int w = 0; w < kNW; ++w) mm = fmaxf(mm, sm_ml[w][r][0]);
+        for (int w = 0; w < NW; ++w) mm = fmaxf(mm, sm_ml[w][r][0]);
         float lt = 0.f;
 #pragma unroll
-        for (int w = 0; w < kNW; ++w) {
+        for (int w = 0; w < NW; ++w) {
             const float mw = sm_ml[w][r][0];
             if (mw != kNegInf) lt += sm_ml[w][r][1] * __builtin_amdgcn_exp2f(mw - mm);
         }
         Mrow[rt] = mm;
         Ltot[rt] = lt;
-        fown[rt] = m[rt] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m[rt] - mm);
+        const float fown = m[rt] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m[rt] - mm);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[dt][rt] *= fown;
     }
-    float *buf = reinterpret_cast<float *>(smem);       // [ROWS][D + 4] floats
-    constexpr int BST = D + 4;
-    for (int w = 0; w < kNW; ++w) {
-        if (wave == w) {
+    float *buf = reinterpret_cast<float *>(smem);       // NW/2 slots of [ROWS][BST] floats
+#pragma unroll
+    for (int half = NW / 2; half >= 1; half >>= 1) {
+        // the staging area (or the previous level's slots) is free to reuse
+        __syncthreads();
+        if (wave >= half && wave < 2 * half) {
+            float *slot = buf + (wave - half) * ROWS * BST;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
-                    float4 *bp = reinterpret_cast<float4 *>(buf + (rt * 16 + l16) * BST + dt * 16 + 4 * g);
-                    const f32x4_t v = o[dt][rt] * fown[rt];
-                    float4 acc = w == 0 ? make_float4(0.f, 0.f, 0.f, 0.f) : *bp;
-                    acc.x += v[0]; acc.y += v[1]; acc.z += v[2]; acc.w += v[3];
-                    if (w < kNW - 1) *bp = acc;
-                    else o[dt][rt] = f32x4_t{acc.x, acc.y, acc.z, acc.w};
+                    const f32x4_t v = o[dt][rt];
+                    *reinterpret_cast<float4 *>(slot + (rt * 16 + l16) * BST + dt * 16 + 4 * g) =
+                        make_float4(v[0], v[1], v[2], v[3]);
                 }
         }
-        if (w < kNW - 1) __syncthreads();
+        __syncthreads();
+        if (wave < half) {
+            const float *slot = buf + wave * ROWS * BST;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    const float4 v = *reinterpret_cast<const float4 *>(slot + (rt * 16 + l16) * BST + dt * 16 + 4 * g);
+                    o[dt][rt] += f32x4_t{v.x, v.y, v.z, v.w};
+                }
+        }
     }
-    if (wave != kNW - 1) return;
+    if (wave != 0) return;
 
-    // ---- the last wave writes the result (or this split's partial)
+    // ---- wave 0 writes the result (or this split's partial)
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const int r = rg * ROWS + rt * 16 + l16;
@@ -641,20 +676,22 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(
     if (lse && lane == 0) lse[rr] = lrun > 0.f ? mrun + logf(lrun) : kNegInf;
 }
 
-template <int D, int KVDT, int RT, bool MAP, bool NT>
+template <int D, int KVDT, int RT, bool MAP, bool NT, int NW>
 int launch_mfma(const dllm_kv_cache &c, const AttnPlan &p, const void *q, int Hq, int b,
                 const int32_t *key_idx, int n_keys, float scale, void *out, int out_dtype,
                 float *lse, void *ws, hipStream_t s) {
     const int G = Hq / c.n_kv_heads;
     const int64_t rows_total = (int64_t)c.B * Hq * b;
     const int64_t blocks = (int64_t)c.B * c.n_kv_heads * p.row_groups * p.splits;
+    if (MAP && p.tiles_per_wave > kMapTableTiles / NW) return DLLM_ESHAPE;   // the key table holds them
+    if (blocks > INT_MAX) return DLLM_ERANGE;
     float *part_o = nullptr, *part_ml = nullptr;
     if (p.splits > 1) {
         part_o = static_cast<float *>(ws);
         part_ml = part_o + (int64_t)p.splits * rows_total * D;
     }
     const float scale_log2 = scale * kLog2e;
-    attn_mfma_kernel<D, KVDT, RT, MAP, NT><<<dim3((unsigned)blocks), dim3(kNW * kWave), 0, s>>>(
+    attn_mfma_kernel<D, KVDT, RT, MAP, NT, NW><<<dim3((unsigned)blocks), dim3(NW * kWave), 0, s>>>(
         c.k, c.v, c.k_scale, c.v_scale, static_cast<const uint16_t *>(q), Hq, c.n_kv_heads, c.L,
         b, G, key_idx, n_keys, scale_log2, p.row_groups, p.splits, p.tiles_per_wave, rows_total,
         out, out_dtype, lse, part_o, part_ml);
@@ -680,19 +717,30 @@ int plan_attention(const dllm_kv_cache &c, int q_dtype, int Hq, int b, int n_key
         return DLLM_OK;
     }
     p->path = 1;
-    p->waves = kNW;
     // 32 rows per workgroup: 64-row waves hold 128 accumulator floats per lane
     // and drop to one wave per SIMD, which measured slower at every shape
     p->row_tiles = 2;
     p->row_groups = cdiv(M, 16 * p->row_tiles);
     const int64_t units = (int64_t)c.B * c.n_kv_heads * p->row_groups;
     const int n_tiles = cdiv(n_keys, 32);
-    // enough workgroups for 2 per CU, but at least 4 key tiles per wave
-    int splits = (int)std::max<int64_t>(1, cdiv64(512, units));
-    splits = std::min(splits, std::max(1, n_tiles / (4 * kNW)));
-    if (has_map) splits = std::max(splits, cdiv(n_tiles, kNW * kMaxMapTiles));
+    const int esz = c.dtype == DLLM_E4M3 ? 1 : 2;
+    // About 8 waves per CU in all.  Few (sequence, KV head, row group) units
+    // first get wider workgroups (8, then 16 waves, while the LDS holds them
+    // and every wave keeps 2 key tiles), and only then key splits, which cost
+    // a partial write and a merge pass.
+    const int64_t want = 2048;
+    int nw = 4;
+    // 8-wave workgroups when the units are few (16 waves would leave 128
+    // VGPRs per lane and spill; measured slower)
+    if (units * nw < want && n_tiles >= 16 &&
+        attn_smem_bytes(c.d_head, esz, p->row_tiles, 8, has_map) <= kLdsBytes)
+        nw = 8;
+    p->waves = nw;
+    int splits = (int)std::max<int64_t>(1, cdiv64(want, units * nw));
+    splits = std::min(splits, std::max(1, n_tiles / (4 * nw)));      // at least 4 tiles per wave
+    if (has_map) splits = std::max(splits, cdiv(n_tiles, kMapTableTiles));   // the table holds them
     p->splits = splits;
-    p->tiles_per_wave = cdiv(n_tiles, splits * kNW);
+    p->tiles_per_wave = cdiv(n_tiles, splits * nw);
     p->ws_bytes = splits > 1 ? (size_t)splits * c.B * Hq * b * (c.d_head + 2) * sizeof(float) : 0;
     return DLLM_OK;
 }
@@ -708,20 +756,38 @@ int launch_attention(const dllm_kv_cache &c, const AttnPlan &p, const void *q, i
         return launch_status();
     }
     const bool e4 = c.dtype == DLLM_E4M3;
-#define DLLM_ATTN(DD, KV, MP, NTV) \
-    launch_mfma<DD, KV, 2, MP, NTV>(c, p, q, Hq, b, key_idx, n_keys, scale, out, out_dtype, lse, ws, s)
-#define DLLM_ATTN_NT(DD, KV, MP) (nt ? DLLM_ATTN(DD, KV, MP, true) : DLLM_ATTN(DD, KV, MP, false))
     const bool map = key_idx != nullptr;
     // stream K/V past the caches when only one row group reads each KV head
     const bool nt = p.row_groups == 1;
+    auto go = [&](auto dd, auto kv, auto mp) -> int {
+        constexpr int DD = decltype(dd)::value, KV = decltype(kv)::value;
+        constexpr bool MP = decltype(mp)::value;
+        constexpr int ES = KV == DLLM_E4M3 ? 1 : 2;
+        auto run = [&](auto ntv, auto nwv) -> int {
+            constexpr bool NTV = decltype(ntv)::value;
+            constexpr int NW = decltype(nwv)::value;
+            if constexpr (attn_smem_bytes(DD, ES, 2, NW, MP) <= kLdsBytes)
+                return launch_mfma<DD, KV, 2, MP, NTV, NW>(c, p, q, Hq, b, key_idx, n_keys, scale, out,
+                                                           out_dtype, lse, ws, s);
+            return DLLM_ESHAPE;                 // never planned
+        };
+        auto pick = [&](auto ntv) -> int {
+            if (p.waves == 4) return run(ntv, std::integral_constant<int, 4>{});
+            if (p.waves == 8) return run(ntv, std::integral_constant<int, 8>{});
+            return DLLM_ESHAPE;
+        };
+        return nt ? pick(std::true_type{}) : pick(std::false_type{});
+    };
+    using I64 = std::integral_constant<int, 64>;
+    using I128 = std::integral_constant<int, 128>;
+    using KB = std::integral_constant<int, DLLM_BF16>;
+    using KE = std::integral_constant<int, DLLM_E4M3>;
     if (c.d_head == 128) {
-        if (e4) return map ? DLLM_ATTN_NT(128, DLLM_E4M3, true) : DLLM_ATTN_NT(128, DLLM_E4M3, false);
-        return map ? DLLM_ATTN_NT(128, DLLM_BF16, true) : DLLM_ATTN_NT(128, DLLM_BF16, false);
+        if (e4) return map ? go(I128{}, KE{}, std::true_type{}) : go(I128{}, KE{}, std::false_type{});
+        return map ? go(I128{}, KB{}, std::true_type{}) : go(I128{}, KB{}, std::false_type{});
     }
     if (e4) return DLLM_ESHAPE;                 // e4m3 needs d % 128 == 0
-    return map ? DLLM_ATTN_NT(64, DLLM_BF16, true) : DLLM_ATTN_NT(64, DLLM_BF16, false);
-#undef DLLM_ATTN_NT
-#undef DLLM_ATTN
+    return map ? go(I64{}, KB{}, std::true_type{}) : go(I64{}, KB{}, std::false_type{});
 }
 
 }  // namespace dllm

@@ -70,6 +70,7 @@ int launch_attention(const dllm_kv_cache &c, const AttnPlan &p, const void *q, i
                      int out_dtype, float *lse, void *ws, hipStream_t s);
 
 struct VocabPlan {
+    int threads;       // workgroup size: 256, or 512 when there are few rows
     int splits;        // workgroups per row
     int64_t chunk;     // elements per split
     size_t ws_bytes;

@@ -3,8 +3,9 @@
 // over the row.  [SWD page, 3.1 and 4.2: per-position max probability and
 // its token; Flash-dLLM page, 3.1: entropy of the step's distribution.]
 //
-// One workgroup of 256 threads streams one row (or one contiguous split of
-// a row) with non-temporal 16-byte loads.  The loop is software-pipelined:
+// One workgroup of 256 threads (512 when there are too few rows to fill the
+// chip) streams one row, or one contiguous split of a row when there are very
+// few rows, with non-temporal 16-byte loads.  The loop is software-pipelined:
 // each thread keeps the next step's two loads in flight while it folds the
 // current two, so a wave never waits on memory with nothing issued.  The few
 // elements before the first 16-byte boundary and after the last are peeled
@@ -21,7 +22,6 @@
 namespace dllm {
 namespace {
 
-constexpr int kThreads = 256;   // four waves; measured ahead of 64, 128 and 512 with the pipelined loop
 constexpr int kUnroll = 2;      // 16-byte loads per thread per step (two steps in flight)
 constexpr float kNegInf = -__builtin_inff();
 
@@ -155,7 +155,7 @@ __device__ __forceinline__ void write_stats(const Acc &a, int64_t row, int32_t *
     entropy[row] = logf(a.s) - kLn2 * a.t / a.s;
 }
 
-template <int DT>
+template <int DT, int kThreads>
 __global__ __launch_bounds__(kThreads) void vocab_stats_kernel(
     const typename Elem<DT>::T *__restrict__ logits, int64_t V, int64_t stride, int64_t chunk,
     int splits, int32_t *__restrict__ argmax, float *__restrict__ maxprob,
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void vocab_stats_kernel(
         }
     }
 
-    // wave butterfly, then the four waves in order
+    // wave butterfly, then the waves in order
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
         Acc other{shfl_xor_f(st.m, o), shfl_xor_f(st.s, o), shfl_xor_f(st.t, o),
@@ -271,7 +271,13 @@ __global__ __launch_bounds__(256) void vocab_merge_kernel(const float4 *__restri
 
 VocabPlan plan_vocab(int64_t N, int64_t V) {
     VocabPlan p;
-    const int64_t target_blocks = 1536;     // one round of 6 four-wave workgroups per CU
+    // 256-thread workgroups take one row each once the rows fill a round of
+    // the chip (6 resident per CU); with fewer rows, 512-thread workgroups
+    // keep more loads in flight per row (measured 25 vs 30 us on 512 rows of
+    // 126464); below one row per CU the rows are split, with a merge pass.
+    const int64_t cus = 256;
+    p.threads = N >= 6 * cus ? 256 : 512;
+    const int64_t target_blocks = cus;
     const int64_t min_chunk = 16384;        // elements per split, at least
     int64_t splits = N > 0 ? cdiv64(target_blocks, N) : 1;
     splits = std::max<int64_t>(1, std::min<int64_t>(splits, cdiv64(V, min_chunk)));
@@ -291,14 +297,18 @@ int launch_vocab(const void *logits, int dtype, int64_t N, int64_t V, int64_t st
     const int64_t blocks = N * p.splits;
     if (blocks > INT_MAX) return DLLM_ERANGE;
     float4 *partial = static_cast<float4 *>(ws);
-    if (dtype == DLLM_BF16)
-        vocab_stats_kernel<DLLM_BF16><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
-            static_cast<const uint16_t *>(logits), V, stride, p.chunk, p.splits, argmax, maxprob,
-            entropy, partial);
-    else
-        vocab_stats_kernel<DLLM_F32><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
-            static_cast<const float *>(logits), V, stride, p.chunk, p.splits, argmax, maxprob,
-            entropy, partial);
+#define DLLM_VOCAB(DT, TT, T)                                                                     \
+    vocab_stats_kernel<DT, T><<<dim3((unsigned)blocks), dim3(T), 0, s>>>(                         \
+        static_cast<const TT *>(logits), V, stride, p.chunk, p.splits, argmax, maxprob, entropy, \
+        partial)
+    if (dtype == DLLM_BF16) {
+        if (p.threads == 256) DLLM_VOCAB(DLLM_BF16, uint16_t, 256);
+        else DLLM_VOCAB(DLLM_BF16, uint16_t, 512);
+    } else {
+        if (p.threads == 256) DLLM_VOCAB(DLLM_F32, float, 256);
+        else DLLM_VOCAB(DLLM_F32, float, 512);
+    }
+#undef DLLM_VOCAB
     int rc = launch_status();
     if (rc != DLLM_OK || p.splits == 1) return rc;
     vocab_merge_kernel<<<dim3((unsigned)cdiv64(N, 256)), dim3(256), 0, s>>>(partial, N, p.splits,

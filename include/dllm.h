@@ -180,7 +180,8 @@ int dllm_block_attention(const dllm_kv_cache *cache, const void *q, int q_dtype,
                          void *out, int out_dtype, float *lse,
                          void *workspace, size_t ws_bytes, void *stream);
 
-/* Workspace bytes dllm_block_attention needs for these shapes (0 if none). */
+/* Workspace bytes dllm_block_attention needs for these shapes, with or
+ * without a key map (0 if none: the keys are not split over workgroups). */
 size_t dllm_block_attention_workspace(const dllm_kv_cache *cache, int q_dtype, int Hq,
                                       int b, int n_keys);
 

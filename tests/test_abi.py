@@ -64,7 +64,13 @@ def test_host_validation_without_gpu(dl):
 def test_workspace_sizes(dl):
     L = dl.lib()
     assert L.dllm_vocab_stats_workspace(32768, 126464) == 0          # one workgroup per row
-    assert L.dllm_vocab_stats_workspace(512, 126464) > 0             # rows split across workgroups
+    assert L.dllm_vocab_stats_workspace(512, 126464) == 0            # one (wider) workgroup per row
+    assert L.dllm_vocab_stats_workspace(64, 126464) > 0              # rows split across workgroups
+    # 4 sequences x 8 KV heads x 8 row groups: 8-wave workgroups, no key split
     desc = dl._KVCache(B=4, L=32768, n_kv_heads=8, d_head=128, dtype=2, k=16, v=16, k_scale=16,
+                       v_scale=16)
+    assert L.dllm_block_attention_workspace(ctypes.byref(desc), 1, 32, 64, 8192) == 0
+    # one sequence: too few units even for 8-wave workgroups, so the keys split
+    desc = dl._KVCache(B=1, L=32768, n_kv_heads=8, d_head=128, dtype=2, k=16, v=16, k_scale=16,
                        v_scale=16)
     assert L.dllm_block_attention_workspace(ctypes.byref(desc), 1, 32, 64, 8192) > 0

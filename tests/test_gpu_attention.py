@@ -92,6 +92,37 @@ def test_attention_bf16_ragged(orc, d, Hq, Hkv, b, L):
     _check(orc, D, cache, q, key_idx=torch.from_numpy(kid).cuda(), label=f"bf16 d{d} map")
 
 
+@pytest.mark.parametrize("d,Hq,Hkv,b,L,dtype", [(64, 1, 1, 32, 4096, W.BF16), (128, 2, 2, 32, 3000, W.BF16),
+                                                (64, 3, 1, 20, 5000, W.BF16)])
+def test_attention_key_splits(orc, d, Hq, Hkv, b, L, dtype):
+    """one sequence with a long context: too few (sequence, KV head) units to
+    fill the chip even with wide workgroups, so the keys are split over
+    workgroups and the partials merged"""
+    D = need_gpu()
+    B = 1
+    cache = _fill(D, B, Hkv, L, d, dtype, seed=L, std=1 / np.sqrt(d))
+    assert D.dllm_block_attention_workspace(cache, W.BF16, Hq, b, L) > 0
+    g = torch.Generator().manual_seed(L + 1)
+    q = (torch.randn((B, Hq, b, d), generator=g) / np.sqrt(d)).bfloat16().cuda()
+    _check(orc, D, cache, q, label=f"split d{d} L{L}")
+    _check(orc, D, cache, (q.float() * 12 * np.sqrt(d)).bfloat16(), label=f"split d{d} L{L} sharp")
+
+
+def test_attention_e4m3_map_key_splits(orc):
+    """e4m3 cache, sinks + rolling window map of 8192 keys, one sequence:
+    8-wave workgroups with the keys split 8 ways"""
+    D = need_gpu()
+    B, Hkv, Hq, L, d, b = 1, 1, 4, 9000, 128, 64
+    S, R = 4, 8188
+    cache = _fill(D, B, Hkv, L, d, W.E4M3, seed=21, std=1 / np.sqrt(d))
+    assert D.dllm_block_attention_workspace(cache, W.BF16, Hq, b, S + R) > 0
+    q = (torch.randn((B, Hq, b, d), generator=torch.Generator().manual_seed(22)) / np.sqrt(d)).bfloat16().cuda()
+    kid = torch.empty((B, S + R), dtype=torch.int32, device="cuda")
+    D.dllm_sink_rolling_map(L, S, R, torch.tensor([L], dtype=torch.int32, device="cuda"), kid)
+    _check(orc, D, cache, q, key_idx=kid, label="e4m3 map split")
+    _check(orc, D, cache, (q.float() * 200).bfloat16(), key_idx=kid, label="e4m3 map split sharp")
+
+
 def test_attention_closed_forms_gpu(orc):
     D = need_gpu()
     B, H, L, d, b = 1, 2, 130, 128, 32
