@@ -127,9 +127,10 @@ class Step:
             self.st = D.StabilityState(B, L, cfg.D, device=dev)
             self.kw = dict(K=cfg.K, tau=cfg.tau, R=cfg.R, alpha=cfg.alpha, beta=cfg.beta,
                            lam=cfg.lam, conf_thresh=cfg.conf_thresh, V=cfg.V)
-        # the decode step number lives on the device, so a captured graph of
-        # several steps replays successive steps
-        self.step_t = torch.zeros(1, dtype=torch.int32, device=dev)
+        # per-sequence decode step numbers live on the device and the
+        # stability kernel advances them, so a captured graph of several steps
+        # replays successive steps
+        self.step_t = torch.zeros(B, dtype=torch.int32, device=dev)
 
     def kernels(self):
         ks = []
@@ -165,9 +166,8 @@ class Step:
             mark("stability", 0)
             B, L = cfg.B, cfg.L
             D.dllm_stability_mask(self.st, self.step_t, None, self.am.view(B, L), self.mp.view(B, L),
-                                  self.en.view(B, L), **self.kw)
+                                  self.en.view(B, L), advance_step=True, **self.kw)
             mark("stability", 1)
-            self.step_t.add_(1)
 
     def algorithmic_bytes(self):
         """bytes each kernel must move (reads + writes), per launch"""

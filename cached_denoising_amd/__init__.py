@@ -38,7 +38,7 @@ class _KVCache(ctypes.Structure):
 
 class _StabParams(ctypes.Structure):
     _fields_ = [("K", ctypes.c_int32), ("D", ctypes.c_int32), ("R", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("tau", ctypes.c_double), ("alpha", ctypes.c_double),
+                ("advance_step", ctypes.c_int32), ("tau", ctypes.c_double), ("alpha", ctypes.c_double),
                 ("beta", ctypes.c_double), ("lam", ctypes.c_double),
                 ("conf_thresh", ctypes.c_double), ("vocab", ctypes.c_int64)]
 
@@ -268,15 +268,18 @@ def dllm_stability_mask(st: StabilityState, step, pos: Optional[torch.Tensor],
                         argmax: torch.Tensor, maxprob: torch.Tensor, entropy: torch.Tensor, *,
                         K: int, tau: float, R: int, alpha: float = 0.0, beta: float = 0.0,
                         lam: float = 0.0, conf_thresh: float = 0.0, V: int = 2,
-                        with_conf: bool = True):
+                        with_conf: bool = True, advance_step: bool = False):
     """One step of history, stability, confidence and window mask; outputs
     land in st.mask, st.conf, st.next_pos, st.count, st.all_stable.  ``step``
-    is an int, or a one-element int32 GPU tensor read when the kernel runs
-    (for captured graphs)."""
+    is an int, or a [B] int32 GPU tensor of per-sequence step numbers read
+    when the kernel runs (for captured graphs); with ``advance_step`` the
+    kernel increments that tensor once it has used it."""
     n = pos.shape[1] if pos is not None else st.L
-    prm = _StabParams(K=K, D=st.D, R=R, reserved=0, tau=tau, alpha=alpha, beta=beta, lam=lam,
-                      conf_thresh=conf_thresh, vocab=V)
+    prm = _StabParams(K=K, D=st.D, R=R, advance_step=int(advance_step), tau=tau, alpha=alpha, beta=beta,
+                      lam=lam, conf_thresh=conf_thresh, vocab=V)
     if isinstance(step, torch.Tensor):
+        if step.dtype != torch.int32 or step.numel() != st.B:
+            raise ValueError("step tensor: [B] int32 per-sequence step numbers")
         step_host, step_dev = 0, _dev(step, "step")
     else:
         step_host, step_dev = int(step), None

@@ -177,7 +177,7 @@ int dllm_stability_reset(int B, int L, int D, int32_t *ring_argmax, float *ring_
                                   t_write, stable, static_cast<hipStream_t>(stream));
 }
 
-int dllm_stability_mask(int B, int L, int step, const int32_t *step_dev, const int32_t *pos, int n,
+int dllm_stability_mask(int B, int L, int step, int32_t *step_dev, const int32_t *pos, int n,
                         const int32_t *argmax, const float *maxprob, const float *entropy,
                         int32_t *ring_argmax, float *ring_maxprob, int32_t *ring_step,
                         float *entropy_latest, int32_t *t_write, uint8_t *stable,
@@ -190,6 +190,7 @@ int dllm_stability_mask(int B, int L, int step, const int32_t *step_dev, const i
     if (n < 0 || n > L) return DLLM_ESHAPE;
     const dllm_stab_params &p = *params;
     if (p.K < 1 || p.D < p.K || p.R < 0 || p.vocab < 2) return DLLM_EINVAL;
+    if (p.advance_step && !step_dev) return DLLM_EINVAL;   // nothing to advance
     if (!(p.tau == p.tau) || !(p.alpha == p.alpha) || !(p.beta == p.beta) ||
         !(p.lambda == p.lambda) || !(p.conf_thresh == p.conf_thresh))
         return DLLM_EINVAL;

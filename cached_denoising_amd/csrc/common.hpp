@@ -83,7 +83,7 @@ int launch_vocab(const void *logits, int dtype, int64_t N, int64_t V, int64_t st
 int launch_stability_reset(int B, int L, int D, int32_t *ring_argmax, float *ring_maxprob,
                            int32_t *ring_step, float *entropy_latest, int32_t *t_write,
                            uint8_t *stable, hipStream_t s);
-int launch_stability(int B, int L, int step, const int32_t *step_dev, const int32_t *pos, int n,
+int launch_stability(int B, int L, int step, int32_t *step_dev, const int32_t *pos, int n,
                      const int32_t *argmax,
                      const float *maxprob, const float *entropy, int32_t *ring_argmax,
                      float *ring_maxprob, int32_t *ring_step, float *entropy_latest,

@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void stability_reset_kernel(
 }
 
 __global__ __launch_bounds__(kThreads) void stability_kernel(
-    int B, int L, int step_arg, const int32_t *__restrict__ step_dev, const int32_t *__restrict__ pos, int n,
+    int B, int L, int step_arg, int32_t *__restrict__ step_dev, int advance, const int32_t *__restrict__ pos, int n,
     const int32_t *__restrict__ argmax, const float *__restrict__ maxprob,
     const float *__restrict__ entropy, int32_t *__restrict__ ring_argmax,
     float *__restrict__ ring_maxprob, int32_t *__restrict__ ring_step,
@@ -50,8 +50,8 @@ __global__ __launch_bounds__(kThreads) void stability_kernel(
     extern __shared__ uint32_t seed_bits[];            // one bit per position
     __shared__ int any_seed;
     __shared__ int wave_cnt[kWaves];
-    const int step = step_dev ? *step_dev : step_arg;
     const int b = blockIdx.x;
+    const int step = step_dev ? step_dev[b] : step_arg;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
@@ -157,6 +157,8 @@ __global__ __launch_bounds__(kThreads) void stability_kernel(
     if (tid == 0) {
         count[b] = base;
         all_stable[b] = none ? 1 : 0;
+        // every thread of this workgroup read step_dev[b] before the barriers above
+        if (advance) step_dev[b] = step + 1;
     }
 }
 
@@ -172,7 +174,7 @@ int launch_stability_reset(int B, int L, int D, int32_t *ring_argmax, float *rin
     return launch_status();
 }
 
-int launch_stability(int B, int L, int step, const int32_t *step_dev, const int32_t *pos, int n,
+int launch_stability(int B, int L, int step, int32_t *step_dev, const int32_t *pos, int n,
                      const int32_t *argmax,
                      const float *maxprob, const float *entropy, int32_t *ring_argmax,
                      float *ring_maxprob, int32_t *ring_step, float *entropy_latest,
@@ -183,7 +185,7 @@ int launch_stability(int B, int L, int step, const int32_t *step_dev, const int3
     const int words = cdiv(L, kThreads) * (kThreads / 32);   // whole 1024-position chunks
     const size_t shmem = sizeof(uint32_t) * (size_t)words;
     stability_kernel<<<dim3((unsigned)B), dim3(kThreads), shmem, s>>>(
-        B, L, step, step_dev, pos, n, argmax, maxprob, entropy, ring_argmax, ring_maxprob, ring_step,
+        B, L, step, step_dev, prm.advance_step, pos, n, argmax, maxprob, entropy, ring_argmax, ring_maxprob, ring_step,
         entropy_latest, t_write, stable, prm.K, prm.D, prm.R, prm.tau, prm.alpha, prm.beta,
         prm.lambda, prm.conf_thresh, hmax, mask, conf, next_pos, count, all_stable);
     return launch_status();

@@ -92,9 +92,12 @@ typedef struct {
  *                [Flash, 3.1]
  *   conf_thresh  positions whose confidence is below it are recomputed
  *                [Flash, 3.1]; <= 0 turns the gate off
- *   vocab        V of the vocab pass (max entropy ln V)                    */
+ *   vocab        V of the vocab pass (max entropy ln V)
+ *   advance_step nonzero: with per-sequence step numbers in device memory,
+ *                each sequence's number is incremented once the call has
+ *                used it (the decode loop's step counter, kept on the GPU) */
 typedef struct {
-    int32_t K, D, R, reserved;
+    int32_t K, D, R, advance_step;
     double tau, alpha, beta, lambda, conf_thresh;
     int64_t vocab;
 } dllm_stab_params;
@@ -237,13 +240,14 @@ int dllm_stability_reset(int B, int L, int D, int32_t *ring_argmax, float *ring_
  *   ring_*     [D, B, L] state; entropy_latest, t_write, stable [B, L] state
  *   mask [B, L] u8, conf [B, L] f32, next_pos [B, L] i32, count [B] i32,
  *   all_stable [B] u8: outputs (conf may be NULL)
- *   step_dev   optional device int32: when non-NULL the step number is read
- *              from it when the kernel runs (`step` is then ignored), so a
- *              captured graph of a decode step can be replayed for successive
- *              steps; the value must be >= 0.  May be NULL.
+ *   step_dev   optional [B] device int32: when non-NULL, sequence b's step
+ *              number is read from step_dev[b] when the kernel runs (`step`
+ *              is then ignored) and, with params->advance_step, written back
+ *              plus one, so a captured graph of a decode step replays as
+ *              successive steps; values must be >= 0.  May be NULL.
  * Limits: L <= 131072, 1 <= K <= D, R >= 0, vocab >= 2.
  * ------------------------------------------------------------------------- */
-int dllm_stability_mask(int B, int L, int step, const int32_t *step_dev, const int32_t *pos, int n,
+int dllm_stability_mask(int B, int L, int step, int32_t *step_dev, const int32_t *pos, int n,
                         const int32_t *argmax, const float *maxprob, const float *entropy,
                         int32_t *ring_argmax, float *ring_maxprob, int32_t *ring_step,
                         float *entropy_latest, int32_t *t_write, uint8_t *stable,

@@ -1,7 +1,8 @@
 """A decode step captured in a HIP graph replays to the same results as the
 same step launched eagerly: every replay is checked bit for bit, with the
-program's own eager work and synchronisations between replays.  The step
-number comes from device memory, so successive replays are successive steps."""
+program's own eager work and synchronisations between replays.  The
+per-sequence step numbers live in device memory and the stability kernel
+advances them, so successive replays are successive steps."""
 import dataclasses
 
 import pytest
@@ -34,7 +35,7 @@ class Step:
         self.vws = torch.empty(max(D.dllm_vocab_stats_workspace(N, cfg.V), 16), dtype=torch.uint8,
                                device="cuda")
         self.st = D.StabilityState(cfg.B, cfg.L, cfg.D)
-        self.step_t = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.step_t = torch.zeros(cfg.B, dtype=torch.int32, device="cuda")
         self.kw = dict(K=cfg.K, tau=cfg.tau, R=cfg.R, V=cfg.V)
 
     def run(self, which):
@@ -44,8 +45,8 @@ class Step:
         D.dllm_vocab_stats(self.logits[which], V=cfg.V, argmax=self.am, maxprob=self.mp,
                            entropy=self.en, workspace=self.vws)
         D.dllm_stability_mask(self.st, self.step_t, None, self.am.view(cfg.B, cfg.L),
-                              self.mp.view(cfg.B, cfg.L), self.en.view(cfg.B, cfg.L), **self.kw)
-        self.step_t.add_(1)
+                              self.mp.view(cfg.B, cfg.L), self.en.view(cfg.B, cfg.L), advance_step=True,
+                              **self.kw)
 
     def snapshot(self):
         st = self.st
@@ -76,7 +77,7 @@ def test_graph_replays_match_eager():
         graphs.append(g)
     torch.cuda.synchronize()
     # capturing runs nothing: the state is still the initial one
-    assert g_step.step_t.item() == 0
+    assert int(g_step.step_t.abs().sum()) == 0
     for i in range(4):
         graphs[i % 2].replay()
         torch.cuda.synchronize()

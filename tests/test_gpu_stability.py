@@ -166,3 +166,32 @@ def test_large_L_and_radius(orc):
         en = rng.uniform(0, 0.3, (B, L)).astype(np.float32)
         _step(orc, D, gst, ost, s, None, torch.from_numpy(am), torch.from_numpy(mp), torch.from_numpy(en),
               kw, "large L")
+
+
+def test_per_sequence_device_steps(orc):
+    """sequences at different decode steps: the [B] device step numbers are
+    read per sequence and advanced by the kernel; each sequence matches the
+    oracle run on its own with its own step numbers"""
+    D = need_gpu()
+    cfg = W.CONFIGS["vocab"]
+    B, L, T = 3, 257, 10
+    start = np.array([0, 5, 11], dtype=np.int32)
+    kw = dict(_kw(cfg), conf_thresh=0.8)
+    ams, mps, ens = _structured(cfg, B, L, T, seed=13)
+    gst = D.StabilityState(B, L, cfg.D)
+    osts = [orc.StabilityState(1, L, cfg.D) for _ in range(B)]
+    step_t = torch.from_numpy(start.copy()).cuda()
+    say("stability per-sequence steps", start.tolist())
+    for s in range(T):
+        D.dllm_stability_mask(gst, step_t, None, torch.from_numpy(ams[s]).cuda(), torch.from_numpy(mps[s]).cuda(),
+                              torch.from_numpy(ens[s]).cuda(), advance_step=True, **kw)
+        torch.cuda.synchronize()
+        for b in range(B):
+            r = orc.stability_step(osts[b], int(start[b]) + s, None, ams[s][b:b + 1], mps[s][b:b + 1],
+                                   ens[s][b:b + 1], **kw)
+            assert np.array_equal(gst.mask[b].cpu().numpy(), r["mask"][0]), (b, s)
+            assert np.array_equal(gst.next_pos[b].cpu().numpy(), r["next_pos"][0]), (b, s)
+            assert int(gst.count[b]) == int(r["count"][0]), (b, s)
+            assert np.array_equal(gst.stable[b].cpu().numpy(), osts[b].stable[0]), (b, s)
+            assert np.array_equal(gst.ring_step[:, b].cpu().numpy(), osts[b].ring_step[:, 0]), (b, s)
+    assert step_t.cpu().tolist() == (start + T).tolist()
