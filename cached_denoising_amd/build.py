@@ -17,7 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libdllm.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["api.hip", "scatter.hip", "attention.hip", "vocab_stats.hip", "stability.hip"]
+SOURCES = ["api.hip", "scatter.hip", "attention.hip", "attention_shared.hip", "vocab_stats.hip",
+           "stability.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

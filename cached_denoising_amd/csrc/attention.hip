@@ -26,7 +26,7 @@
 //   The waves merge through LDS in a fixed binary tree; key splits across
 //   workgroups write (m, l, O~) partials merged by a second kernel.
 // VALU path (float32 queries and cache, any d <= 256): one wave per query.
-#include "common.hpp"
+#include "attn_common.hpp"
 
 #include <climits>
 #include <type_traits>
@@ -34,124 +34,16 @@
 namespace dllm {
 namespace {
 
-constexpr float kNegInf = -__builtin_inff();
-constexpr float kLazy = 8.0f;          // log2 headroom before the running max moves
-constexpr float kMinit = -1.0e30f;     // finite start of the running max
+using namespace attn;
+
 constexpr int kMapTableTiles = 256;    // 32-key tiles of key indices a workgroup's LDS table holds
 constexpr int kStages = 2;             // key tiles per wave in the load pipeline (4 measured no faster)
-
-union Frag {
-    uint4 u;
-    bf16x8_t v;
-};
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    // one v_cvt_pk_bf16_f32: round to nearest even
-    const bf16x2_t p = __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t);
-    return __builtin_bit_cast(uint32_t, p);
-}
-
-// 8 e4m3 codes (two words) -> 8 bf16 (exact)
-__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
-    uint4 r;
-    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
-    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
-    r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
-    r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
-    return r;
-}
-
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef int v2i32_t __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) unsigned char lds_u8;
-
-// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i%4
-// of the 8 bytes addressed by lane 4r + i/4, for r = 0..3
-__device__ __forceinline__ uint2 lds_tr16(const unsigned char *p) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    typedef __attribute__((address_space(3))) v4i16_t lds_v4i16;
-    const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u8 *)p);
-    return __builtin_bit_cast(uint2, r);
-#else
-    (void)p;
-    return make_uint2(0, 0);
-#endif
-}
-
-// ds_read_b64_tr_b8: within each 16-lane group, lane i receives byte i%8 of
-// the 8 bytes addressed by lane 2r + i/8, for r = 0..7
-__device__ __forceinline__ uint2 lds_tr8(const unsigned char *p) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    typedef __attribute__((address_space(3))) v2i32_t lds_v2i32;
-    const v2i32_t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32 *)(lds_u8 *)p);
-    return __builtin_bit_cast(uint2, r);
-#else
-    (void)p;
-    return make_uint2(0, 0);
-#endif
-}
-
-// 16 bytes from global memory straight into LDS: lane i of the wave writes
-// lds_base + 16 i (lds_base is wave-uniform).  NT marks the load
-// non-temporal: right when the rows are read once, wrong when other
-// workgroups re-read them through L2.
-template <bool NT>
-__device__ __forceinline__ void lds_dma16(const unsigned char *src, unsigned char *lds_base) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(lds_u8 *)lds_base, 16, 0,
-                                     NT ? 2 : 0);
-#else
-    (void)src;
-    (void)lds_base;
-#endif
-}
-
-// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left at their maxima)
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// XOR swizzle of the 16-byte chunks of V row rho in LDS: the rows a 16-lane
-// transposed read touches land on distinct banks (bf16: 4 rows, 32-byte
-// windows; e4m3: 8 rows, 16-byte windows, two rows per 256 bytes)
-template <int KVDT>
-__device__ __forceinline__ int vswz(int rho) {
-    return KVDT == DLLM_E4M3 ? ((rho >> 1) & 3) : 2 * (rho & 3);
-}
-
-// key index of tile-local key k (or -1): NULL map means identity over [0, n_keys)
-__device__ __forceinline__ int key_at(const int32_t *kmap, int n_keys, int L, int j) {
-    if (j >= n_keys) return -1;
-    const int k = kmap ? kmap[j] : j;
-    return (k >= 0 && k < L) ? k : -1;
-}
-
-// First dim of k-chunk c (8 dims) held by lane group g in the first product.
-// Any assignment works as long as Q and K agree; this one makes the four lane
-// groups of one key row read 64 contiguous bytes per load instruction.  e4m3
-// rows load two chunks (16 codes) at once, bf16 rows one chunk (8 values).
-template <int KVDT>
-__device__ __forceinline__ int chunk_dim(int c, int g) {
-    if (KVDT == DLLM_E4M3) return ((c >> 1) * 4 + g) * 16 + (c & 1) * 8;
-    return (c * 4 + g) * 8;
-}
-
-// Logical block order that keeps the row groups of one (sequence, KV head,
-// split) on one XCD: workgroups are dealt to the 8 XCDs round robin.
-__device__ __forceinline__ int xcd_remap(int pid, int nblk) {
-    if ((nblk & 7) != 0) return pid;
-    const int per = nblk >> 3;
-    return (pid & 7) * per + (pid >> 3);
-}
 
 // LDS of one MFMA workgroup: the staged queries, kStages V tiles per wave
 // and, with a key map, the workgroup's table of key indices
 constexpr int attn_smem_bytes(int D, int esz, int RT, int NW, bool map) {
     return 16 * RT * (D * 2 + 16) + NW * kStages * 32 * D * esz + (map ? kMapTableTiles * 32 * 4 : 0);
 }
-constexpr int kLdsBytes = 160 * 1024;  // LDS of one gfx950 CU
 
 template <int D, int KVDT, int RT, bool MAP, bool NT, int NW>
 __global__ __launch_bounds__(NW * kWave, 2) void attn_mfma_kernel(
@@ -360,8 +252,7 @@ __global__ __launch_bounds__(NW * kWave, 2) void attn_mfma_kernel(
                 for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
                 mx *= scale_log2;
             }
-            mx = fmaxf(mx, shfl_xor_f(mx, 16));
-            mx = fmaxf(mx, shfl_xor_f(mx, 32));
+            mx = group4_max(mx);
             const bool grow = mx > m[rt] + kLazy;
             if (__ballot(grow)) {
                 if (grow) {
@@ -444,10 +335,7 @@ __global__ __launch_bounds__(NW * kWave, 2) void attn_mfma_kernel(
 
     // ---- row sums over the 4 lane groups
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        l[rt] += shfl_xor_f(l[rt], 16);
-        l[rt] += shfl_xor_f(l[rt], 32);
-    }
+    for (int rt = 0; rt < RT; ++rt) l[rt] = group4_sum(l[rt]);
 
     // ---- merge the waves through LDS: every wave rescales its O to the
     // workgroup's row max, then a fixed binary tree adds them up (at each
@@ -697,13 +585,18 @@ int launch_mfma(const dllm_kv_cache &c, const AttnPlan &p, const void *q, int Hq
         out, out_dtype, lse, part_o, part_ml);
     int rc = launch_status();
     if (rc != DLLM_OK || p.splits == 1) return rc;
-    const int64_t threads = rows_total * (D / 4);
-    attn_merge_kernel<<<dim3((unsigned)cdiv64(threads, 256)), dim3(256), 0, s>>>(
-        part_o, part_ml, rows_total, D, p.splits, out, out_dtype, lse);
-    return launch_status();
+    return launch_attn_merge(part_o, part_ml, rows_total, D, p.splits, out, out_dtype, lse, s);
 }
 
 }  // namespace
+
+int launch_attn_merge(const float *part_o, const float *part_ml, int64_t rows_total, int D,
+                      int splits, void *out, int out_dtype, float *lse, hipStream_t s) {
+    const int64_t threads = rows_total * (D / 4);
+    attn_merge_kernel<<<dim3((unsigned)cdiv64(threads, 256)), dim3(256), 0, s>>>(
+        part_o, part_ml, rows_total, D, splits, out, out_dtype, lse);
+    return launch_status();
+}
 
 int plan_attention(const dllm_kv_cache &c, int q_dtype, int Hq, int b, int n_keys, bool has_map, AttnPlan *p) {
     const int G = Hq / c.n_kv_heads;
@@ -714,6 +607,11 @@ int plan_attention(const dllm_kv_cache &c, int q_dtype, int Hq, int b, int n_key
     p->rows = M;
     if (!mfma) {
         p->path = 0;
+        return DLLM_OK;
+    }
+    // several 32-row groups per KV head: the waves of a workgroup share tiles
+    if (M > 32) {
+        plan_shared(c, Hq, b, cdiv(M, 32), n_keys, has_map, p);
         return DLLM_OK;
     }
     p->path = 1;
@@ -755,6 +653,8 @@ int launch_attention(const dllm_kv_cache &c, const AttnPlan &p, const void *q, i
             c.d_head, b, key_idx, n_keys, scale, out, out_dtype, lse);
         return launch_status();
     }
+    if (p.path == 2)
+        return launch_shared_attention(c, p, q, Hq, b, key_idx, n_keys, scale, out, out_dtype, lse, ws, s);
     const bool e4 = c.dtype == DLLM_E4M3;
     const bool map = key_idx != nullptr;
     // stream K/V past the caches when only one row group reads each KV head

@@ -54,17 +54,26 @@ int launch_sink_rolling(int B, int L, int S, int R, const int32_t *end, int32_t 
                         int n_keys, hipStream_t s);
 
 struct AttnPlan {
-    int path;          // 0: float32 VALU path, 1: MFMA path
+    int path;          // 0: float32 VALU path, 1: MFMA, keys per wave, 2: MFMA, tiles shared by the waves
     int rows;          // query rows per (batch, kv-head): G * b
     int row_tiles;     // 16-row tiles per wave (MFMA path)
     int row_groups;    // workgroups along the rows of one (batch, kv-head)
     int splits;        // key splits across workgroups
     int waves;         // waves per workgroup (MFMA path)
-    int tiles_per_wave;// 32-key tiles per wave
+    int tiles_per_wave;// 32-key tiles per wave (path 2: per workgroup, i.e. per split)
     size_t ws_bytes;   // partial-result workspace
 };
 int plan_attention(const dllm_kv_cache &c, int q_dtype, int Hq, int b, int n_keys, bool has_map,
                    AttnPlan *p);
+// the grouped-query layout (path 2), for more than one 32-row group per KV head
+void plan_shared(const dllm_kv_cache &c, int Hq, int b, int row_groups32, int n_keys, bool has_map,
+                 AttnPlan *p);
+int launch_shared_attention(const dllm_kv_cache &c, const AttnPlan &p, const void *q, int Hq, int b,
+                            const int32_t *key_idx, int n_keys, float scale, void *out,
+                            int out_dtype, float *lse, void *ws, hipStream_t s);
+// merge of the (m, l, O~) partials of key splits, in split order
+int launch_attn_merge(const float *part_o, const float *part_ml, int64_t rows_total, int D,
+                      int splits, void *out, int out_dtype, float *lse, hipStream_t s);
 int launch_attention(const dllm_kv_cache &c, const AttnPlan &p, const void *q, int q_dtype, int Hq,
                      int b, const int32_t *key_idx, int n_keys, float scale, void *out,
                      int out_dtype, float *lse, void *ws, hipStream_t s);

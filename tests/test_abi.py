@@ -66,11 +66,11 @@ def test_workspace_sizes(dl):
     assert L.dllm_vocab_stats_workspace(32768, 126464) == 0          # one workgroup per row
     assert L.dllm_vocab_stats_workspace(512, 126464) == 0            # one (wider) workgroup per row
     assert L.dllm_vocab_stats_workspace(64, 126464) > 0              # rows split across workgroups
-    # 4 sequences x 8 KV heads x 8 row groups: 8-wave workgroups, no key split
+    # 8 sequences x 12 KV heads, one 32-row group each: 8-wave workgroups, no key split
+    desc = dl._KVCache(B=8, L=1024, n_kv_heads=12, d_head=64, dtype=1, k=16, v=16)
+    assert L.dllm_block_attention_workspace(ctypes.byref(desc), 1, 12, 32, 1024) == 0
+    # 4 sequences x 8 KV heads x 256 grouped rows: one workgroup per KV head
+    # shares each tile, and the keys split over 8 workgroups
     desc = dl._KVCache(B=4, L=32768, n_kv_heads=8, d_head=128, dtype=2, k=16, v=16, k_scale=16,
                        v_scale=16)
-    assert L.dllm_block_attention_workspace(ctypes.byref(desc), 1, 32, 64, 8192) == 0
-    # one sequence: too few units even for 8-wave workgroups, so the keys split
-    desc = dl._KVCache(B=1, L=32768, n_kv_heads=8, d_head=128, dtype=2, k=16, v=16, k_scale=16,
-                       v_scale=16)
-    assert L.dllm_block_attention_workspace(ctypes.byref(desc), 1, 32, 64, 8192) > 0
+    assert L.dllm_block_attention_workspace(ctypes.byref(desc), 1, 32, 64, 8192) == 8 * 4 * 32 * 64 * 130 * 4
