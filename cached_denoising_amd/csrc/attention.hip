@@ -437,28 +437,52 @@ __global__ __launch_bounds__(NW * kWave, 2) void attn_mfma_kernel(
     }
 }
 
-// Merge of the key splits: one thread per (row, 4 dims), splits in order.
+// Merge of the key splits: one thread per (row, 4 dims), splits in order,
+// eight splits' loads in flight at once.
 __global__ __launch_bounds__(256) void attn_merge_kernel(
     const float *__restrict__ part_o, const float *__restrict__ part_ml, int64_t rows_total, int D,
     int splits, void *__restrict__ out, int out_dtype, float *__restrict__ lse) {
+    constexpr int kU = 8;                  // splits whose loads are in flight together
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int q4 = D / 4;
     if (t >= rows_total * q4) return;
     const int64_t row = t / q4;
     const int c = (int)(t - row * q4) * 4;
     float mm = kNegInf;
-    for (int s = 0; s < splits; ++s) mm = fmaxf(mm, part_ml[((int64_t)s * rows_total + row) * 2]);
+    for (int s0 = 0; s0 < splits; s0 += kU) {
+        float mv[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+            mv[u] = s0 + u < splits ? part_ml[((int64_t)(s0 + u) * rows_total + row) * 2] : kNegInf;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) mm = fmaxf(mm, mv[u]);
+    }
     float lt = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (mm != kNegInf) {
-        for (int s = 0; s < splits; ++s) {
-            const int64_t pr = (int64_t)s * rows_total + row;
-            const float ms = part_ml[pr * 2];
-            if (ms == kNegInf) continue;
-            const float f = __builtin_amdgcn_exp2f(ms - mm);
-            lt += part_ml[pr * 2 + 1] * f;
-            const float4 v = *reinterpret_cast<const float4 *>(part_o + pr * D + c);
-            acc.x += v.x * f; acc.y += v.y * f; acc.z += v.z * f; acc.w += v.w * f;
+        for (int s0 = 0; s0 < splits; s0 += kU) {
+            float ms[kU], ls[kU];
+            float4 v[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                ms[u] = kNegInf;
+                ls[u] = 0.f;
+                v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (s0 + u < splits) {
+                    const int64_t pr = (int64_t)(s0 + u) * rows_total + row;
+                    ms[u] = part_ml[pr * 2];
+                    ls[u] = part_ml[pr * 2 + 1];
+                    v[u] = *reinterpret_cast<const float4 *>(part_o + pr * D + c);
+                }
+            }
+            // in split order
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                if (ms[u] == kNegInf) continue;
+                const float f = __builtin_amdgcn_exp2f(ms[u] - mm);
+                lt += ls[u] * f;
+                acc.x += v[u].x * f; acc.y += v[u].y * f; acc.z += v[u].z * f; acc.w += v[u].w * f;
+            }
         }
     }
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
