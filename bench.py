@@ -26,9 +26,10 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0      # dense bf16 matrix peak of MI355X
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "cached_denoising_amd", "csrc")
-# the source file of each kernel whose counters a profile summary records
-KERNEL_SRC = {"vocab_stats": "vocab_stats.hip", "attention": "attention.hip",
-              "scatter": "scatter.hip", "stability": "stability.hip"}
+# the source files of each call whose counters a profile summary records
+KERNEL_SRC = {"vocab_stats": ["vocab_stats.hip"],
+              "attention": ["attention.hip", "attention_shared.hip", "attn_common.hpp"],
+              "scatter": ["scatter.hip"], "stability": ["stability.hip"]}
 
 
 def parse():
@@ -58,8 +59,11 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 5}), flush=True)
 
 
-def kernel_sha(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def kernel_sha(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel, config):
@@ -71,7 +75,7 @@ def measured_traffic(kernel, config):
     text = open(path).read()
     m_sha = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     m_tb = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_sha or not m_tb or m_sha.group(1) != kernel_sha(os.path.join(CSRC, KERNEL_SRC[kernel])):
+    if not m_sha or not m_tb or m_sha.group(1) != kernel_sha([os.path.join(CSRC, f) for f in KERNEL_SRC[kernel]]):
         return None
     return float(m_tb.group(1))
 
