@@ -424,10 +424,15 @@ __global__ __launch_bounds__(NW * kWave, 2) void attn_mfma_kernel(
             // partial of this split: unnormalised O~, running max (base 2), sum
             const int64_t prow = (int64_t)split * rows_total + orow;
 #pragma unroll
+            // the output's precision: bf16 partials for a bf16 output, else fp32
             for (int dt = 0; dt < NDT; ++dt) {
                 const f32x4_t v = o[dt][rt];
-                *reinterpret_cast<float4 *>(part_o + prow * D + dt * 16 + 4 * g) =
-                    make_float4(v[0], v[1], v[2], v[3]);
+                if (out_dtype == DLLM_F32)
+                    *reinterpret_cast<float4 *>(part_o + prow * D + dt * 16 + 4 * g) =
+                        make_float4(v[0], v[1], v[2], v[3]);
+                else
+                    *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(part_o) + prow * D + dt * 16 + 4 * g) =
+                        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
             }
             if (g == 0) {
                 part_ml[prow * 2 + 0] = Mrow[rt];
@@ -438,7 +443,9 @@ __global__ __launch_bounds__(NW * kWave, 2) void attn_mfma_kernel(
 }
 
 // Merge of the key splits: one thread per (row, 4 dims), splits in order,
-// eight splits' loads in flight at once.
+// eight splits' loads in flight at once.  The partial O~ is stored in the
+// output's precision (bf16 for a bf16 output, which halves the split
+// traffic; fp32 for an fp32 output); m and l are fp32.
 __global__ __launch_bounds__(256) void attn_merge_kernel(
     const float *__restrict__ part_o, const float *__restrict__ part_ml, int64_t rows_total, int D,
     int splits, void *__restrict__ out, int out_dtype, float *__restrict__ lse) {
@@ -472,7 +479,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
                     const int64_t pr = (int64_t)(s0 + u) * rows_total + row;
                     ms[u] = part_ml[pr * 2];
                     ls[u] = part_ml[pr * 2 + 1];
-                    v[u] = *reinterpret_cast<const float4 *>(part_o + pr * D + c);
+                    if (out_dtype == DLLM_F32) {
+                        v[u] = *reinterpret_cast<const float4 *>(part_o + pr * D + c);
+                    } else {
+                        const uint2 h = *reinterpret_cast<const uint2 *>(
+                            reinterpret_cast<const uint16_t *>(part_o) + pr * D + c);
+                        v[u] = make_float4(bf16lo(h.x), bf16hi(h.x), bf16lo(h.y), bf16hi(h.y));
+                    }
                 }
             }
             // in split order

@@ -4,9 +4,9 @@
 // sinks page, 2.1 and 2.3], laid out for shapes where several 32-row groups
 // of queries read each KV head (G query heads times b block queries > 32).
 //
-// A workgroup of NRG waves owns one (sequence, KV head, row chunk, key
-// split); wave w owns 32 rows of the chunk, and every wave walks the same key
-// tiles.  Each 32-key tile's K rows, V rows and (e4m3) per-key scales are
+// A workgroup of NRG (2 or 4) waves owns one (sequence, KV head, row chunk,
+// key split); wave w owns 32 rows of the chunk, and every wave walks the same
+// key tiles.  Each 32-key tile's K rows, V rows and (e4m3) per-key scales are
 // loaded once per workgroup, straight from HBM into a ring of kNS LDS stages
 // (global_load_lds, no registers), the loads of one tile spread over the
 // waves.  Per tile a wave waits for its own loads, then one workgroup
@@ -456,10 +456,15 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
         } else {
             const int64_t prow = (int64_t)split * rows_total + orow;
 #pragma unroll
+            // the output's precision: bf16 partials for a bf16 output, else fp32
             for (int dt = 0; dt < NDT; ++dt) {
                 const f32x4_t v = o[dt][rt];
-                *reinterpret_cast<float4 *>(part_o + prow * D + dt * 16 + 4 * g) =
-                    make_float4(v[0], v[1], v[2], v[3]);
+                if (out_dtype == DLLM_F32)
+                    *reinterpret_cast<float4 *>(part_o + prow * D + dt * 16 + 4 * g) =
+                        make_float4(v[0], v[1], v[2], v[3]);
+                else
+                    *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(part_o) + prow * D + dt * 16 + 4 * g) =
+                        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
             }
             if (g == 0) {
                 part_ml[prow * 2 + 0] = m[rt];
@@ -496,8 +501,11 @@ int launch_shared(const dllm_kv_cache &c, const AttnPlan &p, const void *q, int 
 
 void plan_shared(const dllm_kv_cache &c, int Hq, int b, int row_groups32, int n_keys, bool has_map,
                  AttnPlan *p) {
-    // waves per workgroup: one per 32-row group of the KV head, 2, 4 or 8
-    const int nrg = row_groups32 >= 5 ? 8 : row_groups32 >= 3 ? 4 : 2;
+    // waves per workgroup: one per 32-row group of the KV head, 2 or 4.  Two
+    // 4-wave workgroups per CU (a KV head's row chunks on one XCD) measured
+    // ahead of one 8-wave workgroup: the two run out of step, so one's
+    // softmax overlaps the other's products (74 against 78 us at longctx).
+    const int nrg = row_groups32 >= 3 ? 4 : 2;
     p->path = 2;
     p->row_tiles = 2;
     p->waves = nrg;
@@ -534,9 +542,6 @@ int launch_shared_attention(const dllm_kv_cache &c, const AttnPlan &p, const voi
                                                          out_dtype, lse, ws, s);
             if (p.waves == 4)
                 return launch_shared<DD, KV, MP, NTV, 4>(c, p, q, Hq, b, key_idx, n_keys, scale, out,
-                                                         out_dtype, lse, ws, s);
-            if (p.waves == 8)
-                return launch_shared<DD, KV, MP, NTV, 8>(c, p, q, Hq, b, key_idx, n_keys, scale, out,
                                                          out_dtype, lse, ws, s);
             return DLLM_ESHAPE;
         };
