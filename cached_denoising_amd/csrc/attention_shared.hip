@@ -80,8 +80,8 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
     constexpr int RPI = 64 / CPR;          // rows per 1 KB direct-to-LDS load
     constexpr int TB = 32 * ROWB;          // bytes of one K (or V) tile as cached
     constexpr int NK = TB / 1024;          // loads per K tile (as many for V)
-    constexpr int NI = 2 * NK + (E4 ? 1 : 0);          // per tile, plus one for the scales
-    constexpr int LMAX = (NI + NRG - 1) / NRG;         // loads one wave issues per tile, at most
+    static_assert(NK % NRG == 0, "every wave issues the same loads");
+    constexpr int LW = 2 * NK / NRG + (E4 ? 1 : 0);    // loads each wave issues per tile
     constexpr int STAGE = 2 * TB + (E4 ? 256 : 0);
     constexpr int BROW = D * 2;            // bytes of one bf16 row
     constexpr int CTB = 32 * BROW;         // one bf16 K (or V) tile
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
     constexpr int SMEM = kNS * STAGE + 2 * CSTAGE + TAB;
     static_assert(TB % 1024 == 0 && CPR <= 16, "tile layout");
     static_assert(SMEM <= kLdsBytes, "LDS of one workgroup");
-    static_assert((kNS - 2) * LMAX < 64, "vmcnt range");
+    static_assert((kNS - 2) * LW < 64, "vmcnt range");
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
 
@@ -130,40 +130,45 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
 
     uint4 qreg[RT][NC];                    // this wave's queries (loaded after the first tiles)
 
-    // ---- loads of tile kt into ring stage `slot`: load j of the tile is
-    // issued by wave j % NRG (K rows, then V rows, then the scales)
+    // ---- loads of tile kt into ring stage `slot`: every wave issues NK/NRG
+    // of the K tile's 1 KB loads, as many of the V tile's, and (e4m3) the
+    // scales of 64/NRG lanes, so every wave has LW loads per tile in flight
     auto issue = [&](int kt, int slot) {
         unsigned char *st = smem + slot * STAGE;
 #pragma unroll
-        for (int u = 0; u < LMAX; ++u) {
-            const int j = wave + u * NRG;
-            if (j < NK) {
-                // chunk position p of the tile: row p / CPR, stored slot p % CPR
-                // holds the row's chunk (p % CPR) ^ kswz(row)
-                const int p = j * 64 + lane;
-                const int r = p / CPR, sl = p % CPR;
-                const int kk = key_of(kt, r);
-                const unsigned char *src = static_cast<const unsigned char *>(ck) +
-                                           (kv_base + (kk < 0 ? 0 : kk)) * ROWB + (sl ^ kswz(r)) * 16;
-                lds_dma16<NT>(src, st + j * 1024);
-            } else if (j < 2 * NK) {
-                // V row rho, stored slot lane % CPR holds chunk (lane % CPR) ^ vswz(rho)
-                const int jv = j - NK;
-                const int rho = RPI * jv + lane / CPR;
-                const int chunk = (lane % CPR) ^ vswz<KVDT>(rho);
-                const int kk = key_of(kt, rho);
-                const unsigned char *src = static_cast<const unsigned char *>(cv) +
-                                           (kv_base + (kk < 0 ? 0 : kk)) * ROWB + chunk * 16;
-                lds_dma16<NT>(src, st + TB + jv * 1024);
-            } else if (E4 && j < NI) {
-                // lanes 0..31: K scales of keys 0..31; lanes 32..63: V scales
+        for (int u = 0; u < NK / NRG; ++u) {
+            // chunk position p of the tile: row p / CPR, stored slot p % CPR
+            // holds the row's chunk (p % CPR) ^ kswz(row)
+            const int j = wave * (NK / NRG) + u;
+            const int p = j * 64 + lane;
+            const int r = p / CPR, sl = p % CPR;
+            const int kk = key_of(kt, r);
+            const unsigned char *src = static_cast<const unsigned char *>(ck) +
+                                       (kv_base + (kk < 0 ? 0 : kk)) * ROWB + (sl ^ kswz(r)) * 16;
+            lds_dma16<NT>(src, st + j * 1024);
+        }
+#pragma unroll
+        for (int u = 0; u < NK / NRG; ++u) {
+            // V row rho, stored slot lane % CPR holds chunk (lane % CPR) ^ vswz(rho)
+            const int jv = wave * (NK / NRG) + u;
+            const int rho = RPI * jv + lane / CPR;
+            const int chunk = (lane % CPR) ^ vswz<KVDT>(rho);
+            const int kk = key_of(kt, rho);
+            const unsigned char *src = static_cast<const unsigned char *>(cv) +
+                                       (kv_base + (kk < 0 ? 0 : kk)) * ROWB + chunk * 16;
+            lds_dma16<NT>(src, st + TB + jv * 1024);
+        }
+        if (E4) {
+            // lanes 0..31: K scales of keys 0..31; lanes 32..63: V scales;
+            // this wave writes lanes [64 w / NRG, 64 (w + 1) / NRG)
+            const int lo = wave * (64 / NRG);
+            if (lane >= lo && lane < lo + 64 / NRG) {
                 const int kk = key_of(kt, lane & 31);
                 const float *src = (lane < 32 ? ksc : vsc) + kv_base + (kk < 0 ? 0 : kk);
                 lds_dma4(src, st + 2 * TB);
             }
         }
     };
-    const int my_loads = (NI - wave + NRG - 1) / NRG;   // loads this wave issues per tile
 
     // ---- e4m3: widen tile kt (ring stage `slot`) into converted stage
     // `cslot`, the whole workgroup sharing the work: each 16-code chunk
@@ -404,25 +409,36 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
         convert_write(0, c0);
     }
 
-    for (int i = 0; i < nt; ++i) {
-        // tiles issued after the one this iteration needs landed
-        const int ahead = CONV ? max(0, min(kNS - 2, nt - 2 - i)) : min(kNS - 2, nt - 1 - i);
+    // one e4m3 step: wait for the next tile's loads, one barrier, refill the
+    // stage this tile used, read the next tile for widening, compute this
+    // one and write the next one back under its first product (slot = i % kNS)
+    auto conv_step = [&](int i, int slot, auto wait) {
         __builtin_amdgcn_sched_barrier(0);
-        vm_wait_upto<(kNS - 2) * LMAX>(ahead * my_loads);
+        wait();
         ring_barrier();
         __builtin_amdgcn_sched_barrier(0);
+        if (i + kNS < nt) issue(t_begin + i + kNS, slot);
+        const bool next = i + 1 < nt;
+        ConvIn cn;
+        if (next) convert_read(t_begin + i + 1, (slot + 1) % kNS, cn);
+        const unsigned char *cs = cstage(slot & 1);
+        compute(t_begin + i, cs, cs + CTB, reinterpret_cast<const float *>(cs + 2 * CTB), [&] {
+            if (next) convert_write((slot + 1) & 1, cn);
+        });
+    };
+    int i = 0;
+    for (; i < nt; ++i) {
         if (CONV) {
-            if (i + kNS < nt) issue(t_begin + i + kNS, i % kNS);
-            // the next tile is read for widening now and written back under
-            // this tile's first product
-            const bool next = i + 1 < nt;
-            ConvIn cn;
-            if (next) convert_read(t_begin + i + 1, (i + 1) % kNS, cn);
-            const unsigned char *cs = cstage(i & 1);
-            compute(t_begin + i, cs, cs + CTB, reinterpret_cast<const float *>(cs + 2 * CTB), [&] {
-                if (next) convert_write((i + 1) & 1, cn);
-            });
+            // tiles issued after the next one
+            const int ahead = max(0, min(kNS - 2, nt - 2 - i));
+            conv_step(i, i % kNS, [&] { vm_wait_upto<(kNS - 2) * LW>(ahead * LW); });
         } else {
+            // tiles issued after this one
+            const int ahead = min(kNS - 2, nt - 1 - i);
+            __builtin_amdgcn_sched_barrier(0);
+            vm_wait_upto<(kNS - 2) * LW>(ahead * LW);
+            ring_barrier();
+            __builtin_amdgcn_sched_barrier(0);
             if (i + kNS - 1 < nt) issue(t_begin + i + kNS - 1, (i + kNS - 1) % kNS);
             const unsigned char *st = ring(i % kNS);
             compute(t_begin + i, st, st + TB, nullptr, [] {});
