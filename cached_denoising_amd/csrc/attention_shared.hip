@@ -132,8 +132,22 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
 
     // ---- loads of tile kt into ring stage `slot`: every wave issues NK/NRG
     // of the K tile's 1 KB loads, as many of the V tile's, and (e4m3) the
-    // scales of 64/NRG lanes, so every wave has LW loads per tile in flight
-    auto issue = [&](int kt, int slot) {
+    // scales of 64/NRG lanes, so every wave has LW loads per tile in flight.
+    // The rows' key indices are looked up first (keys_of) and the loads
+    // issued later (issue), so a key-table read is not waited for on its own.
+    struct TileKeys {
+        int k[NK / NRG], v[NK / NRG], s;
+    };
+    auto keys_of = [&](int kt, TileKeys &tk) {
+#pragma unroll
+        for (int u = 0; u < NK / NRG; ++u) {
+            const int j = wave * (NK / NRG) + u;
+            tk.k[u] = key_of(kt, (j * 64 + lane) / CPR);
+            tk.v[u] = key_of(kt, RPI * j + lane / CPR);
+        }
+        tk.s = E4 ? key_of(kt, lane & 31) : 0;
+    };
+    auto issue = [&](const TileKeys &tk, int slot) {
         unsigned char *st = smem + slot * STAGE;
 #pragma unroll
         for (int u = 0; u < NK / NRG; ++u) {
@@ -142,7 +156,7 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
             const int j = wave * (NK / NRG) + u;
             const int p = j * 64 + lane;
             const int r = p / CPR, sl = p % CPR;
-            const int kk = key_of(kt, r);
+            const int kk = tk.k[u];
             const unsigned char *src = static_cast<const unsigned char *>(ck) +
                                        (kv_base + (kk < 0 ? 0 : kk)) * ROWB + (sl ^ kswz(r)) * 16;
             lds_dma16<NT>(src, st + j * 1024);
@@ -153,7 +167,7 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
             const int jv = wave * (NK / NRG) + u;
             const int rho = RPI * jv + lane / CPR;
             const int chunk = (lane % CPR) ^ vswz<KVDT>(rho);
-            const int kk = key_of(kt, rho);
+            const int kk = tk.v[u];
             const unsigned char *src = static_cast<const unsigned char *>(cv) +
                                        (kv_base + (kk < 0 ? 0 : kk)) * ROWB + chunk * 16;
             lds_dma16<NT>(src, st + TB + jv * 1024);
@@ -163,11 +177,16 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
             // this wave writes lanes [64 w / NRG, 64 (w + 1) / NRG)
             const int lo = wave * (64 / NRG);
             if (lane >= lo && lane < lo + 64 / NRG) {
-                const int kk = key_of(kt, lane & 31);
+                const int kk = tk.s;
                 const float *src = (lane < 32 ? ksc : vsc) + kv_base + (kk < 0 ? 0 : kk);
                 lds_dma4(src, st + 2 * TB);
             }
         }
+    };
+    auto issue_tile = [&](int kt, int slot) {
+        TileKeys tk;
+        keys_of(kt, tk);
+        issue(tk, slot);
     };
 
     // ---- e4m3: widen tile kt (ring stage `slot`) into converted stage
@@ -385,7 +404,7 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
     const int pro = CONV ? kNS : kNS - 1;
 #pragma unroll
     for (int i = 0; i < kNS; ++i)
-        if (i < pro && i < nt) issue(t_begin + i, i);
+        if (i < pro && i < nt) issue_tile(t_begin + i, i);
 
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -417,12 +436,18 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
         wait();
         ring_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        if (i + kNS < nt) issue(t_begin + i + kNS, slot);
+        // the refill's key indices and the next tile's raw chunks are read
+        // now; the refill is issued and the widening written back under this
+        // tile's first product
+        const bool refill = i + kNS < nt;
+        TileKeys tk;
+        if (refill) keys_of(t_begin + i + kNS, tk);
         const bool next = i + 1 < nt;
         ConvIn cn;
         if (next) convert_read(t_begin + i + 1, (slot + 1) % kNS, cn);
         const unsigned char *cs = cstage(slot & 1);
         compute(t_begin + i, cs, cs + CTB, reinterpret_cast<const float *>(cs + 2 * CTB), [&] {
+            if (refill) issue(tk, slot);
             if (next) convert_write((slot + 1) & 1, cn);
         });
     };
@@ -439,7 +464,7 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
             vm_wait_upto<(kNS - 2) * LW>(ahead * LW);
             ring_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            if (i + kNS - 1 < nt) issue(t_begin + i + kNS - 1, (i + kNS - 1) % kNS);
+            if (i + kNS - 1 < nt) issue_tile(t_begin + i + kNS - 1, (i + kNS - 1) % kNS);
             const unsigned char *st = ring(i % kNS);
             compute(t_begin + i, st, st + TB, nullptr, [] {});
         }
