@@ -76,6 +76,9 @@ def lib():
         L.oracle_block_attention.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, i32, P, i32, i32,
                                              P, i32, dbl, P, P, P, i32]
         L.oracle_block_attention.restype = i32
+        L.oracle_facache_merge.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, i32, P, i32, i32,
+                                           P, P, P, i32, dbl, P, P, P, i32]
+        L.oracle_facache_merge.restype = i32
         L.oracle_vocab_stats.argtypes = [i32, P, i64, i64, i64, P, P, P, P, i64]
         L.oracle_vocab_stats.restype = i32
         L.oracle_stability_step.argtypes = [i32, i32, i32, P, i32, P, P, P, P, P, P, P, P, P,
@@ -187,6 +190,65 @@ def block_attention(cache_k, cache_v, k_scale, v_scale, cache_dtype, q, q_dtype,
                                       _ptr(key_idx), n_keys, float(scale), _ptr(out), _ptr(lse),
                                       _ptr(heads), nh)
     _check(rc, "block_attention")
+    return out, lse
+
+
+# ---- N1 ---------------------------------------------------------------------
+
+def facache_key_maps(L: int, b: int, start) -> tuple[np.ndarray, np.ndarray]:
+    """Unchanged and changed key positions of a SAR step, per sequence.
+
+    [LaCache, problem statement and Methodology 1]: within one block's
+    denoising steps the prompt and the masked suffix keep their token ids,
+    only the active block [start, start + b) changes.  Returns
+    (unchanged [B, L - b], block [B, b]), both ascending int32.
+    """
+    start = np.asarray(start, dtype=np.int64).reshape(-1)
+    B = start.size
+    un = np.zeros((B, L - b), dtype=np.int32)
+    blk = np.zeros((B, b), dtype=np.int32)
+    for i, o in enumerate(start):
+        if not 0 <= o <= L - b:
+            raise ValueError("oracle facache_key_maps: block outside the sequence")
+        allpos = np.arange(L)
+        inside = (allpos >= o) & (allpos < o + b)
+        un[i] = allpos[~inside]
+        blk[i] = allpos[inside]
+    return un, blk
+
+
+def facache_merge(cache_k, cache_v, k_scale, v_scale, cache_dtype, q, q_dtype, memo_o, memo_lse,
+                  key_idx=None, scale=0.0, heads=None):
+    """Memoized state (memo_o = O~/l, memo_lse = m + ln l) continued over the
+    listed keys, then normalised, fp64.  Shapes and ``heads`` as in
+    ``block_attention`` with b = n_q; memo_o [B, Hq, n_q, d] and memo_lse
+    [B, Hq, n_q] are float32.
+    """
+    B, Hkv, L, d = cache_k.shape
+    _, Hq, n_q, _ = q.shape
+    q = np.ascontiguousarray(q)
+    memo_o = np.ascontiguousarray(memo_o, dtype=np.float32)
+    memo_lse = np.ascontiguousarray(memo_lse, dtype=np.float32)
+    assert memo_o.shape == (B, Hq, n_q, d) and memo_lse.shape == (B, Hq, n_q)
+    if key_idx is not None:
+        key_idx = np.ascontiguousarray(key_idx, dtype=np.int32)
+        n_keys = key_idx.shape[1]
+    else:
+        n_keys = L
+    if heads is not None:
+        heads = np.ascontiguousarray(heads, dtype=np.int32).reshape(-1, 2)
+        nh = heads.shape[0]
+        out = np.zeros((nh, n_q, d))
+        lse = np.zeros((nh, n_q))
+    else:
+        nh = 0
+        out = np.zeros((B, Hq, n_q, d))
+        lse = np.zeros((B, Hq, n_q))
+    rc = lib().oracle_facache_merge(cache_dtype, B, L, Hkv, d, _ptr(cache_k), _ptr(cache_v),
+                                    _ptr(k_scale), _ptr(v_scale), q_dtype, _ptr(q), Hq, n_q,
+                                    _ptr(memo_o), _ptr(memo_lse), _ptr(key_idx), n_keys,
+                                    float(scale), _ptr(out), _ptr(lse), _ptr(heads), nh)
+    _check(rc, "facache_merge")
     return out, lse
 
 

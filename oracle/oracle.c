@@ -297,6 +297,96 @@ int oracle_block_attention(int cache_dtype, int B, int L, int Hkv, int d,
 }
 
 /* ------------------------------------------------------------------------ */
+/* N1: FACache merge                                                         */
+/* ------------------------------------------------------------------------ */
+
+/* The memoized state of a query over the unchanged keys initialises the
+ * online softmax; the changed keys are then folded in as one more tile
+ * [LaCache, Methodology 1: FACache keeps m, l and O~ of query tiles outside
+ * the active block and, when only the KV tile is new, starts from them]. */
+int oracle_facache_merge(int cache_dtype, int B, int L, int Hkv, int d,
+                         const void *cache_k, const void *cache_v,
+                         const float *k_scale, const float *v_scale,
+                         int q_dtype, const void *q, int Hq, int n_q,
+                         const float *memo_o, const float *memo_lse,
+                         const int32_t *key_idx, int n_keys, double scale,
+                         double *out, double *lse,
+                         const int32_t *heads, int n_heads)
+{
+    int64_t task, n_tasks;
+    int group, err = 0;
+    if (B <= 0 || L <= 0 || Hkv <= 0 || d <= 0 || Hq <= 0 || n_q <= 0) return -1;
+    if (Hq % Hkv != 0 || !memo_o || !memo_lse) return -1;
+    if (cache_dtype == ORC_E4M3 && (d % 128 != 0 || !k_scale || !v_scale)) return -1;
+    if (!key_idx) n_keys = L;
+    if (n_keys < 0) return -1;
+    if (key_idx) {
+        int64_t i;
+        for (i = 0; i < (int64_t)B * n_keys; ++i)
+            if (key_idx[i] < -1 || key_idx[i] >= L) return -1;
+    }
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
+    group = Hq / Hkv;
+    n_tasks = heads ? (int64_t)n_heads : (int64_t)B * Hq;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (task = 0; task < n_tasks; ++task) {
+        int bi, h, kvh, i, j, c;
+        double *s = (double *)malloc(sizeof(double) * (size_t)(n_keys > 0 ? n_keys : 1));
+        double *acc = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!s || !acc) { free(s); free(acc); err = 1; continue; }
+        if (heads) { bi = heads[2 * task]; h = heads[2 * task + 1]; }
+        else { bi = (int)(task / Hq); h = (int)(task % Hq); }
+        kvh = h / group;
+        for (i = 0; i < n_q; ++i) {
+            int64_t row = ((int64_t)bi * Hq + h) * n_q + i;
+            int64_t qrow = row * d;
+            int64_t orow = (task * n_q + i) * d;
+            /* the memoized state: m' = lse, l' = 1, O~' = O (or empty) */
+            double m0 = (double)memo_lse[row];
+            double l0 = m0 == -INFINITY ? 0.0 : 1.0;
+            double m_new = m0, l_new, f0;
+            /* scores of the changed keys */
+            for (j = 0; j < n_keys; ++j) {
+                int key = key_idx ? key_idx[(int64_t)bi * n_keys + j] : j;
+                int64_t krow = ((int64_t)bi * Hkv + kvh) * L + key;
+                double dot = 0.0;
+                if (key < 0) { s[j] = -INFINITY; continue; }
+                for (c = 0; c < d; ++c)
+                    dot += load_src(q_dtype, q, qrow + c) *
+                           cache_value(cache_dtype, cache_k, k_scale, krow, d, c);
+                s[j] = scale * dot;
+                if (s[j] > m_new) m_new = s[j];
+            }
+            if (m_new == -INFINITY) {            /* empty memo and no key */
+                for (c = 0; c < d; ++c) out[orow + c] = 0.0;
+                if (lse) lse[task * n_q + i] = -INFINITY;
+                continue;
+            }
+            /* rescale the memo to the new reference, then add the keys */
+            f0 = l0 > 0.0 ? exp(m0 - m_new) : 0.0;
+            l_new = l0 * f0;
+            for (c = 0; c < d; ++c) acc[c] = l0 > 0.0 ? (double)memo_o[qrow + c] * f0 : 0.0;
+            for (j = 0; j < n_keys; ++j) {
+                int key = key_idx ? key_idx[(int64_t)bi * n_keys + j] : j;
+                int64_t vrow = ((int64_t)bi * Hkv + kvh) * L + key;
+                double p;
+                if (key < 0) continue;
+                p = exp(s[j] - m_new);
+                l_new += p;
+                for (c = 0; c < d; ++c)
+                    acc[c] += p * cache_value(cache_dtype, cache_v, v_scale, vrow, d, c);
+            }
+            for (c = 0; c < d; ++c) out[orow + c] = acc[c] / l_new;
+            if (lse) lse[task * n_q + i] = m_new + log(l_new);
+        }
+        free(s);
+        free(acc);
+    }
+    return err ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* A4: vocab statistics                                                      */
 /* ------------------------------------------------------------------------ */
 

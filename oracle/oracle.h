@@ -90,6 +90,29 @@ int oracle_block_attention(int cache_dtype, int B, int L, int Hkv, int d,
                            double *out, double *lse,
                            const int32_t *heads, int n_heads);
 
+/* ---- N1: FACache merge [LaCache, Methodology 1 (FACache) and 3] --------
+ * For queries whose memoized online-softmax state over the unchanged keys
+ * is given, continue that state over the listed (changed) keys and
+ * normalise.  The memo of a row is stored normalised: memo_o = O~/l and
+ * memo_lse = m + ln l (natural log), i.e. the state (m, l, O~) with its
+ * reference point moved to m' = memo_lse, l' = 1, O~' = memo_o; a row with
+ * memo_lse = -inf has an empty memo (l' = 0, memo_o ignored).
+ * Per query row, with s_j = scale * q . k_j over the listed keys:
+ *   m_new = max(m', max_j s_j)
+ *   l_new = l' e^(m' - m_new) + sum_j e^(s_j - m_new)
+ *   O_new = O~' e^(m' - m_new) + sum_j e^(s_j - m_new) v_j
+ *   out = O_new / l_new, lse = m_new + ln l_new (0 and -inf when l_new = 0).
+ * q: [B, Hq, n_q, d]; memo_o: [B, Hq, n_q, d] float; memo_lse: [B, Hq, n_q]
+ * float; key_idx, cache, scale, heads, out, lse as in A3 (b = n_q). */
+int oracle_facache_merge(int cache_dtype, int B, int L, int Hkv, int d,
+                         const void *cache_k, const void *cache_v,
+                         const float *k_scale, const float *v_scale,
+                         int q_dtype, const void *q, int Hq, int n_q,
+                         const float *memo_o, const float *memo_lse,
+                         const int32_t *key_idx, int n_keys, double scale,
+                         double *out, double *lse,
+                         const int32_t *heads, int n_heads);
+
 /* ---- A4: vocab statistics per row ---------------------------------------
  * p = softmax(x); argmax = lowest index of the largest logit; maxprob =
  * max_j p_j; entropy = -sum p_j ln p_j (terms with p_j = 0 add nothing).
