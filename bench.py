@@ -6,6 +6,14 @@ at a per-sequence offset, vocab 50257 bf16 logits for every position):
     dllm_scatter_kv -> dllm_block_attention -> dllm_vocab_stats -> dllm_stability_mask
 all on one stream with inputs resident in HBM.  Prints one JSON line.
 
+With --config facache a step is the first-layer attention of a later
+denoising step of a LLaDA-shaped block with FACache (B=16, L=2048, 32 heads
+x 128, block 32): scatter the block's K/V, the block's queries over all L
+keys, and the 2016 queries outside the block continued from their memoized
+state over the 32 block keys.  The memo is filled once, before the timed
+steps (the block's first step); a full recompute of all 2048 queries over
+all 2048 keys is timed beside it.
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config gpt2]
 """
 from __future__ import annotations
@@ -29,6 +37,7 @@ CSRC = os.path.join(ROOT, "cached_denoising_amd", "csrc")
 # the source files of each call whose counters a profile summary records
 KERNEL_SRC = {"vocab_stats": ["vocab_stats.hip"],
               "attention": ["attention.hip", "attention_shared.hip", "attn_common.hpp"],
+              "facache_merge": ["attention.hip", "attention_shared.hip", "attn_common.hpp"],
               "scatter": ["scatter.hip"], "stability": ["stability.hip"]}
 
 
@@ -37,7 +46,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="gpt2", choices=["gpt2", "llada", "vocab", "longctx"])
+    ap.add_argument("--config", default="gpt2", choices=["gpt2", "llada", "vocab", "longctx", "facache"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from Python instead of replaying a captured graph")
@@ -83,14 +92,15 @@ def measured_traffic(kernel, config):
 class Step:
     """All device buffers of one workload and the kernels of one step."""
 
-    def __init__(self, D, W, cfg, dev):
+    def __init__(self, D, W, cfg, dev, facache=False):
         import torch
         self.D, self.W, self.cfg, self.dev = D, W, cfg, dev
         B, L, H, d = cfg.B, cfg.L, cfg.Hkv, cfg.d
         kvt = {W.BF16: torch.bfloat16, W.E4M3: torch.uint8, W.F32: torch.float32}[cfg.kv_dtype]
         self.has_attn = cfg.b > 0 and d > 0 and cfg.name != "vocab"
-        self.has_vocab = cfg.V > 0
-        self.has_stab = cfg.name in ("gpt2", "vocab", "tiny")
+        self.has_vocab = cfg.V > 0 and not facache
+        self.has_stab = cfg.name in ("gpt2", "vocab", "tiny") and not facache
+        self.facache = facache
         self.attn_split = False
         if self.has_attn:
             k = torch.empty((B, H, L, d), dtype=kvt, device=dev)
@@ -118,6 +128,18 @@ class Step:
             self.attn_ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
             # a workspace is needed only when the keys are split over workgroups
             self.attn_split = wsb > 0
+        if facache:
+            # the memo of the queries outside the block over the unchanged keys,
+            # filled once (the block's first step)
+            self.n_q = L - cfg.b
+            self.un, self.blk = D.dllm_facache_maps(L, cfg.b, self.pos[:, 0].contiguous())
+            self.qu = W.outside_queries(cfg, device=dev)
+            self.memo_lse = torch.empty((B, cfg.Hq, self.n_q), dtype=torch.float32, device=dev)
+            self.memo_o = D.dllm_block_attention(self.cache, self.qu, key_idx=self.un,
+                                                 out_dtype=torch.float32, lse=self.memo_lse)
+            self.out_u = torch.empty((B, cfg.Hq, self.n_q, d), dtype=torch.bfloat16, device=dev)
+            wsb = D.dllm_facache_merge_workspace(self.cache, W.BF16, cfg.Hq, self.n_q, cfg.b)
+            self.fa_ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
         if self.has_vocab:
             self.logits = W.logits(cfg, device=dev)
             N = self.logits.shape[0]
@@ -140,6 +162,8 @@ class Step:
         ks = []
         if self.has_attn:
             ks += ["scatter", "attention"]
+        if self.facache:
+            ks.append("facache_merge")
         if self.has_vocab:
             ks.append("vocab_stats")
         if self.has_stab:
@@ -161,6 +185,11 @@ class Step:
             D.dllm_block_attention(self.cache, self.q, key_idx=self.key_idx, out=self.out,
                                    workspace=self.attn_ws)
             mark("attention", 1)
+        if self.facache:
+            mark("facache_merge", 0)
+            D.dllm_facache_merge(self.cache, self.qu, self.memo_o, self.memo_lse, key_idx=self.blk,
+                                 out=self.out_u, workspace=self.fa_ws)
+            mark("facache_merge", 1)
         if self.has_vocab:
             mark("vocab_stats", 0)
             D.dllm_vocab_stats(self.logits, V=cfg.V, argmax=self.am, maxprob=self.mp,
@@ -185,6 +214,12 @@ class Step:
             kv = cfg.B * cfg.Hkv * self.n_keys * (cfg.d * esz * 2 + scale_b)
             qo = cfg.B * cfg.Hq * cfg.b * cfg.d * 2 * 2
             out["attention"] = kv + qo
+        if self.facache:
+            rows = cfg.B * cfg.Hq * self.n_q
+            # queries and output in bf16, the memo (O and lse) in fp32, the
+            # block's K/V rows and its key list
+            out["facache_merge"] = (rows * (cfg.d * 2 * 2 + (cfg.d + 1) * 4)
+                                    + cfg.B * cfg.Hkv * cfg.b * cfg.d * 2 * 2 + cfg.B * cfg.b * 4)
         if self.has_vocab:
             out["vocab_stats"] = self.N * cfg.V * 2 + self.N * 12
         if self.has_stab:
@@ -201,7 +236,28 @@ class Step:
         cfg = self.cfg
         if not self.has_attn:
             return {}
-        return {"attention": 4 * cfg.B * cfg.Hq * cfg.b * self.n_keys * cfg.d}
+        out = {"attention": 4 * cfg.B * cfg.Hq * cfg.b * self.n_keys * cfg.d}
+        if self.facache:
+            out["facache_merge"] = 4 * cfg.B * cfg.Hq * self.n_q * cfg.b * cfg.d
+        return out
+
+    def full_recompute_us(self, reps=3):
+        """the first-layer attention without FACache: all L queries over all
+        L keys, timed alone (a full forward's attention)"""
+        import torch
+        cfg = self.cfg
+        qall = self.W.queries(cfg, device=self.dev, b=cfg.L)
+        out = torch.empty((cfg.B, cfg.Hq, cfg.L, cfg.d), dtype=torch.bfloat16, device=self.dev)
+        run = lambda: self.D.dllm_block_attention(self.cache, qall, out=out)
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        return 1000.0 * e0.elapsed_time(e1) / reps
 
 
 def cpu_baseline(step, D, W, cfg):
@@ -239,6 +295,18 @@ def cpu_baseline(step, D, W, cfg):
                           W.BF16, step.pos.cpu().numpy())
         t_total += time.perf_counter() - t0
         parts.append(f"attention on {ns} of {n_heads} (sequence, head) pairs; full scatter")
+    if step.facache:
+        ck, cv = W.as_numpy_bits(step.cache.k), W.as_numpy_bits(step.cache.v)
+        n_heads = cfg.B * cfg.Hq
+        ns = min(n_heads, 8)
+        heads = np.stack([np.arange(ns) % cfg.B, np.arange(ns) % cfg.Hq], 1).astype(np.int32)
+        mo, ml = step.memo_o.cpu().numpy(), step.memo_lse.cpu().numpy()
+        qu = W.as_numpy_bits(step.qu)
+        t0 = time.perf_counter()
+        oracle.facache_merge(ck, cv, None, None, cfg.kv_dtype, qu, W.BF16, mo, ml,
+                             key_idx=step.blk.cpu().numpy(), heads=heads)
+        t_total += (time.perf_counter() - t0) * n_heads / ns
+        parts.append(f"FACache merge on {ns} of {n_heads} (sequence, head) pairs")
     if step.has_stab:
         ost = oracle.StabilityState(cfg.B, cfg.L, cfg.D)
         am = step.am.cpu().numpy().reshape(cfg.B, cfg.L)
@@ -272,8 +340,8 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
-    cfg = W.CONFIGS[args.config]
-    step = Step(D, W, cfg, dev)
+    cfg = W.CONFIGS["llada" if args.config == "facache" else args.config]
+    step = Step(D, W, cfg, dev, facache=args.config == "facache")
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
@@ -338,6 +406,15 @@ def main():
                      "avg_launch_us": round(dom_us, 2), "kernel_timing": kernel_timing})
     if dom == "attention" and step.attn_split:
         roofline["kernel_note"] = "attention call = attn_mfma_kernel + attn_merge_kernel of the key splits"
+    if dom == "facache_merge":
+        roofline["kernel_note"] = "facache_merge call = attn_shared_kernel started from the memo, one key tile"
+    extra = {}
+    if step.facache:
+        full = step.full_recompute_us()
+        fa = per_kernel_us["attention"] + per_kernel_us["facache_merge"]
+        extra = {"full_recompute_attention_us": round(full, 1),
+                 "facache_attention_us": round(fa, 1),
+                 "facache_speedup_vs_full": round(full / fa, 2)}
     cpu = None if args.no_cpu_baseline else cpu_baseline(step, D, W, cfg)
     desc = {
         "gpt2": "GPT-2-small-shaped decode step: B=8, L=1024, 12 heads x d64, bf16 K/V cache, "
@@ -348,9 +425,14 @@ def main():
         "vocab": "vocab-stats sweep: 32768 rows x 126464 bf16 logits, 64-step ring, K=3 tau=0.9 R=3",
         "longctx": "long-context step: B=4, L=32768, 32/8 GQA heads x d128, e4m3 K/V with "
                    "per-128 scales, block 64, 4 sinks + 8188 rolling keys",
+        "facache": "LLaDA-8B-shaped first-layer attention of a later step of a block, with FACache: "
+                   "B=16, L=2048, 32 heads x d128, bf16 K/V, block 32 (scatter, block queries over "
+                   "all keys, 2016 outside queries from their memo over the block keys)",
     }[args.config]
+    metric = METRIC if args.config != "facache" else \
+        "first-layer attention steps/sec with FACache (scatter + block attention + memo merge)"
     line = {
-        "metric": METRIC, "value": round(1000.0 / ms, 2), "unit": "steps/s", "n_gpus": 1,
+        "metric": metric, "value": round(1000.0 / ms, 2), "unit": "steps/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
@@ -359,6 +441,7 @@ def main():
                    "launch": "eager" if graph is None else "hip graph of the timed steps"},
         "kernels_us": {n: round(v, 2) for n, v in per_kernel_us.items()},
         "roofline": roofline,
+        **extra,
         "cpu_baseline": cpu,
         "wall_s": round(t_wall, 3),
     }

@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "F32", "BF16", "E4M3", "DllmError", "lib", "Cache", "StabilityState", "dllm_status_str",
     "dllm_version", "dllm_cache_init", "dllm_scatter_kv", "dllm_sink_rolling_map",
-    "dllm_block_attention", "dllm_block_attention_workspace", "dllm_vocab_stats",
+    "dllm_block_attention", "dllm_block_attention_workspace", "dllm_facache_maps",
+    "dllm_facache_merge", "dllm_facache_merge_workspace", "dllm_vocab_stats",
     "dllm_vocab_stats_workspace", "dllm_stability_reset", "dllm_stability_mask",
 ]
 
@@ -64,6 +65,15 @@ EXPORTS = {
                                             ctypes.c_size_t, ctypes.c_void_p]),
     "dllm_block_attention_workspace": (ctypes.c_size_t, [ctypes.POINTER(_KVCache), ctypes.c_int,
                                                          ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+    "dllm_facache_maps": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "dllm_facache_merge": (ctypes.c_int, [ctypes.POINTER(_KVCache), ctypes.c_void_p, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                          ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "dllm_facache_merge_workspace": (ctypes.c_size_t, [ctypes.POINTER(_KVCache), ctypes.c_int,
+                                                       ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     "dllm_vocab_stats": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -205,6 +215,55 @@ def dllm_block_attention(cache: Cache, q: torch.Tensor, key_idx: Optional[torch.
                                     _dtype_code(out), _dev(lse, "lse"), _dev(workspace, "workspace"),
                                     ws_bytes, _stream())
     _check(rc, "dllm_block_attention")
+    return out
+
+
+def dllm_facache_maps(L: int, blk: int, start: torch.Tensor,
+                      unchanged_idx: Optional[torch.Tensor] = None,
+                      block_idx: Optional[torch.Tensor] = None):
+    """start: [B] int32 block offsets; returns (unchanged_idx [B, L - blk],
+    block_idx [B, blk]) int32."""
+    B = start.shape[0]
+    if unchanged_idx is None:
+        unchanged_idx = torch.empty((B, L - blk), dtype=torch.int32, device=start.device)
+    if block_idx is None:
+        block_idx = torch.empty((B, blk), dtype=torch.int32, device=start.device)
+    rc = lib().dllm_facache_maps(B, L, blk, _dev(start, "start"), _dev(unchanged_idx, "unchanged_idx"),
+                                 _dev(block_idx, "block_idx"), _stream())
+    _check(rc, "dllm_facache_maps")
+    return unchanged_idx, block_idx
+
+
+def dllm_facache_merge_workspace(cache: Cache, q_dtype: int, Hq: int, n_q: int, n_keys: int) -> int:
+    return lib().dllm_facache_merge_workspace(ctypes.byref(cache.desc), q_dtype, Hq, n_q, n_keys)
+
+
+def dllm_facache_merge(cache: Cache, q: torch.Tensor, memo_o: torch.Tensor, memo_lse: torch.Tensor,
+                       key_idx: Optional[torch.Tensor] = None, scale: float = 0.0,
+                       out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                       lse: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None):
+    """q: [B, Hq, n_q, d] queries outside the block; memo_o [B, Hq, n_q, d]
+    and memo_lse [B, Hq, n_q] float32 (a dllm_block_attention output over the
+    unchanged keys); key_idx: [B, n_keys] changed keys.  Returns out."""
+    B, Hq, n_q, d = q.shape
+    if memo_o.dtype != torch.float32 or memo_lse.dtype != torch.float32:
+        raise DllmError("memo_o and memo_lse must be float32")
+    if tuple(memo_o.shape) != (B, Hq, n_q, d) or tuple(memo_lse.shape) != (B, Hq, n_q):
+        raise DllmError("memo shapes must be [B, Hq, n_q, d] and [B, Hq, n_q]")
+    n_keys = key_idx.shape[1] if key_idx is not None else cache.desc.L
+    if out is None:
+        out = torch.empty((B, Hq, n_q, d), dtype=out_dtype or q.dtype, device=q.device)
+    ws_need = dllm_facache_merge_workspace(cache, _dtype_code(q), Hq, n_q, n_keys)
+    if workspace is None and ws_need:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().dllm_facache_merge(ctypes.byref(cache.desc), _dev(q, "q"), _dtype_code(q), Hq, n_q,
+                                  _dev(key_idx, "key_idx"), n_keys, float(scale),
+                                  _dev(memo_o, "memo_o"), _dev(memo_lse, "memo_lse"), _dev(out, "out"),
+                                  _dtype_code(out), _dev(lse, "lse"), _dev(workspace, "workspace"),
+                                  ws_bytes, _stream())
+    _check(rc, "dllm_facache_merge")
     return out
 
 

@@ -139,11 +139,60 @@ int dllm_block_attention(const dllm_kv_cache *cache, const void *q, int q_dtype,
     AttnPlan p;
     if ((rc = plan_attention(*cache, q_dtype, Hq, b, n_keys, key_idx != nullptr, &p)) != DLLM_OK)
         return rc;
-    if (p.path == 1 && (!aligned16(q) || !aligned16(out))) return DLLM_EALIGN;
+    if (p.path != 0 && (!aligned16(q) || !aligned16(out))) return DLLM_EALIGN;
     if (p.ws_bytes > 0 && (!workspace || ws_bytes < p.ws_bytes || !aligned16(workspace)))
         return DLLM_EWORKSPACE;
-    return launch_attention(*cache, p, q, q_dtype, Hq, b, key_idx, n_keys, scale, out, out_dtype,
-                            lse, workspace, static_cast<hipStream_t>(stream));
+    return launch_attention(*cache, p, q, q_dtype, Hq, b, key_idx, n_keys, scale, AttnMemo{}, out,
+                            out_dtype, lse, workspace, static_cast<hipStream_t>(stream));
+}
+
+int dllm_facache_maps(int B, int L, int blk, const int32_t *start, int32_t *unchanged_idx,
+                      int32_t *block_idx, void *stream) {
+    if (B < 1 || blk < 1 || L <= blk) return DLLM_ESHAPE;
+    if (B > 65535) return DLLM_ERANGE;
+    if (!start || !unchanged_idx || !block_idx) return DLLM_EINVAL;
+    return launch_facache_maps(B, L, blk, start, unchanged_idx, block_idx,
+                               static_cast<hipStream_t>(stream));
+}
+
+size_t dllm_facache_merge_workspace(const dllm_kv_cache *cache, int q_dtype, int Hq, int n_q,
+                                    int n_keys) {
+    if (check_cache(cache) != DLLM_OK || Hq < 1 || n_q < 1 || n_keys < 1) return 0;
+    if (Hq % cache->n_kv_heads != 0) return 0;
+    AttnPlan with_map, without;
+    if (plan_facache(*cache, q_dtype, Hq, n_q, n_keys, true, &with_map) != DLLM_OK) return 0;
+    if (plan_facache(*cache, q_dtype, Hq, n_q, n_keys, false, &without) != DLLM_OK) return 0;
+    return with_map.ws_bytes > without.ws_bytes ? with_map.ws_bytes : without.ws_bytes;
+}
+
+int dllm_facache_merge(const dllm_kv_cache *cache, const void *q, int q_dtype, int Hq, int n_q,
+                       const int32_t *key_idx, int n_keys, float scale, const float *memo_o,
+                       const float *memo_lse, void *out, int out_dtype, float *lse,
+                       void *workspace, size_t ws_bytes, void *stream) {
+    int rc = check_cache(cache);
+    if (rc != DLLM_OK) return rc;
+    if (!q || !out || !memo_o || !memo_lse) return DLLM_EINVAL;
+    if (Hq < 1 || n_q < 1) return DLLM_ESHAPE;
+    if (Hq % cache->n_kv_heads != 0) return DLLM_ESHAPE;
+    if (!key_idx) n_keys = cache->L;
+    if (n_keys < 1) return DLLM_ESHAPE;
+    if (q_dtype != DLLM_F32 && q_dtype != DLLM_BF16) return DLLM_EDTYPE;
+    if (out_dtype != DLLM_F32 && out_dtype != DLLM_BF16) return DLLM_EDTYPE;
+    if (!(scale >= 0.f) || std::isinf(scale)) return DLLM_EINVAL;
+    if (scale == 0.f) scale = 1.0f / std::sqrt((float)cache->d_head);
+    if ((int64_t)cache->B * Hq * n_q > INT32_MAX / 4) return DLLM_ERANGE;
+    AttnPlan p;
+    if ((rc = plan_facache(*cache, q_dtype, Hq, n_q, n_keys, key_idx != nullptr, &p)) != DLLM_OK)
+        return rc;
+    if (p.path == 2 && (!aligned16(q) || !aligned16(out) || !aligned16(memo_o)))
+        return DLLM_EALIGN;
+    if (p.ws_bytes > 0 && (!workspace || ws_bytes < p.ws_bytes || !aligned16(workspace)))
+        return DLLM_EWORKSPACE;
+    AttnMemo memo;
+    memo.o = memo_o;
+    memo.lse = memo_lse;
+    return launch_attention(*cache, p, q, q_dtype, Hq, n_q, key_idx, n_keys, scale, memo, out,
+                            out_dtype, lse, workspace, static_cast<hipStream_t>(stream));
 }
 
 size_t dllm_vocab_stats_workspace(int64_t N, int64_t V) {

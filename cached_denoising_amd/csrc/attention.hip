@@ -527,7 +527,8 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(
     const void *__restrict__ ck, const void *__restrict__ cv, const float *__restrict__ ksc,
     const float *__restrict__ vsc, int kv_dtype, const void *__restrict__ q, int q_dtype, int B,
     int Hq, int Hkv, int L, int D, int b, const int32_t *__restrict__ key_idx, int n_keys,
-    float scale, void *__restrict__ out, int out_dtype, float *__restrict__ lse) {
+    float scale, const float *__restrict__ memo_o, const float *__restrict__ memo_lse,
+    void *__restrict__ out, int out_dtype, float *__restrict__ lse) {
     __shared__ float sq[4][256];
     __shared__ float sp[4][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -546,6 +547,17 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(
     __syncthreads();
     const int32_t *kmap = key_idx ? key_idx + (int64_t)bi * n_keys : nullptr;
     float mrun = kNegInf, lrun = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+    if (memo_lse) {
+        // a memoized state (FACache): m = lse, l = 1, O~ = memo_o; -inf is empty
+        const float ml = memo_lse[rr];
+        if (ml != kNegInf) {
+            mrun = ml;
+            lrun = 1.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (lane + 64 * r < D) acc[r] = memo_o[rr * D + lane + 64 * r];
+        }
+    }
     for (int j0 = 0; j0 < n_keys; j0 += 64) {
         const int kk = key_at(kmap, n_keys, L, j0 + lane);
         float sc = kNegInf;
@@ -680,18 +692,37 @@ int plan_attention(const dllm_kv_cache &c, int q_dtype, int Hq, int b, int n_key
     return DLLM_OK;
 }
 
+int plan_facache(const dllm_kv_cache &c, int q_dtype, int Hq, int n_q, int n_keys, bool has_map,
+                 AttnPlan *p) {
+    const int G = Hq / c.n_kv_heads;
+    const int M = G * n_q;
+    const bool mfma = q_dtype == DLLM_BF16 && (c.dtype == DLLM_BF16 || c.dtype == DLLM_E4M3) &&
+                      (c.d_head == 64 || c.d_head == 128);
+    *p = AttnPlan{};
+    p->rows = M;
+    if (!mfma) {
+        p->path = 0;
+        return DLLM_OK;
+    }
+    // the grouped-query layout takes the memo at any row count
+    plan_shared(c, Hq, n_q, cdiv(M, 32), n_keys, has_map, p);
+    return DLLM_OK;
+}
+
 int launch_attention(const dllm_kv_cache &c, const AttnPlan &p, const void *q, int q_dtype, int Hq,
-                     int b, const int32_t *key_idx, int n_keys, float scale, void *out,
-                     int out_dtype, float *lse, void *ws, hipStream_t s) {
+                     int b, const int32_t *key_idx, int n_keys, float scale, const AttnMemo &memo,
+                     void *out, int out_dtype, float *lse, void *ws, hipStream_t s) {
     if (p.path == 0) {
         const int64_t rows_total = (int64_t)c.B * Hq * b;
         attn_valu_kernel<<<dim3((unsigned)cdiv64(rows_total, 4)), dim3(256), 0, s>>>(
             c.k, c.v, c.k_scale, c.v_scale, c.dtype, q, q_dtype, c.B, Hq, c.n_kv_heads, c.L,
-            c.d_head, b, key_idx, n_keys, scale, out, out_dtype, lse);
+            c.d_head, b, key_idx, n_keys, scale, memo.o, memo.lse, out, out_dtype, lse);
         return launch_status();
     }
     if (p.path == 2)
-        return launch_shared_attention(c, p, q, Hq, b, key_idx, n_keys, scale, out, out_dtype, lse, ws, s);
+        return launch_shared_attention(c, p, q, Hq, b, key_idx, n_keys, scale, memo, out, out_dtype,
+                                       lse, ws, s);
+    if (memo.lse) return DLLM_EINVAL;           // never planned: the per-wave path takes no memo
     const bool e4 = c.dtype == DLLM_E4M3;
     const bool map = key_idx != nullptr;
     // stream K/V past the caches when only one row group reads each KV head

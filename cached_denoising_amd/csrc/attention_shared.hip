@@ -20,7 +20,10 @@
 // transposed from the row-major V tile.  Compared with one wave per key run,
 // the K/V bytes cross L2 once per workgroup instead of once per row group,
 // and the query rows are loaded once.  Key splits write (m, l, O~) partials
-// for the merge kernel of the per-wave path.
+// for the merge kernel of the per-wave path.  With a memoized state per row
+// (FACache [LaCache, Methodology 1]: the state of the unchanged keys), the
+// rows start from it instead of the empty state, so only the changed keys
+// are walked.
 #include "attn_common.hpp"
 
 #include <climits>
@@ -65,7 +68,8 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
     const void *__restrict__ ck, const void *__restrict__ cv, const float *__restrict__ ksc,
     const float *__restrict__ vsc, const uint16_t *__restrict__ q, int Hq, int Hkv, int L, int b,
     int G, const int32_t *__restrict__ key_idx, int n_keys, float scale_log2, int row_chunks,
-    int splits, int tiles_per_split, int64_t rows_total, void *__restrict__ out, int out_dtype,
+    int splits, int tiles_per_split, int64_t rows_total, const float *__restrict__ memo_o,
+    const float *__restrict__ memo_lse, void *__restrict__ out, int out_dtype,
     float *__restrict__ lse, float *__restrict__ part_o, float *__restrict__ part_ml) {
     constexpr int RT = 2;                  // 16-row MFMA tiles per wave: 32 rows
     constexpr int NC = D / 32;             // k-chunks of the first product
@@ -417,10 +421,45 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
             if (r < M) qreg[rt][c] = *reinterpret_cast<const uint4 *>(qrow + chunk_dim<DLLM_BF16>(c, g));
         }
     }
-    // The queries and the first tiles land together.  Waiting for every load
-    // here also tells the compiler the query registers are ready, so it adds
-    // no wait of its own inside the loop.
+    // A memoized state (FACache) starts the rows of split 0: O~ = memo_o,
+    // m = memo_lse in base 2 and l = 1, the 1 counted in lane group 0 only
+    // (the row sum adds the four groups); an empty memo (-inf) stays empty.
+    // Its loads go straight into the accumulators, beside the queries'.
+    const bool memo = memo_lse != nullptr && split == 0;
+    float mlse[RT];
+    if (memo) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int r = row0 + rt * 16 + l16;
+            mlse[rt] = kNegInf;
+            if (r < M) {
+                const int gq = r / b, i = r - gq * b;
+                const int64_t orow = ((int64_t)bi * Hq + kvh * G + gq) * b + i;
+                mlse[rt] = memo_lse[orow];
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) {
+                    const float4 v = *reinterpret_cast<const float4 *>(memo_o + orow * D + dt * 16 + 4 * g);
+                    o[dt][rt] = f32x4_t{v.x, v.y, v.z, v.w};
+                }
+            }
+        }
+    }
+    // The queries, the memo and the first tiles land together.  Waiting for
+    // every load here also tells the compiler the query registers are ready,
+    // so it adds no wait of its own inside the loop.
     vm_wait<0>();
+    if (memo) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            if (mlse[rt] == kNegInf) {
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) o[dt][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            } else {
+                m[rt] = mlse[rt] * kLog2e;
+                l[rt] = g == 0 ? 1.f : 0.f;
+            }
+        }
+    }
     if (CONV && nt > 0) {
         ring_barrier();
         ConvIn c0;
@@ -517,8 +556,8 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
 
 template <int D, int KVDT, bool MAP, bool NT, int NRG>
 int launch_shared(const dllm_kv_cache &c, const AttnPlan &p, const void *q, int Hq, int b,
-                  const int32_t *key_idx, int n_keys, float scale, void *out, int out_dtype,
-                  float *lse, void *ws, hipStream_t s) {
+                  const int32_t *key_idx, int n_keys, float scale, const AttnMemo &memo, void *out,
+                  int out_dtype, float *lse, void *ws, hipStream_t s) {
     const int G = Hq / c.n_kv_heads;
     const int64_t rows_total = (int64_t)c.B * Hq * b;
     const int64_t blocks = (int64_t)c.B * c.n_kv_heads * p.row_groups * p.splits;
@@ -532,7 +571,7 @@ int launch_shared(const dllm_kv_cache &c, const AttnPlan &p, const void *q, int 
     attn_shared_kernel<D, KVDT, MAP, NT, NRG><<<dim3((unsigned)blocks), dim3(NRG * kWave), 0, s>>>(
         c.k, c.v, c.k_scale, c.v_scale, static_cast<const uint16_t *>(q), Hq, c.n_kv_heads, c.L,
         b, G, key_idx, n_keys, scale * kLog2e, p.row_groups, p.splits, p.tiles_per_wave, rows_total,
-        out, out_dtype, lse, part_o, part_ml);
+        memo.o, memo.lse, out, out_dtype, lse, part_o, part_ml);
     int rc = launch_status();
     if (rc != DLLM_OK || p.splits == 1) return rc;
     return launch_attn_merge(part_o, part_ml, rows_total, D, p.splits, out, out_dtype, lse, s);
@@ -567,8 +606,8 @@ void plan_shared(const dllm_kv_cache &c, int Hq, int b, int row_groups32, int n_
 }
 
 int launch_shared_attention(const dllm_kv_cache &c, const AttnPlan &p, const void *q, int Hq, int b,
-                            const int32_t *key_idx, int n_keys, float scale, void *out,
-                            int out_dtype, float *lse, void *ws, hipStream_t s) {
+                            const int32_t *key_idx, int n_keys, float scale, const AttnMemo &memo,
+                            void *out, int out_dtype, float *lse, void *ws, hipStream_t s) {
     const bool e4 = c.dtype == DLLM_E4M3;
     const bool map = key_idx != nullptr;
     // stream K/V past the caches when one workgroup reads each tile
@@ -579,11 +618,11 @@ int launch_shared_attention(const dllm_kv_cache &c, const AttnPlan &p, const voi
         auto pick = [&](auto ntv) -> int {
             constexpr bool NTV = decltype(ntv)::value;
             if (p.waves == 2)
-                return launch_shared<DD, KV, MP, NTV, 2>(c, p, q, Hq, b, key_idx, n_keys, scale, out,
-                                                         out_dtype, lse, ws, s);
+                return launch_shared<DD, KV, MP, NTV, 2>(c, p, q, Hq, b, key_idx, n_keys, scale, memo,
+                                                         out, out_dtype, lse, ws, s);
             if (p.waves == 4)
-                return launch_shared<DD, KV, MP, NTV, 4>(c, p, q, Hq, b, key_idx, n_keys, scale, out,
-                                                         out_dtype, lse, ws, s);
+                return launch_shared<DD, KV, MP, NTV, 4>(c, p, q, Hq, b, key_idx, n_keys, scale, memo,
+                                                         out, out_dtype, lse, ws, s);
             return DLLM_ESHAPE;
         };
         return nt ? pick(std::true_type{}) : pick(std::false_type{});

@@ -52,6 +52,8 @@ int launch_scatter(const dllm_kv_cache &c, const void *k_new, const void *v_new,
 
 int launch_sink_rolling(int B, int L, int S, int R, const int32_t *end, int32_t *key_idx,
                         int n_keys, hipStream_t s);
+int launch_facache_maps(int B, int L, int b, const int32_t *start, int32_t *unchanged_idx,
+                        int32_t *block_idx, hipStream_t s);
 
 struct AttnPlan {
     int path;          // 0: float32 VALU path, 1: MFMA, keys per wave, 2: MFMA, tiles shared by the waves
@@ -63,20 +65,31 @@ struct AttnPlan {
     int tiles_per_wave;// 32-key tiles per wave (path 2: per workgroup, i.e. per split)
     size_t ws_bytes;   // partial-result workspace
 };
+// A memoized online-softmax state per query row, stored normalised (o = O~/l
+// as [rows, d] float, lse = m + ln l as [rows] float, natural log; lse = -inf
+// is an empty state).  When given, the attention kernels start each row's
+// state from it instead of the empty state.
+struct AttnMemo {
+    const float *o = nullptr;
+    const float *lse = nullptr;
+};
 int plan_attention(const dllm_kv_cache &c, int q_dtype, int Hq, int b, int n_keys, bool has_map,
                    AttnPlan *p);
+// the plan of a call with a memo: the VALU path or the grouped-query layout
+int plan_facache(const dllm_kv_cache &c, int q_dtype, int Hq, int n_q, int n_keys, bool has_map,
+                 AttnPlan *p);
 // the grouped-query layout (path 2), for more than one 32-row group per KV head
 void plan_shared(const dllm_kv_cache &c, int Hq, int b, int row_groups32, int n_keys, bool has_map,
                  AttnPlan *p);
 int launch_shared_attention(const dllm_kv_cache &c, const AttnPlan &p, const void *q, int Hq, int b,
-                            const int32_t *key_idx, int n_keys, float scale, void *out,
-                            int out_dtype, float *lse, void *ws, hipStream_t s);
+                            const int32_t *key_idx, int n_keys, float scale, const AttnMemo &memo,
+                            void *out, int out_dtype, float *lse, void *ws, hipStream_t s);
 // merge of the (m, l, O~) partials of key splits, in split order
 int launch_attn_merge(const float *part_o, const float *part_ml, int64_t rows_total, int D,
                       int splits, void *out, int out_dtype, float *lse, hipStream_t s);
 int launch_attention(const dllm_kv_cache &c, const AttnPlan &p, const void *q, int q_dtype, int Hq,
-                     int b, const int32_t *key_idx, int n_keys, float scale, void *out,
-                     int out_dtype, float *lse, void *ws, hipStream_t s);
+                     int b, const int32_t *key_idx, int n_keys, float scale, const AttnMemo &memo,
+                     void *out, int out_dtype, float *lse, void *ws, hipStream_t s);
 
 struct VocabPlan {
     int threads;       // workgroup size: 256, or 512 when there are few rows

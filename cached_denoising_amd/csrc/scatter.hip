@@ -176,7 +176,34 @@ __global__ __launch_bounds__(256) void sink_rolling_kernel(int L, int S, int R,
         out[j] = j < ns ? j : (j < ns + nr ? start + (j - ns) : -1);
 }
 
+// Unchanged and changed key positions of one SAR step [LaCache, problem
+// statement and Methodology 1]: only the active block [o, o + b) changes
+// within a block's denoising steps.  Both lists ascending, one thread per
+// position.
+__global__ __launch_bounds__(256) void facache_maps_kernel(int L, int b, const int32_t *__restrict__ start,
+                                                           int32_t *__restrict__ unchanged_idx,
+                                                           int32_t *__restrict__ block_idx) {
+    const int bi = blockIdx.y;
+    int o = start[bi];
+    o = o < 0 ? 0 : (o > L - b ? L - b : o);
+    int32_t *un = unchanged_idx + (int64_t)bi * (L - b);
+    int32_t *blk = block_idx + (int64_t)bi * b;
+    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < L; j += gridDim.x * blockDim.x) {
+        if (j < o) un[j] = j;
+        else if (j < o + b) blk[j - o] = j;
+        else un[j - b] = j;
+    }
+}
+
 }  // namespace
+
+int launch_facache_maps(int B, int L, int b, const int32_t *start, int32_t *unchanged_idx,
+                        int32_t *block_idx, hipStream_t s) {
+    const unsigned gx = (unsigned)std::min(cdiv(L, 256), 64);
+    facache_maps_kernel<<<dim3(gx, (unsigned)B), dim3(256), 0, s>>>(L, b, start, unchanged_idx,
+                                                                     block_idx);
+    return launch_status();
+}
 
 int launch_fill_zero(void *p, size_t bytes, hipStream_t s) {
     if (bytes == 0) return DLLM_OK;

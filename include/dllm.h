@@ -9,6 +9,9 @@
  *   dllm_scatter_kv        write the block's fresh K/V rows into the cache
  *   dllm_sink_rolling_map  build a sink + rolling-window key index map
  *   dllm_block_attention   block queries vs. the cached keys, bidirectional
+ *   dllm_facache_maps      unchanged / changed key lists of a block's steps
+ *   dllm_facache_merge     queries outside the block: memoized softmax state
+ *                          continued over the changed keys only
  *   dllm_vocab_stats       argmax token, max-probability, entropy per row
  *   dllm_stability_reset   clear the per-position decode state
  *   dllm_stability_mask    history ring, stability test, confidence score and
@@ -187,6 +190,60 @@ int dllm_block_attention(const dllm_kv_cache *cache, const void *q, int q_dtype,
  * without a key map (0 if none: the keys are not split over workgroups). */
 size_t dllm_block_attention_workspace(const dllm_kv_cache *cache, int q_dtype, int Hq,
                                       int b, int n_keys);
+
+/* ---------------------------------------------------------------------------
+ * dllm_facache_maps -- the key lists of FACache for one block's denoising
+ * steps [LaCache, problem statement and Methodology 1: within the steps of
+ * one block only the active block's tokens change, the prompt and the masked
+ * suffix keep theirs]: for sequence b with block [o, o + blk), o = start[b],
+ *   unchanged_idx[b, :] = {0..o-1} then {o+blk..L-1}   (L - blk entries)
+ *   block_idx[b, :]     = {o..o+blk-1}                 (blk entries)
+ * both ascending.
+ *   start          [B] int32 device; values are clamped to [0, L - blk]
+ *   unchanged_idx  [B, L - blk] int32 device (output)
+ *   block_idx      [B, blk] int32 device (output)
+ * Needs 1 <= blk < L.
+ * ------------------------------------------------------------------------- */
+int dllm_facache_maps(int B, int L, int blk, const int32_t *start, int32_t *unchanged_idx,
+                      int32_t *block_idx, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * dllm_facache_merge -- FACache for the queries outside the active block
+ * [LaCache, Methodology 1 (FACache) and 3 (inference workflow)]: the online-
+ * softmax state (m, l, O~) of each such query over the unchanged keys is
+ * memoized at the block's first step, and every later step starts each
+ * query's state from the memo and walks only the changed keys, so the
+ * (unchanged query, unchanged key) tiles are never recomputed.
+ * The memo is stored normalised, as the output of dllm_block_attention with
+ * out_dtype = DLLM_F32 and an lse array (the same state with its reference
+ * moved to m' = lse, l' = 1, O~' = O); that call, with the unchanged queries
+ * over key_idx = unchanged_idx, is the memo fill.  Per row:
+ *   m_new = max(memo_lse, max_j s_j),  s_j = scale * q . k_j
+ *   out   = (memo_o e^(memo_lse - m_new) + sum_j e^(s_j - m_new) v_j)
+ *           / (e^(memo_lse - m_new) + sum_j e^(s_j - m_new))
+ *   lse   = m_new + ln(denominator)
+ *   q         [B, Hq, n_q, d] in q_dtype: the queries outside the block
+ *   key_idx   [B, n_keys] int32 device: the changed keys (block_idx of
+ *             dllm_facache_maps), -1 entries are padding; NULL = all L keys
+ *   memo_o    [B, Hq, n_q, d] float32 device, 16-byte aligned
+ *   memo_lse  [B, Hq, n_q] float32 device, natural log; -inf marks an empty
+ *             memo (its memo_o row is ignored); other values must be finite
+ *   out       [B, Hq, n_q, d] in out_dtype (F32 or BF16); lse optional
+ *             [B, Hq, n_q] float32.  out and lse must not overlap the memo.
+ *   cache, q_dtype, scale, workspace: as for dllm_block_attention, with the
+ *             workspace size from dllm_facache_merge_workspace.
+ * The memo and the queries are only read.
+ * ------------------------------------------------------------------------- */
+int dllm_facache_merge(const dllm_kv_cache *cache, const void *q, int q_dtype, int Hq, int n_q,
+                       const int32_t *key_idx, int n_keys, float scale,
+                       const float *memo_o, const float *memo_lse,
+                       void *out, int out_dtype, float *lse,
+                       void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes dllm_facache_merge needs for these shapes, with or without
+ * a key map (0 if the keys are not split over workgroups). */
+size_t dllm_facache_merge_workspace(const dllm_kv_cache *cache, int q_dtype, int Hq,
+                                    int n_q, int n_keys);
 
 /* ---------------------------------------------------------------------------
  * dllm_vocab_stats -- one pass over each row of logits:

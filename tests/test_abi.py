@@ -26,7 +26,8 @@ def test_header_declares_the_boundary():
     names = declared()
     for n in ["dllm_cache_init", "dllm_scatter_kv", "dllm_block_attention", "dllm_vocab_stats",
               "dllm_stability_mask", "dllm_sink_rolling_map", "dllm_stability_reset",
-              "dllm_block_attention_workspace", "dllm_vocab_stats_workspace", "dllm_status_str"]:
+              "dllm_block_attention_workspace", "dllm_vocab_stats_workspace", "dllm_status_str",
+              "dllm_facache_maps", "dllm_facache_merge", "dllm_facache_merge_workspace"]:
         assert n in names
 
 
@@ -59,6 +60,20 @@ def test_host_validation_without_gpu(dl):
     assert L.dllm_stability_mask(1, 4, 0, None, None, 4, 16, 16, 16, 16, 16, 16, 16, 16, 16,
                                  ctypes.byref(prm), 16, 16, 16, 16, 16, None) == -1
     assert L.dllm_sink_rolling_map(1, 10, 4, 8, 16, 16, 11, None) == -3                     # n_keys < S+R
+    assert L.dllm_facache_maps(1, 8, 8, 16, 16, 16, None) == -3                             # block = L
+    assert L.dllm_facache_maps(1, 8, 2, None, 16, 16, None) == -1
+    desc = dl._KVCache(B=1, L=64, n_kv_heads=2, d_head=64, dtype=1, k=16, v=16)
+    # no memo, bad head ratio, bad dtypes, misaligned memo: rejected on the host
+    assert L.dllm_facache_merge(ctypes.byref(desc), 16, 1, 4, 8, None, 0, 0.0, None, 16, 16, 1,
+                                None, None, 0, None) == -1
+    assert L.dllm_facache_merge(ctypes.byref(desc), 16, 1, 3, 8, None, 0, 0.0, 16, 16, 16, 1,
+                                None, None, 0, None) == -3
+    assert L.dllm_facache_merge(ctypes.byref(desc), 16, 2, 4, 8, None, 0, 0.0, 16, 16, 16, 1,
+                                None, None, 0, None) == -2
+    assert L.dllm_facache_merge(ctypes.byref(desc), 16, 1, 4, 8, None, 0, 0.0, 20, 16, 16, 1,
+                                None, None, 0, None) == -4
+    assert L.dllm_facache_merge(ctypes.byref(desc), 16, 1, 4, 8, None, 0, -1.0, 16, 16, 16, 1,
+                                None, None, 0, None) == -1
 
 
 def test_workspace_sizes(dl):
@@ -74,3 +89,7 @@ def test_workspace_sizes(dl):
     desc = dl._KVCache(B=4, L=32768, n_kv_heads=8, d_head=128, dtype=2, k=16, v=16, k_scale=16,
                        v_scale=16)
     assert L.dllm_block_attention_workspace(ctypes.byref(desc), 1, 32, 64, 8192) == 8 * 4 * 32 * 64 * 130 * 4
+    # FACache merge at a LLaDA-shaped step: 16 x 32 heads x 2016 queries
+    # outside the block over the 32 block keys, one tile per workgroup
+    desc = dl._KVCache(B=16, L=2048, n_kv_heads=32, d_head=128, dtype=1, k=16, v=16)
+    assert L.dllm_facache_merge_workspace(ctypes.byref(desc), 1, 32, 2016, 32) == 0

@@ -160,6 +160,28 @@ def queries(cfg: Config, device="cpu", step: int = 0, scale_std: float = 1.0, B=
                   TORCH_DTYPE[cfg.q_dtype])
 
 
+def outside_queries(cfg: Config, device="cpu", B=None, n: Optional[int] = None):
+    """[B, Hq, n, d] queries of the positions outside the active block
+    (n = L - b), unchanged over a block's steps."""
+    B = cfg.B if B is None else B
+    n = cfg.L - cfg.b if n is None else n
+    g = generator(cfg.seed * 7 + 7, device)
+    return _randn((B, cfg.Hq, n, cfg.d), cfg.qkv_std, g, device, TORCH_DTYPE[cfg.q_dtype])
+
+
+def memo_state(B: int, Hq: int, n: int, d: int, seed: int, o_std: float, lse_mean: float,
+               lse_std: float = 1.0, empty_frac: float = 0.0, device="cpu"):
+    """A random memoized softmax state in its stored form: o [B, Hq, n, d]
+    ~ N(0, o_std), lse [B, Hq, n] ~ N(lse_mean, lse_std) float32, with a
+    fraction of rows marked empty (lse = -inf)."""
+    g = generator(seed, "cpu")
+    o = torch.randn((B, Hq, n, d), generator=g) * o_std
+    lse = torch.randn((B, Hq, n), generator=g) * lse_std + lse_mean
+    if empty_frac > 0:
+        lse[torch.rand((B, Hq, n), generator=g) < empty_frac] = float("-inf")
+    return o.to(device), lse.to(device)
+
+
 def logits(cfg: Config, device="cpu", step: int = 0, rows: Optional[int] = None,
            stride: Optional[int] = None, dtype: Optional[int] = None):
     """[rows, stride] logits (only the first V columns are used).
