@@ -28,6 +28,7 @@ import subprocess
 import numpy as np
 
 F32, BF16, E4M3 = 0, 1, 2
+F64 = 9                      # oracle-only: rows of float64 values (fp8_quant_rows)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
@@ -79,6 +80,22 @@ def lib():
         L.oracle_facache_merge.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, i32, P, i32, i32,
                                            P, P, P, i32, dbl, P, P, P, i32]
         L.oracle_facache_merge.restype = i32
+        L.oracle_e8m0_exponent.argtypes = [dbl]
+        L.oracle_e8m0_exponent.restype = i32
+        L.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
+        L.oracle_e8m0_value.restype = dbl
+        L.oracle_fp8_quantize_pow2.argtypes = [P, i32, P, P]
+        L.oracle_fp8_quant_rows.argtypes = [i32, P, i64, i32, i64, P, P]
+        L.oracle_fp8_quant_rows.restype = i32
+        L.oracle_fp8_quant_weight.argtypes = [i32, P, i32, i32, P, P]
+        L.oracle_fp8_quant_weight.restype = i32
+        L.oracle_fp8_gemm.argtypes = [P, P, P, P, i64, i32, i32, P, i64, P]
+        L.oracle_fp8_gemm.restype = i32
+        L.oracle_addnorm.argtypes = [i32, P, P, P, dbl, i64, i32, P, P]
+        L.oracle_addnorm.restype = i32
+        L.oracle_silu.argtypes = [dbl]
+        L.oracle_silu.restype = dbl
+        L.oracle_swiglu.argtypes = [P, P, i64, P]
         L.oracle_vocab_stats.argtypes = [i32, P, i64, i64, i64, P, P, P, P, i64]
         L.oracle_vocab_stats.restype = i32
         L.oracle_stability_step.argtypes = [i32, i32, i32, P, i32, P, P, P, P, P, P, P, P, P,
@@ -250,6 +267,90 @@ def facache_merge(cache_k, cache_v, k_scale, v_scale, cache_dtype, q, q_dtype, m
                                     float(scale), _ptr(out), _ptr(lse), _ptr(heads), nh)
     _check(rc, "facache_merge")
     return out, lse
+
+
+# ---- N2 ---------------------------------------------------------------------
+
+def e8m0_exponent(amax: float) -> int:
+    """smallest e >= -127 with amax <= 448 * 2^e [LaCache, Methodology 2;
+    power-of-two group scales are a reading]"""
+    return lib().oracle_e8m0_exponent(float(amax))
+
+
+def e8m0_value(code: int) -> float:
+    return lib().oracle_e8m0_value(int(code))
+
+
+def fp8_quantize_pow2(x):
+    """one group: (codes uint8, e8m0 code)"""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    codes = np.zeros(x.size, dtype=np.uint8)
+    sc = np.zeros(1, dtype=np.uint8)
+    lib().oracle_fp8_quantize_pow2(_ptr(x), x.size, _ptr(codes), _ptr(sc))
+    return codes, int(sc[0])
+
+
+def fp8_quant_rows(x, dtype):
+    """x: [M, K] float32, bfloat16 bits (uint16) or float64 (dtype F64);
+    returns (codes [M, K] uint8, scales [K/128, M] uint8 E8M0)."""
+    x = np.ascontiguousarray(x)
+    M, K = x.shape
+    codes = np.zeros((M, K), dtype=np.uint8)
+    scales = np.zeros((K // 128, M), dtype=np.uint8)
+    _check(lib().oracle_fp8_quant_rows(dtype, _ptr(x), M, K, K, _ptr(codes), _ptr(scales)), "fp8_quant_rows")
+    return codes, scales
+
+
+def fp8_quant_weight(w, dtype):
+    """w: [N, K]; returns (codes [N, K], scales [N/128, K/128] E8M0)."""
+    w = np.ascontiguousarray(w)
+    N, K = w.shape
+    codes = np.zeros((N, K), dtype=np.uint8)
+    scales = np.zeros((N // 128, K // 128), dtype=np.uint8)
+    _check(lib().oracle_fp8_quant_weight(dtype, _ptr(w), N, K, _ptr(codes), _ptr(scales)), "fp8_quant_weight")
+    return codes, scales
+
+
+def fp8_gemm(a, sa, b, sb, rows=None):
+    """dequant(A) dequant(B)^T in fp64; rows selects output rows of A."""
+    a, sa, b, sb = (np.ascontiguousarray(t, dtype=np.uint8) for t in (a, sa, b, sb))
+    M, K = a.shape
+    N = b.shape[0]
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        c = np.zeros((rows.size, N))
+        n_rows = rows.size
+    else:
+        c = np.zeros((M, N))
+        n_rows = 0
+    _check(lib().oracle_fp8_gemm(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), M, N, K, _ptr(rows), n_rows, _ptr(c)),
+           "fp8_gemm")
+    return c
+
+
+def addnorm(x, res, gamma, eps, dtype):
+    """(res_out in dtype storage, y fp64 [M, K])"""
+    x = np.ascontiguousarray(x)
+    M, K = x.shape
+    res = np.ascontiguousarray(res) if res is not None else None
+    gamma = np.ascontiguousarray(gamma)
+    res_out = np.zeros_like(x)
+    y = np.zeros((M, K))
+    _check(lib().oracle_addnorm(dtype, _ptr(x), _ptr(res), _ptr(gamma), float(eps), M, K, _ptr(res_out), _ptr(y)),
+           "addnorm")
+    return res_out, y
+
+
+def silu(g: float) -> float:
+    return lib().oracle_silu(float(g))
+
+
+def swiglu(g, u):
+    g = np.ascontiguousarray(g, dtype=np.float64)
+    u = np.ascontiguousarray(u, dtype=np.float64)
+    y = np.zeros_like(g)
+    lib().oracle_swiglu(_ptr(g), _ptr(u), g.size, _ptr(y))
+    return y
 
 
 # ---- A4 ---------------------------------------------------------------------

@@ -70,9 +70,15 @@ double oracle_e4m3_value(uint8_t code)
  * the grid in x's binade, divide (exact: power of two), round half to even
  * with rint (the default rounding mode), multiply back, then read the code
  * off the rounded value. */
+static uint8_t e4m3_encode_double(double x);
+
 uint8_t oracle_e4m3_encode(float xf)
 {
-    double x = (double)xf;
+    return e4m3_encode_double((double)xf);
+}
+
+static uint8_t e4m3_encode_double(double x)
+{
     uint8_t sign = 0;
     double a, spacing, r, v;
     int e, E, M;
@@ -384,6 +390,179 @@ int oracle_facache_merge(int cache_dtype, int B, int L, int Hkv, int d,
         free(acc);
     }
     return err ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* N2: per-group FP8 for the FFN                                             */
+/* ------------------------------------------------------------------------ */
+
+/* The group's scale is a power of two 2^e, stored as its E8M0 code e + 127:
+ * the smallest e >= -127 with amax <= 448 * 2^e, so no code saturates.
+ * With amax = f * 2^E, f in [0.5, 1) and 448 = 0.875 * 2^9, that is
+ * e = E - 9 when f <= 0.875, else E - 8. */
+int oracle_e8m0_exponent(double amax)
+{
+    int E, e;
+    double f;
+    if (!(amax > 0.0)) return -127;
+    f = frexp(amax, &E);
+    e = f <= 0.875 ? E - 9 : E - 8;
+    return e < -127 ? -127 : e;
+}
+
+double oracle_e8m0_value(uint8_t code)
+{
+    return ldexp(1.0, (int)code - 127);
+}
+
+void oracle_fp8_quantize_pow2(const double *x, int n, uint8_t *codes, uint8_t *e8m0)
+{
+    double amax = 0.0;
+    int i, e;
+    for (i = 0; i < n; ++i)
+        if (fabs(x[i]) > amax) amax = fabs(x[i]);
+    e = oracle_e8m0_exponent(amax);
+    *e8m0 = (uint8_t)(e + 127);
+    for (i = 0; i < n; ++i)
+        codes[i] = e4m3_encode_double(ldexp(x[i], -e));   /* exact: a power of two */
+}
+
+/* activations: every 1 x 128 group of a row [LaCache, Methodology 2] */
+int oracle_fp8_quant_rows(int dtype, const void *x, int64_t M, int K, int64_t ld,
+                          uint8_t *codes, uint8_t *scales)
+{
+    int64_t m;
+    if (M < 0 || K <= 0 || K % 128 != 0 || ld < K) return -1;
+    if (dtype != ORC_F32 && dtype != ORC_BF16 && dtype != ORC_F64) return -1;
+#pragma omp parallel for schedule(static)
+    for (m = 0; m < M; ++m) {
+        double g[128];
+        int gi, c;
+        for (gi = 0; gi < K / 128; ++gi) {
+            for (c = 0; c < 128; ++c) {
+                int64_t i = m * ld + gi * 128 + c;
+                g[c] = dtype == ORC_F64 ? ((const double *)x)[i] : load_src(dtype, x, i);
+            }
+            oracle_fp8_quantize_pow2(g, 128, codes + m * K + gi * 128, scales + (int64_t)gi * M + m);
+        }
+    }
+    return 0;
+}
+
+/* weights: every 128 x 128 block [LaCache, Methodology 2] */
+int oracle_fp8_quant_weight(int dtype, const void *w, int N, int K, uint8_t *codes, uint8_t *scales)
+{
+    int64_t blk;
+    const int nb = N / 128, kb = K / 128;
+    if (N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0) return -1;
+    if (dtype != ORC_F32 && dtype != ORC_BF16) return -1;
+#pragma omp parallel for schedule(static)
+    for (blk = 0; blk < (int64_t)nb * kb; ++blk) {
+        const int bn = (int)(blk / kb), bk = (int)(blk % kb);
+        double amax = 0.0, v;
+        int r, c, e;
+        for (r = 0; r < 128; ++r)
+            for (c = 0; c < 128; ++c) {
+                v = fabs(load_src(dtype, w, (int64_t)(bn * 128 + r) * K + bk * 128 + c));
+                if (v > amax) amax = v;
+            }
+        e = oracle_e8m0_exponent(amax);
+        scales[blk] = (uint8_t)(e + 127);
+        for (r = 0; r < 128; ++r)
+            for (c = 0; c < 128; ++c) {
+                int64_t i = (int64_t)(bn * 128 + r) * K + bk * 128 + c;
+                codes[i] = e4m3_encode_double(ldexp(load_src(dtype, w, i), -e));
+            }
+    }
+    return 0;
+}
+
+/* C = dequant(A) dequant(B)^T in fp64: element (m, k) of A is
+ * e4m3(a[m, k]) * 2^(sa[k/128, m] - 127), element (n, k) of B is
+ * e4m3(b[n, k]) * 2^(sb[n/128, k/128] - 127).  rows selects output rows. */
+int oracle_fp8_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t *b, const uint8_t *sb,
+                    int64_t M, int N, int K, const int64_t *rows, int64_t n_rows, double *c)
+{
+    int64_t t, n_out = rows ? n_rows : M;
+    double *bd;
+    int64_t i;
+    if (M <= 0 || N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0) return -1;
+    bd = (double *)malloc(sizeof(double) * (size_t)N * K);
+    if (!bd) return -1;
+    for (i = 0; i < (int64_t)N * K; ++i) {
+        const int n = (int)(i / K), k = (int)(i % K);
+        bd[i] = oracle_e4m3_value(b[i]) * oracle_e8m0_value(sb[(n / 128) * (K / 128) + k / 128]);
+    }
+#pragma omp parallel for schedule(dynamic, 4)
+    for (t = 0; t < n_out; ++t) {
+        const int64_t m = rows ? rows[t] : t;
+        double *ad = (double *)malloc(sizeof(double) * (size_t)K);
+        int n, k;
+        if (!ad) continue;
+        for (k = 0; k < K; ++k)
+            ad[k] = oracle_e4m3_value(a[m * K + k]) * oracle_e8m0_value(sa[(int64_t)(k / 128) * M + m]);
+        for (n = 0; n < N; ++n) {
+            double acc = 0.0;
+            const double *br = bd + (int64_t)n * K;
+            for (k = 0; k < K; ++k) acc += ad[k] * br[k];
+            c[t * N + n] = acc;
+        }
+        free(ad);
+    }
+    free(bd);
+    return 0;
+}
+
+/* Add & norm before the FFN: r = x + res in float32, stored in the source
+ * dtype (the residual stream), then y = gamma * r / sqrt(mean(r^2) + eps)
+ * in fp64 (RMS normalisation). */
+int oracle_addnorm(int dtype, const void *x, const void *res, const void *gamma, double eps,
+                   int64_t M, int K, void *res_out, double *y)
+{
+    int64_t m;
+    if (M < 0 || K <= 0 || (dtype != ORC_F32 && dtype != ORC_BF16)) return -1;
+#pragma omp parallel for schedule(static)
+    for (m = 0; m < M; ++m) {
+        double ss = 0.0, inv;
+        int k;
+        for (k = 0; k < K; ++k) {
+            const int64_t i = m * K + k;
+            float r = (float)load_src(dtype, x, i) + (float)(res ? load_src(dtype, res, i) : 0.0);
+            double rv;
+            if (dtype == ORC_BF16) {
+                uint32_t u;
+                uint16_t h;
+                memcpy(&u, &r, sizeof u);
+                /* round to nearest even into bfloat16 (inputs are finite) */
+                u += 0x7fffu + ((u >> 16) & 1u);
+                h = (uint16_t)(u >> 16);
+                if (res_out) ((uint16_t *)res_out)[i] = h;
+                rv = oracle_bf16_value(h);
+            } else {
+                if (res_out) ((float *)res_out)[i] = r;
+                rv = (double)r;
+            }
+            y[i] = rv;
+            ss += rv * rv;
+        }
+        inv = 1.0 / sqrt(ss / K + eps);
+        for (k = 0; k < K; ++k)
+            y[m * K + k] = y[m * K + k] * inv * load_src(dtype, gamma, k);
+    }
+    return 0;
+}
+
+/* SwiGLU: silu(g) * u with silu(g) = g / (1 + e^-g) */
+double oracle_silu(double g)
+{
+    return g / (1.0 + exp(-g));
+}
+
+void oracle_swiglu(const double *g, const double *u, int64_t n, double *y)
+{
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < n; ++i) y[i] = oracle_silu(g[i]) * u[i];
 }
 
 /* ------------------------------------------------------------------------ */

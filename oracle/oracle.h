@@ -35,7 +35,7 @@ extern "C" {
 #endif
 
 /* storage codes, numerically equal to the library's but defined here anew */
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_E4M3 = 2 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_E4M3 = 2, ORC_F64 = 9 };
 
 /* number of OpenMP threads used by the parallel loops; returns the count */
 int oracle_set_threads(int n);
@@ -112,6 +112,33 @@ int oracle_facache_merge(int cache_dtype, int B, int L, int Hkv, int d,
                          const int32_t *key_idx, int n_keys, double scale,
                          double *out, double *lse,
                          const int32_t *heads, int n_heads);
+
+/* ---- N2: per-group FP8 for the FFN [LaCache, Methodology 2] -------------
+ * Activations are quantised in 1 x 128 groups, weights in 128 x 128 blocks,
+ * each group with one power-of-two scale 2^e stored as the E8M0 code e + 127
+ * (the pages give the group shapes only; the scale format is a reading):
+ * e is the smallest integer >= -127 with amax <= 448 * 2^e, and
+ * code = RNE_e4m3(x / 2^e).  An all-zero group gets e = -127. */
+int oracle_e8m0_exponent(double amax);
+double oracle_e8m0_value(uint8_t code);
+void oracle_fp8_quantize_pow2(const double *x, int n, uint8_t *codes, uint8_t *e8m0);
+/* x: [M, ld] rows of dtype (f32, bf16, or ORC_F64 doubles), K % 128 == 0;
+ * codes [M, K]; scales [K/128, M] (group-major, one code per group). */
+int oracle_fp8_quant_rows(int dtype, const void *x, int64_t M, int K, int64_t ld,
+                          uint8_t *codes, uint8_t *scales);
+/* w: [N, K] (f32 or bf16); codes [N, K]; scales [N/128, K/128]. */
+int oracle_fp8_quant_weight(int dtype, const void *w, int N, int K, uint8_t *codes,
+                            uint8_t *scales);
+/* c [n_rows or M, N] = dequant(A) dequant(B)^T in fp64. */
+int oracle_fp8_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t *b, const uint8_t *sb,
+                    int64_t M, int N, int K, const int64_t *rows, int64_t n_rows, double *c);
+/* r = x + res (float32 add, stored in dtype: res_out may be NULL), then
+ * y = gamma * r / sqrt(mean(r^2) + eps) in fp64; res may be NULL (= 0). */
+int oracle_addnorm(int dtype, const void *x, const void *res, const void *gamma, double eps,
+                   int64_t M, int K, void *res_out, double *y);
+double oracle_silu(double g);
+/* y_i = silu(g_i) * u_i, the SwiGLU product of the gate and up halves */
+void oracle_swiglu(const double *g, const double *u, int64_t n, double *y);
 
 /* ---- A4: vocab statistics per row ---------------------------------------
  * p = softmax(x); argmax = lowest index of the largest logit; maxprob =
