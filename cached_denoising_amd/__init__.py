@@ -18,7 +18,9 @@ __all__ = [
     "F32", "BF16", "E4M3", "DllmError", "lib", "Cache", "StabilityState", "dllm_status_str",
     "dllm_version", "dllm_cache_init", "dllm_scatter_kv", "dllm_sink_rolling_map",
     "dllm_block_attention", "dllm_block_attention_workspace", "dllm_facache_maps",
-    "dllm_facache_merge", "dllm_facache_merge_workspace", "dllm_vocab_stats",
+    "dllm_facache_merge", "dllm_facache_merge_workspace", "dllm_fp8_quant_rows",
+    "dllm_fp8_addnorm_quant", "dllm_fp8_quant_weight", "dllm_fp8_gemm", "dllm_fp8_gemm_swiglu",
+    "dllm_vocab_stats",
     "dllm_vocab_stats_workspace", "dllm_stability_reset", "dllm_stability_mask",
 ]
 
@@ -74,6 +76,21 @@ EXPORTS = {
                                           ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "dllm_facache_merge_workspace": (ctypes.c_size_t, [ctypes.POINTER(_KVCache), ctypes.c_int,
                                                        ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+    "dllm_fp8_quant_rows": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                           ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p]),
+    "dllm_fp8_addnorm_quant": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_int, ctypes.c_float, ctypes.c_int64, ctypes.c_int,
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p]),
+    "dllm_fp8_quant_weight": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "dllm_fp8_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_void_p]),
+    "dllm_fp8_gemm_swiglu": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "dllm_vocab_stats": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -265,6 +282,90 @@ def dllm_facache_merge(cache: Cache, q: torch.Tensor, memo_o: torch.Tensor, memo
                                   ws_bytes, _stream())
     _check(rc, "dllm_facache_merge")
     return out
+
+
+def _u8(t: torch.Tensor, name: str):
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise DllmError(f"{name} must be uint8 codes")
+    return _dev(t, name)
+
+
+def dllm_fp8_quant_rows(x: torch.Tensor, codes: Optional[torch.Tensor] = None,
+                        scales: Optional[torch.Tensor] = None):
+    """x: [M, K] float32/bfloat16 (rows may be strided); returns (codes
+    [M, K] uint8, scales [K/128, M] uint8 E8M0)."""
+    M, K = x.shape
+    if x.stride(1) != 1:
+        raise DllmError("x rows must be contiguous")
+    codes = torch.empty((M, K), dtype=torch.uint8, device=x.device) if codes is None else codes
+    scales = torch.empty((K // 128, M), dtype=torch.uint8, device=x.device) if scales is None else scales
+    rc = lib().dllm_fp8_quant_rows(_dev(x, "x", contiguous=False), _dtype_code(x), M, K, x.stride(0),
+                                   _u8(codes, "codes"), _u8(scales, "scales"), _stream())
+    _check(rc, "dllm_fp8_quant_rows")
+    return codes, scales
+
+
+def dllm_fp8_addnorm_quant(x: torch.Tensor, residual: Optional[torch.Tensor], gamma: torch.Tensor,
+                           eps: float = 1e-6, residual_out: Optional[torch.Tensor] = None,
+                           codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
+                           write_residual: bool = True):
+    """r = x + residual (stored in residual_out), y = RMSNorm(r) * gamma,
+    quantised per 1 x 128 group; returns (residual_out, codes, scales)."""
+    M, K = x.shape
+    dev = x.device
+    if write_residual and residual_out is None:
+        residual_out = torch.empty_like(x)
+    codes = torch.empty((M, K), dtype=torch.uint8, device=dev) if codes is None else codes
+    scales = torch.empty((K // 128, M), dtype=torch.uint8, device=dev) if scales is None else scales
+    rc = lib().dllm_fp8_addnorm_quant(_dev(x, "x"), _dev(residual, "residual"), _dev(gamma, "gamma"),
+                                      _dtype_code(x), float(eps), M, K,
+                                      _dev(residual_out, "residual_out") if write_residual else None,
+                                      _u8(codes, "codes"), _u8(scales, "scales"), _stream())
+    _check(rc, "dllm_fp8_addnorm_quant")
+    return residual_out, codes, scales
+
+
+def dllm_fp8_quant_weight(w: torch.Tensor, codes: Optional[torch.Tensor] = None,
+                          scales: Optional[torch.Tensor] = None):
+    """w: [N, K]; returns (codes [N, K], scales [N/128, K/128])."""
+    N, K = w.shape
+    codes = torch.empty((N, K), dtype=torch.uint8, device=w.device) if codes is None else codes
+    scales = torch.empty((N // 128, K // 128), dtype=torch.uint8, device=w.device) if scales is None else scales
+    rc = lib().dllm_fp8_quant_weight(_dev(w, "w"), _dtype_code(w), N, K, _u8(codes, "codes"),
+                                     _u8(scales, "scales"), _stream())
+    _check(rc, "dllm_fp8_quant_weight")
+    return codes, scales
+
+
+def dllm_fp8_gemm(a: torch.Tensor, a_scale: torch.Tensor, w: torch.Tensor, w_scale: torch.Tensor,
+                  out: Optional[torch.Tensor] = None):
+    """C = dequant(A) dequant(W)^T, bf16 [M, N]."""
+    M, K = a.shape
+    N = w.shape[0]
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device) if out is None else out
+    if out.dtype != torch.bfloat16:
+        raise DllmError("out must be bfloat16")
+    rc = lib().dllm_fp8_gemm(_u8(a, "a"), _u8(a_scale, "a_scale"), _u8(w, "w"), _u8(w_scale, "w_scale"),
+                             M, N, K, _dev(out, "out"), _stream())
+    _check(rc, "dllm_fp8_gemm")
+    return out
+
+
+def dllm_fp8_gemm_swiglu(a: torch.Tensor, a_scale: torch.Tensor, w: torch.Tensor, w_scale: torch.Tensor,
+                         out_codes: Optional[torch.Tensor] = None,
+                         out_scales: Optional[torch.Tensor] = None):
+    """h = silu(gate) * up from the interleaved Gate-Up weight, quantised:
+    returns (codes [M, N/2], scales [N/256, M])."""
+    M, K = a.shape
+    N = w.shape[0]
+    dev = a.device
+    out_codes = torch.empty((M, N // 2), dtype=torch.uint8, device=dev) if out_codes is None else out_codes
+    out_scales = torch.empty((N // 256, M), dtype=torch.uint8, device=dev) if out_scales is None else out_scales
+    rc = lib().dllm_fp8_gemm_swiglu(_u8(a, "a"), _u8(a_scale, "a_scale"), _u8(w, "w"),
+                                    _u8(w_scale, "w_scale"), M, N, K, _u8(out_codes, "out_codes"),
+                                    _u8(out_scales, "out_scales"), _stream())
+    _check(rc, "dllm_fp8_gemm_swiglu")
+    return out_codes, out_scales
 
 
 def dllm_vocab_stats_workspace(N: int, V: int) -> int:

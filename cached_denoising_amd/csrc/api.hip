@@ -2,6 +2,7 @@
 // contract of every entry point is documented in include/dllm.h.
 #include "common.hpp"
 
+#include <climits>
 #include <cmath>
 
 using namespace dllm;
@@ -193,6 +194,74 @@ int dllm_facache_merge(const dllm_kv_cache *cache, const void *q, int q_dtype, i
     memo.lse = memo_lse;
     return launch_attention(*cache, p, q, q_dtype, Hq, n_q, key_idx, n_keys, scale, memo, out,
                             out_dtype, lse, workspace, static_cast<hipStream_t>(stream));
+}
+
+int dllm_fp8_quant_rows(const void *x, int dtype, int64_t M, int K, int64_t ld, uint8_t *codes,
+                        uint8_t *scales, void *stream) {
+    if (dtype != DLLM_F32 && dtype != DLLM_BF16) return DLLM_EDTYPE;
+    if (M < 0 || K < 128 || K % 128 != 0 || ld < K) return DLLM_ESHAPE;
+    if (M > INT32_MAX) return DLLM_ERANGE;
+    if (M == 0) return DLLM_OK;
+    if (!x || !codes || !scales) return DLLM_EINVAL;
+    if (!aligned16(x) || !aligned16(codes) || (ld * dtype_size(dtype)) % 16 != 0) return DLLM_EALIGN;
+    return launch_fp8_quant_rows(x, dtype, ld, M, K, codes, scales, static_cast<hipStream_t>(stream));
+}
+
+int dllm_fp8_addnorm_quant(const void *x, const void *residual, const void *gamma, int dtype,
+                           float eps, int64_t M, int K, void *residual_out, uint8_t *codes,
+                           uint8_t *scales, void *stream) {
+    if (dtype != DLLM_F32 && dtype != DLLM_BF16) return DLLM_EDTYPE;
+    if (M < 0 || K < 128 || K % 128 != 0 || K > 16384) return DLLM_ESHAPE;
+    if (M > INT32_MAX) return DLLM_ERANGE;
+    if (!(eps >= 0.f) || std::isinf(eps)) return DLLM_EINVAL;
+    if (M == 0) return DLLM_OK;
+    if (!x || !gamma || !codes || !scales) return DLLM_EINVAL;
+    if (!aligned16(x) || !aligned16(gamma) || !aligned16(codes) || (residual && !aligned16(residual)) ||
+        (residual_out && !aligned16(residual_out)))
+        return DLLM_EALIGN;
+    return launch_fp8_addnorm_quant(x, residual, gamma, dtype, eps, M, K, residual_out, codes, scales,
+                                    static_cast<hipStream_t>(stream));
+}
+
+int dllm_fp8_quant_weight(const void *w, int dtype, int N, int K, uint8_t *codes, uint8_t *scales,
+                          void *stream) {
+    if (dtype != DLLM_F32 && dtype != DLLM_BF16) return DLLM_EDTYPE;
+    if (N < 128 || K < 128 || N % 128 != 0 || K % 128 != 0) return DLLM_ESHAPE;
+    if (!w || !codes || !scales) return DLLM_EINVAL;
+    if (!aligned16(w) || !aligned16(codes)) return DLLM_EALIGN;
+    return launch_fp8_quant_weight(w, dtype, N, K, codes, scales, static_cast<hipStream_t>(stream));
+}
+
+namespace {
+int check_fp8_gemm(const uint8_t *a, const uint8_t *a_scale, const uint8_t *b, const uint8_t *b_scale,
+                   int M, int N, int K) {
+    if (M < 0 || N < 256 || K < 128 || N % 256 != 0 || K % 128 != 0) return DLLM_ESHAPE;
+    if (K > 12288) return DLLM_ERANGE;                // the tile's scales are held in LDS
+    if (!a || !a_scale || !b || !b_scale) return DLLM_EINVAL;
+    if (!aligned16(a) || !aligned16(b)) return DLLM_EALIGN;
+    return DLLM_OK;
+}
+}  // namespace
+
+int dllm_fp8_gemm(const uint8_t *a, const uint8_t *a_scale, const uint8_t *b, const uint8_t *b_scale,
+                  int M, int N, int K, void *c, void *stream) {
+    int rc = check_fp8_gemm(a, a_scale, b, b_scale, M, N, K);
+    if (rc != DLLM_OK) return rc;
+    if (M == 0) return DLLM_OK;
+    if (!c) return DLLM_EINVAL;
+    return launch_fp8_gemm(a, a_scale, b, b_scale, M, N, K, 0, static_cast<uint16_t *>(c), nullptr,
+                           nullptr, static_cast<hipStream_t>(stream));
+}
+
+int dllm_fp8_gemm_swiglu(const uint8_t *a, const uint8_t *a_scale, const uint8_t *b,
+                         const uint8_t *b_scale, int M, int N, int K, uint8_t *out_codes,
+                         uint8_t *out_scales, void *stream) {
+    int rc = check_fp8_gemm(a, a_scale, b, b_scale, M, N, K);
+    if (rc != DLLM_OK) return rc;
+    if (M == 0) return DLLM_OK;
+    if (!out_codes || !out_scales) return DLLM_EINVAL;
+    return launch_fp8_gemm(a, a_scale, b, b_scale, M, N, K, 1, nullptr, out_codes, out_scales,
+                           static_cast<hipStream_t>(stream));
 }
 
 size_t dllm_vocab_stats_workspace(int64_t N, int64_t V) {

@@ -31,6 +31,39 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// float32 -> OCP e4m3fn code, round to nearest even, saturate to +-448.
+// Works on the float's bits: the e4m3 value is the float's significand
+// shifted right so that 3 fraction bits remain (more for results below the
+// e4m3 normal range), rounded half to even on the dropped bits.
+__device__ __forceinline__ uint32_t e4m3_rne(float q) {
+    const uint32_t u = __float_as_uint(q);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return 0x7fu;                  // NaN
+    if (a > 0x43e00000u) return sign | 0x7eu;            // |q| > 448 (incl. inf)
+    const int E = (int)(a >> 23) - 127;                  // unbiased exponent
+    uint32_t r;
+    if (E < -6) {
+        // below 2^-6: count units of 2^-9 (the e4m3 subnormal spacing)
+        const uint32_t mant = (a >> 23) ? ((a & 0x7fffffu) | 0x800000u) : (a & 0x7fffffu);
+        const int sh = (a >> 23) ? (14 - E) : 140;       // q * 2^9 = mant >> sh
+        if (sh >= 32) {
+            r = 0;
+        } else {
+            r = mant >> sh;
+            const uint32_t rem = mant & ((1u << sh) - 1u);
+            const uint32_t half = 1u << (sh - 1);
+            if (rem > half || (rem == half && (r & 1u))) ++r;   // r = 8 is 2^-6: code 0x08
+        }
+    } else {
+        // exponent field E + 7 and the top 3 fraction bits, rounded on the other 20
+        r = ((uint32_t)(E + 7) << 3) | ((a >> 20) & 7u);
+        const uint32_t rem = a & 0xfffffu;
+        if (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ++r;
+    }
+    return sign | r;
+}
+
 // cross-lane helpers on a 64-wide wavefront
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
 __device__ __forceinline__ int shfl_xor_i(int v, int m) { return __shfl_xor(v, m, kWave); }
@@ -90,6 +123,17 @@ int launch_attn_merge(const float *part_o, const float *part_ml, int64_t rows_to
 int launch_attention(const dllm_kv_cache &c, const AttnPlan &p, const void *q, int q_dtype, int Hq,
                      int b, const int32_t *key_idx, int n_keys, float scale, const AttnMemo &memo,
                      void *out, int out_dtype, float *lse, void *ws, hipStream_t s);
+
+// per-group FP8 for the FFN
+int launch_fp8_quant_rows(const void *x, int dtype, int64_t ld, int64_t M, int K, uint8_t *codes,
+                          uint8_t *scales, hipStream_t s);
+int launch_fp8_addnorm_quant(const void *x, const void *res, const void *gamma, int dtype, float eps,
+                             int64_t M, int K, void *res_out, uint8_t *codes, uint8_t *scales,
+                             hipStream_t s);
+int launch_fp8_quant_weight(const void *w, int dtype, int N, int K, uint8_t *codes, uint8_t *scales,
+                            hipStream_t s);
+int launch_fp8_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t *b, const uint8_t *sb, int M,
+                    int N, int K, int epilogue, uint16_t *c, uint8_t *qc, uint8_t *qs, hipStream_t s);
 
 struct VocabPlan {
     int threads;       // workgroup size: 256, or 512 when there are few rows

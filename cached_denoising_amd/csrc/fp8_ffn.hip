@@ -1,0 +1,476 @@
+// Per-group FP8 for the FFN [LaCache explainer, Methodology 2]: activations
+// quantised in 1 x 128 groups and weights in 128 x 128 blocks, the Gate-Up
+// and FF-Out products on FP8 matrix cores, the quantisation fused into the
+// add & norm before the FFN and into the SwiGLU between the two products.
+//
+// Each group's scale is a power of two 2^e, stored as its E8M0 code e + 127
+// (e the smallest >= -127 with amax <= 448 * 2^e), so that gfx950's
+// block-scaled MFMA (v_mfma_scale_f32_32x32x64_f8f6f4) applies the scales of
+// both operands itself: one fp32 accumulator per output element, no
+// per-group rescale on the vector ALU.  Dividing by a power of two is exact,
+// so a code is RNE_e4m3(x * 2^-e).
+//
+// Scale layouts: activations [K/128, M] (one byte per row per group, the
+// rows of one group contiguous, as one k-step of the product reads them);
+// weights [N/128, K/128].
+#include "attn_common.hpp"
+
+#include <climits>
+
+namespace dllm {
+namespace {
+
+using attn::lds_dma16;
+using attn::vm_wait;
+using attn::xcd_remap;
+
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+// smallest e >= -127 with amax <= 448 * 2^e: with amax = f * 2^E,
+// f in [0.5, 1) and 448 = 0.875 * 2^9, e = E - 9 when f <= 0.875, else E - 8
+__device__ __forceinline__ int e8m0_exponent(float amax) {
+    if (!(amax > 0.f)) return -127;
+    int E;
+    const float f = frexpf(amax, &E);
+    const int e = f <= 0.875f ? E - 9 : E - 8;
+    return e < -127 ? -127 : e;
+}
+
+// 8 values of one group -> 8 codes (two words); ldexpf scales exactly
+__device__ __forceinline__ uint2 encode8(const float *x, int e) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t code = e4m3_rne(ldexpf(x[i], -e));
+        if (i < 4) lo |= code << (8 * i);
+        else hi |= code << (8 * (i - 4));
+    }
+    return make_uint2(lo, hi);
+}
+
+template <int DT>
+__device__ __forceinline__ void load8(const void *p, int64_t i, float *x) {
+    if (DT == DLLM_BF16) {
+        const uint4 w = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p) + i);
+        const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[2 * j] = bf16lo(a[j]);
+            x[2 * j + 1] = bf16hi(a[j]);
+        }
+    } else {
+        const float4 *q = reinterpret_cast<const float4 *>(static_cast<const float *>(p) + i);
+        const float4 u = q[0], v = q[1];
+        x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+        x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+    }
+}
+
+__device__ __forceinline__ float max16(float v) {       // over the 16 lanes of a group
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) v = fmaxf(v, shfl_xor_f(v, o));
+    return v;
+}
+
+// ---- activations: 16 lanes per 1 x 128 group, 8 values per lane ------------
+template <int DT>
+__global__ __launch_bounds__(256) void fp8_quant_rows_kernel(const void *__restrict__ x, int64_t ld,
+                                                             int64_t M, int K, uint8_t *__restrict__ codes,
+                                                             uint8_t *__restrict__ scales) {
+    const int G = K / 128;
+    const int64_t grp = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
+    const int l16 = threadIdx.x & 15;
+    const bool live = grp < M * G;
+    const int64_t m = live ? grp / G : 0;
+    const int g = live ? (int)(grp - m * G) : 0;
+    float v[8];
+    if (live) load8<DT>(x, m * ld + g * 128 + l16 * 8, v);
+    else
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.f;
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
+    a = max16(a);                                      // every lane joins the shuffles
+    if (!live) return;
+    const int e = e8m0_exponent(a);
+    *reinterpret_cast<uint2 *>(codes + m * K + g * 128 + l16 * 8) = encode8(v, e);
+    if (l16 == 0) scales[(int64_t)g * M + m] = (uint8_t)(e + 127);
+}
+
+// ---- add & RMS norm, then the 1 x 128 groups of the normalised row ----------
+// One workgroup per row: r = x + res in fp32, rounded to the stream dtype
+// (res_out); y = gamma * r / sqrt(mean(r^2) + eps); the rounded r waits in
+// LDS for the second pass.
+template <int DT>
+__global__ __launch_bounds__(256) void fp8_addnorm_quant_kernel(
+    const void *__restrict__ x, const void *__restrict__ res, const void *__restrict__ gamma,
+    float eps, int64_t M, int K, void *__restrict__ res_out, uint8_t *__restrict__ codes,
+    uint8_t *__restrict__ scales) {
+    extern __shared__ float sr[];                      // K floats
+    __shared__ float red[4];
+    const int64_t m = blockIdx.x;
+    const int tid = threadIdx.x;
+    float ss = 0.f;
+    for (int c = tid * 8; c < K; c += 256 * 8) {
+        float a[8], b[8];
+        load8<DT>(x, m * K + c, a);
+        if (res) load8<DT>(res, m * K + c, b);
+        else
+#pragma unroll
+            for (int i = 0; i < 8; ++i) b[i] = 0.f;
+        float r[8];
+        if (DT == DLLM_BF16) {
+            uint32_t w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint16_t lo = f32_to_bf16(a[2 * i] + b[2 * i]);
+                const uint16_t hi = f32_to_bf16(a[2 * i + 1] + b[2 * i + 1]);
+                w[i] = (uint32_t)lo | ((uint32_t)hi << 16);
+                r[2 * i] = bf16_to_f32(lo);
+                r[2 * i + 1] = bf16_to_f32(hi);
+            }
+            if (res_out)
+                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(res_out) + m * K + c) =
+                    make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) r[i] = a[i] + b[i];
+            if (res_out) {
+                float4 *o = reinterpret_cast<float4 *>(static_cast<float *>(res_out) + m * K + c);
+                o[0] = make_float4(r[0], r[1], r[2], r[3]);
+                o[1] = make_float4(r[4], r[5], r[6], r[7]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            sr[c + i] = r[i];
+            ss = fmaf(r[i], r[i], ss);
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss += shfl_xor_f(ss, o);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    ss = (red[0] + red[1]) + (red[2] + red[3]);
+    const float inv = 1.0f / sqrtf(ss / (float)K + eps);
+    const int G = K / 128;
+    const int l16 = tid & 15;
+    // groups in rounds of 16 (one per 16 lanes); every lane of a round's waves
+    // joins the shuffles
+    for (int g0 = 0; g0 < G; g0 += 16) {
+        const int g = g0 + (tid >> 4);
+        const bool live = g < G;
+        float y[8], gm[8];
+        float a = 0.f;
+        if (live) {
+            load8<DT>(gamma, g * 128 + l16 * 8, gm);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                y[i] = sr[g * 128 + l16 * 8 + i] * inv * gm[i];
+                a = fmaxf(a, fabsf(y[i]));
+            }
+        }
+        a = max16(a);
+        if (!live) continue;
+        const int e = e8m0_exponent(a);
+        *reinterpret_cast<uint2 *>(codes + m * K + g * 128 + l16 * 8) = encode8(y, e);
+        if (l16 == 0) scales[(int64_t)g * M + m] = (uint8_t)(e + 127);
+    }
+}
+
+// ---- weights: one workgroup per 128 x 128 block, 64 values per thread -------
+template <int DT>
+__global__ __launch_bounds__(256) void fp8_quant_weight_kernel(const void *__restrict__ w, int N, int K,
+                                                               uint8_t *__restrict__ codes,
+                                                               uint8_t *__restrict__ scales) {
+    __shared__ float red[4];
+    const int kb = K / 128;
+    const int bn = blockIdx.x / kb, bk = blockIdx.x % kb;
+    const int tid = threadIdx.x;
+    const int r = tid >> 1, h = tid & 1;               // row of the block, half of the row
+    const int64_t base = (int64_t)(bn * 128 + r) * K + bk * 128 + h * 64;
+    float v[64];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) load8<DT>(w, base + j * 8, v + j * 8);
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) a = fmaxf(a, fabsf(v[i]));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) a = fmaxf(a, shfl_xor_f(a, o));
+    if ((tid & 63) == 0) red[tid >> 6] = a;
+    __syncthreads();
+    a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const int e = e8m0_exponent(a);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) *reinterpret_cast<uint2 *>(codes + base + j * 8) = encode8(v + j * 8, e);
+    if (tid == 0) scales[blockIdx.x] = (uint8_t)(e + 127);
+}
+
+// ---- the product: C = dequant(A) dequant(B)^T -------------------------------
+// A [M, K] codes with scales [K/128, M]; B [N, K] codes with scales
+// [N/128, K/128]; fp32 accumulation.  A workgroup of 4 waves owns a 256 x 256
+// tile, each wave 128 x 128 (4 x 4 tiles of 32 x 32), and walks K in steps
+// of 128 (one scale group): per step the A and B tiles (32 KB each) land in
+// one of two LDS stages by direct-to-LDS loads while the other stage is
+// read.  In LDS a 128-byte row keeps its eight 16-byte chunks XOR-swizzled
+// by the row's low 3 bits, so the 8 lanes of a read phase (8 rows, one
+// logical chunk) hit 8 distinct bank groups.
+//
+// Operands of v_mfma_scale_f32_32x32x64_f8f6f4: lane l holds 32 bytes of
+// row l % 32 (A) or of column l % 32 (B), K bytes 32 (l / 32) .. +31 of the
+// 64-byte k-chunk; the same lane half and byte on both sides is the same K
+// index.  Each lane also passes its row's (column's) E8M0 scale, one per
+// 128-wide group, so both scales multiply inside the instruction.  Lane l,
+// register i of the result holds row 8 (i / 4) + 4 (l / 32) + i % 4,
+// column l % 32.
+//
+// EPI 0 writes C in bf16.  EPI 1 is SwiGLU with the 1 x 128 quantisation of
+// its output: B's rows come in pairs of 128-row blocks (gate block j, then
+// up block j), so the wave of tile columns 0..127 holds gate features
+// 128 j .. +127 and its neighbour the matching up features; the neighbour
+// hands its accumulators over through LDS and the gate wave writes
+// silu(gate) * up as codes of [M, N/2] with scales [N/256, M].
+constexpr int kBM = 256, kBN = 256, kBK = 128;
+constexpr int kTileBytes = kBM * kBK;                  // one operand tile of one stage
+constexpr int kGemmLds = 2 * 2 * kTileBytes;           // two stages of A and B: 128 KB
+constexpr int kGemmMaxK = 12288;                       // the scales of 96 k-steps fit beside them
+constexpr int kGemmSmem = kGemmLds + (kGemmMaxK / kBK) * (256 + 2);
+static_assert(kGemmSmem <= attn::kLdsBytes, "LDS of one workgroup");
+
+// the block-scaled product with byte `sel` (0..3) of sa as A's scale
+__device__ __forceinline__ f32x16_t mfma_scaled(const i32x8_t &a, const i32x8_t &b, const f32x16_t &c,
+                                                int sa, int sel, int sb) {
+    switch (sel) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 1, sa, 0, sb);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 2, sa, 0, sb);
+    default: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 3, sa, 0, sb);
+    }
+}
+
+// LDS byte offset of 16-byte chunk c of tile row r
+__device__ __forceinline__ int swz(int r, int c) { return r * kBK + ((c ^ (r & 7)) << 4); }
+
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(
+    const uint8_t *__restrict__ a, const uint8_t *__restrict__ sa, const uint8_t *__restrict__ b,
+    const uint8_t *__restrict__ sb, int M, int N, int K, int tiles_m, int tiles_n,
+    uint16_t *__restrict__ c, uint8_t *__restrict__ qc, uint8_t *__restrict__ qs) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kGemmSmem];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l32 = lane & 31, lh = lane >> 5;
+
+    // tile order: the 8 XCDs each take one contiguous run of the logical
+    // order, which walks groups of 8 tile rows column by column, so the
+    // tiles in flight on one XCD share A rows and B columns in its L2
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int per_group = 8 * tiles_n;
+    const int grp = lid / per_group, first_m = grp * 8;
+    const int gsize = min(tiles_m - first_m, 8);
+    const int in_g = lid - grp * per_group;
+    const int tm = first_m + in_g % gsize, tn = in_g / gsize;
+    const int m0 = tm * kBM, n0 = tn * kBN;
+    const int ksteps = K / kBK;
+
+    // direct-to-LDS loads: wave w issues 1 KB loads u = 0..7 of each tile;
+    // load u covers tile rows 8 (8 w + u) .. +7, lane i row 8 (8 w + u) + i / 8,
+    // stored slot i % 8 holding logical chunk (i % 8) ^ (i / 8)
+    const int lrow = lane >> 3;
+    const int lchunk = (lane & 7) ^ lrow;
+    auto issue = [&](int ks, int stage) {
+        unsigned char *sa_lds = smem + stage * 2 * kTileBytes;
+        unsigned char *sb_lds = sa_lds + kTileBytes;
+        const int64_t k0 = (int64_t)ks * kBK + lchunk * 16;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int r = 8 * (8 * wave + u) + lrow;
+            const int ra = min(m0 + r, M - 1);          // rows past M read row M - 1, never stored
+            lds_dma16<false>(a + (int64_t)ra * K + k0, sa_lds + (8 * wave + u) * 1024);
+            lds_dma16<false>(b + (int64_t)(n0 + r) * K + k0, sb_lds + (8 * wave + u) * 1024);
+        }
+    };
+    // All E8M0 scales of the tile wait in LDS, read once in a prologue: the A
+    // scales of step ks at ssa + 256 ks, packed so that the word at
+    // 128 wm + 4 l32 holds the scales of this lane's row in row tiles 0..3
+    // (the MFMA's op_sel picks the byte), the B scales of the wave's 128
+    // columns at ssb[ksteps wn + ks].  The loop then issues no global load
+    // the compiler sees, so it places no wait of its own (one would also wait
+    // for the direct-to-LDS loads in flight, which it cannot see).
+    unsigned char *ssa = smem + kGemmLds;
+    unsigned char *ssb = ssa + ksteps * 256;
+    issue(0, 0);                                       // the first tiles load under the prologue
+    {
+        // thread t reads row m0 + t of every step (256 threads read one step's
+        // 256 contiguous bytes together), 16 steps' loads in flight at a time
+        const int wq = tid >> 7, rq = (tid >> 5) & 3, lq = tid & 31;   // tid = 128 wm + 32 rt + l32
+        const uint8_t *src = sa + min(m0 + tid, M - 1);
+        unsigned char *dst = ssa + wq * 128 + lq * 4 + rq;
+        for (int k0 = 0; k0 < ksteps; k0 += 16) {
+            uint8_t v[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                if (k0 + j < ksteps) v[j] = src[(int64_t)(k0 + j) * M];
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                if (k0 + j < ksteps) dst[(k0 + j) * 256] = v[j];
+        }
+        if (tid < 2 * ksteps)
+            ssb[tid] = sb[(int64_t)((n0 >> 7) + tid / ksteps) * ksteps + tid % ksteps];
+    }
+
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    for (int ks = 0; ks < ksteps; ++ks) {
+        const int stage = ks & 1;
+        // this wave's loads of step ks have landed; the barrier makes every
+        // wave's loads (and, the first time, the scales) visible and tells
+        // that every wave is done with the stage the next loads refill
+        vm_wait<0>();
+        __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+        asm volatile("s_barrier" ::: "memory");
+        if (ks + 1 < ksteps) issue(ks + 1, stage ^ 1);
+        const int sav = *reinterpret_cast<const int *>(ssa + ks * 256 + wm * 128 + l32 * 4);
+        const int sbv = ssb[wn * ksteps + ks];
+        const unsigned char *at = smem + stage * 2 * kTileBytes + wm * 128 * kBK;
+        const unsigned char *bt = smem + stage * 2 * kTileBytes + kTileBytes + wn * 128 * kBK;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+            const int c0 = kh * 4 + lh * 2;
+            i32x8_t av[4], bv[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int r = t * 32 + l32;
+                const uint4 x0 = *reinterpret_cast<const uint4 *>(at + swz(r, c0));
+                const uint4 x1 = *reinterpret_cast<const uint4 *>(at + swz(r, c0 + 1));
+                av[t] = i32x8_t{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                                (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+                const uint4 y0 = *reinterpret_cast<const uint4 *>(bt + swz(r, c0));
+                const uint4 y1 = *reinterpret_cast<const uint4 *>(bt + swz(r, c0 + 1));
+                bv[t] = i32x8_t{(int)y0.x, (int)y0.y, (int)y0.z, (int)y0.w,
+                                (int)y1.x, (int)y1.y, (int)y1.z, (int)y1.w};
+            }
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct)
+                    acc[rt][ct] = mfma_scaled(av[rt], bv[ct], acc[rt][ct], sav, rt, sbv);
+        }
+    }
+
+    if (EPI == 0) {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int row = m0 + wm * 128 + rt * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
+                if (row >= M) continue;
+                uint16_t *crow = c + (int64_t)row * N + n0 + wn * 128 + l32;
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) crow[ct * 32] = f32_to_bf16(acc[rt][ct][i]);
+            }
+    } else {
+        // the up wave's accumulators go through LDS, one float per (register, lane)
+        __syncthreads();                                // every wave is done with the stages
+        float *up = reinterpret_cast<float *>(smem) + wm * (256 * 64);
+        if (wn == 1) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) up[((rt * 4 + ct) * 16 + i) * 64 + lane] = acc[rt][ct][i];
+        }
+        __syncthreads();
+        if (wn == 0) {
+            const int half_n = N >> 1;
+            const int64_t fcol = (int64_t)(n0 >> 1) + l32;        // feature of column tile 0
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int row = m0 + wm * 128 + rt * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
+                    float y[4], am = 0.f;
+#pragma unroll
+                    for (int ct = 0; ct < 4; ++ct) {
+                        const float g = acc[rt][ct][i];
+                        const float u = up[((rt * 4 + ct) * 16 + i) * 64 + lane];
+                        y[ct] = g / (1.0f + __expf(-g)) * u;
+                        am = fmaxf(am, fabsf(y[ct]));
+                    }
+                    // the row's 128 features: 4 registers x the 32 lanes of this half
+#pragma unroll
+                    for (int o = 16; o >= 1; o >>= 1) am = fmaxf(am, shfl_xor_f(am, o));
+                    if (row >= M) continue;
+                    const int e = e8m0_exponent(am);
+                    uint8_t *qrow = qc + (int64_t)row * half_n + fcol;
+#pragma unroll
+                    for (int ct = 0; ct < 4; ++ct) qrow[ct * 32] = (uint8_t)e4m3_rne(ldexpf(y[ct], -e));
+                    if (l32 == 0) qs[(int64_t)(n0 >> 8) * M + row] = (uint8_t)(e + 127);
+                }
+        }
+    }
+}
+
+}  // namespace
+
+int launch_fp8_quant_rows(const void *x, int dtype, int64_t ld, int64_t M, int K, uint8_t *codes,
+                          uint8_t *scales, hipStream_t s) {
+    if (M == 0) return DLLM_OK;
+    const int64_t threads = M * (K / 128) * 16;
+    const unsigned blocks = (unsigned)cdiv64(threads, 256);
+    if (dtype == DLLM_BF16)
+        fp8_quant_rows_kernel<DLLM_BF16><<<blocks, 256, 0, s>>>(x, ld, M, K, codes, scales);
+    else
+        fp8_quant_rows_kernel<DLLM_F32><<<blocks, 256, 0, s>>>(x, ld, M, K, codes, scales);
+    return launch_status();
+}
+
+int launch_fp8_addnorm_quant(const void *x, const void *res, const void *gamma, int dtype, float eps,
+                             int64_t M, int K, void *res_out, uint8_t *codes, uint8_t *scales,
+                             hipStream_t s) {
+    if (M == 0) return DLLM_OK;
+    const size_t lds = (size_t)K * sizeof(float);
+    if (dtype == DLLM_BF16)
+        fp8_addnorm_quant_kernel<DLLM_BF16><<<(unsigned)M, 256, lds, s>>>(x, res, gamma, eps, M, K, res_out,
+                                                                          codes, scales);
+    else
+        fp8_addnorm_quant_kernel<DLLM_F32><<<(unsigned)M, 256, lds, s>>>(x, res, gamma, eps, M, K, res_out,
+                                                                         codes, scales);
+    return launch_status();
+}
+
+int launch_fp8_quant_weight(const void *w, int dtype, int N, int K, uint8_t *codes, uint8_t *scales,
+                            hipStream_t s) {
+    const unsigned blocks = (unsigned)((N / 128) * (K / 128));
+    if (dtype == DLLM_BF16)
+        fp8_quant_weight_kernel<DLLM_BF16><<<blocks, 256, 0, s>>>(w, N, K, codes, scales);
+    else
+        fp8_quant_weight_kernel<DLLM_F32><<<blocks, 256, 0, s>>>(w, N, K, codes, scales);
+    return launch_status();
+}
+
+int launch_fp8_gemm(const uint8_t *a, const uint8_t *sa, const uint8_t *b, const uint8_t *sb, int M,
+                    int N, int K, int epilogue, uint16_t *c, uint8_t *qc, uint8_t *qs, hipStream_t s) {
+    const int tiles_m = cdiv(M, kBM), tiles_n = N / kBN;
+    const int64_t blocks = (int64_t)tiles_m * tiles_n;
+    if (blocks > INT_MAX) return DLLM_ERANGE;
+    if (epilogue == 0)
+        fp8_gemm_kernel<0><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(a, sa, b, sb, M, N, K, tiles_m,
+                                                                        tiles_n, c, qc, qs);
+    else
+        fp8_gemm_kernel<1><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(a, sa, b, sb, M, N, K, tiles_m,
+                                                                        tiles_n, c, qc, qs);
+    return launch_status();
+}
+
+}  // namespace dllm

@@ -11,39 +11,6 @@
 namespace dllm {
 namespace {
 
-// ---- float32 -> OCP e4m3fn, round to nearest even, saturate to +-448 -----
-// Works on the float's bits: the e4m3 value is the float's significand
-// shifted right so that 3 fraction bits remain (more for results below the
-// e4m3 normal range), rounded half to even on the dropped bits.
-__device__ __forceinline__ uint32_t e4m3_rne(float q) {
-    const uint32_t u = __float_as_uint(q);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7fffffffu;
-    if (a > 0x7f800000u) return 0x7fu;                  // NaN
-    if (a > 0x43e00000u) return sign | 0x7eu;            // |q| > 448 (incl. inf)
-    const int E = (int)(a >> 23) - 127;                  // unbiased exponent
-    uint32_t r;
-    if (E < -6) {
-        // below 2^-6: count units of 2^-9 (the e4m3 subnormal spacing)
-        const uint32_t mant = (a >> 23) ? ((a & 0x7fffffu) | 0x800000u) : (a & 0x7fffffu);
-        const int sh = (a >> 23) ? (14 - E) : 140;       // q * 2^9 = mant >> sh
-        if (sh >= 32) {
-            r = 0;
-        } else {
-            r = mant >> sh;
-            const uint32_t rem = mant & ((1u << sh) - 1u);
-            const uint32_t half = 1u << (sh - 1);
-            if (rem > half || (rem == half && (r & 1u))) ++r;   // r = 8 is 2^-6: code 0x08
-        }
-    } else {
-        // exponent field E + 7 and the top 3 fraction bits, rounded on the other 20
-        r = ((uint32_t)(E + 7) << 3) | ((a >> 20) & 7u);
-        const uint32_t rem = a & 0xfffffu;
-        if (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ++r;
-    }
-    return sign | r;
-}
-
 // ---- plain copy: one 16-byte chunk per thread ------------------------------
 __global__ __launch_bounds__(256) void scatter_copy_kernel(
     const uint4 *__restrict__ k_new, const uint4 *__restrict__ v_new, uint4 *__restrict__ ck,

@@ -12,6 +12,8 @@
  *   dllm_facache_maps      unchanged / changed key lists of a block's steps
  *   dllm_facache_merge     queries outside the block: memoized softmax state
  *                          continued over the changed keys only
+ *   dllm_fp8_*             per-group FP8 FFN: quantisers, add & norm + quant,
+ *                          block-scaled GEMM, GEMM + SwiGLU + quant
  *   dllm_vocab_stats       argmax token, max-probability, entropy per row
  *   dllm_stability_reset   clear the per-position decode state
  *   dllm_stability_mask    history ring, stability test, confidence score and
@@ -244,6 +246,60 @@ int dllm_facache_merge(const dllm_kv_cache *cache, const void *q, int q_dtype, i
  * a key map (0 if the keys are not split over workgroups). */
 size_t dllm_facache_merge_workspace(const dllm_kv_cache *cache, int q_dtype, int Hq,
                                     int n_q, int n_keys);
+
+/* ---------------------------------------------------------------------------
+ * Per-group FP8 for the FFN [LaCache, Methodology 2: Gate-Up and FF-Out in
+ * FP8 with 1 x 128 activation groups and 128 x 128 weight groups, the
+ * quantisation fused into the add & norm and into SwiGLU].
+ * Every group carries one power-of-two scale 2^e stored as the E8M0 byte
+ * e + 127 (the pages fix the group shapes only): e is the smallest integer
+ * >= -127 with amax <= 448 * 2^e, and each code is the OCP e4m3fn value
+ * RNE(x / 2^e), so no code saturates.  An all-zero group gets e = -127.
+ * Layouts (row-major):
+ *   activation codes [M, K] u8, activation scales [K/128, M] u8 (the scales
+ *     of one 128-column group are contiguous over the rows);
+ *   weight codes [N, K] u8 (the product is A . W^T), weight scales
+ *     [N/128, K/128] u8.
+ * K must be a multiple of 128 throughout; code arrays 16-byte aligned.
+ * ------------------------------------------------------------------------- */
+
+/* dllm_fp8_quant_rows -- quantise the 1 x 128 groups of an [M, K] matrix
+ * (rows at stride ld elements, F32 or BF16; ld * size % 16 == 0). */
+int dllm_fp8_quant_rows(const void *x, int dtype, int64_t M, int K, int64_t ld,
+                        uint8_t *codes, uint8_t *scales, void *stream);
+
+/* dllm_fp8_addnorm_quant -- the add & norm before the FFN, fused with the
+ * quantisation of its output: per row, r = x + residual (float32 add,
+ * rounded to dtype and written to residual_out when non-NULL), then
+ * y = gamma * r / sqrt(mean(r^2) + eps) (RMS normalisation, float32), then
+ * the 1 x 128 groups of y as codes and scales.  residual may be NULL (= 0).
+ *   x, residual, residual_out [M, K]; gamma [K]; all of dtype (F32 / BF16)
+ * Limits: K <= 16384, eps >= 0. */
+int dllm_fp8_addnorm_quant(const void *x, const void *residual, const void *gamma, int dtype,
+                           float eps, int64_t M, int K, void *residual_out,
+                           uint8_t *codes, uint8_t *scales, void *stream);
+
+/* dllm_fp8_quant_weight -- quantise the 128 x 128 blocks of a weight
+ * matrix W [N, K] (F32 or BF16; N % 128 == 0). */
+int dllm_fp8_quant_weight(const void *w, int dtype, int N, int K, uint8_t *codes,
+                          uint8_t *scales, void *stream);
+
+/* dllm_fp8_gemm -- C = dequant(A) . dequant(W)^T on the block-scaled FP8
+ * matrix cores with float32 accumulation, C [M, N] bf16 (the FF-Out
+ * product).  N % 256 == 0, 128 <= K <= 12288, any M >= 0. */
+int dllm_fp8_gemm(const uint8_t *a, const uint8_t *a_scale, const uint8_t *w,
+                  const uint8_t *w_scale, int M, int N, int K, void *c, void *stream);
+
+/* dllm_fp8_gemm_swiglu -- the Gate-Up product fused with SwiGLU and the
+ * quantisation of its output: W's rows come in pairs of 128-row blocks,
+ * block 2j holding gate features 128j .. 128j+127 and block 2j+1 the up
+ * features of the same indices; per row and feature f,
+ *   h_f = silu(gate_f) * up_f,  silu(g) = g / (1 + e^-g)  (float32)
+ * and h [M, N/2] is written as codes with scales [N/256, M] (the 1 x 128
+ * groups of h), the input of the FF-Out product.  Limits as dllm_fp8_gemm. */
+int dllm_fp8_gemm_swiglu(const uint8_t *a, const uint8_t *a_scale, const uint8_t *w,
+                         const uint8_t *w_scale, int M, int N, int K, uint8_t *out_codes,
+                         uint8_t *out_scales, void *stream);
 
 /* ---------------------------------------------------------------------------
  * dllm_vocab_stats -- one pass over each row of logits:

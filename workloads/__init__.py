@@ -182,6 +182,44 @@ def memo_state(B: int, Hq: int, n: int, d: int, seed: int, o_std: float, lse_mea
     return o.to(device), lse.to(device)
 
 
+def fp8_codes(shape, seed: int, device="cpu", exp_lo: int = 0, exp_hi: int = 15) -> torch.Tensor:
+    """OCP e4m3fn codes with a uniform sign and mantissa and an exponent field
+    uniform in [exp_lo, exp_hi] (field 0: subnormals; the NaN code of field
+    15 is replaced by the largest finite code), uint8"""
+    g = generator(seed, "cpu")
+    sign = torch.randint(0, 2, shape, generator=g, dtype=torch.int32)
+    e = torch.randint(exp_lo, exp_hi + 1, shape, generator=g, dtype=torch.int32)
+    m = torch.randint(0, 8, shape, generator=g, dtype=torch.int32)
+    c = (sign << 7) | (e << 3) | m
+    c = torch.where((c & 0x7F) == 0x7F, c - 1, c)
+    return c.to(torch.uint8).to(device)
+
+
+def e8m0_codes(shape, seed: int, lo: int, hi: int, device="cpu") -> torch.Tensor:
+    """E8M0 scale codes drawn uniformly from [lo, hi], uint8"""
+    g = generator(seed, "cpu")
+    return torch.randint(lo, hi + 1, shape, generator=g, dtype=torch.int32).to(torch.uint8).to(device)
+
+
+# the FFN of a LLaDA-8B-shaped layer: hidden 4096 (32 heads x 128), SwiGLU
+# width 12288 (the pages give no FFN width; 3x the hidden width is taken)
+FFN_HIDDEN, FFN_INTER = 4096, 12288
+
+
+def ffn_inputs(M: int, seed: int, device="cpu", K: int = FFN_HIDDEN, I: int = FFN_INTER):
+    """hidden states x and residual [M, K] ~ N(0, 1), RMS-norm weight
+    gamma ~ 1 + N(0, 0.1^2) [K], Gate-Up weight [2I, K] with gate and up
+    128-row blocks interleaved ~ N(0, 1/K), FF-Out weight [K, I] ~ N(0, 1/I),
+    all bf16"""
+    g = generator(seed, device)
+    x = _randn((M, K), 1.0, g, device, torch.bfloat16)
+    res = _randn((M, K), 1.0, g, device, torch.bfloat16)
+    gamma = (1.0 + torch.randn((K,), generator=g, device=device) * 0.1).to(torch.bfloat16)
+    w_gu = _randn((2 * I, K), 1.0 / math.sqrt(K), g, device, torch.bfloat16)
+    w_out = _randn((K, I), 1.0 / math.sqrt(I), g, device, torch.bfloat16)
+    return x, res, gamma, w_gu, w_out
+
+
 def logits(cfg: Config, device="cpu", step: int = 0, rows: Optional[int] = None,
            stride: Optional[int] = None, dtype: Optional[int] = None):
     """[rows, stride] logits (only the first V columns are used).
