@@ -16,6 +16,7 @@
 #include "attn_common.hpp"
 
 #include <climits>
+#include <type_traits>
 
 namespace dllm {
 namespace {
@@ -27,26 +28,41 @@ using attn::xcd_remap;
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
-// smallest e >= -127 with amax <= 448 * 2^e: with amax = f * 2^E,
-// f in [0.5, 1) and 448 = 0.875 * 2^9, e = E - 9 when f <= 0.875, else E - 8
+// smallest e >= -127 with amax <= 448 * 2^e.  For a normal amax = f 2^E,
+// f in [1, 2), and 448 = 1.75 * 2^8: e = E - 8 when f <= 1.75 (fraction
+// field <= 0x600000), else E - 7; a subnormal amax takes the same rule
+// through frexpf.
 __device__ __forceinline__ int e8m0_exponent(float amax) {
     if (!(amax > 0.f)) return -127;
-    int E;
-    const float f = frexpf(amax, &E);
-    const int e = f <= 0.875f ? E - 9 : E - 8;
+    const uint32_t u = __float_as_uint(amax);
+    int e;
+    if (u >= 0x00800000u) {
+        e = (int)(u >> 23) - 127 - 8 + ((u & 0x7fffffu) > 0x600000u ? 1 : 0);
+    } else {
+        int E;
+        const float f = frexpf(amax, &E);              // amax = f 2^E, f in [0.5, 1)
+        e = f <= 0.875f ? E - 9 : E - 8;
+    }
     return e < -127 ? -127 : e;
 }
 
-// 8 values of one group -> 8 codes (two words); ldexpf scales exactly
+// 2^-e for an exponent of e8m0_exponent (-e in [-120, 127]: a normal float)
+__device__ __forceinline__ float inv_scale(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
+
+// four values already scaled into [-448, 448] -> four e4m3 codes in one word.
+// gfx950's v_cvt_pk_fp8_f32 rounds to nearest even; over every float32 in
+// [-448, 448] it gives the same codes as the bitwise encoder e4m3_rne (an
+// exhaustive check), so the quantisers keep their results bit for bit.
+__device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+// 8 values of one group -> 8 codes (two words); the power-of-two scale
+// multiplies exactly
 __device__ __forceinline__ uint2 encode8(const float *x, int e) {
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t code = e4m3_rne(ldexpf(x[i], -e));
-        if (i < 4) lo |= code << (8 * i);
-        else hi |= code << (8 * (i - 4));
-    }
-    return make_uint2(lo, hi);
+    const float s = inv_scale(e);
+    return make_uint2(cvt4(x[0] * s, x[1] * s, x[2] * s, x[3] * s), cvt4(x[4] * s, x[5] * s, x[6] * s, x[7] * s));
 }
 
 template <int DT>
@@ -367,57 +383,104 @@ __global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(
         }
     }
 
+    // ---- epilogues: the tile leaves through LDS (the stages are free once
+    // every wave is past its last step) so that global stores are 16 bytes
+    // per lane along the output rows
+    __syncthreads();
     if (EPI == 0) {
+        // each wave's 128 x 128 bf16 block, row-major, 16-byte chunks of a row
+        // XOR-swizzled by the row's low 4 bits
+        unsigned char *blk = smem + wave * (128 * 256);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int row = m0 + wm * 128 + rt * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
-                if (row >= M) continue;
-                uint16_t *crow = c + (int64_t)row * N + n0 + wn * 128 + l32;
-#pragma unroll
-                for (int ct = 0; ct < 4; ++ct) crow[ct * 32] = f32_to_bf16(acc[rt][ct][i]);
-            }
-    } else {
-        // the up wave's accumulators go through LDS, one float per (register, lane)
-        __syncthreads();                                // every wave is done with the stages
-        float *up = reinterpret_cast<float *>(smem) + wm * (256 * 64);
-        if (wn == 1) {
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-                for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) up[((rt * 4 + ct) * 16 + i) * 64 + lane] = acc[rt][ct][i];
-        }
-        __syncthreads();
-        if (wn == 0) {
-            const int half_n = N >> 1;
-            const int64_t fcol = (int64_t)(n0 >> 1) + l32;        // feature of column tile 0
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
+            for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int row = m0 + wm * 128 + rt * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
-                    float y[4], am = 0.f;
-#pragma unroll
-                    for (int ct = 0; ct < 4; ++ct) {
-                        const float g = acc[rt][ct][i];
-                        const float u = up[((rt * 4 + ct) * 16 + i) * 64 + lane];
-                        y[ct] = g / (1.0f + __expf(-g)) * u;
-                        am = fmaxf(am, fabsf(y[ct]));
-                    }
-                    // the row's 128 features: 4 registers x the 32 lanes of this half
-#pragma unroll
-                    for (int o = 16; o >= 1; o >>= 1) am = fmaxf(am, shfl_xor_f(am, o));
-                    if (row >= M) continue;
-                    const int e = e8m0_exponent(am);
-                    uint8_t *qrow = qc + (int64_t)row * half_n + fcol;
-#pragma unroll
-                    for (int ct = 0; ct < 4; ++ct) qrow[ct * 32] = (uint8_t)e4m3_rne(ldexpf(y[ct], -e));
-                    if (l32 == 0) qs[(int64_t)(n0 >> 8) * M + row] = (uint8_t)(e + 127);
+                    const int r = rt * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
+                    const int col = ct * 32 + l32;
+                    *reinterpret_cast<uint16_t *>(blk + r * 256 + ((((col >> 3) ^ (r & 15)) << 4) | ((col & 7) << 1))) =
+                        f32_to_bf16(acc[rt][ct][i]);
                 }
+        __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));   // this wave's writes
+        // 16 lanes per row, 4 rows per pass
+#pragma unroll
+        for (int p = 0; p < 32; ++p) {
+            const int r = p * 4 + (lane >> 4), ch = lane & 15;
+            const uint4 v = *reinterpret_cast<const uint4 *>(blk + r * 256 + ((ch ^ (r & 15)) << 4));
+            const int row = m0 + wm * 128 + r;
+            if (row < M)
+                *reinterpret_cast<uint4 *>(c + (int64_t)row * N + n0 + wn * 128 + ch * 8) = v;
         }
+    } else {
+        // gate (wave wn = 0) and up (wn = 1) of one 128 x 128 block: each of
+        // the pair takes half the rows (row tiles 2 wn, 2 wn + 1) and hands
+        // the other half to its partner.  Straight-line code with selects, so
+        // the register allocator sees one path for both waves.
+        const bool gate_wave = wn == 0;
+        float *xch = reinterpret_cast<float *>(smem) + wm * 16384;   // [giver wn][2 rt][4 ct][16 i][64]
+        auto xidx = [&](int giver, int r2, int ct, int i) { return (((giver * 2 + r2) * 4 + ct) * 16 + i) * 64 + lane; };
+#pragma unroll
+        for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    xch[xidx(wn, r2, ct, i)] = gate_wave ? acc[2 + r2][ct][i] : acc[r2][ct][i];
+        __syncthreads();
+        float h[2][4][16];                              // silu(gate) * up of this wave's rows
+#pragma unroll
+        for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float mine = gate_wave ? acc[r2][ct][i] : acc[2 + r2][ct][i];
+                    const float other = xch[xidx(wn ^ 1, r2, ct, i)];
+                    const float g = gate_wave ? mine : other, u = gate_wave ? other : mine;
+                    h[r2][ct][i] = __fdividef(g, 1.0f + __expf(-g)) * u;
+                }
+        __syncthreads();                                // the partner's half has been read
+        // per row (r2, i): the max over its 4 registers and the 32 lanes of this
+        // half (16-lane rows by DPP rotations, then lanes l and l ^ 16), its
+        // exponent and codes; codes wait in LDS, 16-byte chunks XOR-swizzled
+        unsigned char *qb = smem + wave * 8192;        // [64 rows][128 codes]
+        uint8_t *qsb = smem + 4 * 8192 + wave * 64;    // the rows' E8M0 codes
+#pragma unroll
+        for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float v = fmaxf(fmaxf(fabsf(h[r2][0][i]), fabsf(h[r2][1][i])),
+                                fmaxf(fabsf(h[r2][2][i]), fabsf(h[r2][3][i])));
+                v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false)));
+                v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false)));
+                v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xf, 0xf, false)));
+                v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xf, 0xf, false)));
+                const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+                const int e = e8m0_exponent(fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
+                const float sc = inv_scale(e);
+                const int r = r2 * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);        // row of this wave's 64
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    const int col = ct * 32 + l32;
+                    const uint32_t code =
+                        (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(h[r2][ct][i] * sc, 0.f, 0, false) & 0xffu;
+                    qb[r * 128 + ((((col >> 4) ^ (r & 7)) << 4) | (col & 15))] = (uint8_t)code;
+                }
+                if (l32 == 0) qsb[r] = (uint8_t)(e + 127);
+            }
+        __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));   // this wave's writes
+        // rows 64 wn .. +63 of the pair's block: 8 lanes per row, 8 rows per pass
+        const int half_n = N >> 1;
+        const int rbase = m0 + wm * 128 + wn * 64;
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int r = p * 8 + (lane >> 3), ch = lane & 7;
+            const uint4 v = *reinterpret_cast<const uint4 *>(qb + r * 128 + ((ch ^ (r & 7)) << 4));
+            if (rbase + r < M)
+                *reinterpret_cast<uint4 *>(qc + (int64_t)(rbase + r) * half_n + (n0 >> 1) + ch * 16) = v;
+        }
+        if (rbase + lane < M) qs[(int64_t)(n0 >> 8) * M + rbase + lane] = qsb[lane];
     }
 }
 
