@@ -231,8 +231,8 @@ __global__ __launch_bounds__(256) void fp8_quant_weight_kernel(const void *__res
 // of 128 (one scale group): per step the A and B tiles (32 KB each) land in
 // one of two LDS stages by direct-to-LDS loads while the other stage is
 // read.  In LDS a 128-byte row keeps its eight 16-byte chunks XOR-swizzled
-// by the row's low 3 bits, so the 8 lanes of a read phase (8 rows, one
-// logical chunk) hit 8 distinct bank groups.
+// (swz) so that a read phase of 16 rows at one logical chunk hits all 64
+// banks once.
 //
 // Operands of v_mfma_scale_f32_32x32x64_f8f6f4: lane l holds 32 bytes of
 // row l % 32 (A) or of column l % 32 (B), K bytes 32 (l / 32) .. +31 of the
@@ -266,8 +266,12 @@ __device__ __forceinline__ f32x16_t mfma_scaled(const i32x8_t &a, const i32x8_t 
     }
 }
 
-// LDS byte offset of 16-byte chunk c of tile row r
-__device__ __forceinline__ int swz(int r, int c) { return r * kBK + ((c ^ (r & 7)) << 4); }
+// LDS byte offset of 16-byte chunk c of tile row r.  A read phase of 16
+// lanes takes rows r .. r + 15 at one logical chunk and the 64 banks span 256
+// bytes, i.e. two 128-byte rows: the even rows of the phase share one half of
+// the bank window and the odd rows the other, so the swizzle must give the 8
+// rows of each parity distinct chunks: c ^ ((r >> 1) & 7).
+__device__ __forceinline__ int swz(int r, int c) { return r * kBK + ((c ^ ((r >> 1) & 7)) << 4); }
 
 template <int EPI>
 __global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(
@@ -293,17 +297,19 @@ __global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(
     const int ksteps = K / kBK;
 
     // direct-to-LDS loads: wave w issues 1 KB loads u = 0..7 of each tile;
-    // load u covers tile rows 8 (8 w + u) .. +7, lane i row 8 (8 w + u) + i / 8,
-    // stored slot i % 8 holding logical chunk (i % 8) ^ (i / 8)
+    // load u covers tile rows 8 (8 w + u) .. +7, lane i row r = 8 (8 w + u) +
+    // i / 8, stored slot i % 8, which holds logical chunk (i % 8) ^ ((r >> 1) & 7)
+    // = (i % 8) ^ ((4 (u & 1) + i / 16) & 7)
     const int lrow = lane >> 3;
-    const int lchunk = (lane & 7) ^ lrow;
+    const int lchunk0 = (lane & 7) ^ ((lane >> 4) & 7);
+    const int lchunk1 = (lane & 7) ^ ((4 + (lane >> 4)) & 7);
     auto issue = [&](int ks, int stage) {
         unsigned char *sa_lds = smem + stage * 2 * kTileBytes;
         unsigned char *sb_lds = sa_lds + kTileBytes;
-        const int64_t k0 = (int64_t)ks * kBK + lchunk * 16;
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int r = 8 * (8 * wave + u) + lrow;
+            const int64_t k0 = (int64_t)ks * kBK + ((u & 1) ? lchunk1 : lchunk0) * 16;
             const int ra = min(m0 + r, M - 1);          // rows past M read row M - 1, never stored
             lds_dma16<false>(a + (int64_t)ra * K + k0, sa_lds + (8 * wave + u) * 1024);
             lds_dma16<false>(b + (int64_t)(n0 + r) * K + k0, sb_lds + (8 * wave + u) * 1024);
@@ -354,15 +360,12 @@ __global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(
         vm_wait<0>();
         __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
         asm volatile("s_barrier" ::: "memory");
-        if (ks + 1 < ksteps) issue(ks + 1, stage ^ 1);
         const int sav = *reinterpret_cast<const int *>(ssa + ks * 256 + wm * 128 + l32 * 4);
         const int sbv = ssb[wn * ksteps + ks];
         const unsigned char *at = smem + stage * 2 * kTileBytes + wm * 128 * kBK;
         const unsigned char *bt = smem + stage * 2 * kTileBytes + kTileBytes + wn * 128 * kBK;
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
+        auto read_ops = [&](int kh, i32x8_t *av, i32x8_t *bv) {
             const int c0 = kh * 4 + lh * 2;
-            i32x8_t av[4], bv[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int r = t * 32 + l32;
@@ -375,12 +378,21 @@ __global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(
                 bv[t] = i32x8_t{(int)y0.x, (int)y0.y, (int)y0.z, (int)y0.w,
                                 (int)y1.x, (int)y1.y, (int)y1.z, (int)y1.w};
             }
+        };
+        // the step's operand reads are issued before the refill (the loads'
+        // inline assembly orders every memory access around it), so the
+        // products start as soon as the first operands land
+        i32x8_t av[2][4], bv[2][4];
+        read_ops(0, av[0], bv[0]);
+        read_ops(1, av[1], bv[1]);
+        if (ks + 1 < ksteps) issue(ks + 1, stage ^ 1);
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct)
-                    acc[rt][ct] = mfma_scaled(av[rt], bv[ct], acc[rt][ct], sav, rt, sbv);
-        }
+                    acc[rt][ct] = mfma_scaled(av[kh][rt], bv[kh][ct], acc[rt][ct], sav, rt, sbv);
     }
 
     // ---- epilogues: the tile leaves through LDS (the stages are free once
