@@ -14,6 +14,12 @@ state over the 32 block keys.  The memo is filled once, before the timed
 steps (the block's first step); a full recompute of all 2048 queries over
 all 2048 keys is timed beside it.
 
+With --config ffn a step is the FFN of one LLaDA-shaped layer in per-group
+FP8 on the same 16 x 2048 step (32768 tokens, hidden 4096, SwiGLU width
+12288): add & norm fused with the 1 x 128 quantisation, the Gate-Up product
+fused with SwiGLU and the quantisation of its output, the FF-Out product in
+bf16.  The weights are quantised once, before the timed steps.
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config gpt2]
 """
 from __future__ import annotations
@@ -32,13 +38,16 @@ sys.path.insert(0, ROOT)
 METRIC = "denoise steps/sec (block attn + vocab stats); achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0      # dense bf16 matrix peak of MI355X
+MFMA_FP8_PEAK_TFLOPS = 5000.0       # dense fp8 matrix peak of MI355X
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "cached_denoising_amd", "csrc")
 # the source files of each call whose counters a profile summary records
 KERNEL_SRC = {"vocab_stats": ["vocab_stats.hip"],
               "attention": ["attention.hip", "attention_shared.hip", "attn_common.hpp"],
               "facache_merge": ["attention.hip", "attention_shared.hip", "attn_common.hpp"],
-              "scatter": ["scatter.hip"], "stability": ["stability.hip"]}
+              "scatter": ["scatter.hip"], "stability": ["stability.hip"],
+              "fp8_addnorm": ["fp8_ffn.hip", "common.hpp"], "fp8_gateup": ["fp8_ffn.hip", "common.hpp"],
+              "fp8_ffout": ["fp8_ffn.hip", "common.hpp"]}
 
 
 def parse():
@@ -46,7 +55,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="gpt2", choices=["gpt2", "llada", "vocab", "longctx", "facache"])
+    ap.add_argument("--config", default="gpt2",
+                    choices=["gpt2", "llada", "vocab", "longctx", "facache", "ffn"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from Python instead of replaying a captured graph")
@@ -260,6 +270,87 @@ class Step:
         return 1000.0 * e0.elapsed_time(e1) / reps
 
 
+class FfnStep:
+    """One FFN of a LLaDA-shaped layer in per-group FP8 on M tokens."""
+
+    def __init__(self, D, W, dev, M=16 * 2048):
+        import torch
+        self.D, self.W, self.M = D, W, M
+        self.K, self.I = W.FFN_HIDDEN, W.FFN_INTER
+        self.x, self.res, self.gamma, w_gu, w_out = W.ffn_inputs(M, seed=21, device=dev)
+        self.w_gu_bf16, self.w_out_bf16 = w_gu, w_out
+        self.cgu, self.sgu = D.dllm_fp8_quant_weight(w_gu)
+        self.cout, self.sout = D.dllm_fp8_quant_weight(w_out)
+        self.r_out = torch.empty_like(self.x)
+        self.ca = torch.empty((M, self.K), dtype=torch.uint8, device=dev)
+        self.sa = torch.empty((self.K // 128, M), dtype=torch.uint8, device=dev)
+        self.ch = torch.empty((M, self.I), dtype=torch.uint8, device=dev)
+        self.sh = torch.empty((self.I // 128, M), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((M, self.K), dtype=torch.bfloat16, device=dev)
+        self.facache = False
+
+    def kernels(self):
+        return ["fp8_addnorm", "fp8_gateup", "fp8_ffout"]
+
+    def run(self, events=None):
+        D = self.D
+
+        def mark(name, i):
+            if events is not None:
+                events[name][i].record()
+
+        mark("fp8_addnorm", 0)
+        D.dllm_fp8_addnorm_quant(self.x, self.res, self.gamma, eps=1e-6, residual_out=self.r_out,
+                                 codes=self.ca, scales=self.sa)
+        mark("fp8_addnorm", 1)
+        mark("fp8_gateup", 0)
+        D.dllm_fp8_gemm_swiglu(self.ca, self.sa, self.cgu, self.sgu, out_codes=self.ch, out_scales=self.sh)
+        mark("fp8_gateup", 1)
+        mark("fp8_ffout", 0)
+        D.dllm_fp8_gemm(self.ch, self.sh, self.cout, self.sout, out=self.out)
+        mark("fp8_ffout", 1)
+
+    def algorithmic_bytes(self):
+        M, K, I = self.M, self.K, self.I
+        return {
+            # x, residual in, residual out (bf16), gamma, codes and scales out
+            "fp8_addnorm": M * K * 2 * 3 + K * 2 + M * K + M * K // 128,
+            # activation codes and scales, weight codes and scales, SwiGLU codes and scales out
+            "fp8_gateup": M * K + M * K // 128 + 2 * I * K + 2 * I * K // 16384 + M * I + M * I // 128,
+            "fp8_ffout": M * I + M * I // 128 + K * I + K * I // 16384 + M * K * 2,
+        }
+
+    def algorithmic_flops(self):
+        M, K, I = self.M, self.K, self.I
+        return {"fp8_gateup": 2 * M * 2 * I * K, "fp8_ffout": 2 * M * K * I}
+
+
+def cpu_baseline_ffn(step, W):
+    """The oracle's chain on a bounded sample of token rows: add & norm +
+    quantisation, Gate-Up + SwiGLU + quantisation, FF-Out; scaled to
+    steps/s.  The weight quantisation (once per model) is not timed."""
+    import numpy as np
+
+    import oracle
+    threads = oracle.set_threads(int(os.environ.get("OMP_NUM_THREADS", min(16, os.cpu_count() or 1))))
+    n = 4
+    rows = slice(0, n)
+    cgu, sgu = oracle.fp8_quant_weight(W.as_numpy_bits(step.w_gu_bf16), oracle.BF16)
+    cout, sout = oracle.fp8_quant_weight(W.as_numpy_bits(step.w_out_bf16), oracle.BF16)
+    x, r, g = (W.as_numpy_bits(t) for t in (step.x[rows], step.res[rows], step.gamma))
+    t0 = time.perf_counter()
+    _, y = oracle.addnorm(x, r, g, 1e-6, oracle.BF16)
+    ca, sa = oracle.fp8_quant_rows(y, oracle.F64)
+    c = oracle.fp8_gemm(ca, sa, cgu, sgu)
+    blk = c.reshape(n, c.shape[1] // 256, 2, 128)
+    h = oracle.swiglu(blk[:, :, 0, :].reshape(n, -1), blk[:, :, 1, :].reshape(n, -1))
+    ch, sh = oracle.fp8_quant_rows(h, oracle.F64)
+    oracle.fp8_gemm(ch, sh, cout, sout)
+    dt = (time.perf_counter() - t0) * step.M / n
+    return {"value": 1.0 / dt, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"the FFN chain on {n} of {step.M} token rows, scaled linearly to the step"}
+
+
 def cpu_baseline(step, D, W, cfg):
     """The oracle as it stands, on a bounded sample of the same step, on the
     host's cores; scaled to steps/s."""
@@ -340,8 +431,11 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
-    cfg = W.CONFIGS["llada" if args.config == "facache" else args.config]
-    step = Step(D, W, cfg, dev, facache=args.config == "facache")
+    cfg = W.CONFIGS["llada" if args.config in ("facache", "ffn") else args.config]
+    if args.config == "ffn":
+        step = FfnStep(D, W, dev)
+    else:
+        step = Step(D, W, cfg, dev, facache=args.config == "facache")
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
@@ -391,12 +485,14 @@ def main():
     # bound by the matrix cores when its flops per byte exceed the ridge
     dom = max(per_kernel_us, key=per_kernel_us.get)
     dom_us = per_kernel_us[dom]
-    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     traffic = measured_traffic(dom, args.config)
+    fp8 = dom.startswith("fp8_")
+    peak_mfma = MFMA_FP8_PEAK_TFLOPS if fp8 else MFMA_BF16_PEAK_TFLOPS
+    ridge = peak_mfma * 1e12 / (HBM_PEAK_GBS * 1e9)
     if dom in flops and flops[dom] / alg[dom] > ridge:
         achieved = flops[dom] / (dom_us * 1e-6) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_mfma,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak_mfma, 4),
                     "traffic": traffic, "algorithmic_flops_per_launch": flops[dom]}
     else:
         achieved = alg[dom] / (dom_us * 1e-6) / 1e9
@@ -415,7 +511,12 @@ def main():
         extra = {"full_recompute_attention_us": round(full, 1),
                  "facache_attention_us": round(fa, 1),
                  "facache_speedup_vs_full": round(full / fa, 2)}
-    cpu = None if args.no_cpu_baseline else cpu_baseline(step, D, W, cfg)
+    if args.no_cpu_baseline:
+        cpu = None
+    elif args.config == "ffn":
+        cpu = cpu_baseline_ffn(step, W)
+    else:
+        cpu = cpu_baseline(step, D, W, cfg)
     desc = {
         "gpt2": "GPT-2-small-shaped decode step: B=8, L=1024, 12 heads x d64, bf16 K/V cache, "
                 "block b=32 at a random offset, vocab 50257 bf16 logits for all 8192 positions, "
@@ -425,20 +526,28 @@ def main():
         "vocab": "vocab-stats sweep: 32768 rows x 126464 bf16 logits, 64-step ring, K=3 tau=0.9 R=3",
         "longctx": "long-context step: B=4, L=32768, 32/8 GQA heads x d128, e4m3 K/V with "
                    "per-128 scales, block 64, 4 sinks + 8188 rolling keys",
+        "ffn": "LLaDA-8B-shaped FFN of one layer in per-group FP8 on a 16 x 2048 step: 32768 tokens, "
+               "hidden 4096, SwiGLU width 12288, e4m3 codes with E8M0 scales per 1x128 activation "
+               "group and 128x128 weight block (add & norm + quant, Gate-Up + SwiGLU + quant, "
+               "FF-Out to bf16)",
         "facache": "LLaDA-8B-shaped first-layer attention of a later step of a block, with FACache: "
                    "B=16, L=2048, 32 heads x d128, bf16 K/V, block 32 (scatter, block queries over "
                    "all keys, 2016 outside queries from their memo over the block keys)",
     }[args.config]
-    metric = METRIC if args.config != "facache" else \
-        "first-layer attention steps/sec with FACache (scatter + block attention + memo merge)"
+    metric = {"facache": "first-layer attention steps/sec with FACache (scatter + block attention + memo merge)",
+              "ffn": "FP8 FFN steps/sec (add & norm + quant, Gate-Up + SwiGLU + quant, FF-Out)"}.get(
+        args.config, METRIC)
+    dtype = "e4m3 x e4m3 -> f32 (E8M0 group scales)" if args.config == "ffn" else "bf16"
     line = {
         "metric": metric, "value": round(1000.0 / ms, 2), "unit": "steps/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": desc, "name": cfg.name, "B": cfg.B, "L": cfg.L, "heads": cfg.Hq,
-                   "kv_heads": cfg.Hkv, "d_head": cfg.d, "block": cfg.b, "vocab": cfg.V,
-                   "launch": "eager" if graph is None else "hip graph of the timed steps"},
+        "config": ({"workload": desc, "tokens": step.M, "hidden": step.K, "ffn_width": step.I}
+                   if args.config == "ffn" else
+                   {"workload": desc, "name": cfg.name, "B": cfg.B, "L": cfg.L, "heads": cfg.Hq,
+                    "kv_heads": cfg.Hkv, "d_head": cfg.d, "block": cfg.b, "vocab": cfg.V})
+                  | {"launch": "eager" if graph is None else "hip graph of the timed steps"},
         "kernels_us": {n: round(v, 2) for n, v in per_kernel_us.items()},
         "roofline": roofline,
         **extra,

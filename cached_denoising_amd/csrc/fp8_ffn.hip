@@ -427,43 +427,38 @@ __global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(
     } else {
         // gate (wave wn = 0) and up (wn = 1) of one 128 x 128 block: each of
         // the pair takes half the rows (row tiles 2 wn, 2 wn + 1) and hands
-        // the other half to its partner.  Straight-line code with selects, so
-        // the register allocator sees one path for both waves.
+        // the other half to its partner, one row tile per phase.  Straight-line
+        // code with selects, so the register allocator sees one path for both
+        // waves.  Per row (r2, i): the max over its 4 registers and the 32 lanes
+        // of this half (16-lane rows by DPP rotations, then lanes l and
+        // l ^ 16), its exponent and codes; the codes wait in LDS (16-byte
+        // chunks XOR-swizzled) clear of the exchange.
         const bool gate_wave = wn == 0;
-        float *xch = reinterpret_cast<float *>(smem) + wm * 16384;   // [giver wn][2 rt][4 ct][16 i][64]
-        auto xidx = [&](int giver, int r2, int ct, int i) { return (((giver * 2 + r2) * 4 + ct) * 16 + i) * 64 + lane; };
+        float *xch = reinterpret_cast<float *>(smem) + wm * 8192;    // [giver wn][4 ct][16 i][64]
+        auto xidx = [&](int giver, int ct, int i) { return ((giver * 4 + ct) * 16 + i) * 64 + lane; };
+        unsigned char *qb = smem + 65536 + wave * 8192;               // [64 rows][128 codes]
+        uint8_t *qsb = smem + 65536 + 4 * 8192 + wave * 64;           // the rows' E8M0 codes
 #pragma unroll
-        for (int r2 = 0; r2 < 2; ++r2)
+        for (int r2 = 0; r2 < 2; ++r2) {
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
-                    xch[xidx(wn, r2, ct, i)] = gate_wave ? acc[2 + r2][ct][i] : acc[r2][ct][i];
-        __syncthreads();
-        float h[2][4][16];                              // silu(gate) * up of this wave's rows
-#pragma unroll
-        for (int r2 = 0; r2 < 2; ++r2)
+                    xch[xidx(wn, ct, i)] = gate_wave ? acc[2 + r2][ct][i] : acc[r2][ct][i];
+            __syncthreads();
+            float h[4][16];                             // silu(gate) * up of row tile 2 wn + r2
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const float mine = gate_wave ? acc[r2][ct][i] : acc[2 + r2][ct][i];
-                    const float other = xch[xidx(wn ^ 1, r2, ct, i)];
+                    const float other = xch[xidx(wn ^ 1, ct, i)];
                     const float g = gate_wave ? mine : other, u = gate_wave ? other : mine;
-                    h[r2][ct][i] = __fdividef(g, 1.0f + __expf(-g)) * u;
+                    h[ct][i] = __fdividef(g, 1.0f + __expf(-g)) * u;
                 }
-        __syncthreads();                                // the partner's half has been read
-        // per row (r2, i): the max over its 4 registers and the 32 lanes of this
-        // half (16-lane rows by DPP rotations, then lanes l and l ^ 16), its
-        // exponent and codes; codes wait in LDS, 16-byte chunks XOR-swizzled
-        unsigned char *qb = smem + wave * 8192;        // [64 rows][128 codes]
-        uint8_t *qsb = smem + 4 * 8192 + wave * 64;    // the rows' E8M0 codes
-#pragma unroll
-        for (int r2 = 0; r2 < 2; ++r2)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                float v = fmaxf(fmaxf(fabsf(h[r2][0][i]), fabsf(h[r2][1][i])),
-                                fmaxf(fabsf(h[r2][2][i]), fabsf(h[r2][3][i])));
+                float v = fmaxf(fmaxf(fabsf(h[0][i]), fabsf(h[1][i])), fmaxf(fabsf(h[2][i]), fabsf(h[3][i])));
                 v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false)));
                 v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false)));
                 v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xf, 0xf, false)));
@@ -476,11 +471,13 @@ __global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(
                 for (int ct = 0; ct < 4; ++ct) {
                     const int col = ct * 32 + l32;
                     const uint32_t code =
-                        (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(h[r2][ct][i] * sc, 0.f, 0, false) & 0xffu;
+                        (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(h[ct][i] * sc, 0.f, 0, false) & 0xffu;
                     qb[r * 128 + ((((col >> 4) ^ (r & 7)) << 4) | (col & 15))] = (uint8_t)code;
                 }
                 if (l32 == 0) qsb[r] = (uint8_t)(e + 127);
             }
+            __syncthreads();                            // the exchange is read before it is reused
+        }
         __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));   // this wave's writes
         // rows 64 wn .. +63 of the pair's block: 8 lanes per row, 8 rows per pass
         const int half_n = N >> 1;
