@@ -100,7 +100,17 @@ def lib():
         L.oracle_vocab_stats.restype = i32
         L.oracle_stability_step.argtypes = [i32, i32, i32, P, i32, P, P, P, P, P, P, P, P, P,
                                             i32, dbl, i32, i32, dbl, dbl, dbl, dbl, i64,
-                                            P, P, P, P, P]
+                                            i32, i32, i32, P, P, P, P, P]
+        L.oracle_dynamic_radius.argtypes = [i32, i32, i32, i32]
+        L.oracle_dynamic_radius.restype = i32
+        L.oracle_is_refresh_step.argtypes = [i32, i32]
+        L.oracle_is_refresh_step.restype = i32
+        L.oracle_refresh_interval.argtypes = [i32]
+        L.oracle_refresh_interval.restype = i32
+        L.oracle_cache_quotas.argtypes = [i32, P, i64, dbl, P]
+        L.oracle_cache_quotas.restype = i32
+        L.oracle_evict_by_confidence.argtypes = [i32, i32, P, P, P, i32, P, P, P, P, P]
+        L.oracle_evict_by_confidence.restype = i32
         L.oracle_stability_step.restype = i32
         _lib = L
     return _lib
@@ -391,17 +401,20 @@ class StabilityState:
         self.entropy_latest = np.zeros((B, L), dtype=np.float32)
         self.t_write = np.zeros((B, L), dtype=np.int32)
         self.stable = np.zeros((B, L), dtype=np.uint8)
+        self.cached = np.zeros((B, L), dtype=np.uint8)      # positions holding K/V (N3 budget)
 
     def copy(self):
         c = StabilityState.__new__(StabilityState)
         c.B, c.L, c.D = self.B, self.L, self.D
-        for k in ("ring_argmax", "ring_maxprob", "ring_step", "entropy_latest", "t_write", "stable"):
+        for k in ("ring_argmax", "ring_maxprob", "ring_step", "entropy_latest", "t_write", "stable",
+                  "cached"):
             setattr(c, k, getattr(self, k).copy())
         return c
 
 
 def stability_step(state: StabilityState, step, pos, argmax, maxprob, entropy, *, K, tau, R,
-                   alpha=0.0, beta=0.0, lam=0.0, conf_thresh=0.0, V=2):
+                   alpha=0.0, beta=0.0, lam=0.0, conf_thresh=0.0, V=2, R_early=0, T_steps=0,
+                   refresh_every=0):
     """One step of history update, stability test, confidence and window mask.
 
     pos: [B, n] recomputed positions or None (all L).  argmax/maxprob/entropy
@@ -427,7 +440,51 @@ def stability_step(state: StabilityState, step, pos, argmax, maxprob, entropy, *
                                      _ptr(state.ring_step), _ptr(state.entropy_latest),
                                      _ptr(state.t_write), _ptr(state.stable), int(K), float(tau), D,
                                      int(R), float(alpha), float(beta), float(lam),
-                                     float(conf_thresh), int(V), _ptr(mask), _ptr(conf),
+                                     float(conf_thresh), int(V), int(R_early), int(T_steps),
+                                     int(refresh_every), _ptr(mask), _ptr(conf),
                                      _ptr(next_pos), _ptr(count), _ptr(all_stable))
     _check(rc, "stability_step")
     return dict(mask=mask, conf=conf, next_pos=next_pos, count=count, all_stable=all_stable)
+
+
+# ---- N3 ---------------------------------------------------------------------
+
+def dynamic_radius(R_early: int, R: int, T: int, step: int) -> int:
+    return lib().oracle_dynamic_radius(int(R_early), int(R), int(T), int(step))
+
+
+def is_refresh_step(F: int, step: int) -> bool:
+    return bool(lib().oracle_is_refresh_step(int(F), int(step)))
+
+
+def refresh_interval(T: int) -> int:
+    return lib().oracle_refresh_interval(int(T))
+
+
+def cache_quotas(lens, budget: int, min_frac: float = 0.2):
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    q = np.zeros(lens.size, dtype=np.int32)
+    _check(lib().oracle_cache_quotas(lens.size, _ptr(lens), int(budget), float(min_frac), _ptr(q)),
+           "cache_quotas")
+    return q
+
+
+def evict_by_confidence(state: StabilityState, conf, quota, pos, mask):
+    """In place on state.cached and mask (uint8 [B, L]); conf float32
+    [B, L]; quota int32 [B].  Returns dict(next_pos, count, evicted)."""
+    B, L = state.B, state.L
+    conf = np.ascontiguousarray(conf, dtype=np.float32)
+    quota = np.ascontiguousarray(quota, dtype=np.int32)
+    if pos is not None:
+        pos = np.ascontiguousarray(pos, dtype=np.int32)
+        n = pos.shape[1]
+    else:
+        n = L
+    assert mask.dtype == np.uint8 and mask.flags["C_CONTIGUOUS"]
+    next_pos = np.zeros((B, L), dtype=np.int32)
+    count = np.zeros(B, dtype=np.int32)
+    evicted = np.zeros(B, dtype=np.int32)
+    _check(lib().oracle_evict_by_confidence(B, L, _ptr(conf), _ptr(quota), _ptr(pos), n, _ptr(state.cached),
+                                            _ptr(mask), _ptr(next_pos), _ptr(count), _ptr(evicted)),
+           "evict_by_confidence")
+    return dict(next_pos=next_pos, count=count, evicted=evicted)

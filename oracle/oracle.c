@@ -611,6 +611,118 @@ int oracle_vocab_stats(int dtype, const void *logits, int64_t N, int64_t V,
 /* A5-A7: history ring, stability test, confidence, window mask             */
 /* ------------------------------------------------------------------------ */
 
+/* ------------------------------------------------------------------------ */
+/* N3: radius and refresh schedules, eviction under a budget                 */
+/* ------------------------------------------------------------------------ */
+
+/* [SWD, 4.4]: small (or no) window early, wider late.  The reading: a
+ * linear ramp from R_early at step 0 to R at step T-1, in whole positions
+ * (integer division), R afterwards; T <= 1 keeps R throughout. */
+int oracle_dynamic_radius(int R_early, int R, int T, int step)
+{
+    int s;
+    if (T <= 1) return R;
+    s = step < T - 1 ? step : T - 1;
+    return R_early + (R - R_early) * s / (T - 1);
+}
+
+/* [Flash, 5.1]: a full refresh every F steps; F = 0 never.  Step 0
+ * recomputes everything anyway. */
+int oracle_is_refresh_step(int F, int step)
+{
+    return F > 0 && step > 0 && step % F == 0;
+}
+
+/* [Flash, 5.1]: T in 50..100 -> every 5..10 steps, T < 50 -> every 3..5.
+ * The reading: F = round(T / 10), kept within [3, 10]. */
+int oracle_refresh_interval(int T)
+{
+    int f = (int)floor((double)T / 10.0 + 0.5);
+    return f < 3 ? 3 : (f > 10 ? 10 : f);
+}
+
+/* [Flash, 5.2]: each request is guaranteed ceil(min_frac * len) cached
+ * positions (min_frac = 0.2 on the page); what the budget has left goes to
+ * the requests in arrival order (index order), each up to its length.
+ * Returns -1 when the budget cannot cover the guarantees. */
+int oracle_cache_quotas(int B, const int32_t *len, int64_t budget, double min_frac, int32_t *quota)
+{
+    int b;
+    int64_t need = 0, left;
+    if (B <= 0 || budget < 0 || !(min_frac >= 0.0)) return -1;
+    for (b = 0; b < B; ++b) {
+        double m = ceil(min_frac * (double)len[b]);
+        if (len[b] < 0) return -1;
+        quota[b] = (int32_t)(m > (double)len[b] ? (double)len[b] : m);
+        need += quota[b];
+    }
+    if (need > budget) return -1;
+    left = budget - need;
+    for (b = 0; b < B; ++b) {
+        int64_t extra = (int64_t)len[b] - quota[b];
+        if (extra > left) extra = left;
+        quota[b] += (int32_t)extra;
+        left -= extra;
+    }
+    return 0;
+}
+
+/* ordering of eviction candidates: higher confidence first, then lower
+ * position */
+typedef struct { float conf; int pos; } orc_cand;
+static int cand_order(const void *x, const void *y)
+{
+    const orc_cand *a = (const orc_cand *)x, *b = (const orc_cand *)y;
+    if (a->conf > b->conf) return -1;
+    if (a->conf < b->conf) return 1;
+    return a->pos - b->pos;
+}
+
+/* [Flash, 3.3]: when a sequence's cached positions exceed its quota, the
+ * lowest-confidence positions leave the cache first, a position's K and V
+ * together.  Positions recomputed this step (pos, NULL for all L) hold fresh
+ * K/V and count as cached; of the cached positions the quota[b] with the
+ * highest confidence (ties: lower position) stay, quota < 0 meaning no
+ * limit.  A position without cached K/V must be recomputed before it can be
+ * attended to, so every uncached position joins the next step's mask, and
+ * next_pos / count are compacted again.  evicted[b] counts the positions
+ * this call evicted. */
+int oracle_evict_by_confidence(int B, int L, const float *conf, const int32_t *quota,
+                               const int32_t *pos, int n, uint8_t *cached, uint8_t *mask,
+                               int32_t *next_pos, int32_t *count, int32_t *evicted)
+{
+    int b;
+    if (B <= 0 || L <= 0) return -1;
+    if (!pos) n = L;
+    if (n < 0 || n > L) return -1;
+    for (b = 0; b < B; ++b) {
+        int64_t row = (int64_t)b * L;
+        int i, j, nc = 0, c, ev = 0;
+        orc_cand *cand = (orc_cand *)malloc(sizeof(orc_cand) * (size_t)L);
+        if (!cand) return -1;
+        for (j = 0; j < n; ++j) {
+            int p = pos ? pos[(int64_t)b * n + j] : j;
+            if (p >= 0 && p < L) cached[row + p] = 1;
+        }
+        for (i = 0; i < L; ++i)
+            if (cached[row + i]) { cand[nc].conf = conf[row + i]; cand[nc].pos = i; ++nc; }
+        if (quota[b] >= 0 && nc > quota[b]) {
+            qsort(cand, (size_t)nc, sizeof(orc_cand), cand_order);
+            for (j = quota[b]; j < nc; ++j) { cached[row + cand[j].pos] = 0; ++ev; }
+        }
+        evicted[b] = ev;
+        for (i = 0; i < L; ++i)
+            if (!cached[row + i]) mask[row + i] = 1;
+        c = 0;
+        for (i = 0; i < L; ++i)
+            if (mask[row + i]) next_pos[row + c++] = i;
+        count[b] = c;
+        for (i = c; i < L; ++i) next_pos[row + i] = -1;
+        free(cand);
+    }
+    return 0;
+}
+
 int oracle_stability_step(int B, int L, int step, const int32_t *pos, int n,
                           const int32_t *argmax, const float *maxprob,
                           const float *entropy,
@@ -619,12 +731,14 @@ int oracle_stability_step(int B, int L, int step, const int32_t *pos, int n,
                           int K, double tau, int D, int R,
                           double alpha, double beta, double lambda,
                           double conf_thresh, int64_t V,
+                          int R_early, int T_steps, int refresh_every,
                           uint8_t *mask, double *conf, int32_t *next_pos,
                           int32_t *count, uint8_t *all_stable)
 {
-    int b;
+    int b, R_eff;
     double hmax;
     if (B <= 0 || L <= 0 || step < 0 || K < 1 || D < K || R < 0 || V < 2) return -1;
+    if (R_early < 0 || refresh_every < 0) return -1;
     if (!pos) n = L;
     if (n < 0 || n > L) return -1;
     if (pos) {
@@ -633,6 +747,7 @@ int oracle_stability_step(int B, int L, int step, const int32_t *pos, int n,
             if (pos[i] < -1 || pos[i] >= L) return -1;     /* -1 is padding */
     }
     hmax = log((double)V);                    /* entropy of the uniform row */
+    R_eff = oracle_dynamic_radius(R_early, R, T_steps, step);
 
     for (b = 0; b < B; ++b) {
         int j, i, k, c;
@@ -694,14 +809,16 @@ int oracle_stability_step(int B, int L, int step, const int32_t *pos, int n,
          * nothing to recompute -> full mask and the all-stable flag
          * [SWD, 3.2; 4.2 get_computation_mask] */
         for (i = 0; i < L; ++i) mask[row + i] = 0;
-        if (!any_seed) {
+        if (!any_seed || oracle_is_refresh_step(refresh_every, step)) {
+            /* nothing left to recompute, or a scheduled full refresh
+             * [Flash, 5.1]: the whole sequence */
             for (i = 0; i < L; ++i) mask[row + i] = 1;
         } else {
             for (i = 0; i < L; ++i) {
                 int lo, hi, u;
                 if (!seed[i]) continue;
-                lo = i - R < 0 ? 0 : i - R;
-                hi = i + R > L - 1 ? L - 1 : i + R;
+                lo = i - R_eff < 0 ? 0 : i - R_eff;
+                hi = i + R_eff > L - 1 ? L - 1 : i + R_eff;
                 for (u = lo; u <= hi; ++u) mask[row + u] = 1;
             }
         }

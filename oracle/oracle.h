@@ -160,11 +160,27 @@ int oracle_vocab_stats(int dtype, const void *logits, int64_t N, int64_t V,
  * entropy_latest/t_write [B, L], stable [B, L] (0/1, sticky).
  * Params: K steps, tau (strict >), D ring depth >= K, R radius >= 0,
  * alpha, beta, lambda, conf_thresh (<= 0 disables the gate), vocab V
- * (Hmax = ln V).  Outputs: mask [B, L] (0/1), conf [B, L] double,
+ * (Hmax = ln V), R_early / T_steps (the dynamic radius, T_steps <= 1: off),
+ * refresh_every (0: off).  Outputs: mask [B, L] (0/1), conf [B, L] double,
  * next_pos [B, L] (ascending masked positions, rest -1), count [B],
  * all_stable [B].
  * [SWD, 3.1 stability test; 3.2 window; 3.3 steps c-d; 4.2 scheduler];
  * [Flash, 3.1 cache confidence]. */
+/* ---- N3: radius and refresh schedules, eviction under a budget ----------
+ * dynamic radius [SWD, 4.4]: R_early at step 0 rising linearly to R at step
+ * T-1 (integer division), R after; T <= 1 keeps R.  Refresh [Flash, 5.1]:
+ * every F-th step (s > 0, s % F == 0) recomputes the whole sequence; the
+ * interval for T steps is round(T/10) within [3, 10].  Quotas [Flash, 5.2]
+ * and confidence-ordered eviction [Flash, 3.3]: see oracle.c. */
+int oracle_dynamic_radius(int R_early, int R, int T, int step);
+int oracle_is_refresh_step(int F, int step);
+int oracle_refresh_interval(int T);
+int oracle_cache_quotas(int B, const int32_t *len, int64_t budget, double min_frac,
+                        int32_t *quota);
+int oracle_evict_by_confidence(int B, int L, const float *conf, const int32_t *quota,
+                               const int32_t *pos, int n, uint8_t *cached, uint8_t *mask,
+                               int32_t *next_pos, int32_t *count, int32_t *evicted);
+
 int oracle_stability_step(int B, int L, int step, const int32_t *pos, int n,
                           const int32_t *argmax, const float *maxprob,
                           const float *entropy,
@@ -173,6 +189,7 @@ int oracle_stability_step(int B, int L, int step, const int32_t *pos, int n,
                           int K, double tau, int D, int R,
                           double alpha, double beta, double lambda,
                           double conf_thresh, int64_t V,
+                          int R_early, int T_steps, int refresh_every,
                           uint8_t *mask, double *conf, int32_t *next_pos,
                           int32_t *count, uint8_t *all_stable);
 
