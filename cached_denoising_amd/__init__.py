@@ -22,6 +22,7 @@ __all__ = [
     "dllm_fp8_addnorm_quant", "dllm_fp8_quant_weight", "dllm_fp8_gemm", "dllm_fp8_gemm_swiglu",
     "dllm_vocab_stats",
     "dllm_vocab_stats_workspace", "dllm_stability_reset", "dllm_stability_mask",
+    "dllm_refresh_interval", "dllm_cache_quotas", "dllm_evict_by_confidence",
 ]
 
 F32, BF16, E4M3 = 0, 1, 2
@@ -43,7 +44,9 @@ class _StabParams(ctypes.Structure):
     _fields_ = [("K", ctypes.c_int32), ("D", ctypes.c_int32), ("R", ctypes.c_int32),
                 ("advance_step", ctypes.c_int32), ("tau", ctypes.c_double), ("alpha", ctypes.c_double),
                 ("beta", ctypes.c_double), ("lam", ctypes.c_double),
-                ("conf_thresh", ctypes.c_double), ("vocab", ctypes.c_int64)]
+                ("conf_thresh", ctypes.c_double), ("vocab", ctypes.c_int64),
+                ("R_early", ctypes.c_int32), ("T_steps", ctypes.c_int32),
+                ("refresh_every", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 EXPORTS = {
@@ -108,6 +111,13 @@ EXPORTS = {
                                            ctypes.POINTER(_StabParams), ctypes.c_void_p,
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_void_p, ctypes.c_void_p]),
+    "dllm_refresh_interval": (ctypes.c_int, [ctypes.c_int]),
+    "dllm_cache_quotas": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_double,
+                                         ctypes.c_void_p]),
+    "dllm_evict_by_confidence": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
 }
 
 _lib = None
@@ -413,6 +423,7 @@ class StabilityState:
         self.next_pos = torch.empty((B, L), dtype=torch.int32, device=device)
         self.count = torch.empty((B,), dtype=torch.int32, device=device)
         self.all_stable = torch.empty((B,), dtype=torch.uint8, device=device)
+        self.cached = torch.zeros((B, L), dtype=torch.uint8, device=device)   # K/V held per position
         dllm_stability_reset(self)
 
 
@@ -428,15 +439,19 @@ def dllm_stability_mask(st: StabilityState, step, pos: Optional[torch.Tensor],
                         argmax: torch.Tensor, maxprob: torch.Tensor, entropy: torch.Tensor, *,
                         K: int, tau: float, R: int, alpha: float = 0.0, beta: float = 0.0,
                         lam: float = 0.0, conf_thresh: float = 0.0, V: int = 2,
-                        with_conf: bool = True, advance_step: bool = False):
+                        with_conf: bool = True, advance_step: bool = False, R_early: int = 0,
+                        T_steps: int = 0, refresh_every: int = 0):
     """One step of history, stability, confidence and window mask; outputs
     land in st.mask, st.conf, st.next_pos, st.count, st.all_stable.  ``step``
     is an int, or a [B] int32 GPU tensor of per-sequence step numbers read
     when the kernel runs (for captured graphs); with ``advance_step`` the
-    kernel increments that tensor once it has used it."""
+    kernel increments that tensor once it has used it.  ``R_early`` and
+    ``T_steps`` widen the window radius from R_early to R over T_steps steps;
+    ``refresh_every`` > 0 makes every such step (after step 0) a full refresh."""
     n = pos.shape[1] if pos is not None else st.L
     prm = _StabParams(K=K, D=st.D, R=R, advance_step=int(advance_step), tau=tau, alpha=alpha, beta=beta,
-                      lam=lam, conf_thresh=conf_thresh, vocab=V)
+                      lam=lam, conf_thresh=conf_thresh, vocab=V, R_early=R_early, T_steps=T_steps,
+                      refresh_every=refresh_every, reserved=0)
     if isinstance(step, torch.Tensor):
         if step.dtype != torch.int32 or step.numel() != st.B:
             raise ValueError("step tensor: [B] int32 per-sequence step numbers")
@@ -453,4 +468,37 @@ def dllm_stability_mask(st: StabilityState, step, pos: Optional[torch.Tensor],
                                    _dev(st.next_pos, "next_pos"), _dev(st.count, "count"),
                                    _dev(st.all_stable, "all_stable"), _stream())
     _check(rc, "dllm_stability_mask")
+    return st
+
+
+def dllm_refresh_interval(T: int) -> int:
+    """Full-refresh interval for a trajectory of T steps."""
+    return lib().dllm_refresh_interval(int(T))
+
+
+def dllm_cache_quotas(lens, budget: int, min_frac: float = 0.2):
+    """Per-request cache quotas (host): guaranteed ceil(min_frac * len), the
+    rest of the budget in arrival order.  Returns an int32 numpy array."""
+    import numpy as np
+    ln = np.ascontiguousarray(np.asarray(lens, dtype=np.int32))
+    q = np.zeros_like(ln)
+    rc = lib().dllm_cache_quotas(int(ln.size), ln.ctypes.data, int(budget), float(min_frac), q.ctypes.data)
+    _check(rc, "dllm_cache_quotas")
+    return q
+
+
+def dllm_evict_by_confidence(st: StabilityState, quota: torch.Tensor, pos: Optional[torch.Tensor],
+                             evicted: Optional[torch.Tensor] = None):
+    """Mark the recomputed positions cached, evict the lowest-confidence ones
+    beyond each sequence's quota, and add every uncached position to the next
+    step's mask (st.cached, st.mask, st.next_pos, st.count updated; st.conf is
+    the confidence the preceding stability step wrote)."""
+    if quota.dtype != torch.int32 or quota.numel() != st.B:
+        raise ValueError("quota: [B] int32")
+    n = pos.shape[1] if pos is not None else st.L
+    rc = lib().dllm_evict_by_confidence(st.B, st.L, _dev(st.conf, "conf"), _dev(quota, "quota"),
+                                        _dev(pos, "pos"), n, _dev(st.cached, "cached"), _dev(st.mask, "mask"),
+                                        _dev(st.next_pos, "next_pos"), _dev(st.count, "count"),
+                                        _dev(evicted, "evicted") if evicted is not None else None, _stream())
+    _check(rc, "dllm_evict_by_confidence")
     return st

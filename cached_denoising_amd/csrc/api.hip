@@ -309,6 +309,7 @@ int dllm_stability_mask(int B, int L, int step, int32_t *step_dev, const int32_t
     const dllm_stab_params &p = *params;
     if (p.K < 1 || p.D < p.K || p.R < 0 || p.vocab < 2) return DLLM_EINVAL;
     if (p.advance_step && !step_dev) return DLLM_EINVAL;   // nothing to advance
+    if (p.R_early < 0 || p.T_steps < 0 || p.refresh_every < 0 || p.reserved != 0) return DLLM_EINVAL;
     if (!(p.tau == p.tau) || !(p.alpha == p.alpha) || !(p.beta == p.beta) ||
         !(p.lambda == p.lambda) || !(p.conf_thresh == p.conf_thresh))
         return DLLM_EINVAL;
@@ -322,6 +323,42 @@ int dllm_stability_mask(int B, int L, int step, int32_t *step_dev, const int32_t
                             ring_maxprob, ring_step, entropy_latest, t_write, stable, p, hmax,
                             mask, conf, next_pos, count, all_stable,
                             static_cast<hipStream_t>(stream));
+}
+
+int dllm_refresh_interval(int T) {
+    const int f = (int)std::floor((double)T / 10.0 + 0.5);
+    return f < 3 ? 3 : (f > 10 ? 10 : f);
+}
+
+int dllm_cache_quotas(int B, const int32_t *len, int64_t budget, double min_frac, int32_t *quota) {
+    if (B < 1 || !len || !quota || budget < 0 || !(min_frac >= 0.0)) return DLLM_EINVAL;
+    int64_t need = 0;
+    for (int b = 0; b < B; ++b) {
+        if (len[b] < 0) return DLLM_EINVAL;
+        const double m = std::ceil(min_frac * (double)len[b]);
+        quota[b] = (int32_t)(m > (double)len[b] ? (double)len[b] : m);
+        need += quota[b];
+    }
+    if (need > budget) return DLLM_ERANGE;
+    int64_t left = budget - need;
+    for (int b = 0; b < B; ++b) {
+        const int64_t extra = std::min<int64_t>((int64_t)len[b] - quota[b], left);
+        quota[b] += (int32_t)extra;
+        left -= extra;
+    }
+    return DLLM_OK;
+}
+
+int dllm_evict_by_confidence(int B, int L, const float *conf, const int32_t *quota,
+                             const int32_t *pos, int n, uint8_t *cached, uint8_t *mask,
+                             int32_t *next_pos, int32_t *count, int32_t *evicted, void *stream) {
+    if (B < 1 || L < 1) return DLLM_ESHAPE;
+    if (B > 65535 || L > 131072) return DLLM_ERANGE;
+    if (!pos && n != L && n != 0) return DLLM_ESHAPE;
+    if (n < 0 || n > L) return DLLM_ESHAPE;
+    if (!conf || !quota || !cached || !mask || !next_pos || !count) return DLLM_EINVAL;
+    return launch_evict(B, L, conf, quota, pos, n, cached, mask, next_pos, count, evicted,
+                        static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -124,6 +124,10 @@ int launch_attention(const dllm_kv_cache &c, const AttnPlan &p, const void *q, i
                      int b, const int32_t *key_idx, int n_keys, float scale, const AttnMemo &memo,
                      void *out, int out_dtype, float *lse, void *ws, hipStream_t s);
 
+int launch_evict(int B, int L, const float *conf, const int32_t *quota, const int32_t *pos, int n,
+                 uint8_t *cached, uint8_t *mask, int32_t *next_pos, int32_t *count, int32_t *evicted,
+                 hipStream_t s);
+
 // per-group FP8 for the FFN
 int launch_fp8_quant_rows(const void *x, int dtype, int64_t ld, int64_t M, int K, uint8_t *codes,
                           uint8_t *scales, hipStream_t s);

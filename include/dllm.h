@@ -18,6 +18,8 @@
  *   dllm_stability_reset   clear the per-position decode state
  *   dllm_stability_mask    history ring, stability test, confidence score and
  *                          window expansion -> next step's compute mask
+ *   dllm_evict_by_confidence / dllm_cache_quotas / dllm_refresh_interval
+ *                          budgeted cache and refresh schedule
  *
  * Page titles cited below (section numbers are the pages' own):
  *   [SWD]     Stable Window Decoding blog page on temporal stability in
@@ -100,11 +102,21 @@ typedef struct {
  *   vocab        V of the vocab pass (max entropy ln V)
  *   advance_step nonzero: with per-sequence step numbers in device memory,
  *                each sequence's number is incremented once the call has
- *                used it (the decode loop's step counter, kept on the GPU) */
+ *                used it (the decode loop's step counter, kept on the GPU)
+ *   R_early, T_steps
+ *                the window radius widens over the trajectory [SWD, 4.4]:
+ *                at step s it is R_early + (R - R_early) * min(s, T_steps-1)
+ *                / (T_steps - 1) (integer division); T_steps <= 1 keeps R
+ *   refresh_every
+ *                every refresh_every-th step (s > 0) recomputes the whole
+ *                sequence [Flash, 5.1]; 0 never (dllm_refresh_interval gives
+ *                the pages' interval for a trajectory length)
+ *   reserved     must be 0 */
 typedef struct {
     int32_t K, D, R, advance_step;
     double tau, alpha, beta, lambda, conf_thresh;
     int64_t vocab;
+    int32_t R_early, T_steps, refresh_every, reserved;
 } dllm_stab_params;
 
 /* Human-readable name of a status code (static string). */
@@ -367,6 +379,48 @@ int dllm_stability_mask(int B, int L, int step, int32_t *step_dev, const int32_t
                         const dllm_stab_params *params,
                         uint8_t *mask, float *conf, int32_t *next_pos, int32_t *count,
                         uint8_t *all_stable, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * dllm_refresh_interval -- the full-refresh interval for a trajectory of T
+ * denoising steps [Flash, 5.1: every 5-10 steps for T in 50..100, every 3-5
+ * below 50]: round(T / 10) kept within [3, 10].  Host only.
+ * ------------------------------------------------------------------------- */
+int dllm_refresh_interval(int T);
+
+/* ---------------------------------------------------------------------------
+ * dllm_cache_quotas -- per-request shares of a cache budget in positions
+ * [Flash, 5.2: each request keeps at least a fraction (0.2 on the page) of
+ * its length; the rest goes by arrival].  quota[b] = ceil(min_frac * len[b])
+ * (at most len[b]), then what the budget has left is handed out in index
+ * order, each request up to len[b].  Host arrays.  DLLM_ERANGE when the
+ * budget cannot cover the guaranteed shares.
+ * ------------------------------------------------------------------------- */
+int dllm_cache_quotas(int B, const int32_t *len, int64_t budget, double min_frac, int32_t *quota);
+
+/* ---------------------------------------------------------------------------
+ * dllm_evict_by_confidence -- keep a sequence's cached K/V within its quota
+ * [Flash, 3.3: the lowest-confidence positions leave first, a position's K
+ * and V together; per-request quotas, 5.2].  Per sequence b:
+ *  1. the positions recomputed this step (pos, or NULL for all L) hold fresh
+ *     K/V and are marked cached;
+ *  2. when more than quota[b] positions are cached (quota < 0: no limit), the
+ *     quota[b] with the highest conf stay (ties: the lower position), the
+ *     rest are evicted (cached = 0);
+ *  3. every uncached position must be recomputed before it is attended to:
+ *     mask |= !cached, and next_pos / count are compacted again.
+ * Run after dllm_stability_mask, with its conf, mask, next_pos and count.
+ *   conf      [B, L] float32 device (not NaN)
+ *   quota     [B] int32 device
+ *   pos, n    [B, n] int32 device, -1 padding (entries outside [0, L) are
+ *             skipped); NULL with n = L: every position, NULL with n = 0: none
+ *   cached    [B, L] u8 device state (0/1), in/out; all 0 before step 0
+ *   mask, next_pos, count   as written by dllm_stability_mask (updated)
+ *   evicted   optional [B] int32: positions evicted by this call
+ * Limits: L <= 131072, B <= 65535.
+ * ------------------------------------------------------------------------- */
+int dllm_evict_by_confidence(int B, int L, const float *conf, const int32_t *quota,
+                             const int32_t *pos, int n, uint8_t *cached, uint8_t *mask,
+                             int32_t *next_pos, int32_t *count, int32_t *evicted, void *stream);
 
 #ifdef __cplusplus
 }

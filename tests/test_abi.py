@@ -27,7 +27,8 @@ def test_header_declares_the_boundary():
     for n in ["dllm_cache_init", "dllm_scatter_kv", "dllm_block_attention", "dllm_vocab_stats",
               "dllm_stability_mask", "dllm_sink_rolling_map", "dllm_stability_reset",
               "dllm_block_attention_workspace", "dllm_vocab_stats_workspace", "dllm_status_str",
-              "dllm_facache_maps", "dllm_facache_merge", "dllm_facache_merge_workspace"]:
+              "dllm_facache_maps", "dllm_facache_merge", "dllm_facache_merge_workspace",
+              "dllm_evict_by_confidence", "dllm_cache_quotas", "dllm_refresh_interval"]:
         assert n in names
 
 
@@ -59,6 +60,18 @@ def test_host_validation_without_gpu(dl):
     prm = dl._StabParams(K=3, D=2, R=1, tau=0.9, vocab=10)                                  # D < K
     assert L.dllm_stability_mask(1, 4, 0, None, None, 4, 16, 16, 16, 16, 16, 16, 16, 16, 16,
                                  ctypes.byref(prm), 16, 16, 16, 16, 16, None) == -1
+    prm = dl._StabParams(K=3, D=3, R=1, tau=0.9, vocab=10, refresh_every=-1)                # bad schedule
+    assert L.dllm_stability_mask(1, 4, 0, None, None, 4, 16, 16, 16, 16, 16, 16, 16, 16, 16,
+                                 ctypes.byref(prm), 16, 16, 16, 16, 16, None) == -1
+    prm = dl._StabParams(K=3, D=3, R=1, tau=0.9, vocab=10, reserved=1)
+    assert L.dllm_stability_mask(1, 4, 0, None, None, 4, 16, 16, 16, 16, 16, 16, 16, 16, 16,
+                                 ctypes.byref(prm), 16, 16, 16, 16, 16, None) == -1
+    # eviction: shapes and limits before any launch
+    assert L.dllm_evict_by_confidence(1, 0, 16, 16, None, 0, 16, 16, 16, 16, None, None) == -3
+    assert L.dllm_evict_by_confidence(1, 8, 16, 16, None, 5, 16, 16, 16, 16, None, None) == -3
+    assert L.dllm_evict_by_confidence(1, 8, 16, 16, 16, 9, 16, 16, 16, 16, None, None) == -3
+    assert L.dllm_evict_by_confidence(1, 1 << 18, 16, 16, None, 0, 16, 16, 16, 16, None, None) == -5
+    assert L.dllm_evict_by_confidence(1, 8, None, 16, None, 8, 16, 16, 16, 16, None, None) == -1
     assert L.dllm_sink_rolling_map(1, 10, 4, 8, 16, 16, 11, None) == -3                     # n_keys < S+R
     assert L.dllm_facache_maps(1, 8, 8, 16, 16, 16, None) == -3                             # block = L
     assert L.dllm_facache_maps(1, 8, 2, None, 16, 16, None) == -1
@@ -93,3 +106,23 @@ def test_workspace_sizes(dl):
     # outside the block over the 32 block keys, one tile per workgroup
     desc = dl._KVCache(B=16, L=2048, n_kv_heads=32, d_head=128, dtype=1, k=16, v=16)
     assert L.dllm_facache_merge_workspace(ctypes.byref(desc), 1, 32, 2016, 32) == 0
+
+
+def test_host_policies_match_the_oracle(dl, orc):
+    """refresh interval and quotas are host arithmetic: equal to the oracle's"""
+    import numpy as np
+    for T in list(range(0, 130)) + [400, 4096]:
+        assert dl.dllm_refresh_interval(T) == orc.refresh_interval(T), T
+    rng = np.random.default_rng(3)
+    for trial in range(200):
+        lens = rng.integers(0, 300, size=int(rng.integers(1, 9)))
+        frac = float(rng.choice([0.0, 0.2, 0.5, 1.0]))
+        need = int(np.minimum(np.ceil(frac * lens), lens).sum())
+        budget = int(rng.integers(max(0, need - 20), lens.sum() + 50))
+        try:
+            ref = orc.cache_quotas(lens, budget, min_frac=frac)
+        except ValueError:
+            with pytest.raises(dl.DllmError):
+                dl.dllm_cache_quotas(lens, budget, frac)
+            continue
+        assert np.array_equal(dl.dllm_cache_quotas(lens, budget, frac), ref), trial
