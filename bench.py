@@ -20,6 +20,15 @@ FP8 on the same 16 x 2048 step (32768 tokens, hidden 4096, SwiGLU width
 fused with SwiGLU and the quantisation of its output, the FF-Out product in
 bf16.  The weights are quantised once, before the timed steps.
 
+With --config policies a step is the decode policies on the vocab sweep's
+64 x 512 positions: the stability mask with the window radius ramped from
+0 to 3 over the 64-step trajectory and a full refresh at the interval for
+that length, then the eviction of the lowest-confidence cached positions
+beyond each sequence's quota (half the positions shared out with a 20%
+guarantee per request).  The step statistics are computed once, before the
+timed steps.  The eviction alone is also timed at the long-context shape
+(4 x 32768, quota 8192).
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config gpt2]
 """
 from __future__ import annotations
@@ -47,7 +56,7 @@ KERNEL_SRC = {"vocab_stats": ["vocab_stats.hip"],
               "facache_merge": ["attention.hip", "attention_shared.hip", "attn_common.hpp"],
               "scatter": ["scatter.hip"], "stability": ["stability.hip"],
               "fp8_addnorm": ["fp8_ffn.hip", "common.hpp"], "fp8_gateup": ["fp8_ffn.hip", "common.hpp"],
-              "fp8_ffout": ["fp8_ffn.hip", "common.hpp"]}
+              "fp8_ffout": ["fp8_ffn.hip", "common.hpp"], "evict": ["stability.hip"]}
 
 
 def parse():
@@ -56,7 +65,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="gpt2",
-                    choices=["gpt2", "llada", "vocab", "longctx", "facache", "ffn"])
+                    choices=["gpt2", "llada", "vocab", "longctx", "facache", "ffn", "policies"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from Python instead of replaying a captured graph")
@@ -325,6 +334,106 @@ class FfnStep:
         return {"fp8_gateup": 2 * M * 2 * I * K, "fp8_ffout": 2 * M * K * I}
 
 
+class PolicyStep:
+    """Stability mask with the ramped radius and refresh schedule, then the
+    quota eviction, on B x L positions with fixed step statistics."""
+
+    def __init__(self, D, W, cfg, dev):
+        import torch
+        self.D, self.W, self.cfg = D, W, cfg
+        B, L = cfg.B, cfg.L
+        self.B, self.L = B, L
+        logits = W.logits(cfg, device=dev)
+        am, mp, en = D.dllm_vocab_stats(logits, V=cfg.V)
+        del logits
+        self.am, self.mp, self.en = am.view(B, L), mp.view(B, L), en.view(B, L)
+        self.st = D.StabilityState(B, L, cfg.D, device=dev)
+        self.refresh = D.dllm_refresh_interval(cfg.T)
+        self.kw = dict(K=cfg.K, tau=cfg.tau, R=cfg.R, alpha=cfg.alpha, beta=cfg.beta, lam=cfg.lam,
+                       conf_thresh=cfg.conf_thresh, V=cfg.V, R_early=0, T_steps=cfg.T,
+                       refresh_every=self.refresh)
+        self.quota_host = D.dllm_cache_quotas([L] * B, B * L // 2, 0.2)
+        self.quota = torch.from_numpy(self.quota_host).to(dev)
+        self.evicted = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.step_t = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.facache = False
+        self.attn_split = False
+
+    def kernels(self):
+        return ["stability", "evict"]
+
+    def run(self, events=None):
+        D = self.D
+
+        def mark(name, i):
+            if events is not None:
+                events[name][i].record()
+
+        mark("stability", 0)
+        D.dllm_stability_mask(self.st, self.step_t, None, self.am, self.mp, self.en, advance_step=True,
+                              **self.kw)
+        mark("stability", 1)
+        mark("evict", 0)
+        D.dllm_evict_by_confidence(self.st, self.quota, None, self.evicted)
+        mark("evict", 1)
+
+    def algorithmic_bytes(self):
+        BL, K = self.B * self.L, self.cfg.K
+        return {
+            # as the decode step's stability kernel
+            "stability": BL * (12 + 12 + 12 * (K - 1) + 2 * 9 + 9),
+            # conf (4), cached read and write (2), mask read and write (2),
+            # next positions (4), quota and counts
+            "evict": BL * 12 + self.B * 12,
+        }
+
+    def algorithmic_flops(self):
+        return {}
+
+    def evict_longctx_us(self, W, dev, reps=20):
+        """the eviction alone on 4 x 32768 positions with a quota of 8192
+        (the sink + rolling budget of the long-context workload), every
+        position recomputed: the selection runs on each call"""
+        import numpy as np
+        import torch
+        c = W.CONFIGS["longctx"]
+        st = self.D.StabilityState(c.B, c.L, 2, device=dev)
+        g = torch.Generator(device="cpu").manual_seed(c.seed)
+        st.conf.copy_(torch.floor(torch.rand((c.B, c.L), generator=g) * 4096) / 4096)
+        st.mask.zero_()
+        quota = torch.full((c.B,), c.sinks + c.rolling, dtype=torch.int32, device=dev)
+        run = lambda: self.D.dllm_evict_by_confidence(st, quota, None)
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        return 1000.0 * e0.elapsed_time(e1) / reps
+
+
+def cpu_baseline_policies(step, W):
+    """The oracle's stability step and eviction on the whole step (the
+    bench's shape is small enough)."""
+    import numpy as np
+
+    import oracle
+    threads = oracle.set_threads(int(os.environ.get("OMP_NUM_THREADS", min(16, os.cpu_count() or 1))))
+    B, L, cfg = step.B, step.L, step.cfg
+    ost = oracle.StabilityState(B, L, cfg.D)
+    am, mp, en = (t.cpu().numpy() for t in (step.am, step.mp, step.en))
+    reps = 6
+    t0 = time.perf_counter()
+    for s in range(reps):
+        r = oracle.stability_step(ost, s, None, am, mp, en, **step.kw)
+        oracle.evict_by_confidence(ost, r["conf"].astype(np.float32), step.quota_host, None, r["mask"])
+    dt = (time.perf_counter() - t0) / reps
+    return {"value": 1.0 / dt, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} whole steps (stability step + eviction, {B} x {L} positions)"}
+
+
 def cpu_baseline_ffn(step, W):
     """The oracle's chain on a bounded sample of token rows: add & norm +
     quantisation, Gate-Up + SwiGLU + quantisation, FF-Out; scaled to
@@ -431,9 +540,11 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
-    cfg = W.CONFIGS["llada" if args.config in ("facache", "ffn") else args.config]
+    cfg = W.CONFIGS[{"facache": "llada", "ffn": "llada", "policies": "vocab"}.get(args.config, args.config)]
     if args.config == "ffn":
         step = FfnStep(D, W, dev)
+    elif args.config == "policies":
+        step = PolicyStep(D, W, cfg, dev)
     else:
         step = Step(D, W, cfg, dev, facache=args.config == "facache")
     for _ in range(args.warmup):
@@ -473,7 +584,13 @@ def main():
     if graph is None:
         kernel_timing = "HIP events on the launch stream, in the timed region"
     else:
-        kernel_timing = "HIP events on the launch stream, eager pass of the same steps after the timed region"
+        kernel_timing = ("HIP events on the launch stream, eager pass of the same steps after the timed "
+                         "region, queued behind a spin kernel so that no host launch gap falls inside an "
+                         "event pair")
+        # the spin keeps the GPU busy while the host queues the whole pass;
+        # about 150 us of host time per launch, at least 20 ms (2.4 GHz clock)
+        spin_s = max(0.02, 150e-6 * args.steps * len(names))
+        torch.cuda._sleep(int(spin_s * 2.4e9))
         for i in range(args.steps):
             step.run({n: events[n][i] for n in names})
         torch.cuda.synchronize()
@@ -511,10 +628,15 @@ def main():
         extra = {"full_recompute_attention_us": round(full, 1),
                  "facache_attention_us": round(fa, 1),
                  "facache_speedup_vs_full": round(full / fa, 2)}
+    if args.config == "policies":
+        extra = {"evict_longctx_us": round(step.evict_longctx_us(W, dev), 2),
+                 "refresh_every": step.refresh}
     if args.no_cpu_baseline:
         cpu = None
     elif args.config == "ffn":
         cpu = cpu_baseline_ffn(step, W)
+    elif args.config == "policies":
+        cpu = cpu_baseline_policies(step, W)
     else:
         cpu = cpu_baseline(step, D, W, cfg)
     desc = {
@@ -530,14 +652,20 @@ def main():
                "hidden 4096, SwiGLU width 12288, e4m3 codes with E8M0 scales per 1x128 activation "
                "group and 128x128 weight block (add & norm + quant, Gate-Up + SwiGLU + quant, "
                "FF-Out to bf16)",
+        "policies": "decode policies on the vocab sweep's 64 x 512 positions: stability mask with the "
+                    "window radius ramped 0 -> 3 over 64 steps and a full refresh every 6 steps, then "
+                    "confidence-ordered eviction to per-request quotas (half the positions, 20% "
+                    "guaranteed each)",
         "facache": "LLaDA-8B-shaped first-layer attention of a later step of a block, with FACache: "
                    "B=16, L=2048, 32 heads x d128, bf16 K/V, block 32 (scatter, block queries over "
                    "all keys, 2016 outside queries from their memo over the block keys)",
     }[args.config]
     metric = {"facache": "first-layer attention steps/sec with FACache (scatter + block attention + memo merge)",
-              "ffn": "FP8 FFN steps/sec (add & norm + quant, Gate-Up + SwiGLU + quant, FF-Out)"}.get(
+              "ffn": "FP8 FFN steps/sec (add & norm + quant, Gate-Up + SwiGLU + quant, FF-Out)",
+              "policies": "decode-policy steps/sec (stability mask with ramp + refresh, quota eviction)"}.get(
         args.config, METRIC)
-    dtype = "e4m3 x e4m3 -> f32 (E8M0 group scales)" if args.config == "ffn" else "bf16"
+    dtype = {"ffn": "e4m3 x e4m3 -> f32 (E8M0 group scales)", "policies": "f64 decisions, f32 keys"}.get(
+        args.config, "bf16")
     line = {
         "metric": metric, "value": round(1000.0 / ms, 2), "unit": "steps/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),

@@ -189,141 +189,291 @@ __device__ __forceinline__ uint32_t conf_key(float c) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The selection histogram is kept in 16 copies (a lane adds to copy lane % 16)
+// 257 words apart, so that the lanes of a wave counting one digit -- the
+// top key byte of confidences within a binade is shared -- land on 16
+// different banks instead of serialising on one word.
+constexpr int kHistCopies = 16;
+constexpr int kHistStride = 257;
+
+// The digit at which the `need`-th largest key lies, from the 256-bin
+// histogram: one wave, four bins per lane from the top, a lane scan of the
+// counts.  Writes the digit and the count of keys above it, and leaves the
+// histogram cleared for the next pass.
+__device__ __forceinline__ void select_digit(int *hist, int need, int lane, int *s_sel) {
+    int h[4];
+    int tot = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int d = 255 - 4 * lane - k;
+        int c = 0;
+#pragma unroll
+        for (int cp = 0; cp < kHistCopies; ++cp) c += hist[cp * kHistStride + d];
+#pragma unroll
+        for (int cp = 0; cp < kHistCopies; ++cp) hist[cp * kHistStride + d] = 0;
+        h[k] = c;
+        tot += c;
+    }
+    int incl = tot;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int t = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += t;
+    }
+    const uint64_t hit = __ballot(incl >= need);
+    const int first = hit ? __ffsll((unsigned long long)hit) - 1 : kWave - 1;
+    if (lane == first) {
+        int run = incl - tot;
+        int d = 255 - 4 * lane - 3, above = run + h[0] + h[1] + h[2];
+        bool found = false;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (!found && run + h[k] >= need) {
+                d = 255 - 4 * lane - k;
+                above = run;
+                found = true;
+            }
+            run += h[k];
+        }
+        s_sel[0] = d;
+        s_sel[1] = above;
+    }
+}
+
+// Sequences up to this length keep their keys in LDS through the selection
+// (4 bytes each: 128 KB at the limit, with the bitsets and the histogram
+// copies within the CU's 160 KB); longer ones read them from memory per pass.
+constexpr int kEvictKeysLds = 32768;
+constexpr int kEvictUnroll = 8;     // positions per thread in flight in the load pass
+constexpr int kPassUnroll = 4;      // positions per thread per step of the LDS passes
+
+// Exclusive prefix over the workgroup of one int per thread (thread order),
+// and the total.  Uses `tmp` (kWaves ints, not to be reused by the caller
+// without a barrier); contains one barrier.
+__device__ __forceinline__ int block_exclusive_scan(int v, int lane, int wave, int *tmp, int &total) {
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int t = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += t;
+    }
+    if (lane == kWave - 1) tmp[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+    for (int w = 0; w < kWaves; ++w) {
+        const int t = tmp[w];
+        before += w < wave ? t : 0;
+        total += t;
+    }
+    return before + incl - v;
+}
+
+// The lowest r set bits of x (r >= 0).
+__device__ __forceinline__ uint32_t lowest_set_bits(uint32_t x, int r) {
+    uint32_t y = x;
+    for (int j = 0; j < r && y; ++j) y &= y - 1;
+    return x ^ y;
+}
+
+template <bool KEYS_LDS>
 __global__ __launch_bounds__(kThreads) void evict_kernel(
     int L, const float *__restrict__ conf, const int32_t *__restrict__ quota,
     const int32_t *__restrict__ pos, int n, uint8_t *__restrict__ cached, uint8_t *__restrict__ mask,
     int32_t *__restrict__ next_pos, int32_t *__restrict__ count, int32_t *__restrict__ evicted) {
-    extern __shared__ uint32_t cbits[];                // cached, then kept: one bit per position each
-    __shared__ int hist[256];
-    __shared__ int wave_cnt[kWaves];
+    // dynamic LDS: cached bits (kept bits once decided), mask bits (the next
+    // mask once decided), then the keys (0 for an uncached position)
+    extern __shared__ uint32_t cbits[];
+    // the selection histogram; afterwards the at-threshold bits, then the
+    // per-word prefix of the next mask
+    __shared__ int hist[kHistCopies * kHistStride];
+    __shared__ int tmp[3][kWaves];                     // one per scan
     __shared__ int s_sel[2];                           // the digit found, the count above it
     const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int q = quota[b];
     const int64_t rowoff = (int64_t)b * L;
     const int words = (L + 31) >> 5;
-    uint32_t *kbits = cbits + words;
+    uint32_t *mbits = cbits + words;
+    uint32_t *keys = mbits + words;
+    uint32_t *abits = reinterpret_cast<uint32_t *>(hist);
     const float *cf = conf + rowoff;
+    const uint8_t *cr = cached + rowoff;
+    const uint8_t *mr = mask + rowoff;
+    const bool all_fresh = !pos && n == L;             // every position recomputed
 
-    // the cached flags as bits: a wave's ballot over 64 positions is two words
-    for (int i0 = 0; i0 < L; i0 += kThreads) {
-        const int i = i0 + tid;
-        const uint64_t bal = __ballot(i < L && cached[rowoff + i] != 0);
-        const int w0 = (i0 + wave * kWave) >> 5;
-        if (lane == 0 && w0 < words) { cbits[w0] = (uint32_t)bal; kbits[w0] = 0; }
-        if (lane == 1 && w0 + 1 < words) { cbits[w0 + 1] = (uint32_t)(bal >> 32); kbits[w0 + 1] = 0; }
+    for (int k = tid; k < kHistCopies * kHistStride; k += kThreads) hist[k] = 0;
+    // load pass: cached and mask flags as bits (a wave's ballot over 64
+    // positions is two words) and the keys; kEvictUnroll loads per thread
+    // are issued before their results are used
+    for (int i0 = 0; i0 < L; i0 += kThreads * kEvictUnroll) {
+        uint8_t cv[kEvictUnroll], mv[kEvictUnroll];
+        float fv[kEvictUnroll];
+#pragma unroll
+        for (int u = 0; u < kEvictUnroll; ++u) {
+            const int i = i0 + u * kThreads + tid;
+            cv[u] = i < L ? (all_fresh ? 1 : cr[i]) : 0;
+            mv[u] = i < L ? mr[i] : 0;
+            if (KEYS_LDS) fv[u] = i < L ? cf[i] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kEvictUnroll; ++u) {
+            const int c0 = i0 + u * kThreads;
+            const int i = c0 + tid;
+            const uint64_t bc = __ballot(cv[u] != 0);
+            const uint64_t bm = __ballot(mv[u] != 0);
+            const int w0 = (c0 + wave * kWave) >> 5;
+            if (lane == 0 && w0 < words) { cbits[w0] = (uint32_t)bc; mbits[w0] = (uint32_t)bm; }
+            if (lane == 1 && w0 + 1 < words) {
+                cbits[w0 + 1] = (uint32_t)(bc >> 32);
+                mbits[w0 + 1] = (uint32_t)(bm >> 32);
+            }
+            if (KEYS_LDS && i < L) keys[i] = conf_key(fv[u]);
+        }
     }
     __syncthreads();
-    // this step's recomputed positions hold fresh K/V
-    for (int j = tid; j < n; j += kThreads) {
-        const int p = pos ? pos[(int64_t)b * n + j] : j;
-        if (p >= 0 && p < L) atomicOr(&cbits[p >> 5], 1u << (p & 31));
+    // this step's recomputed positions hold fresh K/V.  The lanes of a wave
+    // whose positions share a bitset word (runs of a sorted list) OR their
+    // bits together first, so that one atomic per word and wave is issued.
+    if (pos) {
+        for (int j0 = 0; j0 < n; j0 += kThreads) {
+            const int j = j0 + tid;
+            const int p = j < n ? pos[(int64_t)b * n + j] : -1;
+            const bool ok = p >= 0 && p < L;
+            const int w = ok ? p >> 5 : -1;
+            uint32_t v = ok ? 1u << (p & 31) : 0u;
+            const int wprev = __shfl_up(w, 1, kWave);
+            const bool head = lane == 0 || !ok || w != wprev;
+            const uint64_t heads = __ballot(head);
+            const int seg = __popcll(heads & ((2ull << lane) - 1ull));   // heads at or below the lane
+#pragma unroll
+            for (int d = 1; d < kWave; d <<= 1) {
+                const uint32_t ov = __shfl_down(v, d, kWave);
+                const int os = __shfl_down(seg, d, kWave);
+                if (lane + d < kWave && os == seg) v |= ov;
+            }
+            if (head && ok) atomicOr(&cbits[w], v);
+        }
+        __syncthreads();
     }
-    __syncthreads();
     auto is_cached = [&](int i) { return (cbits[i >> 5] >> (i & 31)) & 1u; };
+    // the key of a cached position; 0 (below every key of a float that is
+    // not NaN) for an uncached one
+    auto key_of = [&](int i) { return KEYS_LDS ? keys[i] : (is_cached(i) ? conf_key(cf[i]) : 0u); };
     int nc = 0;
-    for (int w = tid; w < words; w += kThreads) nc += __popc(cbits[w]);
-    for (int o = 32; o >= 1; o >>= 1) nc += __shfl_xor(nc, o, kWave);
-    if (lane == 0) wave_cnt[wave] = nc;
-    __syncthreads();
-    nc = 0;
-    for (int w = 0; w < kWaves; ++w) nc += wave_cnt[w];
-    __syncthreads();                                    // wave_cnt is reused
-    const int q = quota[b];
-    int ev = 0;
+    for (int i0 = 0; i0 < L; i0 += kThreads * kPassUnroll) {
+        bool c[kPassUnroll];
+#pragma unroll
+        for (int u = 0; u < kPassUnroll; ++u) {
+            const int i = i0 + u * kThreads + tid;
+            c[u] = i < L && is_cached(i);
+            if (KEYS_LDS && i < L && !c[u]) keys[i] = 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kPassUnroll; ++u) {
+            if (i0 + u * kThreads >= L) break;          // uniform over the workgroup
+            const uint64_t bal = __ballot(c[u]);
+            if (lane == 0) nc += __popcll(bal);
+        }
+    }
+    int nc_total;
+    block_exclusive_scan(nc, lane, wave, tmp[0], nc_total);   // also: keys and hist settled
+    nc = nc_total;
+    const bool select = q >= 0 && nc > q;
 
-    if (q >= 0 && nc > q) {
-        // radix select of the q-th largest key among the cached positions
-        uint32_t prefix = 0, pmask = 0;
-        int need = q;                                   // still to keep at or below the prefix
+    // radix select of the q-th largest key among the cached positions: the
+    // threshold key T, and how many positions at T stay (`need`)
+    uint32_t prefix = 0;
+    int need = q;
+    if (select) {
+        uint32_t pmask = 0;
+        int *my_hist = hist + (lane & (kHistCopies - 1)) * kHistStride;
         for (int shift = 24; shift >= 0; shift -= 8) {
-            for (int k = tid; k < 256; k += kThreads) hist[k] = 0;
-            __syncthreads();
+#pragma unroll 4
             for (int i = tid; i < L; i += kThreads) {
-                if (!is_cached(i)) continue;
-                const uint32_t key = conf_key(cf[i]);
-                if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+                const uint32_t key = key_of(i);
+                if (key && (key & pmask) == prefix) atomicAdd(&my_hist[(key >> shift) & 255], 1);
             }
             __syncthreads();
-            if (tid == 0) {
-                int above = 0, d = 255;
-                for (; d > 0; --d) {
-                    if (above + hist[d] >= need) break;
-                    above += hist[d];
-                }
-                s_sel[0] = d;
-                s_sel[1] = above;
-            }
+            if (wave == 0) select_digit(hist, need, lane, s_sel);
             __syncthreads();
             prefix |= (uint32_t)s_sel[0] << shift;
             pmask |= 255u << shift;
             need -= s_sel[1];
-            __syncthreads();                            // s_sel and hist are reused
         }
-        // prefix = T; keep keys above T, and the first `need` positions at T
-        int base = 0;
-        for (int i0 = 0; i0 < L; i0 += kThreads) {
-            const int i = i0 + tid;
-            uint32_t key = 0;
-            bool c = false;
-            if (i < L) {
-                c = is_cached(i) != 0;
-                key = c ? conf_key(cf[i]) : 0u;
+        // the positions above T (in place of the cached bits: a wave reads and
+        // writes only the two words of its own 64 positions) and at T
+        for (int i0 = 0; i0 < L; i0 += kThreads * kPassUnroll) {
+            uint32_t kk[kPassUnroll];
+#pragma unroll
+            for (int u = 0; u < kPassUnroll; ++u) {
+                const int i = i0 + u * kThreads + tid;
+                kk[u] = i < L ? key_of(i) : 0u;
             }
-            const bool at = c && key == prefix;
-            const uint64_t bal = __ballot(at);
-            if (lane == 0) wave_cnt[wave] = __popcll(bal);
-            __syncthreads();
-            int off = base;
-            for (int w = 0; w < wave; ++w) off += wave_cnt[w];
-            int chunk = 0;
-            for (int w = 0; w < kWaves; ++w) chunk += wave_cnt[w];
-            const uint64_t below = lane ? (bal & ((~0ull) >> (64 - lane))) : 0ull;
-            const bool keep = c && (key > prefix || (at && off + __popcll(below) < need));
-            if (keep) atomicOr(&kbits[i >> 5], 1u << (i & 31));
-            if (c && !keep) ++ev;
-            base += chunk;
-            __syncthreads();                            // wave_cnt is reused
+#pragma unroll
+            for (int u = 0; u < kPassUnroll; ++u) {
+                if (i0 + u * kThreads >= L) break;      // uniform over the workgroup
+                const uint64_t ba = __ballot(kk[u] > prefix);
+                const uint64_t bt = __ballot(kk[u] != 0 && kk[u] == prefix);
+                const int w0 = (i0 + u * kThreads + wave * kWave) >> 5;
+                if (lane == 0 && w0 < words) { cbits[w0] = (uint32_t)ba; abits[w0] = (uint32_t)bt; }
+                if (lane == 1 && w0 + 1 < words) {
+                    cbits[w0 + 1] = (uint32_t)(ba >> 32);
+                    abits[w0 + 1] = (uint32_t)(bt >> 32);
+                }
+            }
         }
-    } else {
-        for (int w = tid; w < words; w += kThreads) kbits[w] = cbits[w];
+        __syncthreads();
+    }
+
+    // each thread owns a run of whole words, in position order
+    const int wpt = (words + kThreads - 1) / kThreads;
+    const int w_lo = min(words, tid * wpt), w_hi = min(words, w_lo + wpt);
+    if (select) {
+        // the first `need` positions at T (position order) stay
+        int n_at = 0;
+        for (int w = w_lo; w < w_hi; ++w) n_at += __popc(abits[w]);
+        int unused;
+        int at_off = block_exclusive_scan(n_at, lane, wave, tmp[1], unused);
+        for (int w = w_lo; w < w_hi; ++w) {
+            const uint32_t aw = abits[w];
+            const int r = max(0, min(need - at_off, __popc(aw)));
+            cbits[w] |= lowest_set_bits(aw, r);
+            at_off += __popc(aw);
+        }
+    }
+    // every uncached position joins the mask
+    int n_on = 0;
+    for (int w = w_lo; w < w_hi; ++w) {
+        const int valid = min(32, L - 32 * w);
+        const uint32_t vmask = valid == 32 ? ~0u : ((1u << valid) - 1u);
+        const uint32_t on = (mbits[w] | ~cbits[w]) & vmask;
+        mbits[w] = on;
+        n_on += __popc(on);
+    }
+    int n_total;
+    int on_off = block_exclusive_scan(n_on, lane, wave, tmp[2], n_total);
+    uint32_t *wpref = abits;                            // the at bits are used up
+    for (int w = w_lo; w < w_hi; ++w) {
+        wpref[w] = (uint32_t)on_off;
+        on_off += __popc(mbits[w]);
     }
     __syncthreads();
 
-    // the uncached positions join the mask; ascending compaction
-    int base = 0;
-    for (int i0 = 0; i0 < L; i0 += kThreads) {
-        const int i = i0 + tid;
-        bool on = false;
-        if (i < L) {
-            const bool kept = (kbits[i >> 5] >> (i & 31)) & 1u;
-            cached[rowoff + i] = kept ? 1 : 0;
-            on = mask[rowoff + i] != 0 || !kept;
-            mask[rowoff + i] = on ? 1 : 0;
-        }
-        const uint64_t bal = __ballot(on);
-        if (lane == 0) wave_cnt[wave] = __popcll(bal);
-        __syncthreads();
-        int off = base;
-        for (int w = 0; w < wave; ++w) off += wave_cnt[w];
-        int chunk = 0;
-        for (int w = 0; w < kWaves; ++w) chunk += wave_cnt[w];
-        if (on) {
-            const uint64_t below = lane ? (bal & ((~0ull) >> (64 - lane))) : 0ull;
-            next_pos[rowoff + off + __popcll(below)] = i;
-        }
-        base += chunk;
-        __syncthreads();
+    // store pass: flags and the compacted mask, position-strided
+#pragma unroll 8
+    for (int i = tid; i < L; i += kThreads) {
+        const int w = i >> 5, bit = i & 31;
+        const uint32_t mw = mbits[w];
+        const bool on = (mw >> bit) & 1u;
+        cached[rowoff + i] = (uint8_t)((cbits[w] >> bit) & 1u);
+        mask[rowoff + i] = on ? 1 : 0;
+        if (on) next_pos[rowoff + wpref[w] + __popc(mw & ((1u << bit) - 1u))] = i;
     }
-    for (int i = base + tid; i < L; i += kThreads) next_pos[rowoff + i] = -1;
-    // the evicted count: a sum over the threads in a fixed order
-    for (int o = 32; o >= 1; o >>= 1) ev += __shfl_xor(ev, o, kWave);
-    if (lane == 0) wave_cnt[wave] = ev;
-    __syncthreads();
+    for (int i = n_total + tid; i < L; i += kThreads) next_pos[rowoff + i] = -1;
     if (tid == 0) {
-        int tot = 0;
-        for (int w = 0; w < kWaves; ++w) tot += wave_cnt[w];
-        count[b] = base;
-        if (evicted) evicted[b] = tot;
+        count[b] = n_total;
+        if (evicted) evicted[b] = select ? nc - q : 0;
     }
 }
 
@@ -333,9 +483,14 @@ int launch_evict(int B, int L, const float *conf, const int32_t *quota, const in
                  uint8_t *cached, uint8_t *mask, int32_t *next_pos, int32_t *count, int32_t *evicted,
                  hipStream_t s) {
     if (L > kMaxL) return DLLM_ERANGE;
-    const size_t shmem = 2 * sizeof(uint32_t) * (size_t)((L + 31) / 32);
-    evict_kernel<<<dim3((unsigned)B), dim3(kThreads), shmem, s>>>(L, conf, quota, pos, n, cached, mask,
-                                                                  next_pos, count, evicted);
+    // two bitsets (cached, mask), then the keys when they fit
+    const size_t bits = 2 * sizeof(uint32_t) * (size_t)((L + 31) / 32);
+    if (L <= kEvictKeysLds)
+        evict_kernel<true><<<dim3((unsigned)B), dim3(kThreads), bits + sizeof(uint32_t) * (size_t)L, s>>>(
+            L, conf, quota, pos, n, cached, mask, next_pos, count, evicted);
+    else
+        evict_kernel<false><<<dim3((unsigned)B), dim3(kThreads), bits, s>>>(L, conf, quota, pos, n, cached,
+                                                                           mask, next_pos, count, evicted);
     return launch_status();
 }
 

@@ -91,6 +91,21 @@ def test_evict_degenerate(orc):
                 np.array([1, 100, 776], np.int32), None, "all equal")
 
 
+def test_evict_keys_beyond_lds(orc):
+    """beyond 32768 positions a sequence's keys are read from memory on each
+    selection pass: 2 x 70001 (ragged) with quotas of a third and of all but one"""
+    D = need_gpu()
+    rng = np.random.default_rng(16)
+    B, L = 2, 70001
+    conf = _conf(rng, B, L, "grid")
+    cached = (rng.random((B, L)) < 0.7).astype(np.uint8)
+    mask = (rng.random((B, L)) < 0.1).astype(np.uint8)
+    pos = np.stack([rng.permutation(L)[:300] for _ in range(B)]).astype(np.int32)
+    quota = np.array([L // 3, int(cached[1].sum()) + 290], np.int32)
+    r = _evict_case(orc, D, B, L, conf, cached, mask, quota, pos, "beyond lds")
+    assert r["evicted"][0] > 0
+
+
 @pytest.mark.parametrize("shape", ["longctx", "vocab"])
 def test_evict_full_size(orc, shape):
     """the long-context shape (4 x 32768) with a cache of 8192 positions per
