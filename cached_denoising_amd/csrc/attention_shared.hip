@@ -42,6 +42,16 @@ constexpr int kTableKeys = 2048;       // key indices of one split held in LDS (
 // multiple of 16) at one logical chunk; the swizzle sends those 8 rows to 8
 // distinct 16-byte bank groups.
 __device__ __forceinline__ int kswz(int kappa) { return (kappa & 3) | ((kappa >> 1) & 4); }
+// The same for 256-byte rows (bf16, d = 128), read in 16-lane phases over the
+// 64 banks: a phase touches rows {0..3, 8..11, 16..19, 24..27} + 4t at one
+// logical chunk, and these 16 rows go to 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int kswz16(int kappa) { return (kappa & 3) | ((kappa >> 1) & 12); }
+// V rows of 256 bytes: a 32-lane phase of the transposed reads touches rows
+// {0..3, 8..11} (+4) at logical chunks {2dt, 2dt+1}; bits 1..3 separate those
+// 8 rows, bit 0 separates neighbouring rows for the widening's writes.
+__device__ __forceinline__ int vswz16(int rho) { return 2 * ((rho & 3) | ((rho >> 1) & 4)) | (rho & 1); }
+__device__ __forceinline__ int vswz_bf16(int rho) { return vswz<DLLM_BF16>(rho); }
+__device__ __forceinline__ int vswz_e4m3(int rho) { return vswz<DLLM_E4M3>(rho); }
 
 // s_waitcnt vmcnt(n) for a wave-uniform n in [0, MAXN]
 template <int MAXN>
@@ -89,7 +99,13 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
     constexpr int STAGE = 2 * TB + (E4 ? 256 : 0);
     constexpr int BROW = D * 2;            // bytes of one bf16 row
     constexpr int CTB = 32 * BROW;         // one bf16 K (or V) tile
-    constexpr int CSTAGE = CONV ? 2 * CTB + 3 * 128 : 0;   // + per-key kfac, bias, vfac
+    // swizzles of the bf16 operand tiles, and of the ring stages as loaded
+    // (the operand tiles themselves for bf16; read linearly for widening)
+    auto kswz_b = [](int r) { return BROW == 256 ? kswz16(r) : kswz(r); };
+    auto vswz_b = [](int r) { return BROW == 256 ? vswz16(r) : vswz_bf16(r); };
+    auto kswz_r = [&](int r) { return CONV ? kswz(r) : kswz_b(r); };
+    auto vswz_r = [&](int r) { return CONV ? vswz_e4m3(r) : vswz_b(r); };
+    constexpr int CSTAGE = CONV ? 2 * CTB + 3 * 128 + 16 : 0;   // + per-key kfac, bias, vfac; full flag
     constexpr int TAB = MAP ? kTableKeys * 4 : 0;
     constexpr int SMEM = kNS * STAGE + 2 * CSTAGE + TAB;
     static_assert(TB % 1024 == 0 && CPR <= 16, "tile layout");
@@ -162,7 +178,7 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
             const int r = p / CPR, sl = p % CPR;
             const int kk = tk.k[u];
             const unsigned char *src = static_cast<const unsigned char *>(ck) +
-                                       (kv_base + (kk < 0 ? 0 : kk)) * ROWB + (sl ^ kswz(r)) * 16;
+                                       (kv_base + (kk < 0 ? 0 : kk)) * ROWB + (sl ^ kswz_r(r)) * 16;
             lds_dma16<NT>(src, st + j * 1024);
         }
 #pragma unroll
@@ -170,7 +186,7 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
             // V row rho, stored slot lane % CPR holds chunk (lane % CPR) ^ vswz(rho)
             const int jv = wave * (NK / NRG) + u;
             const int rho = RPI * jv + lane / CPR;
-            const int chunk = (lane % CPR) ^ vswz<KVDT>(rho);
+            const int chunk = (lane % CPR) ^ vswz_r(rho);
             const int kk = tk.v[u];
             const unsigned char *src = static_cast<const unsigned char *>(cv) +
                                        (kv_base + (kk < 0 ? 0 : kk)) * ROWB + chunk * 16;
@@ -198,8 +214,9 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
     // becomes two bf16 chunks in the bf16 layouts the reads expect (K chunks
     // swizzled by kswz, V chunks by the bf16 vswz).  Threads 0..31 also
     // write the per-key factors: kfac = K scale * scale * log2(e), the mask
-    // bias (0, or -inf for a missing key) and vfac = V scale.  Split in a
-    // read half and a write half, so the reads can be issued early.
+    // bias (0, or -inf for a missing key) and vfac = V scale, and wave 0
+    // whether all 32 keys are present.  Split in a read half and a write
+    // half, so the reads can be issued early.
     constexpr int NCH = 32 * CPR;          // 16-code chunks per K (or V) tile
     constexpr int PER = CONV ? (2 * NCH + NRG * kWave - 1) / (NRG * kWave) : 1;
     struct ConvIn {
@@ -235,18 +252,23 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
                 const bool isv = idx >= NCH;
                 const int ci = isv ? idx - NCH : idx;
                 const int r = ci / CPR, sl = ci % CPR;
-                const int gc = sl ^ (isv ? vswz<DLLM_E4M3>(r) : kswz(r));   // the row's chunk in slot sl
-                const int sw = isv ? vswz<DLLM_BF16>(r) : kswz(r);
+                const int gc = sl ^ (isv ? vswz_r(r) : kswz_r(r));   // the row's chunk in slot sl
+                const int sw = isv ? vswz_b(r) : kswz_b(r);
                 unsigned char *row = cs + (isv ? CTB : 0) + r * BROW;
                 const uint4 w = ci_.w[it];
                 *reinterpret_cast<uint4 *>(row + ((2 * gc) ^ sw) * 16) = e4m3x8_to_bf16(w.x, w.y);
                 *reinterpret_cast<uint4 *>(row + ((2 * gc + 1) ^ sw) * 16) = e4m3x8_to_bf16(w.z, w.w);
             }
+            float *fac = reinterpret_cast<float *>(cs + 2 * CTB);
             if (threadIdx.x < 32) {
-                float *fac = reinterpret_cast<float *>(cs + 2 * CTB);
                 fac[threadIdx.x] = ci_.ks * scale_log2;
                 fac[32 + threadIdx.x] = ci_.present ? 0.f : kNegInf;
                 fac[64 + threadIdx.x] = ci_.vs;
+            }
+            if (wave == 0) {
+                // lanes 32..63 repeat keys 0..31
+                const bool all = __ballot(ci_.present) == ~0ull;
+                if (lane == 0) reinterpret_cast<int *>(fac)[96] = all ? 1 : 0;
             }
         } else {
             (void)cslot; (void)ci_;
@@ -271,6 +293,7 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
         bool full = true;
         uint32_t present = ~0u;
         if (CONV) {
+            full = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int *>(fac)[96]) != 0;
             const float4 *f4 = reinterpret_cast<const float4 *>(fac);
             const float4 a0 = f4[2 * g], a1 = f4[2 * g + 1];
             const float4 b0 = f4[8 + 2 * g], b1 = f4[8 + 2 * g + 1];
@@ -295,7 +318,7 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
             const unsigned char *krow = kb + kappa * BROW;
 #pragma unroll
             for (int c = 0; c < NC; ++c)
-                ka[t][c] = *reinterpret_cast<const uint4 *>(krow + ((c * 4 + g) ^ kswz(kappa)) * 16);
+                ka[t][c] = *reinterpret_cast<const uint4 *>(krow + ((c * 4 + g) ^ kswz_b(kappa)) * 16);
         }
         // V^T operands, read transposed from the row-major bf16 tile now, so
         // the reads are in flight during the first product: local lane j
@@ -306,8 +329,8 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
         for (int dt = 0; dt < NDT; ++dt) {
             const int r0 = 8 * g + (l16 >> 2), r1 = r0 + 4;
             const int cl = 2 * dt + ((l16 & 3) >> 1);
-            const uint2 lo = lds_tr16(vb + r0 * BROW + (cl ^ vswz<DLLM_BF16>(r0)) * 16 + 8 * (l16 & 1));
-            const uint2 hi = lds_tr16(vb + r1 * BROW + (cl ^ vswz<DLLM_BF16>(r1)) * 16 + 8 * (l16 & 1));
+            const uint2 lo = lds_tr16(vb + r0 * BROW + (cl ^ vswz_b(r0)) * 16 + 8 * (l16 & 1));
+            const uint2 hi = lds_tr16(vb + r1 * BROW + (cl ^ vswz_b(r1)) * 16 + 8 * (l16 & 1));
             vop[dt] = make_uint4(lo.x, lo.y, hi.x, hi.y);
         }
         f32x4_t sacc[RT][2];
@@ -325,58 +348,84 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
 
         side();      // independent work (the next tile's widening) under the products
 
-        // scores in base 2 (a missing key gets -inf) and the row maxima of
-        // both row tiles first, so the rare rescale is one branch per tile and
-        // the rest of the tile is one straight block for the scheduler
-        float x[RT][8], mx[RT];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
+        // scores in base 2 relative to the running max, y = x - m, and their
+        // row maxima for both row tiles first, so the rare rescale is one
+        // branch per tile and the rest of the tile is one straight block for
+        // the scheduler.  A tile with every key present folds the subtraction
+        // into the scaling FMA; one with missing keys adds their -inf bias.
+        float y[RT][8], ymx[RT];
+        auto scores = [&](int rt, float *xo) {
             const f32x4_t s0 = sacc[rt][0], s1 = sacc[rt][1];
             const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
             if (CONV) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[rt][e] = fmaf(sv[e], kfac[e], kbias[e]);
+                for (int e = 0; e < 8; ++e) xo[e] = fmaf(sv[e], kfac[e], kbias[e]);
             } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[rt][e] = sv[e] * scale_log2;
+                for (int e = 0; e < 8; ++e) xo[e] = sv[e] * scale_log2;
                 if (!full) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
-                        if (!((present >> (8 * g + e)) & 1u)) x[rt][e] = kNegInf;
+                        if (!((present >> (8 * g + e)) & 1u)) xo[e] = kNegInf;
                 }
             }
-            float v = fmaxf(fmaxf(x[rt][0], x[rt][1]), fmaxf(x[rt][2], x[rt][3]));
-            v = fmaxf(v, fmaxf(fmaxf(x[rt][4], x[rt][5]), fmaxf(x[rt][6], x[rt][7])));
-            mx[rt] = group4_max(v);
+        };
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            if (full) {
+                const f32x4_t s0 = sacc[rt][0], s1 = sacc[rt][1];
+                const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[rt][e] = fmaf(sv[e], CONV ? kfac[e] : scale_log2, -m[rt]);
+            } else {
+                float x[8];
+                scores(rt, x);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[rt][e] = x[e] - m[rt];
+            }
+            float v = fmaxf(fmaxf(y[rt][0], y[rt][1]), y[rt][2]);
+            v = fmaxf(fmaxf(v, y[rt][3]), y[rt][4]);
+            v = fmaxf(fmaxf(v, y[rt][5]), y[rt][6]);
+            v = fmaxf(v, y[rt][7]);
+            ymx[rt] = group4_max(v);
         }
         // the reference max moves only when a tile's max exceeds it by more
-        // than kLazy, so the O rescale is rare
+        // than kLazy, so the O rescale is rare.  The rescale recomputes the
+        // scores from the products: y is relative to the old max, which is
+        // still the finite start value before a row's first key.
         bool grow[RT], any = false;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            grow[rt] = mx[rt] > m[rt] + kLazy;
+            grow[rt] = ymx[rt] > kLazy;
             any = any || grow[rt];
         }
         if (__ballot(any)) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
                 if (grow[rt]) {
-                    const float corr = __builtin_amdgcn_exp2f(m[rt] - mx[rt]);
+                    float x[8];
+                    scores(rt, x);
+                    float v = x[0];
+#pragma unroll
+                    for (int e = 1; e < 8; ++e) v = fmaxf(v, x[e]);
+                    const float mx = group4_max(v);
+                    const float corr = __builtin_amdgcn_exp2f(m[rt] - mx);
                     l[rt] *= corr;
 #pragma unroll
                     for (int dt = 0; dt < NDT; ++dt) o[dt][rt] *= corr;
-                    m[rt] = mx[rt];
+                    m[rt] = mx;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) y[rt][e] = x[e] - mx;
                 }
             }
         }
         Frag pf[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            const float mref = m[rt];
             float p[8], ps = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                p[e] = __builtin_amdgcn_exp2f(x[rt][e] - mref);
+                p[e] = __builtin_amdgcn_exp2f(y[rt][e]);
                 ps += p[e];
             }
             l[rt] += ps;
