@@ -112,6 +112,10 @@ def lib():
         L.oracle_evict_by_confidence.argtypes = [i32, i32, P, P, P, i32, P, P, P, P, P]
         L.oracle_evict_by_confidence.restype = i32
         L.oracle_stability_step.restype = i32
+        L.oracle_parallel_width.argtypes = [i32, i32, i32, i32]
+        L.oracle_parallel_width.restype = i32
+        L.oracle_self_verify.argtypes = [i32, i32, P, i32, P, P, i32, dbl, P, P, P, P, P, P, P, P]
+        L.oracle_self_verify.restype = i32
         _lib = L
     return _lib
 
@@ -488,3 +492,29 @@ def evict_by_confidence(state: StabilityState, conf, quota, pos, mask):
                                             _ptr(mask), _ptr(next_pos), _ptr(count), _ptr(evicted)),
            "evict_by_confidence")
     return dict(next_pos=next_pos, count=count, evicted=evicted)
+
+
+def parallel_width(w_early: int, w_late: int, T: int, step: int) -> int:
+    return lib().oracle_parallel_width(int(w_early), int(w_late), int(T), int(step))
+
+
+def self_verify(L: int, dec_pos, p_marg, p_joint, W: int, tau: float, mask, stable=None, cached=None):
+    """Self-verification of one step's parallel decodes.  dec_pos int32 [B, n]
+    (-1 padding), p_marg float32 [B, n], p_joint float32 [B, n, W-1]; mask,
+    stable, cached uint8 [B, L] are updated in place.  Returns dict(rollback,
+    next_pos, count, n_rollback, rb_pos)."""
+    dec_pos = np.ascontiguousarray(dec_pos, dtype=np.int32)
+    B, n = dec_pos.shape
+    p_marg = np.ascontiguousarray(p_marg, dtype=np.float32).reshape(B, n)
+    p_joint = np.ascontiguousarray(p_joint, dtype=np.float32).reshape(B, n, W - 1)
+    for a in (mask, stable, cached):
+        assert a is None or (a.dtype == np.uint8 and a.flags["C_CONTIGUOUS"] and a.shape == (B, L))
+    rollback = np.zeros((B, L), dtype=np.uint8)
+    next_pos = np.zeros((B, L), dtype=np.int32)
+    count = np.zeros(B, dtype=np.int32)
+    n_rb = np.zeros(B, dtype=np.int32)
+    rb_pos = np.zeros((B, n), dtype=np.int32)
+    _check(lib().oracle_self_verify(B, L, _ptr(dec_pos), n, _ptr(p_marg), _ptr(p_joint), int(W), float(tau),
+                                    _ptr(rollback), _ptr(mask), _ptr(stable), _ptr(cached), _ptr(next_pos),
+                                    _ptr(count), _ptr(n_rb), _ptr(rb_pos)), "self_verify")
+    return dict(rollback=rollback, next_pos=next_pos, count=count, n_rollback=n_rb, rb_pos=rb_pos)

@@ -834,3 +834,88 @@ int oracle_stability_step(int B, int L, int step, const int32_t *pos, int n,
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* N4: self-verification of tokens decoded in parallel                       */
+/* ------------------------------------------------------------------------ */
+
+/* [Flash, 4.1]: many positions per step early in the trajectory (8-16 on the
+ * page), few late (2-4).  The reading: a linear ramp in whole positions from
+ * w_early at step 0 to w_late at step T-1 (integer division, rounding toward
+ * w_early), w_late afterwards; T <= 1 keeps w_late. */
+int oracle_parallel_width(int w_early, int w_late, int T, int step)
+{
+    int s;
+    if (T <= 1) return w_late;
+    s = step < T - 1 ? step : T - 1;
+    return w_early - (w_early - w_late) * s / (T - 1);
+}
+
+/* [Flash, 4.2-4.3]: for two positions decoded in the same step, at most W-1
+ * apart (a window of W consecutive positions), the conflict score is the
+ * pair's joint probability over the product of the two marginals; a score
+ * below tau is a conflict (a zero product never is).  Every position decoded
+ * this step that lies between the two (both included) is withdrawn: it is
+ * regenerated serially, so its stable flag and its cached K/V are dropped and
+ * it joins the next step's mask.
+ *   dec_pos [B, n]: positions decoded this step (-1 padding)
+ *   p_marg  [B, n]: the probability of each decoded token
+ *   p_joint [B, n, W-1]: entry (j, d-1) is P(token at dec_pos[j], token at
+ *                        dec_pos[j]+d), read when that position is decoded too
+ * Outputs: rollback [B, L] (1 = withdrawn), n_rollback [B], rb_pos [B, n]
+ * (withdrawn positions ascending, -1 after); mask |= rollback, stable and
+ * cached (either may be NULL) cleared at withdrawn positions; next_pos and
+ * count recompacted from the mask. */
+int oracle_self_verify(int B, int L, const int32_t *dec_pos, int n, const float *p_marg,
+                       const float *p_joint, int W, double tau, uint8_t *rollback,
+                       uint8_t *mask, uint8_t *stable, uint8_t *cached, int32_t *next_pos,
+                       int32_t *count, int32_t *n_rollback, int32_t *rb_pos)
+{
+    int b;
+    if (B <= 0 || L <= 0 || n < 0 || W < 2 || !(tau >= 0.0)) return -1;
+    for (b = 0; b < B; ++b) {
+        int64_t row = (int64_t)b * L;
+        const int32_t *dp = dec_pos + (int64_t)b * n;
+        const float *pm = p_marg + (int64_t)b * n;
+        int j, k, d, i, c, nr;
+        for (j = 0; j < n; ++j)
+            if (dp[j] < -1 || dp[j] >= L) return -1;
+        for (i = 0; i < L; ++i) rollback[row + i] = 0;
+        for (j = 0; j < n; ++j) {
+            if (dp[j] < 0) continue;
+            for (d = 1; d < W; ++d) {
+                int partner = -1;
+                for (k = 0; k < n; ++k)
+                    if (dp[k] == dp[j] + d) { partner = k; break; }
+                if (partner < 0) continue;
+                {
+                    double prod = (double)pm[j] * (double)pm[partner];
+                    double joint = (double)p_joint[((int64_t)b * n + j) * (W - 1) + (d - 1)];
+                    if (prod > 0.0 && joint / prod < tau) {
+                        /* withdraw every decoded position in [dp[j], dp[j] + d] */
+                        for (k = 0; k < n; ++k)
+                            if (dp[k] >= dp[j] && dp[k] <= dp[j] + d) rollback[row + dp[k]] = 1;
+                    }
+                }
+            }
+        }
+        nr = 0;
+        for (i = 0; i < L; ++i) {
+            if (!rollback[row + i]) continue;
+            mask[row + i] = 1;
+            if (stable) stable[row + i] = 0;
+            if (cached) cached[row + i] = 0;
+            if (rb_pos && nr < n) rb_pos[(int64_t)b * n + nr] = i;
+            ++nr;
+        }
+        if (rb_pos)
+            for (k = nr; k < n; ++k) rb_pos[(int64_t)b * n + k] = -1;
+        if (n_rollback) n_rollback[b] = nr;
+        c = 0;
+        for (i = 0; i < L; ++i)
+            if (mask[row + i]) next_pos[row + c++] = i;
+        count[b] = c;
+        for (i = c; i < L; ++i) next_pos[row + i] = -1;
+    }
+    return 0;
+}

@@ -181,6 +181,15 @@ int oracle_evict_by_confidence(int B, int L, const float *conf, const int32_t *q
                                const int32_t *pos, int n, uint8_t *cached, uint8_t *mask,
                                int32_t *next_pos, int32_t *count, int32_t *evicted);
 
+/* N4 [Flash, 4.1-4.3]: the parallel width ramps from w_early at step 0 to
+ * w_late at step T-1; the self-verification of a step's parallel decodes and
+ * the withdrawal of conflicting spans: see oracle.c. */
+int oracle_parallel_width(int w_early, int w_late, int T, int step);
+int oracle_self_verify(int B, int L, const int32_t *dec_pos, int n, const float *p_marg,
+                       const float *p_joint, int W, double tau, uint8_t *rollback,
+                       uint8_t *mask, uint8_t *stable, uint8_t *cached, int32_t *next_pos,
+                       int32_t *count, int32_t *n_rollback, int32_t *rb_pos);
+
 int oracle_stability_step(int B, int L, int step, const int32_t *pos, int n,
                           const int32_t *argmax, const float *maxprob,
                           const float *entropy,
