@@ -23,6 +23,7 @@ __all__ = [
     "dllm_vocab_stats",
     "dllm_vocab_stats_workspace", "dllm_stability_reset", "dllm_stability_mask",
     "dllm_refresh_interval", "dllm_cache_quotas", "dllm_evict_by_confidence",
+    "dllm_parallel_width", "dllm_self_verify",
 ]
 
 F32, BF16, E4M3 = 0, 1, 2
@@ -118,6 +119,12 @@ EXPORTS = {
                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "dllm_parallel_width": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+    "dllm_self_verify": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_double,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
 }
 
 _lib = None
@@ -502,3 +509,37 @@ def dllm_evict_by_confidence(st: StabilityState, quota: torch.Tensor, pos: Optio
                                         _dev(evicted, "evicted") if evicted is not None else None, _stream())
     _check(rc, "dllm_evict_by_confidence")
     return st
+
+
+def dllm_parallel_width(w_early: int, w_late: int, T: int, step: int) -> int:
+    """Positions decoded in parallel at a step: w_early falling to w_late."""
+    return lib().dllm_parallel_width(int(w_early), int(w_late), int(T), int(step))
+
+
+def dllm_self_verify(st: StabilityState, dec_pos: torch.Tensor, p_marg: torch.Tensor,
+                     p_joint: torch.Tensor, W: int, tau: float = 0.5, rollback: Optional[torch.Tensor] = None,
+                     n_rollback: Optional[torch.Tensor] = None, rb_pos: Optional[torch.Tensor] = None,
+                     update_stable: bool = True, update_cached: bool = True):
+    """Conflict check of the step's parallel decodes (dec_pos [B, n] int32,
+    ascending then -1; p_marg [B, n] and p_joint [B, n, W-1] float32).
+    Withdrawn positions go into st.mask (and out of st.stable / st.cached);
+    st.next_pos / st.count are compacted again.  Returns the [B, L] u8
+    withdrawal flags."""
+    B, n = dec_pos.shape
+    if dec_pos.dtype != torch.int32 or B != st.B:
+        raise ValueError("dec_pos: [B, n] int32")
+    if p_marg.dtype != torch.float32 or p_marg.numel() != B * n:
+        raise ValueError("p_marg: [B, n] float32")
+    if p_joint.dtype != torch.float32 or p_joint.numel() != B * n * (W - 1):
+        raise ValueError("p_joint: [B, n, W-1] float32")
+    if rollback is None:
+        rollback = torch.empty((st.B, st.L), dtype=torch.uint8, device=st.mask.device)
+    rc = lib().dllm_self_verify(st.B, st.L, _dev(dec_pos, "dec_pos"), n, _dev(p_marg, "p_marg"),
+                                _dev(p_joint, "p_joint"), int(W), float(tau), _dev(rollback, "rollback"),
+                                _dev(st.mask, "mask"), _dev(st.stable, "stable") if update_stable else None,
+                                _dev(st.cached, "cached") if update_cached else None,
+                                _dev(st.next_pos, "next_pos"), _dev(st.count, "count"),
+                                _dev(n_rollback, "n_rollback") if n_rollback is not None else None,
+                                _dev(rb_pos, "rb_pos") if rb_pos is not None else None, _stream())
+    _check(rc, "dllm_self_verify")
+    return rollback

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libdllm.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["api.hip", "scatter.hip", "attention.hip", "attention_shared.hip", "vocab_stats.hip",
-           "stability.hip", "fp8_ffn.hip"]
+           "stability.hip", "fp8_ffn.hip", "verify.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -361,4 +361,23 @@ int dllm_evict_by_confidence(int B, int L, const float *conf, const int32_t *quo
                         static_cast<hipStream_t>(stream));
 }
 
+int dllm_parallel_width(int w_early, int w_late, int T, int step) {
+    if (T <= 1) return w_late;
+    const int st = step < T - 1 ? (step < 0 ? 0 : step) : T - 1;
+    return w_early - (w_early - w_late) * st / (T - 1);
+}
+
+int dllm_self_verify(int B, int L, const int32_t *dec_pos, int n, const float *p_marg,
+                     const float *p_joint, int W, double tau, uint8_t *rollback, uint8_t *mask,
+                     uint8_t *stable, uint8_t *cached, int32_t *next_pos, int32_t *count,
+                     int32_t *n_rollback, int32_t *rb_pos, void *stream) {
+    if (B < 1 || L < 1 || n < 0 || n > L) return DLLM_ESHAPE;
+    if (B > 65535 || L > 131072) return DLLM_ERANGE;
+    if (W < 2 || W > 8 || !(tau >= 0.0)) return DLLM_EINVAL;
+    if (n > 0 && (!dec_pos || !p_marg || !p_joint)) return DLLM_EINVAL;
+    if (!rollback || !mask || !next_pos || !count) return DLLM_EINVAL;
+    return launch_self_verify(B, L, dec_pos, n, p_marg, p_joint, W, tau, rollback, mask, stable, cached,
+                              next_pos, count, n_rollback, rb_pos, static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

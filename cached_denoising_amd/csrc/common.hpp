@@ -124,6 +124,10 @@ int launch_attention(const dllm_kv_cache &c, const AttnPlan &p, const void *q, i
                      int b, const int32_t *key_idx, int n_keys, float scale, const AttnMemo &memo,
                      void *out, int out_dtype, float *lse, void *ws, hipStream_t s);
 
+int launch_self_verify(int B, int L, const int32_t *dec_pos, int n, const float *p_marg,
+                       const float *p_joint, int W, double tau, uint8_t *rollback, uint8_t *mask,
+                       uint8_t *stable, uint8_t *cached, int32_t *next_pos, int32_t *count,
+                       int32_t *n_rollback, int32_t *rb_pos, hipStream_t s);
 int launch_evict(int B, int L, const float *conf, const int32_t *quota, const int32_t *pos, int n,
                  uint8_t *cached, uint8_t *mask, int32_t *next_pos, int32_t *count, int32_t *evicted,
                  hipStream_t s);

@@ -20,6 +20,8 @@
  *                          window expansion -> next step's compute mask
  *   dllm_evict_by_confidence / dllm_cache_quotas / dllm_refresh_interval
  *                          budgeted cache and refresh schedule
+ *   dllm_self_verify / dllm_parallel_width
+ *                          conflict check of a step's parallel decodes
  *
  * Page titles cited below (section numbers are the pages' own):
  *   [SWD]     Stable Window Decoding blog page on temporal stability in
@@ -421,6 +423,44 @@ int dllm_cache_quotas(int B, const int32_t *len, int64_t budget, double min_frac
 int dllm_evict_by_confidence(int B, int L, const float *conf, const int32_t *quota,
                              const int32_t *pos, int n, uint8_t *cached, uint8_t *mask,
                              int32_t *next_pos, int32_t *count, int32_t *evicted, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * dllm_parallel_width -- how many positions a step decodes in parallel
+ * [Flash, 4.1: many early in the trajectory (8-16 on the page), few late
+ * (2-4)]: w_early at step 0 falling linearly to w_late at step T-1 (integer
+ * division), w_late afterwards; T <= 1 gives w_late.  Host only.
+ * ------------------------------------------------------------------------- */
+int dllm_parallel_width(int w_early, int w_late, int T, int step);
+
+/* ---------------------------------------------------------------------------
+ * dllm_self_verify -- check the tokens a step decoded in parallel and
+ * withdraw conflicting spans [Flash, 4.2 and 4.3].  Per sequence b, for two
+ * decoded positions a < c with c - a < W, the conflict score is
+ * P(tok_a, tok_c) / (P(tok_a) P(tok_c)), in float64; a score below tau (0.5
+ * on the page) is a conflict, a zero product never is.  Every position
+ * decoded this step in [a, c] is withdrawn: rollback = 1, mask = 1, stable =
+ * 0 and cached = 0 there (it is regenerated serially and its K/V
+ * recomputed); next_pos / count are compacted from the mask again.
+ *   dec_pos   [B, n] int32 device: the positions decoded this step,
+ *             ascending, then -1 padding (as a compacted mask lists them)
+ *   p_marg    [B, n] float32 device: the probability of each decoded token
+ *   p_joint   [B, n, W-1] float32 device: entry (j, d-1) is the joint
+ *             probability of the tokens at dec_pos[j] and dec_pos[j] + d,
+ *             read only when that position was decoded too (the pages leave
+ *             its computation to the model's verification pass)
+ *   W         window of positions, 2..8 (3-5 on the page); tau >= 0
+ *   rollback  [B, L] u8 device out; mask [B, L] u8 in/out; stable, cached
+ *             [B, L] u8 in/out or NULL; next_pos [B, L], count [B] out
+ *   n_rollback [B] int32 out or NULL; rb_pos [B, n] int32 out or NULL: the
+ *             withdrawn positions ascending, -1 after
+ * A sequence whose list is not ascending (or has a position outside [0, L),
+ * or padding before a position) is left unchanged with count = -1 (and
+ * n_rollback = -1).  Limits: L <= 131072, B <= 65535.
+ * ------------------------------------------------------------------------- */
+int dllm_self_verify(int B, int L, const int32_t *dec_pos, int n, const float *p_marg,
+                     const float *p_joint, int W, double tau, uint8_t *rollback, uint8_t *mask,
+                     uint8_t *stable, uint8_t *cached, int32_t *next_pos, int32_t *count,
+                     int32_t *n_rollback, int32_t *rb_pos, void *stream);
 
 #ifdef __cplusplus
 }

@@ -858,7 +858,7 @@ int oracle_parallel_width(int w_early, int w_late, int T, int step)
  * this step that lies between the two (both included) is withdrawn: it is
  * regenerated serially, so its stable flag and its cached K/V are dropped and
  * it joins the next step's mask.
- *   dec_pos [B, n]: positions decoded this step (-1 padding)
+ *   dec_pos [B, n]: positions decoded this step, ascending, then -1 padding
  *   p_marg  [B, n]: the probability of each decoded token
  *   p_joint [B, n, W-1]: entry (j, d-1) is P(token at dec_pos[j], token at
  *                        dec_pos[j]+d), read when that position is decoded too
@@ -877,9 +877,14 @@ int oracle_self_verify(int B, int L, const int32_t *dec_pos, int n, const float 
         int64_t row = (int64_t)b * L;
         const int32_t *dp = dec_pos + (int64_t)b * n;
         const float *pm = p_marg + (int64_t)b * n;
-        int j, k, d, i, c, nr;
-        for (j = 0; j < n; ++j)
-            if (dp[j] < -1 || dp[j] >= L) return -1;
+        int j, k, d, i, c, nr, nv = 0;
+        /* the decoded positions ascending, then -1 padding (the order in
+         * which a step's compacted mask lists them) */
+        while (nv < n && dp[nv] >= 0) ++nv;
+        for (j = 0; j < n; ++j) {
+            if (j < nv && (dp[j] >= L || (j + 1 < nv && dp[j + 1] <= dp[j]))) return -1;
+            if (j >= nv && dp[j] != -1) return -1;
+        }
         for (i = 0; i < L; ++i) rollback[row + i] = 0;
         for (j = 0; j < n; ++j) {
             if (dp[j] < 0) continue;

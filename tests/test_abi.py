@@ -28,7 +28,8 @@ def test_header_declares_the_boundary():
               "dllm_stability_mask", "dllm_sink_rolling_map", "dllm_stability_reset",
               "dllm_block_attention_workspace", "dllm_vocab_stats_workspace", "dllm_status_str",
               "dllm_facache_maps", "dllm_facache_merge", "dllm_facache_merge_workspace",
-              "dllm_evict_by_confidence", "dllm_cache_quotas", "dllm_refresh_interval"]:
+              "dllm_evict_by_confidence", "dllm_cache_quotas", "dllm_refresh_interval",
+              "dllm_self_verify", "dllm_parallel_width"]:
         assert n in names
 
 
@@ -72,6 +73,12 @@ def test_host_validation_without_gpu(dl):
     assert L.dllm_evict_by_confidence(1, 8, 16, 16, 16, 9, 16, 16, 16, 16, None, None) == -3
     assert L.dllm_evict_by_confidence(1, 1 << 18, 16, 16, None, 0, 16, 16, 16, 16, None, None) == -5
     assert L.dllm_evict_by_confidence(1, 8, None, 16, None, 8, 16, 16, 16, 16, None, None) == -1
+    # self-verification: window, threshold, shapes and limits before any launch
+    sv = lambda B, Ln, n, W, tau, dp=16: L.dllm_self_verify(B, Ln, dp, n, 16, 16, W, tau, 16, 16, None, None,
+                                                            16, 16, None, None, None)
+    assert sv(1, 8, 2, 1, 0.5) == -1 and sv(1, 8, 2, 9, 0.5) == -1 and sv(1, 8, 2, 3, -0.5) == -1
+    assert sv(1, 8, 2, 3, float("nan")) == -1 and sv(1, 8, 9, 3, 0.5) == -3 and sv(0, 8, 2, 3, 0.5) == -3
+    assert sv(1, 1 << 18, 2, 3, 0.5) == -5 and sv(1, 8, 2, 3, 0.5, dp=None) == -1
     assert L.dllm_sink_rolling_map(1, 10, 4, 8, 16, 16, 11, None) == -3                     # n_keys < S+R
     assert L.dllm_facache_maps(1, 8, 8, 16, 16, 16, None) == -3                             # block = L
     assert L.dllm_facache_maps(1, 8, 2, None, 16, 16, None) == -1
@@ -113,6 +120,9 @@ def test_host_policies_match_the_oracle(dl, orc):
     import numpy as np
     for T in list(range(0, 130)) + [400, 4096]:
         assert dl.dllm_refresh_interval(T) == orc.refresh_interval(T), T
+    for w0, w1, T in [(16, 2, 64), (8, 4, 10), (4, 4, 3), (16, 2, 1)]:
+        for step in range(T + 3):
+            assert dl.dllm_parallel_width(w0, w1, T, step) == orc.parallel_width(w0, w1, T, step)
     rng = np.random.default_rng(3)
     for trial in range(200):
         lens = rng.integers(0, 300, size=int(rng.integers(1, 9)))

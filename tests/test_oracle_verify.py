@@ -145,3 +145,8 @@ def test_bad_arguments(orc):
     with pytest.raises(ValueError):
         orc.self_verify(8, np.array([[1]], np.int32), [[0.5]], np.zeros((1, 1, 0)), 1, 0.5,
                         np.zeros((1, 8), np.uint8))
+    # the positions come ascending, padding only after them
+    for bad in ([3, 2], [2, 2], [-1, 4], [1, -2]):
+        with pytest.raises(ValueError):
+            orc.self_verify(8, np.array([bad], np.int32), [[0.5, 0.5]], np.zeros((1, 2, 2)), 3, 0.5,
+                            np.zeros((1, 8), np.uint8))
