@@ -29,6 +29,13 @@ guarantee per request).  The step statistics are computed once, before the
 timed steps.  The eviction alone is also timed at the long-context shape
 (4 x 32768, quota 8192).
 
+With --config verify a step is the self-verification of one step's
+parallel decodes on the vocab sweep's 64 x 512 positions: 16 positions
+decoded per sequence (the early parallel width), a window of 4 positions,
+tau 0.5, seeded marginals and pair joints with planted conflicts.  The same
+kernel is also timed at the long-context shape (4 x 32768, its 64-position
+block decoded at once).
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config gpt2]
 """
 from __future__ import annotations
@@ -56,7 +63,8 @@ KERNEL_SRC = {"vocab_stats": ["vocab_stats.hip"],
               "facache_merge": ["attention.hip", "attention_shared.hip", "attn_common.hpp"],
               "scatter": ["scatter.hip"], "stability": ["stability.hip"],
               "fp8_addnorm": ["fp8_ffn.hip", "common.hpp"], "fp8_gateup": ["fp8_ffn.hip", "common.hpp"],
-              "fp8_ffout": ["fp8_ffn.hip", "common.hpp"], "evict": ["stability.hip"]}
+              "fp8_ffout": ["fp8_ffn.hip", "common.hpp"], "evict": ["stability.hip"],
+              "verify": ["verify.hip"]}
 
 
 def parse():
@@ -65,7 +73,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="gpt2",
-                    choices=["gpt2", "llada", "vocab", "longctx", "facache", "ffn", "policies"])
+                    choices=["gpt2", "llada", "vocab", "longctx", "facache", "ffn", "policies", "verify"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from Python instead of replaying a captured graph")
@@ -414,6 +422,101 @@ class PolicyStep:
         return 1000.0 * e0.elapsed_time(e1) / reps
 
 
+def verify_inputs(B, L, n, Wn, seed, dev, block_at_end=False):
+    """seeded decodes: n ascending positions per sequence in a cluster,
+    marginals U(0.3, 1), pair joints = marginal^2 x a log-normal factor, a
+    tenth of them scaled below the conflict threshold"""
+    import torch
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    if block_at_end:
+        dec = torch.arange(L - n, L, dtype=torch.int32).repeat(B, 1)
+    else:
+        starts = torch.randint(0, L - 2 * n + 1, (B, 1), generator=g)
+        picks = torch.rand((B, 2 * n), generator=g).argsort(dim=1)[:, :n].sort(dim=1).values
+        dec = (starts + picks).to(torch.int32)
+    pm = 0.3 + 0.7 * torch.rand((B, n), generator=g)
+    fac = torch.exp(0.4 * torch.randn((B, n, Wn - 1), generator=g))
+    fac = torch.where(torch.rand((B, n, Wn - 1), generator=g) < 0.1, fac * 0.3, fac)
+    pj = pm[:, :, None] * pm[:, :, None] * fac
+    return dec.to(dev), pm.float().to(dev), pj.float().to(dev)
+
+
+class VerifyStep:
+    """Self-verification of one step's parallel decodes."""
+
+    def __init__(self, D, W, cfg, dev):
+        import torch
+        self.D, self.W, self.cfg = D, W, cfg
+        self.B, self.L, self.n, self.Wn, self.tau = cfg.B, cfg.L, 16, 4, 0.5
+        self.dec, self.pm, self.pj = verify_inputs(self.B, self.L, self.n, self.Wn, 4242, dev)
+        self.st = D.StabilityState(self.B, self.L, 2, device=dev)
+        self.st.mask.zero_()
+        self.st.stable.fill_(1)
+        self.st.cached.fill_(1)
+        self.rollback = torch.empty((self.B, self.L), dtype=torch.uint8, device=dev)
+        self.nrb = torch.zeros(self.B, dtype=torch.int32, device=dev)
+        self.rbp = torch.empty((self.B, self.n), dtype=torch.int32, device=dev)
+        self.facache = False
+        self.attn_split = False
+
+    def kernels(self):
+        return ["verify"]
+
+    def run(self, events=None):
+        if events is not None:
+            events["verify"][0].record()
+        self.D.dllm_self_verify(self.st, self.dec, self.pm, self.pj, self.Wn, self.tau, rollback=self.rollback,
+                                n_rollback=self.nrb, rb_pos=self.rbp)
+        if events is not None:
+            events["verify"][1].record()
+
+    def algorithmic_bytes(self):
+        B, L, n, Wn = self.B, self.L, self.n, self.Wn
+        # decodes in (positions, marginals, joints); withdrawal flags out, the
+        # mask read, next positions out; counts
+        return {"verify": B * (n * (8 + 4 * (Wn - 1)) + L * (1 + 1 + 4) + 12)}
+
+    def algorithmic_flops(self):
+        return {}
+
+    def longctx_us(self, dev, reps=20):
+        """the same call at the long-context shape: 4 x 32768, the 64-position
+        block at the end decoded at once"""
+        import torch
+        c = self.W.CONFIGS["longctx"]
+        dec, pm, pj = verify_inputs(c.B, c.L, c.b, self.Wn, 4243, dev, block_at_end=True)
+        st = self.D.StabilityState(c.B, c.L, 2, device=dev)
+        st.mask.zero_()
+        rb = torch.empty((c.B, c.L), dtype=torch.uint8, device=dev)
+        run = lambda: self.D.dllm_self_verify(st, dec, pm, pj, self.Wn, self.tau, rollback=rb)
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        return 1000.0 * e0.elapsed_time(e1) / reps
+
+
+def cpu_baseline_verify(step, W):
+    """The oracle's self-verification on the whole step."""
+    import numpy as np
+
+    import oracle
+    threads = oracle.set_threads(int(os.environ.get("OMP_NUM_THREADS", min(16, os.cpu_count() or 1))))
+    dec, pm, pj = (t.cpu().numpy() for t in (step.dec, step.pm, step.pj))
+    reps = 20
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        mask = np.zeros((step.B, step.L), np.uint8)
+        oracle.self_verify(step.L, dec, pm, pj, step.Wn, step.tau, mask)
+    dt = (time.perf_counter() - t0) / reps
+    return {"value": 1.0 / dt, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} whole steps ({step.B} x {step.L} positions, {step.n} decoded each)"}
+
+
 def cpu_baseline_policies(step, W):
     """The oracle's stability step and eviction on the whole step (the
     bench's shape is small enough)."""
@@ -540,11 +643,14 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
-    cfg = W.CONFIGS[{"facache": "llada", "ffn": "llada", "policies": "vocab"}.get(args.config, args.config)]
+    cfg = W.CONFIGS[{"facache": "llada", "ffn": "llada", "policies": "vocab", "verify": "vocab"}.get(
+        args.config, args.config)]
     if args.config == "ffn":
         step = FfnStep(D, W, dev)
     elif args.config == "policies":
         step = PolicyStep(D, W, cfg, dev)
+    elif args.config == "verify":
+        step = VerifyStep(D, W, cfg, dev)
     else:
         step = Step(D, W, cfg, dev, facache=args.config == "facache")
     for _ in range(args.warmup):
@@ -631,12 +737,17 @@ def main():
     if args.config == "policies":
         extra = {"evict_longctx_us": round(step.evict_longctx_us(W, dev), 2),
                  "refresh_every": step.refresh}
+    if args.config == "verify":
+        extra = {"verify_longctx_us": round(step.longctx_us(dev), 2),
+                 "withdrawn_per_step": int(step.nrb.sum().item())}
     if args.no_cpu_baseline:
         cpu = None
     elif args.config == "ffn":
         cpu = cpu_baseline_ffn(step, W)
     elif args.config == "policies":
         cpu = cpu_baseline_policies(step, W)
+    elif args.config == "verify":
+        cpu = cpu_baseline_verify(step, W)
     else:
         cpu = cpu_baseline(step, D, W, cfg)
     desc = {
@@ -656,15 +767,20 @@ def main():
                     "window radius ramped 0 -> 3 over 64 steps and a full refresh every 6 steps, then "
                     "confidence-ordered eviction to per-request quotas (half the positions, 20% "
                     "guaranteed each)",
+        "verify": "self-verification of one step's parallel decodes on the vocab sweep's 64 x 512 "
+                  "positions: 16 decoded per sequence, window 4, tau 0.5, conflicts planted in a tenth "
+                  "of the pair joints",
         "facache": "LLaDA-8B-shaped first-layer attention of a later step of a block, with FACache: "
                    "B=16, L=2048, 32 heads x d128, bf16 K/V, block 32 (scatter, block queries over "
                    "all keys, 2016 outside queries from their memo over the block keys)",
     }[args.config]
     metric = {"facache": "first-layer attention steps/sec with FACache (scatter + block attention + memo merge)",
               "ffn": "FP8 FFN steps/sec (add & norm + quant, Gate-Up + SwiGLU + quant, FF-Out)",
-              "policies": "decode-policy steps/sec (stability mask with ramp + refresh, quota eviction)"}.get(
+              "policies": "decode-policy steps/sec (stability mask with ramp + refresh, quota eviction)",
+              "verify": "self-verification steps/sec (conflict scores, withdrawal, mask recompaction)"}.get(
         args.config, METRIC)
-    dtype = {"ffn": "e4m3 x e4m3 -> f32 (E8M0 group scales)", "policies": "f64 decisions, f32 keys"}.get(
+    dtype = {"ffn": "e4m3 x e4m3 -> f32 (E8M0 group scales)", "policies": "f64 decisions, f32 keys",
+             "verify": "f64 scores"}.get(
         args.config, "bf16")
     line = {
         "metric": metric, "value": round(1000.0 / ms, 2), "unit": "steps/s", "n_gpus": 1,

@@ -67,6 +67,31 @@ __device__ __forceinline__ uint32_t e4m3_rne(float q) {
 // cross-lane helpers on a 64-wide wavefront
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
 __device__ __forceinline__ int shfl_xor_i(int v, int m) { return __shfl_xor(v, m, kWave); }
+// the lanes of a wave below this one, as a ballot mask
+__device__ __forceinline__ uint64_t lanes_below(int lane) { return lane ? (~0ull) >> (64 - lane) : 0ull; }
+
+// Exclusive prefix over a workgroup of NW waves of one int per thread
+// (thread order), and the total.  Uses `tmp` (NW ints, not to be reused by
+// the caller without a barrier); contains one barrier.
+template <int NW>
+__device__ __forceinline__ int block_exclusive_scan(int v, int lane, int wave, int *tmp, int &total) {
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int t = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += t;
+    }
+    if (lane == kWave - 1) tmp[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+    for (int w = 0; w < NW; ++w) {
+        const int t = tmp[w];
+        before += w < wave ? t : 0;
+        total += t;
+    }
+    return before + incl - v;
+}
 
 __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ constexpr int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -247,28 +247,6 @@ constexpr int kEvictKeysLds = 32768;
 constexpr int kEvictUnroll = 8;     // positions per thread in flight in the load pass
 constexpr int kPassUnroll = 4;      // positions per thread per step of the LDS passes
 
-// Exclusive prefix over the workgroup of one int per thread (thread order),
-// and the total.  Uses `tmp` (kWaves ints, not to be reused by the caller
-// without a barrier); contains one barrier.
-__device__ __forceinline__ int block_exclusive_scan(int v, int lane, int wave, int *tmp, int &total) {
-    int incl = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int t = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += t;
-    }
-    if (lane == kWave - 1) tmp[wave] = incl;
-    __syncthreads();
-    int before = 0;
-    total = 0;
-    for (int w = 0; w < kWaves; ++w) {
-        const int t = tmp[w];
-        before += w < wave ? t : 0;
-        total += t;
-    }
-    return before + incl - v;
-}
-
 // The lowest r set bits of x (r >= 0).
 __device__ __forceinline__ uint32_t lowest_set_bits(uint32_t x, int r) {
     uint32_t y = x;
@@ -377,7 +355,7 @@ __global__ __launch_bounds__(kThreads) void evict_kernel(
         }
     }
     int nc_total;
-    block_exclusive_scan(nc, lane, wave, tmp[0], nc_total);   // also: keys and hist settled
+    block_exclusive_scan<kWaves>(nc, lane, wave, tmp[0], nc_total);   // also: keys and hist settled
     nc = nc_total;
     const bool select = q >= 0 && nc > q;
 
@@ -434,7 +412,7 @@ __global__ __launch_bounds__(kThreads) void evict_kernel(
         int n_at = 0;
         for (int w = w_lo; w < w_hi; ++w) n_at += __popc(abits[w]);
         int unused;
-        int at_off = block_exclusive_scan(n_at, lane, wave, tmp[1], unused);
+        int at_off = block_exclusive_scan<kWaves>(n_at, lane, wave, tmp[1], unused);
         for (int w = w_lo; w < w_hi; ++w) {
             const uint32_t aw = abits[w];
             const int r = max(0, min(need - at_off, __popc(aw)));
@@ -452,7 +430,7 @@ __global__ __launch_bounds__(kThreads) void evict_kernel(
         n_on += __popc(on);
     }
     int n_total;
-    int on_off = block_exclusive_scan(n_on, lane, wave, tmp[2], n_total);
+    int on_off = block_exclusive_scan<kWaves>(n_on, lane, wave, tmp[2], n_total);
     uint32_t *wpref = abits;                            // the at bits are used up
     for (int w = w_lo; w < w_hi; ++w) {
         wpref[w] = (uint32_t)on_off;

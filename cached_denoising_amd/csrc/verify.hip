@@ -13,8 +13,10 @@
 //      d entries of an ascending list; entries are taken in chunks with a
 //      halo of W-1 earlier entries in LDS, and an entry is withdrawn when a
 //      conflicting pair starting at most W-1 entries before it covers it;
-//   3. one pass over the positions writes the withdrawal flags, updates the
-//      mask, stable and cached flags, and compacts the mask into next_pos;
+//   3. the mask is loaded as bits (kVUnroll loads per thread in flight),
+//      each thread owns whole words of it for one scan of the next mask,
+//      and one pass over the positions stores the withdrawal flags, the
+//      mask, the stable and cached flags and the compacted mask;
 //   4. the withdrawn positions are listed in ascending order.
 #include "common.hpp"
 
@@ -24,18 +26,18 @@ namespace {
 constexpr int kVThreads = 1024;
 constexpr int kVWaves = kVThreads / kWave;
 constexpr int kMaxWin = 8;          // W: pairs at distance 1 .. W-1
-constexpr int kMaxLV = 131072;      // withdrawal bits stay within 16 KB of LDS
+constexpr int kMaxLV = 131072;      // bits and prefixes stay within 48 KB of LDS
 
-// order of a wave's lanes below this one
-__device__ __forceinline__ uint64_t lanes_below(int lane) { return lane ? (~0ull) >> (64 - lane) : 0ull; }
-
+constexpr int kVUnroll = 8;         // positions per thread in flight in the mask load
 __global__ __launch_bounds__(kVThreads) void verify_kernel(
     int L, const int32_t *__restrict__ dec_pos, int n, const float *__restrict__ p_marg,
     const float *__restrict__ p_joint, int W, double tau, uint8_t *__restrict__ rollback,
     uint8_t *__restrict__ mask, uint8_t *__restrict__ stable, uint8_t *__restrict__ cached,
     int32_t *__restrict__ next_pos, int32_t *__restrict__ count, int32_t *__restrict__ n_rollback,
     int32_t *__restrict__ rb_pos) {
-    extern __shared__ uint32_t rbits[];                // withdrawn positions, one bit each
+    // dynamic LDS: withdrawn positions, then the mask (the next mask once
+    // decided), then a prefix per mask word, one bit (word) each
+    extern __shared__ uint32_t rbits[];
     __shared__ int s_pos[kVThreads + kMaxWin];         // a chunk of entries after its halo
     __shared__ uint8_t s_cb[kVThreads + kMaxWin];      // their conflict bits
     __shared__ int wave_cnt[2][kVWaves];               // per-wave counts, double-buffered
@@ -48,6 +50,8 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(
     const int H = W - 1;
     const float *pj = p_joint + (int64_t)b * n * H;
     const int words = (L + 31) >> 5;
+    uint32_t *mbits = rbits + words;
+    int *wpref = reinterpret_cast<int *>(mbits + words);
 
     for (int w = tid; w < words; w += kVThreads) rbits[w] = 0;
     if (tid == 0) {
@@ -115,35 +119,57 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(
         __syncthreads();                                // the buffers are refilled
     }
 
-    // 3. flags, mask and the compacted mask, position-strided
-    int base = 0;
-    for (int i0 = 0, par = 0; i0 < L; i0 += kVThreads, par ^= 1) {
-        const int i = i0 + tid;
-        bool on = false;
-        if (i < L) {
-            const bool rb = (rbits[i >> 5] >> (i & 31)) & 1u;
-            rollback[rowoff + i] = rb ? 1 : 0;
-            on = rb || mask[rowoff + i] != 0;
-            if (rb) {
-                mask[rowoff + i] = 1;
-                if (stable) stable[rowoff + i] = 0;
-                if (cached) cached[rowoff + i] = 0;
-            }
+    // 3. the mask as bits (a wave's ballot over 64 positions is two words)
+    const uint8_t *mr = mask + rowoff;
+    for (int i0 = 0; i0 < L; i0 += kVThreads * kVUnroll) {
+        uint8_t mv[kVUnroll];
+#pragma unroll
+        for (int u = 0; u < kVUnroll; ++u) {
+            const int i = i0 + u * kVThreads + tid;
+            mv[u] = i < L ? mr[i] : 0;
         }
-        const uint64_t bal = __ballot(on);
-        if (lane == 0) wave_cnt[par][wave] = __popcll(bal);
-        __syncthreads();
-        int off = base, chunk = 0;
-        for (int w = 0; w < kVWaves; ++w) {
-            const int v = wave_cnt[par][w];
-            off += w < wave ? v : 0;
-            chunk += v;
+#pragma unroll
+        for (int u = 0; u < kVUnroll; ++u) {
+            const int c0 = i0 + u * kVThreads;
+            if (c0 >= L) break;                         // uniform over the workgroup
+            const uint64_t bm = __ballot(mv[u] != 0);
+            const int w0 = (c0 + wave * kWave) >> 5;
+            if (lane == 0 && w0 < words) mbits[w0] = (uint32_t)bm;
+            if (lane == 1 && w0 + 1 < words) mbits[w0 + 1] = (uint32_t)(bm >> 32);
         }
-        if (on) next_pos[rowoff + off + __popcll(bal & lanes_below(lane))] = i;
-        base += chunk;
+    }
+    __syncthreads();
+    // the next mask, and its prefix per word: each thread owns a run of words
+    const int wpt = (words + kVThreads - 1) / kVThreads;
+    const int w_lo = min(words, tid * wpt), w_hi = min(words, w_lo + wpt);
+    int n_on = 0;
+    for (int w = w_lo; w < w_hi; ++w) {
+        const uint32_t on = mbits[w] | rbits[w];
+        mbits[w] = on;
+        n_on += __popc(on);
+    }
+    int base;
+    int on_off = block_exclusive_scan<kVWaves>(n_on, lane, wave, wave_cnt[0], base);
+    for (int w = w_lo; w < w_hi; ++w) {
+        wpref[w] = on_off;
+        on_off += __popc(mbits[w]);
+    }
+    __syncthreads();
+    // store pass, position-strided
+#pragma unroll 4
+    for (int i = tid; i < L; i += kVThreads) {
+        const int w = i >> 5, bit = i & 31;
+        const bool rb = (rbits[w] >> bit) & 1u;
+        const uint32_t mw = mbits[w];
+        rollback[rowoff + i] = rb ? 1 : 0;
+        if (rb) {
+            mask[rowoff + i] = 1;
+            if (stable) stable[rowoff + i] = 0;
+            if (cached) cached[rowoff + i] = 0;
+        }
+        if ((mw >> bit) & 1u) next_pos[rowoff + wpref[w] + __popc(mw & ((1u << bit) - 1u))] = i;
     }
     for (int i = base + tid; i < L; i += kVThreads) next_pos[rowoff + i] = -1;
-    __syncthreads();                                    // wave_cnt is reused
 
     // 4. the withdrawn positions in list (ascending) order
     int nr = 0;
@@ -182,7 +208,7 @@ int launch_self_verify(int B, int L, const int32_t *dec_pos, int n, const float 
                        uint8_t *stable, uint8_t *cached, int32_t *next_pos, int32_t *count,
                        int32_t *n_rollback, int32_t *rb_pos, hipStream_t s) {
     if (L > kMaxLV || W > kMaxWin) return DLLM_ERANGE;
-    const size_t shmem = sizeof(uint32_t) * (size_t)((L + 31) / 32);
+    const size_t shmem = 3 * sizeof(uint32_t) * (size_t)((L + 31) / 32);   // withdrawn, mask, prefix
     verify_kernel<<<dim3((unsigned)B), dim3(kVThreads), shmem, s>>>(
         L, dec_pos, n, p_marg, p_joint, W, tau, rollback, mask, stable, cached, next_pos, count,
         n_rollback, rb_pos);
