@@ -691,12 +691,15 @@ def main():
         kernel_timing = "HIP events on the launch stream, in the timed region"
     else:
         kernel_timing = ("HIP events on the launch stream, eager pass of the same steps after the timed "
-                         "region, queued behind a spin kernel so that no host launch gap falls inside an "
-                         "event pair")
-        # the spin keeps the GPU busy while the host queues the whole pass;
-        # about 150 us of host time per launch, at least 20 ms (2.4 GHz clock)
-        spin_s = max(0.02, 150e-6 * args.steps * len(names))
-        torch.cuda._sleep(int(spin_s * 2.4e9))
+                         "region, queued behind replays of the timed graph so that no host launch gap "
+                         "falls inside an event pair")
+        # replays of the timed graph keep the GPU busy (and its clocks where
+        # the timed region had them) while the host queues the whole pass:
+        # about 150 us of host time per launch, at least 20 ms
+        busy_s = max(0.02, 150e-6 * args.steps * len(names))
+        graph_s = max(1e-6, ms * args.steps / 1000.0)
+        for _ in range(min(200, max(1, int(busy_s / graph_s) + 1))):
+            graph.replay()
         for i in range(args.steps):
             step.run({n: events[n][i] for n in names})
         torch.cuda.synchronize()
