@@ -41,8 +41,14 @@ constexpr int kStages = 2;             // key tiles per wave in the load pipelin
 
 // LDS of one MFMA workgroup: the staged queries, kStages V tiles per wave
 // and, with a key map, the workgroup's table of key indices
-constexpr int attn_smem_bytes(int D, int esz, int RT, int NW, bool map) {
+constexpr int attn_stage_bytes(int D, int esz, int RT, int NW, bool map) {
     return 16 * RT * (D * 2 + 16) + NW * kStages * 32 * D * esz + (map ? kMapTableTiles * 32 * 4 : 0);
+}
+// the staging area, or the waves' exchange of O~ at the end if that is larger
+constexpr int attn_smem_bytes(int D, int esz, int RT, int NW, bool map) {
+    return attn_stage_bytes(D, esz, RT, NW, map) > NW * 16 * RT * (D + 4) * 4
+               ? attn_stage_bytes(D, esz, RT, NW, map)
+               : NW * 16 * RT * (D + 4) * 4;
 }
 
 template <int D, int KVDT, int RT, bool MAP, bool NT, int NW>
@@ -66,12 +72,12 @@ __global__ __launch_bounds__(NW * kWave, 2) void attn_mfma_kernel(
     constexpr int MT = kMapTableTiles / NW;                      // table tiles per wave
     constexpr int TAB = MAP ? kMapTableTiles * 32 * 4 : 0;       // per-wave key index tables
     constexpr int S = kStages;
-    constexpr int SMEM = QBYTES + NW * S * VTILE + TAB;
-    constexpr int BST = D + 4;                                   // merge-buffer row stride (floats)
+    constexpr int BST = D + 4;                                   // exchange row stride (floats)
+    constexpr int SMEM = attn_smem_bytes(D, ESZ, RT, NW, MAP);
     static_assert(S >= 2 && S <= 4, "pipeline depth");
-    static_assert(SMEM == attn_smem_bytes(D, ESZ, RT, NW, MAP), "LDS layout");
+    static_assert(attn_stage_bytes(D, ESZ, RT, NW, MAP) == QBYTES + NW * S * VTILE + TAB, "LDS layout");
     static_assert(SMEM <= kLdsBytes, "LDS of one workgroup");
-    static_assert(SMEM >= (NW / 2) * ROWS * BST * 4, "merge buffers must fit in the staging area");
+    static_assert(SMEM >= NW * ROWS * BST * 4, "the exchange fits");
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
     __shared__ float sm_ml[NW][ROWS][2];
@@ -94,19 +100,24 @@ __global__ __launch_bounds__(NW * kWave, 2) void attn_mfma_kernel(
     const int32_t *kmap = MAP ? key_idx + (int64_t)bi * n_keys : nullptr;
 
     // ---- queries: the B operand of S^T = K Q^T.  All waves of the workgroup
-    // use the same rows, so they are staged once in LDS; rows past M are zero.
+    // use the same rows, so they are staged once in LDS; rows past M are
+    // zero.  Their loads go out first and are written to LDS after the first
+    // key tiles' loads, so the two latencies overlap.
     unsigned char *qs = smem;
-    for (int idx = threadIdx.x; idx < ROWS * (D / 8); idx += NW * kWave) {
+    constexpr int QN = ROWS * (D / 8);                   // 16-byte chunks of the staged rows
+    constexpr int QIT = (QN + NW * kWave - 1) / (NW * kWave);
+    uint4 qv[QIT];
+#pragma unroll
+    for (int it = 0; it < QIT; ++it) {
+        const int idx = threadIdx.x + it * NW * kWave;
         const int r = idx / (D / 8), c8 = idx % (D / 8);
         const int rr = rg * ROWS + r;
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (rr < M) {
+        qv[it] = make_uint4(0, 0, 0, 0);
+        if (idx < QN && rr < M) {
             const int gq = rr / b, i = rr - gq * b;
-            w = *reinterpret_cast<const uint4 *>(q + (((int64_t)bi * Hq + kvh * G + gq) * b + i) * D + c8 * 8);
+            qv[it] = *reinterpret_cast<const uint4 *>(q + (((int64_t)bi * Hq + kvh * G + gq) * b + i) * D + c8 * 8);
         }
-        *reinterpret_cast<uint4 *>(qs + r * QSTR + c8 * 16) = w;
     }
-    __syncthreads();
 
     f32x4_t o[NDT][RT];
 #pragma unroll
@@ -321,6 +332,14 @@ __global__ __launch_bounds__(NW * kWave, 2) void attn_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < S - 1; ++i)
         if (t_begin + i < t_end) issue(t_begin + i, T[i], vbase + i * VTILE);
+    __builtin_amdgcn_sched_barrier(0);
+    // the queries into LDS (their loads were issued before the tiles')
+#pragma unroll
+    for (int it = 0; it < QIT; ++it) {
+        const int idx = threadIdx.x + it * NW * kWave;
+        if (idx < QN) *reinterpret_cast<uint4 *>(qs + (idx / (D / 8)) * QSTR + (idx % (D / 8)) * 16) = qv[it];
+    }
+    __syncthreads();
     for (int kt = t_begin; kt < t_end; kt += S) {
 #pragma unroll
         for (int j = 0; j < S; ++j) {
@@ -337,9 +356,22 @@ __global__ __launch_bounds__(NW * kWave, 2) void attn_mfma_kernel(
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) l[rt] = group4_sum(l[rt]);
 
-    // ---- merge the waves through LDS: every wave rescales its O to the
-    // workgroup's row max, then a fixed binary tree adds them up (at each
-    // level the upper half of the remaining waves hands its O to the lower)
+    // ---- merge the waves through LDS in one exchange: once every wave is
+    // done with the staging area, each stores its unnormalised O~ and its
+    // (m, l) per row there; after one more barrier every thread combines
+    // one (row, 4 dims) over the waves in order, each wave's share scaled by
+    // 2^(m_w - M) with M the row's largest m, and writes the result (or this
+    // split's partial).  m starts finite, so a wave without keys adds 0.
+    float *buf = reinterpret_cast<float *>(smem);       // [NW][ROWS][BST] floats
+    __syncthreads();
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const f32x4_t v = o[dt][rt];
+            *reinterpret_cast<float4 *>(buf + (wave * ROWS + rt * 16 + l16) * BST + dt * 16 + 4 * g) =
+                make_float4(v[0], v[1], v[2], v[3]);
+        }
     if (g == 0) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -348,95 +380,50 @@ __global__ __launch_bounds__(NW * kWave, 2) void attn_mfma_kernel(
         }
     }
     __syncthreads();
-    float Mrow[RT], Ltot[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const int r = rt * 16 + l16;
-        float mm = kNegInf;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) mm = fmaxf(mm, sm_ml[w][r][0]);
-        float lt = 0.f;
+    constexpr int Q4 = D / 4;
+    for (int idx = threadIdx.x; idx < ROWS * Q4; idx += NW * kWave) {
+        const int r = idx / Q4, c = (idx % Q4) * 4;
+        const int rr = rg * ROWS + r;
+        if (rr >= M) continue;
+        float mw[NW], mm = kMinit;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-            const float mw = sm_ml[w][r][0];
-            if (mw != kNegInf) lt += sm_ml[w][r][1] * __builtin_amdgcn_exp2f(mw - mm);
+            mw[w] = sm_ml[w][r][0];
+            mm = fmaxf(mm, mw[w]);
         }
-        Mrow[rt] = mm;
-        Ltot[rt] = lt;
-        const float fown = m[rt] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m[rt] - mm);
+        float lt = 0.f;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[dt][rt] *= fown;
-    }
-    float *buf = reinterpret_cast<float *>(smem);       // NW/2 slots of [ROWS][BST] floats
-#pragma unroll
-    for (int half = NW / 2; half >= 1; half >>= 1) {
-        // the staging area (or the previous level's slots) is free to reuse
-        __syncthreads();
-        if (wave >= half && wave < 2 * half) {
-            float *slot = buf + (wave - half) * ROWS * BST;
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    const f32x4_t v = o[dt][rt];
-                    *reinterpret_cast<float4 *>(slot + (rt * 16 + l16) * BST + dt * 16 + 4 * g) =
-                        make_float4(v[0], v[1], v[2], v[3]);
-                }
+        for (int w = 0; w < NW; ++w) {
+            const float f = __builtin_amdgcn_exp2f(mw[w] - mm);
+            lt += sm_ml[w][r][1] * f;
+            const float4 v = *reinterpret_cast<const float4 *>(buf + (w * ROWS + r) * BST + c);
+            acc += f32x4_t{v.x, v.y, v.z, v.w} * f;
         }
-        __syncthreads();
-        if (wave < half) {
-            const float *slot = buf + wave * ROWS * BST;
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    const float4 v = *reinterpret_cast<const float4 *>(slot + (rt * 16 + l16) * BST + dt * 16 + 4 * g);
-                    o[dt][rt] += f32x4_t{v.x, v.y, v.z, v.w};
-                }
-        }
-    }
-    if (wave != 0) return;
-
-    // ---- wave 0 writes the result (or this split's partial)
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const int r = rg * ROWS + rt * 16 + l16;
-        if (r >= M) continue;
-        const int gq = r / b, i = r - gq * b;
+        const int gq = rr / b, i = rr - gq * b;
         const int64_t orow = ((int64_t)bi * Hq + kvh * G + gq) * b + i;
         if (splits == 1) {
-            const float inv = Ltot[rt] > 0.f ? 1.0f / Ltot[rt] : 0.f;
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-                const f32x4_t v = o[dt][rt] * inv;
-                const int64_t off = orow * D + dt * 16 + 4 * g;
-                if (out_dtype == DLLM_F32) {
-                    *reinterpret_cast<float4 *>(static_cast<float *>(out) + off) =
-                        make_float4(v[0], v[1], v[2], v[3]);
-                } else {
-                    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + off) =
-                        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-                }
-            }
-            if (lse && g == 0)
-                lse[orow] = Ltot[rt] > 0.f ? Mrow[rt] * kLn2 + logf(Ltot[rt]) : kNegInf;
+            const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+            const f32x4_t v = acc * inv;
+            const int64_t off = orow * D + c;
+            if (out_dtype == DLLM_F32)
+                *reinterpret_cast<float4 *>(static_cast<float *>(out) + off) = make_float4(v[0], v[1], v[2], v[3]);
+            else
+                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + off) =
+                    make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+            if (lse && c == 0) lse[orow] = lt > 0.f ? mm * kLn2 + logf(lt) : kNegInf;
         } else {
-            // partial of this split: unnormalised O~, running max (base 2), sum
+            // partial of this split: unnormalised O~, running max (base 2), sum,
+            // O~ in the output's precision (bf16 partials for a bf16 output)
             const int64_t prow = (int64_t)split * rows_total + orow;
-#pragma unroll
-            // the output's precision: bf16 partials for a bf16 output, else fp32
-            for (int dt = 0; dt < NDT; ++dt) {
-                const f32x4_t v = o[dt][rt];
-                if (out_dtype == DLLM_F32)
-                    *reinterpret_cast<float4 *>(part_o + prow * D + dt * 16 + 4 * g) =
-                        make_float4(v[0], v[1], v[2], v[3]);
-                else
-                    *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(part_o) + prow * D + dt * 16 + 4 * g) =
-                        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-            }
-            if (g == 0) {
-                part_ml[prow * 2 + 0] = Mrow[rt];
-                part_ml[prow * 2 + 1] = Ltot[rt];
+            if (out_dtype == DLLM_F32)
+                *reinterpret_cast<float4 *>(part_o + prow * D + c) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            else
+                *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(part_o) + prow * D + c) =
+                    make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+            if (c == 0) {
+                part_ml[prow * 2 + 0] = mm;
+                part_ml[prow * 2 + 1] = lt;
             }
         }
     }
