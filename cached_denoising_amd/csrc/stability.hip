@@ -113,10 +113,16 @@ __global__ __launch_bounds__(kThreads) void stability_kernel(
         const int i = i0 + tid;
         bool seed = false;
         if (i < L) {
-            const double h = (double)entropy_latest[rowoff + i];
-            const double dt = (double)(step - t_write[rowoff + i]);
             const bool st = stable[rowoff + i] != 0;
-            const double cf = alpha * (1.0 - h / hmax) + beta * exp(-lambda * dt);
+            // with the gate off (alpha = beta = 0) the score is +0 whatever the
+            // entropy and age; a zero beta drops the float64 exponential, whose
+            // term would add +0
+            double cf = 0.0;
+            if (alpha != 0.0 || beta != 0.0) {
+                const double h = (double)entropy_latest[rowoff + i];
+                const double dt = (double)(step - t_write[rowoff + i]);
+                cf = alpha * (1.0 - h / hmax) + (beta != 0.0 ? beta * exp(-lambda * dt) : 0.0);
+            }
             if (conf) conf[rowoff + i] = (float)cf;
             seed = !st || cf < conf_thresh;
         }
