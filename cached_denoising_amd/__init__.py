@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "F32", "BF16", "E4M3", "DllmError", "lib", "Cache", "StabilityState", "dllm_status_str",
     "dllm_version", "dllm_cache_init", "dllm_scatter_kv", "dllm_sink_rolling_map",
-    "dllm_block_attention", "dllm_block_attention_workspace", "dllm_facache_maps",
+    "dllm_block_attention", "dllm_block_attention_workspace", "dllm_scatter_attention",
+    "dllm_facache_maps",
     "dllm_facache_merge", "dllm_facache_merge_workspace", "dllm_fp8_quant_rows",
     "dllm_fp8_addnorm_quant", "dllm_fp8_quant_weight", "dllm_fp8_gemm", "dllm_fp8_gemm_swiglu",
     "dllm_vocab_stats",
@@ -69,6 +70,13 @@ EXPORTS = {
                                             ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
                                             ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_size_t, ctypes.c_void_p]),
+    "dllm_scatter_attention": (ctypes.c_int, [ctypes.POINTER(_KVCache), ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                              ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_void_p, ctypes.c_int, ctypes.c_float,
+                                              ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "dllm_block_attention_workspace": (ctypes.c_size_t, [ctypes.POINTER(_KVCache), ctypes.c_int,
                                                          ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     "dllm_facache_maps": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
@@ -249,6 +257,31 @@ def dllm_block_attention(cache: Cache, q: torch.Tensor, key_idx: Optional[torch.
                                     _dtype_code(out), _dev(lse, "lse"), _dev(workspace, "workspace"),
                                     ws_bytes, _stream())
     _check(rc, "dllm_block_attention")
+    return out
+
+
+def dllm_scatter_attention(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, pos: torch.Tensor,
+                           q: torch.Tensor, key_idx: Optional[torch.Tensor] = None, scale: float = 0.0,
+                           out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                           lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                           bad_count: Optional[torch.Tensor] = None):
+    """dllm_scatter_kv(cache, k_new, v_new, pos) then dllm_block_attention(cache,
+    q, ...) in one call; returns out [B, Hq, b, d]."""
+    B, Hq, b, d = q.shape
+    n = pos.shape[1]
+    n_keys = key_idx.shape[1] if key_idx is not None else cache.desc.L
+    if out is None:
+        out = torch.empty((B, Hq, b, d), dtype=out_dtype or q.dtype, device=q.device)
+    ws_need = dllm_block_attention_workspace(cache, _dtype_code(q), Hq, b, n_keys)
+    if workspace is None and ws_need:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().dllm_scatter_attention(ctypes.byref(cache.desc), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                                      _dtype_code(k_new), _dev(pos, "pos"), n, _dev(bad_count, "bad_count"),
+                                      _dev(q, "q"), _dtype_code(q), Hq, b, _dev(key_idx, "key_idx"), n_keys,
+                                      float(scale), _dev(out, "out"), _dtype_code(out), _dev(lse, "lse"),
+                                      _dev(workspace, "workspace"), ws_bytes, _stream())
+    _check(rc, "dllm_scatter_attention")
     return out
 
 

@@ -147,6 +147,45 @@ int dllm_block_attention(const dllm_kv_cache *cache, const void *q, int q_dtype,
                             out_dtype, lse, workspace, static_cast<hipStream_t>(stream));
 }
 
+int dllm_scatter_attention(const dllm_kv_cache *cache, const void *k_new, const void *v_new,
+                           int src_dtype, const int32_t *pos, int n, int32_t *bad_count,
+                           const void *q, int q_dtype, int Hq, int b, const int32_t *key_idx,
+                           int n_keys, float scale, void *out, int out_dtype, float *lse,
+                           void *workspace, size_t ws_bytes, void *stream) {
+    // the checks of dllm_scatter_kv, then those of dllm_block_attention
+    int rc = check_cache(cache);
+    if (rc != DLLM_OK) return rc;
+    if (n < 0) return DLLM_EINVAL;
+    if (n > 0) {
+        if (!k_new || !v_new || !pos) return DLLM_EINVAL;
+        if (cache->dtype == DLLM_E4M3) {
+            if (src_dtype != DLLM_F32 && src_dtype != DLLM_BF16) return DLLM_EDTYPE;
+        } else if (src_dtype != cache->dtype) {
+            return DLLM_EDTYPE;
+        }
+        if (!aligned16(k_new) || !aligned16(v_new)) return DLLM_EALIGN;
+    }
+    if (!q || !out) return DLLM_EINVAL;
+    if (Hq < 1 || b < 1) return DLLM_ESHAPE;
+    if (Hq % cache->n_kv_heads != 0) return DLLM_ESHAPE;
+    if (!key_idx) n_keys = cache->L;
+    if (n_keys < 1) return DLLM_ESHAPE;
+    if (q_dtype != DLLM_F32 && q_dtype != DLLM_BF16) return DLLM_EDTYPE;
+    if (out_dtype != DLLM_F32 && out_dtype != DLLM_BF16) return DLLM_EDTYPE;
+    if (!(scale >= 0.f) || std::isinf(scale)) return DLLM_EINVAL;
+    if (scale == 0.f) scale = 1.0f / std::sqrt((float)cache->d_head);
+    if ((int64_t)cache->B * Hq * b > INT32_MAX / 4) return DLLM_ERANGE;
+    AttnPlan p;
+    if ((rc = plan_attention(*cache, q_dtype, Hq, b, n_keys, key_idx != nullptr, &p)) != DLLM_OK)
+        return rc;
+    if (p.path != 0 && (!aligned16(q) || !aligned16(out))) return DLLM_EALIGN;
+    if (p.ws_bytes > 0 && (!workspace || ws_bytes < p.ws_bytes || !aligned16(workspace)))
+        return DLLM_EWORKSPACE;
+    return launch_scatter_attention(*cache, p, k_new, v_new, src_dtype, pos, n, bad_count, q, q_dtype,
+                                    Hq, b, key_idx, n_keys, scale, out, out_dtype, lse, workspace,
+                                    static_cast<hipStream_t>(stream));
+}
+
 int dllm_facache_maps(int B, int L, int blk, const int32_t *start, int32_t *unchanged_idx,
                       int32_t *block_idx, void *stream) {
     if (B < 1 || blk < 1 || L <= blk) return DLLM_ESHAPE;

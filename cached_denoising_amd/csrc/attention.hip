@@ -57,7 +57,7 @@ __global__ __launch_bounds__(NW * kWave, 2) void attn_mfma_kernel(
     const float *__restrict__ vsc, const uint16_t *__restrict__ q, int Hq, int Hkv, int L, int b,
     int G, const int32_t *__restrict__ key_idx, int n_keys, float scale_log2, int row_groups,
     int splits, int tiles_per_wave, int64_t rows_total, void *__restrict__ out, int out_dtype,
-    float *__restrict__ lse, float *__restrict__ part_o, float *__restrict__ part_ml) {
+    float *__restrict__ lse, float *__restrict__ part_o, float *__restrict__ part_ml, ScatterIn sc) {
     constexpr int NC = D / 32;           // k-chunks of the first product
     constexpr int NDT = D / 16;          // dim tiles of the second product
     constexpr int ROWS = 16 * RT;        // rows per workgroup
@@ -116,6 +116,34 @@ __global__ __launch_bounds__(NW * kWave, 2) void attn_mfma_kernel(
         if (idx < QN && rr < M) {
             const int gq = rr / b, i = rr - gq * b;
             qv[it] = *reinterpret_cast<const uint4 *>(q + (((int64_t)bi * Hq + kvh * G + gq) * b + i) * D + c8 * 8);
+        }
+    }
+
+    // ---- with the block's fresh rows (bf16 cache, no key map): this
+    // workgroup first writes the rows whose positions fall in its own key
+    // range into the cache, exactly as the scatter would, and every wave
+    // waits for the stores before any tile load, so its loads see them; no
+    // other workgroup reads these keys in this call
+    if constexpr (KVDT == DLLM_BF16 && !MAP) {
+        if (sc.pos) {
+            const int key_lo = split * NW * tiles_per_wave * 32;
+            const int key_hi = key_lo + NW * tiles_per_wave * 32;
+            for (int idx = threadIdx.x; idx < sc.n * CPR; idx += NW * kWave) {
+                const int j = idx / CPR, c = idx - (idx / CPR) * CPR;
+                const int64_t src = (((int64_t)bi * sc.n + j) * Hkv + kvh) * CPR + c;
+                const uint4 kw = sc.k_new[src];
+                const uint4 vw = sc.v_new[src];
+                const int p = sc.pos[(int64_t)bi * sc.n + j];
+                if (p < 0 || p >= L) {
+                    if (p != -1 && sc.bad && c == 0 && kvh == 0 && split == 0) atomicAdd(sc.bad, 1);
+                    continue;
+                }
+                if (p < key_lo || p >= key_hi) continue;
+                sc.ck[(kv_base + p) * CPR + c] = kw;
+                sc.cv[(kv_base + p) * CPR + c] = vw;
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
         }
     }
 
@@ -603,7 +631,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(
 template <int D, int KVDT, int RT, bool MAP, bool NT, int NW>
 int launch_mfma(const dllm_kv_cache &c, const AttnPlan &p, const void *q, int Hq, int b,
                 const int32_t *key_idx, int n_keys, float scale, void *out, int out_dtype,
-                float *lse, void *ws, hipStream_t s) {
+                float *lse, void *ws, hipStream_t s, const ScatterIn &sc) {
     const int G = Hq / c.n_kv_heads;
     const int64_t rows_total = (int64_t)c.B * Hq * b;
     const int64_t blocks = (int64_t)c.B * c.n_kv_heads * p.row_groups * p.splits;
@@ -618,7 +646,7 @@ int launch_mfma(const dllm_kv_cache &c, const AttnPlan &p, const void *q, int Hq
     attn_mfma_kernel<D, KVDT, RT, MAP, NT, NW><<<dim3((unsigned)blocks), dim3(NW * kWave), 0, s>>>(
         c.k, c.v, c.k_scale, c.v_scale, static_cast<const uint16_t *>(q), Hq, c.n_kv_heads, c.L,
         b, G, key_idx, n_keys, scale_log2, p.row_groups, p.splits, p.tiles_per_wave, rows_total,
-        out, out_dtype, lse, part_o, part_ml);
+        out, out_dtype, lse, part_o, part_ml, sc);
     int rc = launch_status();
     if (rc != DLLM_OK || p.splits == 1) return rc;
     return launch_attn_merge(part_o, part_ml, rows_total, D, p.splits, out, out_dtype, lse, s);
@@ -696,9 +724,10 @@ int plan_facache(const dllm_kv_cache &c, int q_dtype, int Hq, int n_q, int n_key
     return DLLM_OK;
 }
 
-int launch_attention(const dllm_kv_cache &c, const AttnPlan &p, const void *q, int q_dtype, int Hq,
-                     int b, const int32_t *key_idx, int n_keys, float scale, const AttnMemo &memo,
-                     void *out, int out_dtype, float *lse, void *ws, hipStream_t s) {
+static int launch_attention_sc(const dllm_kv_cache &c, const AttnPlan &p, const void *q, int q_dtype,
+                               int Hq, int b, const int32_t *key_idx, int n_keys, float scale,
+                               const AttnMemo &memo, void *out, int out_dtype, float *lse, void *ws,
+                               hipStream_t s, const ScatterIn &sc) {
     if (p.path == 0) {
         const int64_t rows_total = (int64_t)c.B * Hq * b;
         attn_valu_kernel<<<dim3((unsigned)cdiv64(rows_total, 4)), dim3(256), 0, s>>>(
@@ -723,7 +752,7 @@ int launch_attention(const dllm_kv_cache &c, const AttnPlan &p, const void *q, i
             constexpr int NW = decltype(nwv)::value;
             if constexpr (attn_smem_bytes(DD, ES, 2, NW, MP) <= kLdsBytes)
                 return launch_mfma<DD, KV, 2, MP, NTV, NW>(c, p, q, Hq, b, key_idx, n_keys, scale, out,
-                                                           out_dtype, lse, ws, s);
+                                                           out_dtype, lse, ws, s, sc);
             return DLLM_ESHAPE;                 // never planned
         };
         auto pick = [&](auto ntv) -> int {
@@ -743,6 +772,38 @@ int launch_attention(const dllm_kv_cache &c, const AttnPlan &p, const void *q, i
     }
     if (e4) return DLLM_ESHAPE;                 // e4m3 needs d % 128 == 0
     return map ? go(I64{}, KB{}, std::true_type{}) : go(I64{}, KB{}, std::false_type{});
+}
+
+int launch_attention(const dllm_kv_cache &c, const AttnPlan &p, const void *q, int q_dtype, int Hq,
+                     int b, const int32_t *key_idx, int n_keys, float scale, const AttnMemo &memo,
+                     void *out, int out_dtype, float *lse, void *ws, hipStream_t s) {
+    return launch_attention_sc(c, p, q, q_dtype, Hq, b, key_idx, n_keys, scale, memo, out, out_dtype, lse,
+                               ws, s, ScatterIn{});
+}
+
+int launch_scatter_attention(const dllm_kv_cache &c, const AttnPlan &p, const void *k_new,
+                             const void *v_new, int src_dtype, const int32_t *pos, int n,
+                             int32_t *bad, const void *q, int q_dtype, int Hq, int b,
+                             const int32_t *key_idx, int n_keys, float scale, void *out,
+                             int out_dtype, float *lse, void *ws, hipStream_t s) {
+    // one launch where the per-wave kernel reads the keys in place (bf16
+    // cache and rows, no key map); otherwise the scatter, then the attention
+    if (n > 0 && p.path == 1 && !key_idx && c.dtype == DLLM_BF16 && src_dtype == DLLM_BF16) {
+        ScatterIn sc;
+        sc.k_new = static_cast<const uint4 *>(k_new);
+        sc.v_new = static_cast<const uint4 *>(v_new);
+        sc.ck = static_cast<uint4 *>(c.k);
+        sc.cv = static_cast<uint4 *>(c.v);
+        sc.pos = pos;
+        sc.n = n;
+        sc.bad = bad;
+        return launch_attention_sc(c, p, q, q_dtype, Hq, b, key_idx, n_keys, scale, AttnMemo{}, out,
+                                   out_dtype, lse, ws, s, sc);
+    }
+    int rc = launch_scatter(c, k_new, v_new, src_dtype, pos, n, bad, s);
+    if (rc != DLLM_OK) return rc;
+    return launch_attention(c, p, q, q_dtype, Hq, b, key_idx, n_keys, scale, AttnMemo{}, out, out_dtype,
+                            lse, ws, s);
 }
 
 }  // namespace dllm

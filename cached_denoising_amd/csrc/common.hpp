@@ -131,6 +131,15 @@ struct AttnMemo {
     const float *o = nullptr;
     const float *lse = nullptr;
 };
+// the block's fresh K/V rows, written by the attention kernel itself (see
+// launch_scatter_attention); pos == nullptr: none
+struct ScatterIn {
+    const uint4 *k_new = nullptr, *v_new = nullptr;   // [B, n, Hkv, d] as 16-byte chunks
+    uint4 *ck = nullptr, *cv = nullptr;               // the cache's K and V
+    const int32_t *pos = nullptr;                     // [B, n]
+    int n = 0;
+    int32_t *bad = nullptr;
+};
 int plan_attention(const dllm_kv_cache &c, int q_dtype, int Hq, int b, int n_keys, bool has_map,
                    AttnPlan *p);
 // the plan of a call with a memo: the VALU path or the grouped-query layout
@@ -145,6 +154,13 @@ int launch_shared_attention(const dllm_kv_cache &c, const AttnPlan &p, const voi
 // merge of the (m, l, O~) partials of key splits, in split order
 int launch_attn_merge(const float *part_o, const float *part_ml, int64_t rows_total, int D,
                       int splits, void *out, int out_dtype, float *lse, hipStream_t s);
+// the scatter then the attention, in one launch when the per-wave layout
+// takes the call (bf16 cache and rows, no key map)
+int launch_scatter_attention(const dllm_kv_cache &c, const AttnPlan &p, const void *k_new,
+                             const void *v_new, int src_dtype, const int32_t *pos, int n,
+                             int32_t *bad, const void *q, int q_dtype, int Hq, int b,
+                             const int32_t *key_idx, int n_keys, float scale, void *out,
+                             int out_dtype, float *lse, void *ws, hipStream_t s);
 int launch_attention(const dllm_kv_cache &c, const AttnPlan &p, const void *q, int q_dtype, int Hq,
                      int b, const int32_t *key_idx, int n_keys, float scale, const AttnMemo &memo,
                      void *out, int out_dtype, float *lse, void *ws, hipStream_t s);

@@ -7,6 +7,7 @@
  *
  *   dllm_cache_init        describe and clear a persistent per-layer K/V cache
  *   dllm_scatter_kv        write the block's fresh K/V rows into the cache
+ *   dllm_scatter_attention the scatter and the block attention in one call
  *   dllm_sink_rolling_map  build a sink + rolling-window key index map
  *   dllm_block_attention   block queries vs. the cached keys, bidirectional
  *   dllm_facache_maps      unchanged / changed key lists of a block's steps
@@ -206,6 +207,26 @@ int dllm_block_attention(const dllm_kv_cache *cache, const void *q, int q_dtype,
  * without a key map (0 if none: the keys are not split over workgroups). */
 size_t dllm_block_attention_workspace(const dllm_kv_cache *cache, int q_dtype, int Hq,
                                       int b, int n_keys);
+
+/* ---------------------------------------------------------------------------
+ * dllm_scatter_attention -- dllm_scatter_kv then dllm_block_attention, as one
+ * call: the block's fresh K/V rows go into the cache and the block's queries
+ * attend over the cache with them [LaCache, Methodology 3: the step
+ * recomputes the block, writes its K/V, and attends over the whole cached
+ * context].  Arguments as for the two calls (k_new, v_new, src_dtype, pos,
+ * n, bad_count as for dllm_scatter_kv; the rest as for dllm_block_attention,
+ * with the same workspace).  The cache and out afterwards hold exactly what
+ * the two calls in sequence leave.  With a bf16 cache and bf16 rows and no
+ * key map, when the block's queries fit one 32-row group per KV head, the
+ * attention kernel writes the rows itself (each workgroup the positions in
+ * its own key range) before it loads any key tile; otherwise the two kernels
+ * run in sequence on the stream.
+ * ------------------------------------------------------------------------- */
+int dllm_scatter_attention(const dllm_kv_cache *cache, const void *k_new, const void *v_new,
+                           int src_dtype, const int32_t *pos, int n, int32_t *bad_count,
+                           const void *q, int q_dtype, int Hq, int b, const int32_t *key_idx,
+                           int n_keys, float scale, void *out, int out_dtype, float *lse,
+                           void *workspace, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
  * dllm_facache_maps -- the key lists of FACache for one block's denoising

@@ -24,7 +24,8 @@ def dl():
 
 def test_header_declares_the_boundary():
     names = declared()
-    for n in ["dllm_cache_init", "dllm_scatter_kv", "dllm_block_attention", "dllm_vocab_stats",
+    for n in ["dllm_cache_init", "dllm_scatter_kv", "dllm_block_attention", "dllm_scatter_attention",
+              "dllm_vocab_stats",
               "dllm_stability_mask", "dllm_sink_rolling_map", "dllm_stability_reset",
               "dllm_block_attention_workspace", "dllm_vocab_stats_workspace", "dllm_status_str",
               "dllm_facache_maps", "dllm_facache_merge", "dllm_facache_merge_workspace",
