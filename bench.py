@@ -1,9 +1,10 @@
 """Benchmark of one decode step of the cached masked-diffusion hot path.
 
-A step is one pass over the four kernels of the GPT-2-small-shaped workload
+A step is one pass over the calls of the GPT-2-small-shaped workload
 (B=8 sequences of L=1024, 12 heads x 64, bf16 K/V cache, active block of 32
 at a per-sequence offset, vocab 50257 bf16 logits for every position):
-    dllm_scatter_kv -> dllm_block_attention -> dllm_vocab_stats -> dllm_stability_mask
+    dllm_scatter_attention (the scatter of the block's K/V rows, then the
+    block attention) -> dllm_vocab_stats -> dllm_stability_mask
 all on one stream with inputs resident in HBM.  Prints one JSON line.
 
 With --config facache a step is the first-layer attention of a later
@@ -59,11 +60,12 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "cached_denoising_amd", "csrc")
 # the source files of each call whose counters a profile summary records
 KERNEL_SRC = {"vocab_stats": ["vocab_stats.hip"],
-              "attention": ["attention.hip", "attention_shared.hip", "attn_common.hpp"],
               "facache_merge": ["attention.hip", "attention_shared.hip", "attn_common.hpp"],
+              "scatter_attention": ["attention.hip", "attention_shared.hip", "attn_common.hpp", "scatter.hip"],
               "scatter": ["scatter.hip"], "stability": ["stability.hip"],
-              "fp8_addnorm": ["fp8_ffn.hip", "common.hpp"], "fp8_gateup": ["fp8_ffn.hip", "common.hpp"],
-              "fp8_ffout": ["fp8_ffn.hip", "common.hpp"], "evict": ["stability.hip"],
+              "fp8_addnorm": ["fp8_ffn.hip", "common.hpp", "attn_common.hpp"],
+              "fp8_gateup": ["fp8_ffn.hip", "common.hpp", "attn_common.hpp"],
+              "fp8_ffout": ["fp8_ffn.hip", "common.hpp", "attn_common.hpp"], "evict": ["stability.hip"],
               "verify": ["verify.hip"]}
 
 
@@ -188,7 +190,7 @@ class Step:
     def kernels(self):
         ks = []
         if self.has_attn:
-            ks += ["scatter", "attention"]
+            ks.append("scatter_attention")
         if self.facache:
             ks.append("facache_merge")
         if self.has_vocab:
@@ -205,13 +207,12 @@ class Step:
                 events[name][i].record()
 
         if self.has_attn:
-            mark("scatter", 0)
-            D.dllm_scatter_kv(self.cache, self.kn, self.vn, self.pos)
-            mark("scatter", 1)
-            mark("attention", 0)
-            D.dllm_block_attention(self.cache, self.q, key_idx=self.key_idx, out=self.out,
-                                   workspace=self.attn_ws)
-            mark("attention", 1)
+            # the block's fresh K/V rows into the cache, then its queries over
+            # the keys, in one call
+            mark("scatter_attention", 0)
+            D.dllm_scatter_attention(self.cache, self.kn, self.vn, self.pos, self.q, key_idx=self.key_idx,
+                                     out=self.out, workspace=self.attn_ws)
+            mark("scatter_attention", 1)
         if self.facache:
             mark("facache_merge", 0)
             D.dllm_facache_merge(self.cache, self.qu, self.memo_o, self.memo_lse, key_idx=self.blk,
@@ -237,10 +238,13 @@ class Step:
             esz = 1 if cfg.kv_dtype == self.W.E4M3 else 2
             rows = cfg.B * cfg.b * cfg.Hkv
             scale_b = 4 * 2 if cfg.kv_dtype == self.W.E4M3 else 0
-            out["scatter"] = rows * cfg.d * (2 * 2 + 2 * esz) + rows * scale_b + cfg.B * cfg.b * 4
+            # the scatter: fresh bf16 rows in, cache rows (and scales) out,
+            # positions; the attention: the selected keys' K and V rows (and
+            # scales), queries in and output out, all bf16
+            scatter = rows * cfg.d * (2 * 2 + 2 * esz) + rows * scale_b + cfg.B * cfg.b * 4
             kv = cfg.B * cfg.Hkv * self.n_keys * (cfg.d * esz * 2 + scale_b)
             qo = cfg.B * cfg.Hq * cfg.b * cfg.d * 2 * 2
-            out["attention"] = kv + qo
+            out["scatter_attention"] = scatter + kv + qo
         if self.facache:
             rows = cfg.B * cfg.Hq * self.n_q
             # queries and output in bf16, the memo (O and lse) in fp32, the
@@ -263,7 +267,7 @@ class Step:
         cfg = self.cfg
         if not self.has_attn:
             return {}
-        out = {"attention": 4 * cfg.B * cfg.Hq * cfg.b * self.n_keys * cfg.d}
+        out = {"scatter_attention": 4 * cfg.B * cfg.Hq * cfg.b * self.n_keys * cfg.d}
         if self.facache:
             out["facache_merge"] = 4 * cfg.B * cfg.Hq * self.n_q * cfg.b * cfg.d
         return out
@@ -726,14 +730,21 @@ def main():
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
     roofline.update({"kernel": dom, "algorithmic_bytes_per_launch": alg[dom],
                      "avg_launch_us": round(dom_us, 2), "kernel_timing": kernel_timing})
-    if dom == "attention" and step.attn_split:
-        roofline["kernel_note"] = "attention call = attn_mfma_kernel + attn_merge_kernel of the key splits"
+    if dom == "scatter_attention":
+        fused = step.cfg.kv_dtype == W.BF16 and step.key_idx is None
+        roofline["kernel_note"] = (
+            "dllm_scatter_attention call = " +
+            ("attn_mfma_kernel writing the block's rows itself" if fused else
+             "scatter kernel, then the attention kernel") +
+            (" + attn_merge_kernel of the key splits" if step.attn_split else ""))
     if dom == "facache_merge":
         roofline["kernel_note"] = "facache_merge call = attn_shared_kernel started from the memo, one key tile"
     extra = {}
     if step.facache:
         full = step.full_recompute_us()
-        fa = per_kernel_us["attention"] + per_kernel_us["facache_merge"]
+        # the block's scatter is inside the first call: the FACache side
+        # carries it and the full recompute does not
+        fa = per_kernel_us["scatter_attention"] + per_kernel_us["facache_merge"]
         extra = {"full_recompute_attention_us": round(full, 1),
                  "facache_attention_us": round(fa, 1),
                  "facache_speedup_vs_full": round(full / fa, 2)}
