@@ -92,3 +92,61 @@ def test_scatter_attention_rows_land_where_the_oracle_puts_them(orc):
     orc.scatter_kv(ck, cv, None, None, W.BF16, bits(kn), bits(vn), W.BF16, pos.cpu().numpy())
     got_k, got_v, _, _ = cache_np(c1)
     assert np.array_equal(got_k, ck) and np.array_equal(got_v, cv)
+
+
+@pytest.mark.parametrize("name,n_heads", [("gpt2", None), ("llada", 24), ("longctx", 10)])
+def test_scatter_attention_full_size(orc, name, n_heads):
+    """the call as the bench step makes it, at the workload's full size: the
+    block's rows land in the cache (bf16: the fresh bytes themselves; e4m3:
+    the oracle's quantisation of them), and the output matches the oracle on
+    the cache the call leaves (every head at the gpt2 size, sampled heads at
+    the others)"""
+    D = need_gpu()
+    cfg = W.CONFIGS[name]
+    say("scatter_attention full", name)
+    cache = new_cache(D, cfg.B, cfg.Hkv, cfg.L, cfg.d, cfg.kv_dtype)
+    k, v = W.kv_rows(cfg, device="cuda")
+    D.dllm_scatter_kv(cache, k, v, torch.arange(cfg.L, dtype=torch.int32, device="cuda").repeat(cfg.B, 1))
+    del k, v
+    kn, vn = W.kv_rows(cfg, device="cuda", which="fresh")
+    pos = W.block_positions(cfg, "cuda")
+    kid = None
+    if cfg.sinks:
+        end = (pos[:, -1] + 1).contiguous()
+        kid = torch.empty((cfg.B, cfg.sinks + cfg.rolling), dtype=torch.int32, device="cuda")
+        D.dllm_sink_rolling_map(cfg.L, cfg.sinks, cfg.rolling, end, kid)
+    q = W.queries(cfg, device="cuda")
+    lse = torch.empty((cfg.B, cfg.Hq, cfg.b), dtype=torch.float32, device="cuda")
+    out = D.dllm_scatter_attention(cache, kn, vn, pos, q, key_idx=kid, lse=lse)
+    torch.cuda.synchronize()
+    p = pos.long()
+    bi = torch.arange(cfg.B, device="cuda")[:, None]
+    got_k = cache.k[bi, :, p].cpu()                    # [B, b, Hkv, d]
+    got_v = cache.v[bi, :, p].cpu()
+    if cfg.kv_dtype == W.BF16:
+        assert torch.equal(got_k.view(torch.int16), kn.cpu().view(torch.int16))
+        assert torch.equal(got_v.view(torch.int16), vn.cpu().view(torch.int16))
+    else:
+        for src, got, sc in ((kn, got_k, cache.k_scale), (vn, got_v, cache.v_scale)):
+            # a few rows quantised by the oracle, codes and scale
+            for j, h in ((0, 0), (cfg.b - 1, cfg.Hkv - 1), (cfg.b // 2, 1)):
+                x = orc.bf16_value(bits(src)[-1, j, h])
+                codes, scale = orc.e4m3_quantize_group(x)
+                assert np.array_equal(got[-1, j, h].numpy(), codes), (j, h)
+                assert float(sc[-1, h, int(pos[-1, j]), 0]) == scale, (j, h)
+    ck, cv, ks, vs = cache_np(cache)
+    kid_np = kid.cpu().numpy() if kid is not None else None
+    if n_heads is None:
+        ref, ref_lse = orc.block_attention(ck, cv, ks, vs, cfg.kv_dtype, bits(q), W.BF16, key_idx=kid_np)
+        out_s, lse_s = out, lse
+    else:
+        rng = np.random.default_rng(5)
+        heads = np.stack([rng.integers(0, cfg.B, n_heads), rng.integers(0, cfg.Hq, n_heads)], 1).astype(np.int32)
+        ref, ref_lse = orc.block_attention(ck, cv, ks, vs, cfg.kv_dtype, bits(q), W.BF16, key_idx=kid_np,
+                                           heads=heads)
+        out_s = torch.stack([out[b_, h_] for b_, h_ in heads])
+        lse_s = torch.stack([lse[b_, h_] for b_, h_ in heads])
+    e_abs, e_norm = attn_errors(out_s, ref)
+    bar = 6e-2 if cfg.kv_dtype == W.E4M3 else 2e-2
+    assert e_abs <= bar and e_norm <= 1e-2, (name, e_abs, e_norm)
+    assert np.all(np.abs(lse_s.cpu().numpy() - ref_lse) <= 1e-3), name
