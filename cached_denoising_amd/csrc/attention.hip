@@ -139,8 +139,10 @@ __global__ __launch_bounds__(NW * kWave, 2) void attn_mfma_kernel(
                     continue;
                 }
                 if (p < key_lo || p >= key_hi) continue;
-                sc.ck[(kv_base + p) * CPR + c] = kw;
-                sc.cv[(kv_base + p) * CPR + c] = vw;
+                // through the kernel's own cache pointers, so the tile loads
+                // below stay ordered after these stores
+                const_cast<uint4 *>(static_cast<const uint4 *>(ck))[(kv_base + p) * CPR + c] = kw;
+                const_cast<uint4 *>(static_cast<const uint4 *>(cv))[(kv_base + p) * CPR + c] = vw;
             }
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
@@ -792,8 +794,6 @@ int launch_scatter_attention(const dllm_kv_cache &c, const AttnPlan &p, const vo
         ScatterIn sc;
         sc.k_new = static_cast<const uint4 *>(k_new);
         sc.v_new = static_cast<const uint4 *>(v_new);
-        sc.ck = static_cast<uint4 *>(c.k);
-        sc.cv = static_cast<uint4 *>(c.v);
         sc.pos = pos;
         sc.n = n;
         sc.bad = bad;

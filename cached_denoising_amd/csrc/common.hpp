@@ -135,7 +135,6 @@ struct AttnMemo {
 // launch_scatter_attention); pos == nullptr: none
 struct ScatterIn {
     const uint4 *k_new = nullptr, *v_new = nullptr;   // [B, n, Hkv, d] as 16-byte chunks
-    uint4 *ck = nullptr, *cv = nullptr;               // the cache's K and V
     const int32_t *pos = nullptr;                     // [B, n]
     int n = 0;
     int32_t *bad = nullptr;
