@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void scatter_copy_kernel(
     cv[dst] = vw;
 }
 
-// ---- e4m3 quantise: 16 lanes per 128-element group, 8 elements per lane ----
+// ---- e4m3 quantise: 32 lanes per 128-element group, 4 elements per lane ----
 template <int SRC>
 __global__ __launch_bounds__(256) void scatter_e4m3_kernel(
     const void *__restrict__ k_new, const void *__restrict__ v_new, uint8_t *__restrict__ ck,
@@ -44,8 +44,8 @@ __global__ __launch_bounds__(256) void scatter_e4m3_kernel(
     const int32_t *__restrict__ pos, int n, int Hkv, int L, int d, int64_t n_groups,
     int32_t *__restrict__ bad) {
     const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t grp = gt >> 4;                       // global group id over (b, j, h, g)
-    const int lane16 = threadIdx.x & 15;
+    const int64_t grp = gt >> 5;                       // global group id over (b, j, h, g)
+    const int l32 = threadIdx.x & 31;
     const bool live = grp < n_groups;
     const int ng = d >> 7;
     const int64_t row = live ? grp / ng : 0;           // (b, j, h)
@@ -55,65 +55,58 @@ __global__ __launch_bounds__(256) void scatter_e4m3_kernel(
     const int b = (int)(bj / n);
     const int p = live ? pos[bj] : -1;
     const bool ok = live && p >= 0 && p < L;
-    if (live && !ok && p != -1 && bad && lane16 == 0 && h == 0 && g == 0) atomicAdd(bad, 1);
+    if (live && !ok && p != -1 && bad && l32 == 0 && h == 0 && g == 0) atomicAdd(bad, 1);
 
     // every lane takes part in the shuffles below; dead lanes contribute 0
-    const int64_t src = row * d + g * 128 + lane16 * 8;
-    float xk[8], xv[8];
+    const int64_t src = row * d + g * 128 + l32 * 4;
+    float xk[4], xv[4];
     if (live) {           // not gated on the position: the loads issue together
         if (SRC == DLLM_BF16) {
-            const uint4 wk = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(k_new) + src);
-            const uint4 wv = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(v_new) + src);
-            const uint32_t a[4] = {wk.x, wk.y, wk.z, wk.w}, c[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                xk[2 * i] = bf16lo(a[i]); xk[2 * i + 1] = bf16hi(a[i]);
-                xv[2 * i] = bf16lo(c[i]); xv[2 * i + 1] = bf16hi(c[i]);
-            }
+            const uint2 wk = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(k_new) + src);
+            const uint2 wv = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(v_new) + src);
+            xk[0] = bf16lo(wk.x); xk[1] = bf16hi(wk.x); xk[2] = bf16lo(wk.y); xk[3] = bf16hi(wk.y);
+            xv[0] = bf16lo(wv.x); xv[1] = bf16hi(wv.x); xv[2] = bf16lo(wv.y); xv[3] = bf16hi(wv.y);
         } else {
-            const float4 *pk = reinterpret_cast<const float4 *>(static_cast<const float *>(k_new) + src);
-            const float4 *pv = reinterpret_cast<const float4 *>(static_cast<const float *>(v_new) + src);
-            const float4 k0 = pk[0], k1 = pk[1], v0 = pv[0], v1 = pv[1];
+            const float4 k0 = *reinterpret_cast<const float4 *>(static_cast<const float *>(k_new) + src);
+            const float4 v0 = *reinterpret_cast<const float4 *>(static_cast<const float *>(v_new) + src);
             xk[0] = k0.x; xk[1] = k0.y; xk[2] = k0.z; xk[3] = k0.w;
-            xk[4] = k1.x; xk[5] = k1.y; xk[6] = k1.z; xk[7] = k1.w;
             xv[0] = v0.x; xv[1] = v0.y; xv[2] = v0.z; xv[3] = v0.w;
-            xv[4] = v1.x; xv[5] = v1.y; xv[6] = v1.z; xv[7] = v1.w;
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) xk[i] = xv[i] = 0.f;
+        for (int i = 0; i < 4; ++i) xk[i] = xv[i] = 0.f;
     }
     if (!ok) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) xk[i] = xv[i] = 0.f;
+        for (int i = 0; i < 4; ++i) xk[i] = xv[i] = 0.f;
     }
     float ak = 0.f, av = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
         ak = fmaxf(ak, fabsf(xk[i]));
         av = fmaxf(av, fabsf(xv[i]));
     }
 #pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) {                 // max over the 16 lanes of the group
+    for (int o = 16; o >= 1; o >>= 1) {                // max over the 32 lanes of the group
         ak = fmaxf(ak, __shfl_xor(ak, o, kWave));
         av = fmaxf(av, __shfl_xor(av, o, kWave));
     }
     if (!ok) return;
     const float sk = ak / 448.0f;                      // IEEE float32 divides
     const float sv = av / 448.0f;
-    uint32_t lok = 0, hik = 0, lov = 0, hiv = 0;
+    uint32_t ck4 = 0, cv4 = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
         const uint32_t ek = ak == 0.f ? 0u : e4m3_rne(xk[i] / sk);
         const uint32_t ev = av == 0.f ? 0u : e4m3_rne(xv[i] / sv);
-        if (i < 4) { lok |= ek << (8 * i); lov |= ev << (8 * i); }
-        else { hik |= ek << (8 * (i - 4)); hiv |= ev << (8 * (i - 4)); }
+        ck4 |= ek << (8 * i);
+        cv4 |= ev << (8 * i);
     }
     const int64_t drow = ((int64_t)b * Hkv + h) * L + p;
-    const int64_t dst = drow * d + g * 128 + lane16 * 8;
-    *reinterpret_cast<uint2 *>(ck + dst) = make_uint2(lok, hik);
-    *reinterpret_cast<uint2 *>(cv + dst) = make_uint2(lov, hiv);
-    if (lane16 == 0) {
+    const int64_t dst = drow * d + g * 128 + l32 * 4;
+    *reinterpret_cast<uint32_t *>(ck + dst) = ck4;
+    *reinterpret_cast<uint32_t *>(cv + dst) = cv4;
+    if (l32 == 0) {
         ks[drow * ng + g] = ak == 0.f ? 0.f : sk;
         vs[drow * ng + g] = av == 0.f ? 0.f : sv;
     }
@@ -189,7 +182,7 @@ int launch_scatter(const dllm_kv_cache &c, const void *k_new, const void *v_new,
     const int64_t rows = (int64_t)c.B * n * Hkv;
     if (c.dtype == DLLM_E4M3) {
         const int64_t groups = rows * (d / 128);
-        const int64_t threads = groups * 16;
+        const int64_t threads = groups * 32;
         const unsigned blocks = (unsigned)cdiv64(threads, 256);
         if (src_dtype == DLLM_BF16)
             scatter_e4m3_kernel<DLLM_BF16><<<blocks, 256, 0, s>>>(
