@@ -156,7 +156,9 @@ int dllm_cache_init(dllm_kv_cache *cache, int B, int L, int n_kv_heads, int d_he
  *                 code = round-to-nearest-even(x/scale) on the e4m3 grid,
  *                 saturating at +-448; an all-zero group gets scale 0
  *                 [LaCache, Methodology 2: per-group 1x128 FP8].
- *   pos           [B, n] int32 device; -1 = padding.
+ *   pos           [B, n] int32 device; -1 = padding.  A position given
+ *                 twice for one sequence leaves one of its rows,
+ *                 unspecified which.
  *   bad_count     optional device int32; out-of-range positions (other than
  *                 -1) are skipped and atomically added here.  May be NULL.
  * n == 0 is a no-op.
@@ -220,7 +222,9 @@ size_t dllm_block_attention_workspace(const dllm_kv_cache *cache, int q_dtype, i
  * key map, when the block's queries fit one 32-row group per KV head, the
  * attention kernel writes the rows itself (each workgroup the positions in
  * its own key range) before it loads any key tile; otherwise the two kernels
- * run in sequence on the stream.
+ * run in sequence on the stream.  A position given twice for one sequence
+ * leaves one of its rows, unspecified which.  Errors: those of the two calls,
+ * all checked before anything is enqueued.
  * ------------------------------------------------------------------------- */
 int dllm_scatter_attention(const dllm_kv_cache *cache, const void *k_new, const void *v_new,
                            int src_dtype, const int32_t *pos, int n, int32_t *bad_count,
