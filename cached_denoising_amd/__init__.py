@@ -24,7 +24,7 @@ __all__ = [
     "dllm_vocab_stats",
     "dllm_vocab_stats_workspace", "dllm_stability_reset", "dllm_stability_mask",
     "dllm_refresh_interval", "dllm_cache_quotas", "dllm_evict_by_confidence",
-    "dllm_parallel_width", "dllm_self_verify",
+    "dllm_parallel_width", "dllm_self_verify", "dllm_confidence_decay", "dllm_check_positions",
 ]
 
 F32, BF16, E4M3 = 0, 1, 2
@@ -45,10 +45,10 @@ class _KVCache(ctypes.Structure):
 class _StabParams(ctypes.Structure):
     _fields_ = [("K", ctypes.c_int32), ("D", ctypes.c_int32), ("R", ctypes.c_int32),
                 ("advance_step", ctypes.c_int32), ("tau", ctypes.c_double), ("alpha", ctypes.c_double),
-                ("beta", ctypes.c_double), ("lam", ctypes.c_double),
-                ("conf_thresh", ctypes.c_double), ("vocab", ctypes.c_int64),
+                ("beta", ctypes.c_double), ("conf_thresh", ctypes.c_double),
+                ("decay", ctypes.c_void_p), ("vocab", ctypes.c_int64),
                 ("R_early", ctypes.c_int32), ("T_steps", ctypes.c_int32),
-                ("refresh_every", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("refresh_every", ctypes.c_int32), ("n_decay", ctypes.c_int32)]
 
 
 EXPORTS = {
@@ -121,6 +121,9 @@ EXPORTS = {
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_void_p, ctypes.c_void_p]),
     "dllm_refresh_interval": (ctypes.c_int, [ctypes.c_int]),
+    "dllm_confidence_decay": (ctypes.c_int, [ctypes.c_double, ctypes.c_int, ctypes.c_void_p]),
+    "dllm_check_positions": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "dllm_cache_quotas": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_double,
                                          ctypes.c_void_p]),
     "dllm_evict_by_confidence": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
@@ -190,6 +193,74 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
+_I32 = (torch.int32,)
+_FLOAT = (torch.float32, torch.bfloat16)
+_CODES = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _want(t: Optional[torch.Tensor], name: str, shape=None, dtypes=None, numel=None,
+          required: bool = True):
+    """Shape and dtype checks of a tensor argument, before any pointer
+    reaches the library: a mismatch raises instead of letting a kernel read
+    or write past a buffer."""
+    if t is None:
+        if required:
+            raise DllmError(f"{name} is required")
+        return
+    if not isinstance(t, torch.Tensor):
+        raise DllmError(f"{name} must be a torch.Tensor")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise DllmError(f"{name}: dtype {t.dtype}, expected one of {[str(d) for d in dtypes]}")
+    if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise DllmError(f"{name}: shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+    if numel is not None and t.numel() != int(numel):
+        raise DllmError(f"{name}: {t.numel()} elements, expected {int(numel)}")
+
+
+_CACHE_TORCH = {F32: (torch.float32,), BF16: (torch.bfloat16,), E4M3: _FLOAT}
+
+
+def _want_rows(cache, k_new, v_new, pos):
+    """fresh rows [B, n, Hkv, d] in the cache's source dtype, positions [B, n] int32"""
+    B, Hkv, d = cache.desc.B, cache.desc.n_kv_heads, cache.desc.d_head
+    _want(pos, "pos", dtypes=_I32)
+    if pos.dim() != 2 or pos.shape[0] != B:
+        raise DllmError(f"pos: shape {tuple(pos.shape)}, expected [{B}, n]")
+    n = pos.shape[1]
+    _want(k_new, "k_new", (B, n, Hkv, d), _CACHE_TORCH[cache.desc.dtype])
+    _want(v_new, "v_new", (B, n, Hkv, d), (k_new.dtype,))
+    return n
+
+
+def _want_queries(cache, q):
+    _want(q, "q", dtypes=_FLOAT)
+    if q.dim() != 4 or q.shape[0] != cache.desc.B or q.shape[3] != cache.desc.d_head:
+        raise DllmError(f"q: shape {tuple(q.shape)}, expected [{cache.desc.B}, Hq, b, {cache.desc.d_head}]")
+    if q.shape[1] % cache.desc.n_kv_heads != 0:
+        raise DllmError(f"q: {q.shape[1]} query heads, not a multiple of {cache.desc.n_kv_heads} KV heads")
+    return q.shape
+
+
+def _want_key_map(cache, key_idx):
+    if key_idx is None:
+        return cache.desc.L
+    _want(key_idx, "key_idx", dtypes=_I32)
+    if key_idx.dim() != 2 or key_idx.shape[0] != cache.desc.B:
+        raise DllmError(f"key_idx: shape {tuple(key_idx.shape)}, expected [{cache.desc.B}, n_keys]")
+    return key_idx.shape[1]
+
+
+def _want_out(out, lse, B, Hq, b, d):
+    _want(out, "out", (B, Hq, b, d), _FLOAT)
+    _want(lse, "lse", (B, Hq, b), (torch.float32,), required=False)
+
+
+def _want_counter(t, name):
+    _want(t, name, dtypes=_I32, required=False)
+    if t is not None and t.numel() < 1:
+        raise DllmError(f"{name} must hold at least one int32")
+
+
 class Cache:
     """One layer's persistent K/V cache: the C descriptor plus the tensors it
     points to (kept alive here)."""
@@ -219,7 +290,8 @@ def dllm_cache_init(k: torch.Tensor, v: torch.Tensor, dtype: Optional[int] = Non
 def dllm_scatter_kv(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, pos: torch.Tensor,
                     bad_count: Optional[torch.Tensor] = None):
     """k_new, v_new: [B, n, Hkv, d]; pos: [B, n] int32 (-1 = padding)."""
-    n = pos.shape[1]
+    n = _want_rows(cache, k_new, v_new, pos)
+    _want_counter(bad_count, "bad_count")
     rc = lib().dllm_scatter_kv(ctypes.byref(cache.desc), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
                                _dtype_code(k_new), _dev(pos, "pos"), n, _dev(bad_count, "bad_count"),
                                _stream())
@@ -228,7 +300,11 @@ def dllm_scatter_kv(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, pos:
 
 def dllm_sink_rolling_map(L: int, S: int, R: int, end: torch.Tensor, key_idx: torch.Tensor):
     """key_idx[b] = sinks [0, min(S, e)) then [max(S, e-R), e), -1 padded."""
+    _want(key_idx, "key_idx", dtypes=_I32)
+    if key_idx.dim() != 2:
+        raise DllmError("key_idx must be [B, n_keys]")
     B, n_keys = key_idx.shape
+    _want(end, "end", (B,), _I32)
     rc = lib().dllm_sink_rolling_map(B, L, S, R, _dev(end, "end"), _dev(key_idx, "key_idx"), n_keys,
                                      _stream())
     _check(rc, "dllm_sink_rolling_map")
@@ -244,10 +320,11 @@ def dllm_block_attention(cache: Cache, q: torch.Tensor, key_idx: Optional[torch.
                          out_dtype: Optional[torch.dtype] = None, lse: Optional[torch.Tensor] = None,
                          workspace: Optional[torch.Tensor] = None):
     """q: [B, Hq, b, d]; returns out [B, Hq, b, d] (and fills lse if given)."""
-    B, Hq, b, d = q.shape
-    n_keys = key_idx.shape[1] if key_idx is not None else cache.desc.L
+    B, Hq, b, d = _want_queries(cache, q)
+    n_keys = _want_key_map(cache, key_idx)
     if out is None:
         out = torch.empty((B, Hq, b, d), dtype=out_dtype or q.dtype, device=q.device)
+    _want_out(out, lse, B, Hq, b, d)
     ws_need = dllm_block_attention_workspace(cache, _dtype_code(q), Hq, b, n_keys)
     if workspace is None and ws_need:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
@@ -267,11 +344,13 @@ def dllm_scatter_attention(cache: Cache, k_new: torch.Tensor, v_new: torch.Tenso
                            bad_count: Optional[torch.Tensor] = None):
     """dllm_scatter_kv(cache, k_new, v_new, pos) then dllm_block_attention(cache,
     q, ...) in one call; returns out [B, Hq, b, d]."""
-    B, Hq, b, d = q.shape
-    n = pos.shape[1]
-    n_keys = key_idx.shape[1] if key_idx is not None else cache.desc.L
+    B, Hq, b, d = _want_queries(cache, q)
+    n = _want_rows(cache, k_new, v_new, pos)
+    _want_counter(bad_count, "bad_count")
+    n_keys = _want_key_map(cache, key_idx)
     if out is None:
         out = torch.empty((B, Hq, b, d), dtype=out_dtype or q.dtype, device=q.device)
+    _want_out(out, lse, B, Hq, b, d)
     ws_need = dllm_block_attention_workspace(cache, _dtype_code(q), Hq, b, n_keys)
     if workspace is None and ws_need:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
@@ -290,11 +369,18 @@ def dllm_facache_maps(L: int, blk: int, start: torch.Tensor,
                       block_idx: Optional[torch.Tensor] = None):
     """start: [B] int32 block offsets; returns (unchanged_idx [B, L - blk],
     block_idx [B, blk]) int32."""
+    _want(start, "start", dtypes=_I32)
+    if start.dim() != 1:
+        raise DllmError("start must be [B]")
     B = start.shape[0]
+    if not 1 <= blk < L:
+        raise DllmError(f"block length {blk} must be in [1, L) with L = {L}")
     if unchanged_idx is None:
         unchanged_idx = torch.empty((B, L - blk), dtype=torch.int32, device=start.device)
     if block_idx is None:
         block_idx = torch.empty((B, blk), dtype=torch.int32, device=start.device)
+    _want(unchanged_idx, "unchanged_idx", (B, L - blk), _I32)
+    _want(block_idx, "block_idx", (B, blk), _I32)
     rc = lib().dllm_facache_maps(B, L, blk, _dev(start, "start"), _dev(unchanged_idx, "unchanged_idx"),
                                  _dev(block_idx, "block_idx"), _stream())
     _check(rc, "dllm_facache_maps")
@@ -313,14 +399,15 @@ def dllm_facache_merge(cache: Cache, q: torch.Tensor, memo_o: torch.Tensor, memo
     """q: [B, Hq, n_q, d] queries outside the block; memo_o [B, Hq, n_q, d]
     and memo_lse [B, Hq, n_q] float32 (a dllm_block_attention output over the
     unchanged keys); key_idx: [B, n_keys] changed keys.  Returns out."""
-    B, Hq, n_q, d = q.shape
+    B, Hq, n_q, d = _want_queries(cache, q)
     if memo_o.dtype != torch.float32 or memo_lse.dtype != torch.float32:
         raise DllmError("memo_o and memo_lse must be float32")
     if tuple(memo_o.shape) != (B, Hq, n_q, d) or tuple(memo_lse.shape) != (B, Hq, n_q):
         raise DllmError("memo shapes must be [B, Hq, n_q, d] and [B, Hq, n_q]")
-    n_keys = key_idx.shape[1] if key_idx is not None else cache.desc.L
+    n_keys = _want_key_map(cache, key_idx)
     if out is None:
         out = torch.empty((B, Hq, n_q, d), dtype=out_dtype or q.dtype, device=q.device)
+    _want_out(out, lse, B, Hq, n_q, d)
     ws_need = dllm_facache_merge_workspace(cache, _dtype_code(q), Hq, n_q, n_keys)
     if workspace is None and ws_need:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
@@ -344,11 +431,16 @@ def dllm_fp8_quant_rows(x: torch.Tensor, codes: Optional[torch.Tensor] = None,
                         scales: Optional[torch.Tensor] = None):
     """x: [M, K] float32/bfloat16 (rows may be strided); returns (codes
     [M, K] uint8, scales [K/128, M] uint8 E8M0)."""
+    _want(x, "x", dtypes=_FLOAT)
+    if x.dim() != 2:
+        raise DllmError("x must be [M, K]")
     M, K = x.shape
     if x.stride(1) != 1:
         raise DllmError("x rows must be contiguous")
     codes = torch.empty((M, K), dtype=torch.uint8, device=x.device) if codes is None else codes
     scales = torch.empty((K // 128, M), dtype=torch.uint8, device=x.device) if scales is None else scales
+    _want(codes, "codes", (M, K), _CODES)
+    _want(scales, "scales", (K // 128, M), _CODES)
     rc = lib().dllm_fp8_quant_rows(_dev(x, "x", contiguous=False), _dtype_code(x), M, K, x.stride(0),
                                    _u8(codes, "codes"), _u8(scales, "scales"), _stream())
     _check(rc, "dllm_fp8_quant_rows")
@@ -361,12 +453,21 @@ def dllm_fp8_addnorm_quant(x: torch.Tensor, residual: Optional[torch.Tensor], ga
                            write_residual: bool = True):
     """r = x + residual (stored in residual_out), y = RMSNorm(r) * gamma,
     quantised per 1 x 128 group; returns (residual_out, codes, scales)."""
+    _want(x, "x", dtypes=_FLOAT)
+    if x.dim() != 2:
+        raise DllmError("x must be [M, K]")
     M, K = x.shape
     dev = x.device
+    _want(residual, "residual", (M, K), (x.dtype,), required=False)
+    _want(gamma, "gamma", (K,), (x.dtype,))
     if write_residual and residual_out is None:
         residual_out = torch.empty_like(x)
+    if write_residual:
+        _want(residual_out, "residual_out", (M, K), (x.dtype,))
     codes = torch.empty((M, K), dtype=torch.uint8, device=dev) if codes is None else codes
     scales = torch.empty((K // 128, M), dtype=torch.uint8, device=dev) if scales is None else scales
+    _want(codes, "codes", (M, K), _CODES)
+    _want(scales, "scales", (K // 128, M), _CODES)
     rc = lib().dllm_fp8_addnorm_quant(_dev(x, "x"), _dev(residual, "residual"), _dev(gamma, "gamma"),
                                       _dtype_code(x), float(eps), M, K,
                                       _dev(residual_out, "residual_out") if write_residual else None,
@@ -378,23 +479,38 @@ def dllm_fp8_addnorm_quant(x: torch.Tensor, residual: Optional[torch.Tensor], ga
 def dllm_fp8_quant_weight(w: torch.Tensor, codes: Optional[torch.Tensor] = None,
                           scales: Optional[torch.Tensor] = None):
     """w: [N, K]; returns (codes [N, K], scales [N/128, K/128])."""
+    _want(w, "w", dtypes=_FLOAT)
+    if w.dim() != 2:
+        raise DllmError("w must be [N, K]")
     N, K = w.shape
     codes = torch.empty((N, K), dtype=torch.uint8, device=w.device) if codes is None else codes
     scales = torch.empty((N // 128, K // 128), dtype=torch.uint8, device=w.device) if scales is None else scales
+    _want(codes, "codes", (N, K), _CODES)
+    _want(scales, "scales", (N // 128, K // 128), _CODES)
     rc = lib().dllm_fp8_quant_weight(_dev(w, "w"), _dtype_code(w), N, K, _u8(codes, "codes"),
                                      _u8(scales, "scales"), _stream())
     _check(rc, "dllm_fp8_quant_weight")
     return codes, scales
 
 
+def _want_gemm(a, a_scale, w, w_scale):
+    _want(a, "a", dtypes=_CODES)
+    _want(w, "w", dtypes=_CODES)
+    if a.dim() != 2 or w.dim() != 2 or a.shape[1] != w.shape[1]:
+        raise DllmError(f"a [M, K] and w [N, K] disagree: {tuple(a.shape)}, {tuple(w.shape)}")
+    M, K = a.shape
+    N = w.shape[0]
+    _want(a_scale, "a_scale", (K // 128, M), _CODES)
+    _want(w_scale, "w_scale", (N // 128, K // 128), _CODES)
+    return M, K, N
+
+
 def dllm_fp8_gemm(a: torch.Tensor, a_scale: torch.Tensor, w: torch.Tensor, w_scale: torch.Tensor,
                   out: Optional[torch.Tensor] = None):
     """C = dequant(A) dequant(W)^T, bf16 [M, N]."""
-    M, K = a.shape
-    N = w.shape[0]
+    M, K, N = _want_gemm(a, a_scale, w, w_scale)
     out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device) if out is None else out
-    if out.dtype != torch.bfloat16:
-        raise DllmError("out must be bfloat16")
+    _want(out, "out", (M, N), (torch.bfloat16,))
     rc = lib().dllm_fp8_gemm(_u8(a, "a"), _u8(a_scale, "a_scale"), _u8(w, "w"), _u8(w_scale, "w_scale"),
                              M, N, K, _dev(out, "out"), _stream())
     _check(rc, "dllm_fp8_gemm")
@@ -406,11 +522,12 @@ def dllm_fp8_gemm_swiglu(a: torch.Tensor, a_scale: torch.Tensor, w: torch.Tensor
                          out_scales: Optional[torch.Tensor] = None):
     """h = silu(gate) * up from the interleaved Gate-Up weight, quantised:
     returns (codes [M, N/2], scales [N/256, M])."""
-    M, K = a.shape
-    N = w.shape[0]
+    M, K, N = _want_gemm(a, a_scale, w, w_scale)
     dev = a.device
     out_codes = torch.empty((M, N // 2), dtype=torch.uint8, device=dev) if out_codes is None else out_codes
     out_scales = torch.empty((N // 256, M), dtype=torch.uint8, device=dev) if out_scales is None else out_scales
+    _want(out_codes, "out_codes", (M, N // 2), _CODES)
+    _want(out_scales, "out_scales", (N // 256, M), _CODES)
     rc = lib().dllm_fp8_gemm_swiglu(_u8(a, "a"), _u8(a_scale, "a_scale"), _u8(w, "w"),
                                     _u8(w_scale, "w_scale"), M, N, K, _u8(out_codes, "out_codes"),
                                     _u8(out_scales, "out_scales"), _stream())
@@ -427,14 +544,22 @@ def dllm_vocab_stats(logits: torch.Tensor, V: Optional[int] = None,
                      entropy: Optional[torch.Tensor] = None,
                      workspace: Optional[torch.Tensor] = None):
     """logits: [N, >= V] (rows may be a strided view); returns (argmax, maxprob, entropy)."""
+    _want(logits, "logits", dtypes=_FLOAT)
+    if logits.dim() != 2:
+        raise DllmError("logits must be [N, >= V]")
     N = logits.shape[0]
     V = logits.shape[1] if V is None else V
+    if not 1 <= V <= logits.shape[1]:
+        raise DllmError(f"V = {V} must be in [1, {logits.shape[1]}]")
     if logits.stride(1) != 1:
         raise DllmError("logits rows must be contiguous")
     dev = logits.device
     argmax = torch.empty(N, dtype=torch.int32, device=dev) if argmax is None else argmax
     maxprob = torch.empty(N, dtype=torch.float32, device=dev) if maxprob is None else maxprob
     entropy = torch.empty(N, dtype=torch.float32, device=dev) if entropy is None else entropy
+    _want(argmax, "argmax", (N,), _I32)
+    _want(maxprob, "maxprob", (N,), (torch.float32,))
+    _want(entropy, "entropy", (N,), (torch.float32,))
     ws_need = dllm_vocab_stats_workspace(N, V)
     if workspace is None and ws_need:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
@@ -464,7 +589,46 @@ class StabilityState:
         self.count = torch.empty((B,), dtype=torch.int32, device=device)
         self.all_stable = torch.empty((B,), dtype=torch.uint8, device=device)
         self.cached = torch.zeros((B, L), dtype=torch.uint8, device=device)   # K/V held per position
+        self._decay = {}                      # (lambda, n) -> device table of exp(-lambda k)
         dllm_stability_reset(self)
+
+    def decay_table(self, lam: float, n: int = 4096) -> torch.Tensor:
+        """The device copy of dllm_confidence_decay(lam, n), made once per
+        (lam, n) and kept with the state (call it before capturing a graph)."""
+        key = (float(lam), int(n))
+        t = self._decay.get(key)
+        if t is None:
+            if torch.cuda.is_current_stream_capturing():
+                raise DllmError("the decay table must be made before graph capture: call decay_table() first")
+            t = dllm_confidence_decay(lam, n).to(self.mask.device)
+            self._decay[key] = t
+        return t
+
+
+def dllm_confidence_decay(lam: float, n: int = 4096) -> torch.Tensor:
+    """Host table exp(-lam * k), k = 0 .. n-1, float64 (CPU tensor)."""
+    t = torch.empty(int(n), dtype=torch.float64)
+    rc = lib().dllm_confidence_decay(float(lam), int(n), t.data_ptr())
+    _check(rc, "dllm_confidence_decay")
+    return t
+
+
+def dllm_check_positions(L: int, pos: torch.Tensor, bad: Optional[torch.Tensor] = None,
+                         dup: Optional[torch.Tensor] = None):
+    """Per sequence: entries of pos [B, n] outside [0, L) (other than -1),
+    and entries repeating an earlier position.  Returns (bad, dup) [B] int32."""
+    _want(pos, "pos", dtypes=_I32)
+    if pos.dim() != 2:
+        raise DllmError("pos must be [B, n]")
+    B, n = pos.shape
+    bad = torch.empty(B, dtype=torch.int32, device=pos.device) if bad is None else bad
+    dup = torch.empty(B, dtype=torch.int32, device=pos.device) if dup is None else dup
+    _want(bad, "bad", (B,), _I32)
+    _want(dup, "dup", (B,), _I32)
+    rc = lib().dllm_check_positions(B, int(L), _dev(pos, "pos"), n, _dev(bad, "bad"), _dev(dup, "dup"),
+                                    _stream())
+    _check(rc, "dllm_check_positions")
+    return bad, dup
 
 
 def dllm_stability_reset(st: StabilityState):
@@ -480,18 +644,29 @@ def dllm_stability_mask(st: StabilityState, step, pos: Optional[torch.Tensor],
                         K: int, tau: float, R: int, alpha: float = 0.0, beta: float = 0.0,
                         lam: float = 0.0, conf_thresh: float = 0.0, V: int = 2,
                         with_conf: bool = True, advance_step: bool = False, R_early: int = 0,
-                        T_steps: int = 0, refresh_every: int = 0):
+                        T_steps: int = 0, refresh_every: int = 0, n_decay: int = 4096):
     """One step of history, stability, confidence and window mask; outputs
     land in st.mask, st.conf, st.next_pos, st.count, st.all_stable.  ``step``
     is an int, or a [B] int32 GPU tensor of per-sequence step numbers read
     when the kernel runs (for captured graphs); with ``advance_step`` the
     kernel increments that tensor once it has used it.  ``R_early`` and
     ``T_steps`` widen the window radius from R_early to R over T_steps steps;
-    ``refresh_every`` > 0 makes every such step (after step 0) a full refresh."""
+    ``refresh_every`` > 0 makes every such step (after step 0) a full refresh.
+    The confidence's age factor exp(-lam * dt) is read from the state's
+    n_decay-entry table (ages past the end read its last entry)."""
+    if pos is not None:
+        _want(pos, "pos", dtypes=_I32)
+        if pos.dim() != 2 or pos.shape[0] != st.B:
+            raise DllmError(f"pos: shape {tuple(pos.shape)}, expected [{st.B}, n]")
     n = pos.shape[1] if pos is not None else st.L
+    _want(argmax, "argmax", dtypes=_I32, numel=st.B * n)
+    _want(maxprob, "maxprob", dtypes=(torch.float32,), numel=st.B * n)
+    _want(entropy, "entropy", dtypes=(torch.float32,), numel=st.B * n)
+    decay = st.decay_table(lam, n_decay) if beta != 0.0 else None
     prm = _StabParams(K=K, D=st.D, R=R, advance_step=int(advance_step), tau=tau, alpha=alpha, beta=beta,
-                      lam=lam, conf_thresh=conf_thresh, vocab=V, R_early=R_early, T_steps=T_steps,
-                      refresh_every=refresh_every, reserved=0)
+                      conf_thresh=conf_thresh, decay=decay.data_ptr() if decay is not None else None,
+                      vocab=V, R_early=R_early, T_steps=T_steps, refresh_every=refresh_every,
+                      n_decay=int(n_decay) if decay is not None else 0)
     if isinstance(step, torch.Tensor):
         if step.dtype != torch.int32 or step.numel() != st.B:
             raise ValueError("step tensor: [B] int32 per-sequence step numbers")
@@ -535,6 +710,11 @@ def dllm_evict_by_confidence(st: StabilityState, quota: torch.Tensor, pos: Optio
     the confidence the preceding stability step wrote)."""
     if quota.dtype != torch.int32 or quota.numel() != st.B:
         raise ValueError("quota: [B] int32")
+    if pos is not None:
+        _want(pos, "pos", dtypes=_I32)
+        if pos.dim() != 2 or pos.shape[0] != st.B:
+            raise DllmError(f"pos: shape {tuple(pos.shape)}, expected [{st.B}, n]")
+    _want(evicted, "evicted", (st.B,), _I32, required=False)
     n = pos.shape[1] if pos is not None else st.L
     rc = lib().dllm_evict_by_confidence(st.B, st.L, _dev(st.conf, "conf"), _dev(quota, "quota"),
                                         _dev(pos, "pos"), n, _dev(st.cached, "cached"), _dev(st.mask, "mask"),

@@ -27,6 +27,9 @@ FLAGS = [
     # no packed-fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# files whose float64 decisions must equal the plain definition's: no fused
+# multiply-add anywhere in them
+PER_FILE = {"stability.hip": ["-ffp-contract=off"], "verify.hip": ["-ffp-contract=off"]}
 
 
 def hipcc() -> str:
@@ -42,7 +45,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [cc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *FLAGS, *PER_FILE.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

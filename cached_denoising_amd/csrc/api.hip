@@ -348,10 +348,13 @@ int dllm_stability_mask(int B, int L, int step, int32_t *step_dev, const int32_t
     const dllm_stab_params &p = *params;
     if (p.K < 1 || p.D < p.K || p.R < 0 || p.vocab < 2) return DLLM_EINVAL;
     if (p.advance_step && !step_dev) return DLLM_EINVAL;   // nothing to advance
-    if (p.R_early < 0 || p.T_steps < 0 || p.refresh_every < 0 || p.reserved != 0) return DLLM_EINVAL;
+    if (p.R_early < 0 || p.T_steps < 0 || p.refresh_every < 0) return DLLM_EINVAL;
     if (!(p.tau == p.tau) || !(p.alpha == p.alpha) || !(p.beta == p.beta) ||
-        !(p.lambda == p.lambda) || !(p.conf_thresh == p.conf_thresh))
+        !(p.conf_thresh == p.conf_thresh))
         return DLLM_EINVAL;
+    // the age factor is read from the caller's table whenever beta is not 0
+    if (p.beta != 0.0 && (!p.decay || p.n_decay < 1)) return DLLM_EINVAL;
+    if (p.beta != 0.0 && ((uintptr_t)p.decay & 7u) != 0) return DLLM_EALIGN;
     if ((n > 0 && (!argmax || !maxprob || !entropy)) || !ring_argmax || !ring_maxprob ||
         !ring_step || !entropy_latest || !t_write || !stable || !mask || !next_pos || !count ||
         !all_stable)
@@ -362,6 +365,21 @@ int dllm_stability_mask(int B, int L, int step, int32_t *step_dev, const int32_t
                             ring_maxprob, ring_step, entropy_latest, t_write, stable, p, hmax,
                             mask, conf, next_pos, count, all_stable,
                             static_cast<hipStream_t>(stream));
+}
+
+int dllm_confidence_decay(double lambda, int n, double *table) {
+    if (!table || n < 1 || !(lambda >= 0.0) || std::isinf(lambda)) return DLLM_EINVAL;
+    // the C library's exp of the float64 product, one value per age
+    for (int k = 0; k < n; ++k) table[k] = std::exp(-lambda * (double)k);
+    return DLLM_OK;
+}
+
+int dllm_check_positions(int B, int L, const int32_t *pos, int n, int32_t *bad, int32_t *dup,
+                         void *stream) {
+    if (B < 1 || L < 1 || n < 0) return DLLM_ESHAPE;
+    if (B > 65535 || L > 131072) return DLLM_ERANGE;
+    if ((n > 0 && !pos) || !bad || !dup) return DLLM_EINVAL;
+    return launch_check_positions(B, L, pos, n, bad, dup, static_cast<hipStream_t>(stream));
 }
 
 int dllm_refresh_interval(int T) {

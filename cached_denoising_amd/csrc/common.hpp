@@ -110,6 +110,8 @@ int launch_scatter(const dllm_kv_cache &c, const void *k_new, const void *v_new,
 
 int launch_sink_rolling(int B, int L, int S, int R, const int32_t *end, int32_t *key_idx,
                         int n_keys, hipStream_t s);
+int launch_check_positions(int B, int L, const int32_t *pos, int n, int32_t *bad, int32_t *dup,
+                           hipStream_t s);
 int launch_facache_maps(int B, int L, int b, const int32_t *start, int32_t *unchanged_idx,
                         int32_t *block_idx, hipStream_t s);
 

@@ -136,6 +136,46 @@ __global__ __launch_bounds__(256) void sink_rolling_kernel(int L, int S, int R,
         out[j] = j < ns ? j : (j < ns + nr ? start + (j - ns) : -1);
 }
 
+// Debug check of a position list: per sequence, the entries outside [0, L)
+// (other than the padding -1) and the entries repeating a position already
+// seen.  One workgroup per sequence marks each position in an LDS bitset; the
+// old word of the atomic OR tells whether the bit was set before.  Which of
+// two equal entries counts as the repeat depends on the order of the
+// atomics, their number does not.
+constexpr int kCheckThreads = 1024;
+__global__ __launch_bounds__(kCheckThreads) void check_positions_kernel(int L, const int32_t *__restrict__ pos,
+                                                                        int n, int32_t *__restrict__ bad,
+                                                                        int32_t *__restrict__ dup) {
+    extern __shared__ uint32_t seen[];
+    __shared__ int part[2][kCheckThreads / kWave];
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int words = (L + 31) >> 5;
+    for (int w = tid; w < words; w += kCheckThreads) seen[w] = 0;
+    __syncthreads();
+    int nb = 0, nd = 0;
+    const int32_t *row = pos + (int64_t)b * n;
+    for (int j = tid; j < n; j += kCheckThreads) {
+        const int p = row[j];
+        if (p == -1) continue;
+        if (p < 0 || p >= L) { ++nb; continue; }
+        const uint32_t bit = 1u << (p & 31);
+        if (atomicOr(&seen[p >> 5], bit) & bit) ++nd;
+    }
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) {
+        nb += __shfl_xor(nb, o, kWave);
+        nd += __shfl_xor(nd, o, kWave);
+    }
+    if (lane == 0) { part[0][wave] = nb; part[1][wave] = nd; }
+    __syncthreads();
+    if (tid == 0) {
+        int tb = 0, td = 0;
+        for (int w = 0; w < kCheckThreads / kWave; ++w) { tb += part[0][w]; td += part[1][w]; }
+        bad[b] = tb;
+        dup[b] = td;
+    }
+}
+
 // Unchanged and changed key positions of one SAR step [LaCache, problem
 // statement and Methodology 1]: only the active block [o, o + b) changes
 // within a block's denoising steps.  Both lists ascending, one thread per
@@ -200,6 +240,13 @@ int launch_scatter(const dllm_kv_cache &c, const void *k_new, const void *v_new,
     scatter_copy_kernel<<<(unsigned)cdiv64(total, 256), 256, 0, s>>>(
         static_cast<const uint4 *>(k_new), static_cast<const uint4 *>(v_new),
         static_cast<uint4 *>(c.k), static_cast<uint4 *>(c.v), pos, n, Hkv, L, cpr, total, bad);
+    return launch_status();
+}
+
+int launch_check_positions(int B, int L, const int32_t *pos, int n, int32_t *bad, int32_t *dup,
+                           hipStream_t s) {
+    const size_t shmem = sizeof(uint32_t) * (size_t)((L + 31) / 32);   // <= 16 KB for L <= 131072
+    check_positions_kernel<<<dim3((unsigned)B), dim3(kCheckThreads), shmem, s>>>(L, pos, n, bad, dup);
     return launch_status();
 }
 

@@ -12,12 +12,19 @@
 //   - SWD page, 4.4: the window radius may widen over the trajectory (small
 //     or none early, larger late): a linear ramp from R_early to R.
 //   - Flash-dLLM page, 5.1: a full refresh every few steps.
-// The decisions (mean > tau, conf < threshold) are taken in float64.
+// The decisions (mean > tau, conf < threshold) are taken in float64, each
+// value a chain of single IEEE operations on the same inputs as the plain
+// definition: this file is compiled without floating-point contraction (no
+// fused multiply-add), and the age factor exp(-lambda dt) is read from a
+// table the host computed, so the confidence and every decision on it equal
+// the definition's float64 values bit for bit.
 //
 // Also the budgeted cache of Flash-dLLM 3.3 and 5.2: per sequence, the
 // cached positions beyond its quota leave the cache lowest confidence first,
 // and every position without cached K/V joins the next step's mask.
 #include "common.hpp"
+
+#pragma clang fp contract(off)
 
 namespace dllm {
 namespace {
@@ -51,8 +58,8 @@ __global__ __launch_bounds__(kThreads) void stability_kernel(
     float *__restrict__ ring_maxprob, int32_t *__restrict__ ring_step,
     float *__restrict__ entropy_latest, int32_t *__restrict__ t_write,
     uint8_t *__restrict__ stable, int K, int D, int R, int R_early, int T_steps, int refresh_every,
-    double tau, double alpha, double beta,
-    double lambda, double conf_thresh, double hmax, uint8_t *__restrict__ mask,
+    double tau, double alpha, double beta, const double *__restrict__ decay, int n_decay,
+    double conf_thresh, double hmax, uint8_t *__restrict__ mask,
     float *__restrict__ conf, int32_t *__restrict__ next_pos, int32_t *__restrict__ count,
     uint8_t *__restrict__ all_stable) {
     extern __shared__ uint32_t seed_bits[];            // one bit per position
@@ -115,13 +122,17 @@ __global__ __launch_bounds__(kThreads) void stability_kernel(
         if (i < L) {
             const bool st = stable[rowoff + i] != 0;
             // with the gate off (alpha = beta = 0) the score is +0 whatever the
-            // entropy and age; a zero beta drops the float64 exponential, whose
-            // term would add +0
+            // entropy and age; a zero beta drops the age term, which would add
+            // +0 (the table is then not read)
             double cf = 0.0;
             if (alpha != 0.0 || beta != 0.0) {
                 const double h = (double)entropy_latest[rowoff + i];
-                const double dt = (double)(step - t_write[rowoff + i]);
-                cf = alpha * (1.0 - h / hmax) + (beta != 0.0 ? beta * exp(-lambda * dt) : 0.0);
+                double age = 0.0;
+                if (beta != 0.0) {
+                    const int dt = step - t_write[rowoff + i];
+                    age = beta * decay[dt < 0 ? 0 : min(dt, n_decay - 1)];
+                }
+                cf = alpha * (1.0 - h / hmax) + age;
             }
             if (conf) conf[rowoff + i] = (float)cf;
             seed = !st || cf < conf_thresh;
@@ -502,7 +513,7 @@ int launch_stability(int B, int L, int step, int32_t *step_dev, const int32_t *p
         B, L, step, step_dev, prm.advance_step, pos, n, argmax, maxprob, entropy, ring_argmax, ring_maxprob, ring_step,
         entropy_latest, t_write, stable, prm.K, prm.D, prm.R, prm.R_early, prm.T_steps,
         prm.refresh_every, prm.tau, prm.alpha, prm.beta,
-        prm.lambda, prm.conf_thresh, hmax, mask, conf, next_pos, count, all_stable);
+        prm.decay, prm.n_decay, prm.conf_thresh, hmax, mask, conf, next_pos, count, all_stable);
     return launch_status();
 }
 

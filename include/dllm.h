@@ -46,8 +46,11 @@
  *     nothing; a HIP launch error returns DLLM_EHIP.
  *   - An index of -1 in a position list or key map is padding and is
  *     skipped; any other index outside [0, L) is skipped too and counted in
- *     the optional `bad_count` where a call has one.  Duplicate positions
- *     within one sequence in a single call are a caller error (racing writes).
+ *     the optional `bad_count` where a call has one.  A position given
+ *     twice for one sequence in a single scatter is a caller error: the
+ *     cache row at that position is then unspecified (its 16-byte chunks
+ *     may come from either fresh row, and an e4m3 row's codes may pair with
+ *     the other row's scale).  dllm_check_positions finds such lists.
  *   - Results are bitwise reproducible run to run: reductions merge in a
  *     fixed order and use no floating-point atomics.
  */
@@ -97,9 +100,17 @@ typedef struct {
  *   R            window radius around each position to recompute [SWD, 3.2]
  *   tau          stability threshold: mean max-prob over the K steps must
  *                exceed it (strictly) [SWD, 3.1]
- *   alpha, beta, lambda
+ *   alpha, beta, decay, n_decay
  *                cache confidence alpha*(1 - H/ln V) + beta*exp(-lambda*dt)
- *                [Flash, 3.1]
+ *                [Flash, 3.1].  The exponential comes from a table:
+ *                decay is a DEVICE array of n_decay float64 values,
+ *                decay[k] = exp(-lambda*k) as dllm_confidence_decay writes
+ *                it on the host, read at k = min(dt, n_decay - 1) (dt < 0
+ *                reads k = 0); so every value of the score is plain IEEE
+ *                float64 arithmetic (no fused multiply-add) on host-computed
+ *                inputs.  n_decay >= the trajectory length makes the
+ *                lookup exact.  With beta = 0 the table is not read and may
+ *                be NULL.
  *   conf_thresh  positions whose confidence is below it are recomputed
  *                [Flash, 3.1]; <= 0 turns the gate off
  *   vocab        V of the vocab pass (max entropy ln V)
@@ -113,13 +124,13 @@ typedef struct {
  *   refresh_every
  *                every refresh_every-th step (s > 0) recomputes the whole
  *                sequence [Flash, 5.1]; 0 never (dllm_refresh_interval gives
- *                the pages' interval for a trajectory length)
- *   reserved     must be 0 */
+ *                the pages' interval for a trajectory length) */
 typedef struct {
     int32_t K, D, R, advance_step;
-    double tau, alpha, beta, lambda, conf_thresh;
+    double tau, alpha, beta, conf_thresh;
+    const double *decay;
     int64_t vocab;
-    int32_t R_early, T_steps, refresh_every, reserved;
+    int32_t R_early, T_steps, refresh_every, n_decay;
 } dllm_stab_params;
 
 /* Human-readable name of a status code (static string). */
@@ -156,9 +167,8 @@ int dllm_cache_init(dllm_kv_cache *cache, int B, int L, int n_kv_heads, int d_he
  *                 code = round-to-nearest-even(x/scale) on the e4m3 grid,
  *                 saturating at +-448; an all-zero group gets scale 0
  *                 [LaCache, Methodology 2: per-group 1x128 FP8].
- *   pos           [B, n] int32 device; -1 = padding.  A position given
- *                 twice for one sequence leaves one of its rows,
- *                 unspecified which.
+ *   pos           [B, n] int32 device; -1 = padding.  Positions must be
+ *                 distinct within a sequence (see the conventions above).
  *   bad_count     optional device int32; out-of-range positions (other than
  *                 -1) are skipped and atomically added here.  May be NULL.
  * n == 0 is a no-op.
@@ -166,6 +176,21 @@ int dllm_cache_init(dllm_kv_cache *cache, int B, int L, int n_kv_heads, int d_he
 int dllm_scatter_kv(const dllm_kv_cache *cache, const void *k_new, const void *v_new,
                     int src_dtype, const int32_t *pos, int n, int32_t *bad_count,
                     void *stream);
+
+/* ---------------------------------------------------------------------------
+ * dllm_check_positions -- the debug check of a scatter's position list
+ * [Sinks, 5.1 warns that cache rows written to the wrong place corrupt every
+ * later step]: per sequence b, bad[b] = the entries of pos[b, :] outside
+ * [0, L) other than the padding value -1, and dup[b] = the entries that
+ * repeat a position an earlier entry of the same sequence holds (n_valid -
+ * n_distinct).  A list is a valid dllm_scatter_kv argument iff both are 0.
+ *   pos      [B, n] int32 device
+ *   bad, dup [B] int32 device outputs
+ * Limits: 1 <= L <= 131072 (one bit per position in on-chip memory),
+ * B <= 65535, n >= 0.
+ * ------------------------------------------------------------------------- */
+int dllm_check_positions(int B, int L, const int32_t *pos, int n, int32_t *bad, int32_t *dup,
+                         void *stream);
 
 /* ---------------------------------------------------------------------------
  * dllm_sink_rolling_map -- key index map of S attention sinks plus a rolling
@@ -222,9 +247,9 @@ size_t dllm_block_attention_workspace(const dllm_kv_cache *cache, int q_dtype, i
  * key map, when the block's queries fit one 32-row group per KV head, the
  * attention kernel writes the rows itself (each workgroup the positions in
  * its own key range) before it loads any key tile; otherwise the two kernels
- * run in sequence on the stream.  A position given twice for one sequence
- * leaves one of its rows, unspecified which.  Errors: those of the two calls,
- * all checked before anything is enqueued.
+ * run in sequence on the stream.  Positions must be distinct within a
+ * sequence, as for dllm_scatter_kv.  Errors: those of the two calls, all
+ * checked before anything is enqueued.
  * ------------------------------------------------------------------------- */
 int dllm_scatter_attention(const dllm_kv_cache *cache, const void *k_new, const void *v_new,
                            int src_dtype, const int32_t *pos, int n, int32_t *bad_count,
@@ -378,8 +403,11 @@ int dllm_stability_reset(int B, int L, int D, int32_t *ring_argmax, float *ring_
  *     ring holds the steps s, s-1, ..., s-K+1, all with one argmax, and the
  *     mean of their max-probs (float64, oldest first) exceeds tau; stable
  *     is never cleared [SWD, 3.1 and 4.2];
- *  3. conf = alpha(1 - H/ln V) + beta exp(-lambda (s - t_write)) in float64
- *     for every position, H = entropy_latest [Flash, 3.1];
+ *  3. conf = alpha(1 - H/ln V) + beta decay[min(s - t_write, n_decay - 1)]
+ *     in float64 for every position, H = entropy_latest, decay[k] =
+ *     exp(-lambda k) [Flash, 3.1]; the division, subtraction, products and
+ *     sum are single IEEE operations, none fused, and conf is their value
+ *     rounded once to float32;
  *  4. seed = not stable, or conf < conf_thresh; mask[j] = 1 when a seed lies
  *     within R of j (clamped to the sequence); with no seed at all the mask
  *     is all ones and all_stable = 1 [SWD, 3.2 and 4.2];
@@ -397,7 +425,8 @@ int dllm_stability_reset(int B, int L, int D, int32_t *ring_argmax, float *ring_
  *              is then ignored) and, with params->advance_step, written back
  *              plus one, so a captured graph of a decode step replays as
  *              successive steps; values must be >= 0.  May be NULL.
- * Limits: L <= 131072, 1 <= K <= D, R >= 0, vocab >= 2.
+ * Limits: L <= 131072, 1 <= K <= D, R >= 0, vocab >= 2; with beta != 0 a
+ * non-NULL 8-byte aligned decay table and n_decay >= 1.
  * ------------------------------------------------------------------------- */
 int dllm_stability_mask(int B, int L, int step, int32_t *step_dev, const int32_t *pos, int n,
                         const int32_t *argmax, const float *maxprob, const float *entropy,
@@ -406,6 +435,16 @@ int dllm_stability_mask(int B, int L, int step, int32_t *step_dev, const int32_t
                         const dllm_stab_params *params,
                         uint8_t *mask, float *conf, int32_t *next_pos, int32_t *count,
                         uint8_t *all_stable, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * dllm_confidence_decay -- the age factor of the cache confidence [Flash,
+ * 3.1: beta exp(-lambda (t - t_write))] as a table: table[k] =
+ * exp(-lambda * k) for k = 0 .. n-1, float64, computed on the host with the
+ * C library's exp.  HOST array of n values; the caller copies it to the
+ * device once and passes it as dllm_stab_params.decay.  Returns DLLM_EINVAL
+ * for a NULL table, n < 1 or a lambda that is negative or not finite.
+ * ------------------------------------------------------------------------- */
+int dllm_confidence_decay(double lambda, int n, double *table);
 
 /* ---------------------------------------------------------------------------
  * dllm_refresh_interval -- the full-refresh interval for a trajectory of T

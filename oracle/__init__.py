@@ -72,6 +72,8 @@ def lib():
         L.oracle_e4m3_quantize_group.argtypes = [P, i32, P, P]
         L.oracle_scatter_kv.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, i32, P, P, P, i32]
         L.oracle_scatter_kv.restype = i32
+        L.oracle_check_positions.argtypes = [i32, i32, P, i32, P, P]
+        L.oracle_check_positions.restype = i32
         L.oracle_sink_rolling_keys.argtypes = [i32, i32, i32, P]
         L.oracle_sink_rolling_keys.restype = i32
         L.oracle_block_attention.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, i32, P, i32, i32,
@@ -99,7 +101,7 @@ def lib():
         L.oracle_vocab_stats.argtypes = [i32, P, i64, i64, i64, P, P, P, P, i64]
         L.oracle_vocab_stats.restype = i32
         L.oracle_stability_step.argtypes = [i32, i32, i32, P, i32, P, P, P, P, P, P, P, P, P,
-                                            i32, dbl, i32, i32, dbl, dbl, dbl, dbl, i64,
+                                            i32, dbl, i32, i32, dbl, dbl, dbl, i32, dbl, i64,
                                             i32, i32, i32, P, P, P, P, P]
         L.oracle_dynamic_radius.argtypes = [i32, i32, i32, i32]
         L.oracle_dynamic_radius.restype = i32
@@ -181,6 +183,17 @@ def scatter_kv(cache_k, cache_v, k_scale, v_scale, cache_dtype, k_new, v_new, sr
 
 
 # ---- A2 ---------------------------------------------------------------------
+
+def check_positions(L: int, pos):
+    """(bad, dup) per sequence of pos [B, n] int32: entries outside [0, L)
+    other than -1, and entries repeating an earlier entry."""
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    B, n = pos.shape
+    bad = np.zeros(B, np.int32)
+    dup = np.zeros(B, np.int32)
+    _check(lib().oracle_check_positions(B, int(L), _ptr(pos), n, _ptr(bad), _ptr(dup)), "check_positions")
+    return bad, dup
+
 
 def sink_rolling_keys(S: int, R: int, end: int) -> np.ndarray:
     out = np.zeros(S + R, dtype=np.int32)
@@ -418,11 +431,12 @@ class StabilityState:
 
 def stability_step(state: StabilityState, step, pos, argmax, maxprob, entropy, *, K, tau, R,
                    alpha=0.0, beta=0.0, lam=0.0, conf_thresh=0.0, V=2, R_early=0, T_steps=0,
-                   refresh_every=0):
+                   refresh_every=0, n_decay=4096):
     """One step of history update, stability test, confidence and window mask.
 
     pos: [B, n] recomputed positions or None (all L).  argmax/maxprob/entropy
-    are [B, n] (float32 maxprob/entropy).  Returns dict with mask, conf,
+    are [B, n] (float32 maxprob/entropy).  The confidence's age s - t_write is
+    clamped to [0, n_decay - 1].  Returns dict with mask, conf (float64),
     next_pos, count, all_stable.  ``state`` is updated in place.
     """
     B, L, D = state.B, state.L, state.D
@@ -443,7 +457,7 @@ def stability_step(state: StabilityState, step, pos, argmax, maxprob, entropy, *
                                      _ptr(entropy), _ptr(state.ring_argmax), _ptr(state.ring_maxprob),
                                      _ptr(state.ring_step), _ptr(state.entropy_latest),
                                      _ptr(state.t_write), _ptr(state.stable), int(K), float(tau), D,
-                                     int(R), float(alpha), float(beta), float(lam),
+                                     int(R), float(alpha), float(beta), float(lam), int(n_decay),
                                      float(conf_thresh), int(V), int(R_early), int(T_steps),
                                      int(refresh_every), _ptr(mask), _ptr(conf),
                                      _ptr(next_pos), _ptr(count), _ptr(all_stable))

@@ -607,6 +607,30 @@ int oracle_vocab_stats(int dtype, const void *logits, int64_t N, int64_t V,
     return 0;
 }
 
+/* Validity of a scatter's position list ([Sinks, 5.1]: rows written to the
+ * wrong cache slot corrupt every later step): per sequence, the entries
+ * outside [0, L) other than the padding -1, and the entries equal to an
+ * earlier entry of the same sequence. */
+int oracle_check_positions(int B, int L, const int32_t *pos, int n, int32_t *bad, int32_t *dup)
+{
+    int b, j, i;
+    if (B <= 0 || L <= 0 || n < 0) return -1;
+    for (b = 0; b < B; ++b) {
+        const int32_t *row = pos + (int64_t)b * n;
+        int nb = 0, nd = 0;
+        for (j = 0; j < n; ++j) {
+            int p = row[j];
+            if (p == -1) continue;
+            if (p < 0 || p >= L) { ++nb; continue; }
+            for (i = 0; i < j; ++i)
+                if (row[i] == p) { ++nd; break; }
+        }
+        bad[b] = nb;
+        dup[b] = nd;
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* A5-A7: history ring, stability test, confidence, window mask             */
 /* ------------------------------------------------------------------------ */
@@ -729,7 +753,7 @@ int oracle_stability_step(int B, int L, int step, const int32_t *pos, int n,
                           int32_t *ring_argmax, float *ring_maxprob, int32_t *ring_step,
                           float *entropy_latest, int32_t *t_write, uint8_t *stable,
                           int K, double tau, int D, int R,
-                          double alpha, double beta, double lambda,
+                          double alpha, double beta, double lambda, int n_decay,
                           double conf_thresh, int64_t V,
                           int R_early, int T_steps, int refresh_every,
                           uint8_t *mask, double *conf, int32_t *next_pos,
@@ -738,6 +762,7 @@ int oracle_stability_step(int B, int L, int step, const int32_t *pos, int n,
     int b, R_eff;
     double hmax;
     if (B <= 0 || L <= 0 || step < 0 || K < 1 || D < K || R < 0 || V < 2) return -1;
+    if (n_decay < 1) return -1;
     if (R_early < 0 || refresh_every < 0) return -1;
     if (!pos) n = L;
     if (n < 0 || n > L) return -1;
@@ -794,11 +819,15 @@ int oracle_stability_step(int B, int L, int step, const int32_t *pos, int n,
 
         /* cache confidence alpha(1 - H/Hmax) + beta exp(-lambda (s - t_write))
          * for every position; below the threshold its cache is refreshed
-         * [Flash, 3.1] */
+         * [Flash, 3.1].  The age is clamped to [0, n_decay - 1]. */
         for (i = 0; i < L; ++i) {
             double h = (double)entropy_latest[row + i];
-            double dt = (double)(step - t_write[row + i]);
-            double cf = alpha * (1.0 - h / hmax) + beta * exp(-lambda * dt);
+            int age = step - t_write[row + i];
+            double dt, cf;
+            if (age < 0) age = 0;
+            if (age > n_decay - 1) age = n_decay - 1;
+            dt = (double)age;
+            cf = alpha * (1.0 - h / hmax) + beta * exp(-lambda * dt);
             int low = cf < conf_thresh;
             conf[row + i] = cf;
             seed[i] = (uint8_t)(!stable[row + i] || low);

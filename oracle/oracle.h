@@ -190,13 +190,24 @@ int oracle_self_verify(int B, int L, const int32_t *dec_pos, int n, const float 
                        uint8_t *mask, uint8_t *stable, uint8_t *cached, int32_t *next_pos,
                        int32_t *count, int32_t *n_rollback, int32_t *rb_pos);
 
+/* Validity of a scatter's position list: per sequence b, bad[b] = entries
+ * outside [0, L) other than -1, dup[b] = entries equal to an earlier entry
+ * of the same sequence.  See oracle.c. */
+int oracle_check_positions(int B, int L, const int32_t *pos, int n, int32_t *bad, int32_t *dup);
+
+/* A5-A7 [SWD, 3.1-3.3 and 4.2; Flash, 3.1]: record, stability test,
+ * confidence alpha(1 - H/ln V) + beta exp(-lambda dt), window mask and
+ * compaction for one step.  The age dt = s - t_write is clamped to
+ * [0, n_decay - 1] (n_decay >= 1): the library reads the age factor from a
+ * table of n_decay entries, and with n_decay above every age the clamp never
+ * applies.  See oracle.c. */
 int oracle_stability_step(int B, int L, int step, const int32_t *pos, int n,
                           const int32_t *argmax, const float *maxprob,
                           const float *entropy,
                           int32_t *ring_argmax, float *ring_maxprob, int32_t *ring_step,
                           float *entropy_latest, int32_t *t_write, uint8_t *stable,
                           int K, double tau, int D, int R,
-                          double alpha, double beta, double lambda,
+                          double alpha, double beta, double lambda, int n_decay,
                           double conf_thresh, int64_t V,
                           int R_early, int T_steps, int refresh_every,
                           uint8_t *mask, double *conf, int32_t *next_pos,

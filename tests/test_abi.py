@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
               "dllm_block_attention_workspace", "dllm_vocab_stats_workspace", "dllm_status_str",
               "dllm_facache_maps", "dllm_facache_merge", "dllm_facache_merge_workspace",
               "dllm_evict_by_confidence", "dllm_cache_quotas", "dllm_refresh_interval",
-              "dllm_self_verify", "dllm_parallel_width"]:
+              "dllm_self_verify", "dllm_parallel_width", "dllm_confidence_decay",
+              "dllm_check_positions"]:
         assert n in names
 
 
@@ -65,9 +66,20 @@ def test_host_validation_without_gpu(dl):
     prm = dl._StabParams(K=3, D=3, R=1, tau=0.9, vocab=10, refresh_every=-1)                # bad schedule
     assert L.dllm_stability_mask(1, 4, 0, None, None, 4, 16, 16, 16, 16, 16, 16, 16, 16, 16,
                                  ctypes.byref(prm), 16, 16, 16, 16, 16, None) == -1
-    prm = dl._StabParams(K=3, D=3, R=1, tau=0.9, vocab=10, reserved=1)
+    prm = dl._StabParams(K=3, D=3, R=1, tau=0.9, vocab=10, alpha=0.7, beta=0.3)               # no decay table
     assert L.dllm_stability_mask(1, 4, 0, None, None, 4, 16, 16, 16, 16, 16, 16, 16, 16, 16,
                                  ctypes.byref(prm), 16, 16, 16, 16, 16, None) == -1
+    prm = dl._StabParams(K=3, D=3, R=1, tau=0.9, vocab=10, alpha=0.7, beta=0.3, decay=16, n_decay=0)
+    assert L.dllm_stability_mask(1, 4, 0, None, None, 4, 16, 16, 16, 16, 16, 16, 16, 16, 16,
+                                 ctypes.byref(prm), 16, 16, 16, 16, 16, None) == -1
+    prm = dl._StabParams(K=3, D=3, R=1, tau=0.9, vocab=10, alpha=0.7, beta=0.3, decay=20, n_decay=8)
+    assert L.dllm_stability_mask(1, 4, 0, None, None, 4, 16, 16, 16, 16, 16, 16, 16, 16, 16,
+                                 ctypes.byref(prm), 16, 16, 16, 16, 16, None) == -4          # misaligned table
+    # position check: shapes and limits before any launch
+    assert L.dllm_check_positions(0, 8, 16, 2, 16, 16, None) == -3
+    assert L.dllm_check_positions(1, 1 << 18, 16, 2, 16, 16, None) == -5
+    assert L.dllm_check_positions(1, 8, None, 2, 16, 16, None) == -1
+    assert L.dllm_check_positions(1, 8, 16, 2, None, 16, None) == -1
     # eviction: shapes and limits before any launch
     assert L.dllm_evict_by_confidence(1, 0, 16, 16, None, 0, 16, 16, 16, 16, None, None) == -3
     assert L.dllm_evict_by_confidence(1, 8, 16, 16, None, 5, 16, 16, 16, 16, None, None) == -3
@@ -137,3 +149,24 @@ def test_host_policies_match_the_oracle(dl, orc):
                 dl.dllm_cache_quotas(lens, budget, frac)
             continue
         assert np.array_equal(dl.dllm_cache_quotas(lens, budget, frac), ref), trial
+
+
+def test_confidence_decay_table(dl, orc):
+    """the host table is exp(-lambda k) from the C library, the same function
+    the oracle's confidence calls: equal bit for bit to Python's math.exp of
+    the same float64 product, with bad arguments rejected"""
+    import math
+
+    import numpy as np
+    for lam in (3.0 / 16, 3.0 / 64, 0.25, 0.0, 1e-3, 7.5):
+        t = dl.dllm_confidence_decay(lam, 300).numpy()
+        ref = np.array([math.exp(-lam * float(k)) for k in range(300)])
+        assert np.array_equal(t.view(np.uint64), ref.view(np.uint64)), lam
+        assert t[0] == 1.0 and (np.diff(t) <= 0).all()
+    L = dl.lib()
+    buf = (ctypes.c_double * 4)()
+    assert L.dllm_confidence_decay(0.1, 0, buf) == -1
+    assert L.dllm_confidence_decay(-0.1, 4, buf) == -1
+    assert L.dllm_confidence_decay(float("nan"), 4, buf) == -1
+    assert L.dllm_confidence_decay(float("inf"), 4, buf) == -1
+    assert L.dllm_confidence_decay(0.1, 4, None) == -1

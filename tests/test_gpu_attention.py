@@ -214,3 +214,87 @@ def test_attention_deterministic():
     a = D.dllm_block_attention(cache, q).clone()
     b = D.dllm_block_attention(cache, q)
     assert torch.equal(a, b)
+
+
+def _llada_cache(D, cfg):
+    cache = new_cache(D, cfg.B, cfg.Hkv, cfg.L, cfg.d, W.BF16)
+    k, v = W.kv_rows(cfg, device="cuda")
+    D.dllm_scatter_kv(cache, k, v, torch.arange(cfg.L, dtype=torch.int32, device="cuda").repeat(cfg.B, 1))
+    kn, vn = W.kv_rows(cfg, device="cuda", which="fresh")
+    D.dllm_scatter_kv(cache, kn, vn, W.block_positions(cfg, "cuda"))
+    return cache
+
+
+def test_attention_llada_sharp_sampled(orc):
+    """the LLaDA-shaped step with queries scaled so that the scores have a
+    standard deviation of about 3 (a peaked softmax), sampled heads"""
+    D = need_gpu()
+    cfg = W.CONFIGS["llada"]
+    cache = _llada_cache(D, cfg)
+    q = (W.queries(cfg, device="cuda").float() * W.sharp_query_scale(cfg)).bfloat16()
+    rng = np.random.default_rng(12)
+    heads = np.stack([rng.integers(0, cfg.B, 24), rng.integers(0, cfg.Hq, 24)], 1).astype(np.int32)
+    _check(orc, D, cache, q, label="llada sharp", heads=heads)
+
+
+def _longctx(D, cfg, dtype, k, v):
+    cache = new_cache(D, cfg.B, cfg.Hkv, cfg.L, cfg.d, dtype)
+    D.dllm_scatter_kv(cache, k, v, torch.arange(cfg.L, dtype=torch.int32, device="cuda").repeat(cfg.B, 1))
+    kn, vn = W.kv_rows(cfg, device="cuda", which="fresh")
+    D.dllm_scatter_kv(cache, kn, vn, W.block_positions(cfg, "cuda"))
+    return cache
+
+
+def _longctx_map(D, cfg):
+    pos = W.block_positions(cfg, "cuda")
+    kid = torch.empty((cfg.B, cfg.sinks + cfg.rolling), dtype=torch.int32, device="cuda")
+    D.dllm_sink_rolling_map(cfg.L, cfg.sinks, cfg.rolling, (pos[:, -1] + 1).contiguous(), kid)
+    return kid
+
+
+def test_attention_longctx_sharp_sampled(orc):
+    """the long-context step (e4m3 cache, sink + rolling map) with queries
+    scaled to a score standard deviation of about 3, sampled heads"""
+    D = need_gpu()
+    cfg = W.CONFIGS["longctx"]
+    k, v = W.kv_rows(cfg, device="cuda")
+    cache = _longctx(D, cfg, W.E4M3, k, v)
+    del k, v
+    kid = _longctx_map(D, cfg)
+    q = (W.queries(cfg, device="cuda").float() * W.sharp_query_scale(cfg)).bfloat16()
+    rng = np.random.default_rng(13)
+    heads = np.stack([rng.integers(0, cfg.B, 10), rng.integers(0, cfg.Hq, 10)], 1).astype(np.int32)
+    _check(orc, D, cache, q, key_idx=kid, label="longctx sharp", heads=heads)
+
+
+def test_attention_longctx_e4m3_vs_unquantised(orc):
+    """the FP8 cache's own error: the same bf16 rows scattered once into an
+    e4m3 cache (per-128 scales) and once into a bf16 cache; the e4m3 call's
+    output against the oracle's attention on the bf16 cache, at the stated
+    fp8 bar (6e-2 max-abs) and at 6e-2 of max |O| (the derived bar for fp8
+    against unquantised K/V), sampled heads of the long-context step"""
+    D = need_gpu()
+    cfg = W.CONFIGS["longctx"]
+    k, v = W.kv_rows(cfg, device="cuda")
+    c8 = _longctx(D, cfg, W.E4M3, k, v)
+    c16 = _longctx(D, cfg, W.BF16, k, v)
+    del k, v
+    kid = _longctx_map(D, cfg)
+    q = W.queries(cfg, device="cuda")
+    say("attention longctx e4m3 vs bf16 cache")
+    out = D.dllm_block_attention(c8, q, key_idx=kid)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(14)
+    heads = np.stack([rng.integers(0, cfg.B, 10), rng.integers(0, cfg.Hq, 10)], 1).astype(np.int32)
+    ck, cv, _, _ = cache_np(c16)
+    ref, _ = orc.block_attention(ck, cv, None, None, W.BF16, bits(q), W.BF16, key_idx=kid.cpu().numpy(),
+                                 heads=heads)
+    got = torch.stack([out[b_, h_] for b_, h_ in heads])
+    e_abs, e_norm = attn_errors(got, ref)
+    assert e_abs <= 6e-2 and e_norm <= 6e-2, (e_abs, e_norm)
+    # and the same call against the oracle on the quantised bytes is far closer
+    ck8, cv8, ks8, vs8 = cache_np(c8)
+    ref8, _ = orc.block_attention(ck8, cv8, ks8, vs8, W.E4M3, bits(q), W.BF16, key_idx=kid.cpu().numpy(),
+                                  heads=heads)
+    e8_abs, e8_norm = attn_errors(got, ref8)
+    assert e8_norm <= 1e-2 and e8_norm < e_norm, (e8_norm, e_norm)

@@ -193,16 +193,21 @@ def test_dynamic_radius_and_refresh(orc):
     assert n_refresh == 7
 
 
-def test_trajectory_with_quotas(orc):
+@pytest.mark.parametrize("gate", ["pages", "entropy only"])
+def test_trajectory_with_quotas(orc, gate):
     """stability step, then eviction under per-request quotas, over 20 steps
-    of the vocab sweep's shape.  The confidence is 1 - H / log V (alpha 1,
-    beta 0): a division and a subtraction in float64 then one rounding, so
-    both sides hold the same float32 confidences and take every eviction
-    decision on the same values."""
+    of the vocab sweep's shape, with the pages' confidence (alpha 0.7, beta
+    0.3, lambda 3/T, threshold 0.8) and with the entropy term alone (alpha 1,
+    beta 0).  Both sides compute the same float64 confidence and round it
+    once, so they rank and evict on bit-identical float32 values."""
     D = need_gpu()
     cfg = W.CONFIGS["vocab"]
     B, L, T = cfg.B, cfg.L, 20
-    kw = dict(_stab_kw(cfg), alpha=1.0, beta=0.0, lam=0.0, conf_thresh=0.0)
+    if gate == "pages":
+        kw = _stab_kw(cfg)
+        assert (kw["alpha"], kw["beta"], kw["lam"], kw["conf_thresh"]) == (0.7, 0.3, 3.0 / 64, 0.8)
+    else:
+        kw = dict(_stab_kw(cfg), alpha=1.0, beta=0.0, lam=0.0, conf_thresh=0.0)
     lens = np.full(B, L)
     quota = orc.cache_quotas(lens, B * L * 3 // 5, min_frac=0.2)
     assert np.array_equal(D.dllm_cache_quotas(lens, B * L * 3 // 5, 0.2), quota)
@@ -224,7 +229,7 @@ def test_trajectory_with_quotas(orc):
         torch.cuda.synchronize()
         r = orc.stability_step(ost, s, pos, a, m, e, **kw)
         conf32 = r["conf"].astype(np.float32)
-        assert np.array_equal(gst.conf.cpu().numpy(), conf32), ("conf", s)
+        assert np.array_equal(gst.conf.cpu().numpy().view(np.uint32), conf32.view(np.uint32)), ("conf", s)
         mask = r["mask"].copy()
         re = orc.evict_by_confidence(ost, conf32, quota, pos, mask)
         assert np.array_equal(gst.cached.cpu().numpy(), ost.cached), ("cached", s)

@@ -132,3 +132,26 @@ def test_sink_rolling_map_bitwise(orc):
             row = np.full(S + R + 3, -1, np.int32)
             row[:len(ref)] = ref
             assert np.array_equal(got[i], row), (L, S, R, e)
+
+
+@pytest.mark.parametrize("B,L,n", [(3, 97, 40), (2, 131072, 5000), (4, 1024, 0), (1, 64, 64)])
+def test_check_positions_gpu(orc, B, L, n):
+    """the debug check of position lists, bit-exact counts against the
+    oracle: random lists with planted repeats, padding and bad entries, a
+    maximum-length sequence, an empty list and a full permutation"""
+    D = need_gpu()
+    rng = np.random.default_rng(L + n)
+    if n == L:
+        pos = np.stack([rng.permutation(L) for _ in range(B)]).astype(np.int32)
+    else:
+        pos = rng.integers(-2, L + 2, (B, n)).astype(np.int32)
+        if n:
+            pos[0, n // 2:] = pos[0, :n - n // 2]            # half the first row repeats
+            pos[-1, ::5] = -1
+    say("check_positions", B, L, n)
+    bad, dup = D.dllm_check_positions(L, torch.from_numpy(pos).cuda())
+    torch.cuda.synchronize()
+    obad, odup = orc.check_positions(L, pos)
+    assert np.array_equal(bad.cpu().numpy(), obad) and np.array_equal(dup.cpu().numpy(), odup)
+    if n == L:
+        assert not obad.any() and not odup.any()

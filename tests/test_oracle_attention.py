@@ -116,6 +116,28 @@ def test_scatter_rejects_bad_positions(orc):
 
 # ---- A2 -----------------------------------------------------------------------
 
+def test_check_positions(orc):
+    """the position check against a set-based count (valid entries minus
+    distinct valid entries) on random lists with planted repeats, padding and
+    out-of-range entries, and its closed forms"""
+    rng = np.random.default_rng(17)
+    for trial in range(300):
+        B, L, n = int(rng.integers(1, 4)), int(rng.integers(1, 40)), int(rng.integers(0, 30))
+        pos = rng.integers(-3, L + 3, (B, n)).astype(np.int32)
+        if n and trial % 3 == 0:
+            pos[:, -1] = pos[:, 0]                       # a planted repeat
+        bad, dup = orc.check_positions(L, pos)
+        for b in range(B):
+            row = pos[b].tolist()
+            valid = [p for p in row if 0 <= p < L]
+            assert bad[b] == sum(1 for p in row if p != -1 and not 0 <= p < L), trial
+            assert dup[b] == len(valid) - len(set(valid)), trial
+    assert [x.tolist() for x in orc.check_positions(8, np.arange(8, dtype=np.int32)[None])] == [[0], [0]]
+    assert [x.tolist() for x in orc.check_positions(8, np.full((1, 5), 3, np.int32))] == [[0], [4]]
+    assert [x.tolist() for x in orc.check_positions(8, np.full((1, 5), -1, np.int32))] == [[0], [0]]
+    assert [x.tolist() for x in orc.check_positions(8, np.array([[8, -2, 7, 7]], np.int32))] == [[2], [1]]
+
+
 def test_sink_rolling_page_example(orc):
     g = json.load(open(os.path.join(GOLD, "sinks_rolling_example.json")))
     C, S, R = g["total_cache_C"], g["sinks_S"], g["rolling_R"]

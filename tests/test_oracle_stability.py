@@ -159,6 +159,29 @@ def test_confidence_closed_forms(orc):
     assert r["all_stable"][0] == 1 and r["mask"][0].tolist() == [1] * L
 
 
+def test_confidence_age_clamp(orc):
+    """the age s - t_write is clamped to [0, n_decay - 1]: a position 10 steps
+    old with a 3-entry table scores as one 2 steps old with a table long
+    enough, and a table longer than every age changes nothing"""
+    V, L = 512, 3
+    pos, am, mp, en = _no_update(1)
+
+    def conf(step, t_write, n_decay):
+        st = _state(orc, 1, L, 4)
+        st.stable[:] = 1
+        st.entropy_latest[0] = np.array([0.0, 1.5, 4.0], np.float32)
+        st.t_write[0] = t_write
+        return orc.stability_step(st, step, pos, am, mp, en, K=3, tau=0.9, R=0, alpha=0.7, beta=0.3,
+                                  lam=0.25, conf_thresh=0.0, V=V, n_decay=n_decay)["conf"][0]
+    assert np.array_equal(conf(10, 0, 3), conf(2, 0, 4096))
+    assert np.array_equal(conf(10, 0, 11), conf(10, 0, 4096))
+    assert not np.array_equal(conf(10, 0, 10), conf(10, 0, 4096))
+    assert np.array_equal(conf(3, 7, 4096), conf(7, 7, 4096))     # negative age reads age 0
+    # H = 0 at age 0 is alpha + beta exactly; the entropy term falls with H
+    c = conf(5, 5, 1)
+    assert c[0] == 0.7 + 0.3 and c[0] > c[1] > c[2]
+
+
 def test_confidence_gate_refresh_timing(orc):
     """a certain (H = 0) stable position falls below 0.8 once
     0.7 + 0.3 exp(-3 dt / T) < 0.8, i.e. dt > T ln 3 / 3 (= 5.86 at T = 16)"""
