@@ -25,9 +25,11 @@ __all__ = [
     "dllm_vocab_stats_workspace", "dllm_stability_reset", "dllm_stability_mask",
     "dllm_refresh_interval", "dllm_cache_quotas", "dllm_evict_by_confidence",
     "dllm_parallel_width", "dllm_self_verify", "dllm_confidence_decay", "dllm_check_positions",
+    "dllm_scatter_attention_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 F32, BF16, E4M3 = 0, 1, 2
+NOALLOC_SCRATCH_BYTES = 64 << 20      # DLLM_NOALLOC_SCRATCH_BYTES of include/dllm.h
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdllm.so")
 
 
@@ -77,6 +79,13 @@ EXPORTS = {
                                               ctypes.c_void_p, ctypes.c_int, ctypes.c_float,
                                               ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                                               ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "dllm_scatter_attention_noalloc": (ctypes.c_int, [ctypes.POINTER(_KVCache), ctypes.c_void_p,
+                                                      ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                                      ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                                      ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                      ctypes.c_void_p, ctypes.c_int, ctypes.c_float,
+                                                      ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                                      ctypes.c_void_p]),
     "dllm_block_attention_workspace": (ctypes.c_size_t, [ctypes.POINTER(_KVCache), ctypes.c_int,
                                                          ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     "dllm_facache_maps": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
@@ -361,6 +370,27 @@ def dllm_scatter_attention(cache: Cache, k_new: torch.Tensor, v_new: torch.Tenso
                                       float(scale), _dev(out, "out"), _dtype_code(out), _dev(lse, "lse"),
                                       _dev(workspace, "workspace"), ws_bytes, _stream())
     _check(rc, "dllm_scatter_attention")
+    return out
+
+
+def dllm_scatter_attention_noalloc(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, pos: torch.Tensor,
+                                   q: torch.Tensor, out: torch.Tensor, key_idx: Optional[torch.Tensor] = None,
+                                   scale: float = 0.0, lse: Optional[torch.Tensor] = None,
+                                   bad_count: Optional[torch.Tensor] = None):
+    """dllm_scatter_attention without a workspace: the library's own per-GPU
+    scratch holds the key-split partials, and nothing is allocated (the caller
+    passes ``out``).  Calls that overlap on one GPU race on that scratch."""
+    B, Hq, b, d = _want_queries(cache, q)
+    n = _want_rows(cache, k_new, v_new, pos)
+    _want_counter(bad_count, "bad_count")
+    n_keys = _want_key_map(cache, key_idx)
+    _want_out(out, lse, B, Hq, b, d)
+    rc = lib().dllm_scatter_attention_noalloc(ctypes.byref(cache.desc), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                                              _dtype_code(k_new), _dev(pos, "pos"), n,
+                                              _dev(bad_count, "bad_count"), _dev(q, "q"), _dtype_code(q), Hq, b,
+                                              _dev(key_idx, "key_idx"), n_keys, float(scale), _dev(out, "out"),
+                                              _dtype_code(out), _dev(lse, "lse"), _stream())
+    _check(rc, "dllm_scatter_attention_noalloc")
     return out
 
 

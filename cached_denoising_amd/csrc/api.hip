@@ -4,10 +4,38 @@
 
 #include <climits>
 #include <cmath>
+#include <mutex>
 
 using namespace dllm;
 
+// Scratch of dllm_scatter_attention_noalloc: the key-split partials of its
+// attention kernels.  The loader gives every GPU the library runs on its own
+// copy, held until the process ends.  In host code `scratch` is a host-side
+// stand-in for the symbol, not a device address: the device address comes
+// from hipGetSymbolAddress, once per device (scratch_on_current_device).
+static __device__ __align__(256) unsigned char scratch[DLLM_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices] = {};
+
+// the device address of the current device's scratch array, looked up on the
+// first call on that device (with that device current)
+int scratch_on_current_device(void **ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return DLLM_EHIP;
+    if (dev < 0 || dev >= kMaxDevices) return DLLM_ERANGE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DLLM_EHIP;
+        g_scratch_dev[dev] = p;
+    }
+    *ptr = g_scratch_dev[dev];
+    return DLLM_OK;
+}
 
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -147,12 +175,15 @@ int dllm_block_attention(const dllm_kv_cache *cache, const void *q, int q_dtype,
                             out_dtype, lse, workspace, static_cast<hipStream_t>(stream));
 }
 
-int dllm_scatter_attention(const dllm_kv_cache *cache, const void *k_new, const void *v_new,
-                           int src_dtype, const int32_t *pos, int n, int32_t *bad_count,
-                           const void *q, int q_dtype, int Hq, int b, const int32_t *key_idx,
-                           int n_keys, float scale, void *out, int out_dtype, float *lse,
-                           void *workspace, size_t ws_bytes, void *stream) {
-    // the checks of dllm_scatter_kv, then those of dllm_block_attention
+}  // extern "C"
+
+namespace {
+// the checks of dllm_scatter_kv, then those of dllm_block_attention (without
+// the workspace's), and the plan; scale and n_keys come back resolved
+int check_scatter_attention(const dllm_kv_cache *cache, const void *k_new, const void *v_new,
+                            int src_dtype, const int32_t *pos, int n, const void *q, int q_dtype,
+                            int Hq, int b, const int32_t *key_idx, int &n_keys, float &scale,
+                            void *out, int out_dtype, AttnPlan *p) {
     int rc = check_cache(cache);
     if (rc != DLLM_OK) return rc;
     if (n < 0) return DLLM_EINVAL;
@@ -175,14 +206,45 @@ int dllm_scatter_attention(const dllm_kv_cache *cache, const void *k_new, const 
     if (!(scale >= 0.f) || std::isinf(scale)) return DLLM_EINVAL;
     if (scale == 0.f) scale = 1.0f / std::sqrt((float)cache->d_head);
     if ((int64_t)cache->B * Hq * b > INT32_MAX / 4) return DLLM_ERANGE;
-    AttnPlan p;
-    if ((rc = plan_attention(*cache, q_dtype, Hq, b, n_keys, key_idx != nullptr, &p)) != DLLM_OK)
+    if ((rc = plan_attention(*cache, q_dtype, Hq, b, n_keys, key_idx != nullptr, p)) != DLLM_OK)
         return rc;
-    if (p.path != 0 && (!aligned16(q) || !aligned16(out))) return DLLM_EALIGN;
+    if (p->path != 0 && (!aligned16(q) || !aligned16(out))) return DLLM_EALIGN;
+    return DLLM_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int dllm_scatter_attention(const dllm_kv_cache *cache, const void *k_new, const void *v_new,
+                           int src_dtype, const int32_t *pos, int n, int32_t *bad_count,
+                           const void *q, int q_dtype, int Hq, int b, const int32_t *key_idx,
+                           int n_keys, float scale, void *out, int out_dtype, float *lse,
+                           void *workspace, size_t ws_bytes, void *stream) {
+    AttnPlan p;
+    int rc = check_scatter_attention(cache, k_new, v_new, src_dtype, pos, n, q, q_dtype, Hq, b, key_idx,
+                                     n_keys, scale, out, out_dtype, &p);
+    if (rc != DLLM_OK) return rc;
     if (p.ws_bytes > 0 && (!workspace || ws_bytes < p.ws_bytes || !aligned16(workspace)))
         return DLLM_EWORKSPACE;
     return launch_scatter_attention(*cache, p, k_new, v_new, src_dtype, pos, n, bad_count, q, q_dtype,
                                     Hq, b, key_idx, n_keys, scale, out, out_dtype, lse, workspace,
+                                    static_cast<hipStream_t>(stream));
+}
+
+int dllm_scatter_attention_noalloc(const dllm_kv_cache *cache, const void *k_new, const void *v_new,
+                                   int src_dtype, const int32_t *pos, int n, int32_t *bad_count,
+                                   const void *q, int q_dtype, int Hq, int b, const int32_t *key_idx,
+                                   int n_keys, float scale, void *out, int out_dtype, float *lse,
+                                   void *stream) {
+    AttnPlan p;
+    int rc = check_scatter_attention(cache, k_new, v_new, src_dtype, pos, n, q, q_dtype, Hq, b, key_idx,
+                                     n_keys, scale, out, out_dtype, &p);
+    if (rc != DLLM_OK) return rc;
+    if (p.ws_bytes > DLLM_NOALLOC_SCRATCH_BYTES) return DLLM_ERANGE;
+    void *ws = nullptr;
+    if (p.ws_bytes > 0 && (rc = scratch_on_current_device(&ws)) != DLLM_OK) return rc;
+    return launch_scatter_attention(*cache, p, k_new, v_new, src_dtype, pos, n, bad_count, q, q_dtype,
+                                    Hq, b, key_idx, n_keys, scale, out, out_dtype, lse, ws,
                                     static_cast<hipStream_t>(stream));
 }
 

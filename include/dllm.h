@@ -258,6 +258,28 @@ int dllm_scatter_attention(const dllm_kv_cache *cache, const void *k_new, const 
                            void *workspace, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * dllm_scatter_attention_noalloc -- dllm_scatter_attention for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same arguments without the
+ * workspace, the same kernels and bit-identical results.  The key-split
+ * partials go to a scratch array inside the library, one per GPU, of
+ * DLLM_NOALLOC_SCRATCH_BYTES; a call whose partials need more returns
+ * DLLM_ERANGE before anything is enqueued (dllm_block_attention_workspace
+ * gives the size).  The call allocates nothing.  The first call on a device
+ * looks that device's array up (a host-side query, no allocation).  Every
+ * call on one GPU shares its array: calls that overlap on one GPU (two
+ * streams, or two threads) race on it; calls on one stream are ordered and
+ * safe.  The array keeps the last call's partials, which no later call reads
+ * before writing.
+ * ------------------------------------------------------------------------- */
+#define DLLM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int dllm_scatter_attention_noalloc(const dllm_kv_cache *cache, const void *k_new, const void *v_new,
+                                   int src_dtype, const int32_t *pos, int n, int32_t *bad_count,
+                                   const void *q, int q_dtype, int Hq, int b, const int32_t *key_idx,
+                                   int n_keys, float scale, void *out, int out_dtype, float *lse,
+                                   void *stream);
+
+/* ---------------------------------------------------------------------------
  * dllm_facache_maps -- the key lists of FACache for one block's denoising
  * steps [LaCache, problem statement and Methodology 1: within the steps of
  * one block only the active block's tokens change, the prompt and the masked

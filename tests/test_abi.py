@@ -170,3 +170,19 @@ def test_confidence_decay_table(dl, orc):
     assert L.dllm_confidence_decay(float("nan"), 4, buf) == -1
     assert L.dllm_confidence_decay(float("inf"), 4, buf) == -1
     assert L.dllm_confidence_decay(0.1, 4, None) == -1
+
+
+def test_noalloc_scratch_limit(dl):
+    """the allocation-free call rejects, on the host, a call whose key-split
+    partials exceed the library's per-GPU scratch"""
+    L = dl.lib()
+    desc = dl._KVCache(B=1, L=200000, n_kv_heads=8, d_head=128, dtype=2, k=16, v=16, k_scale=16, v_scale=16)
+    need = L.dllm_block_attention_workspace(ctypes.byref(desc), 1, 32, 64, 131072)
+    assert need > dl.NOALLOC_SCRATCH_BYTES
+    assert L.dllm_scatter_attention_noalloc(ctypes.byref(desc), 16, 16, 1, 16, 64, None, 16, 1, 32, 64, 16,
+                                            131072, 0.0, 16, 1, None, None) == -5
+    # argument errors are those of dllm_scatter_attention
+    assert L.dllm_scatter_attention_noalloc(ctypes.byref(desc), 16, 16, 7, 16, 64, None, 16, 1, 32, 64, 16,
+                                            131072, 0.0, 16, 1, None, None) == -2
+    assert L.dllm_scatter_attention_noalloc(ctypes.byref(desc), 16, 16, 1, 16, 64, None, None, 1, 32, 64, 16,
+                                            131072, 0.0, 16, 1, None, None) == -1
