@@ -459,70 +459,92 @@ __global__ __launch_bounds__(NW * kWave, 2) void attn_mfma_kernel(
     }
 }
 
-// Merge of the key splits: one thread per (row, 4 dims), splits in order,
-// eight splits' loads in flight at once.  The partial O~ is stored in the
-// output's precision (bf16 for a bf16 output, which halves the split
-// traffic; fp32 for an fp32 output); m and l are fp32.
+// Merge of the key splits: one thread per (row, 8 dims), splits in order.
+// The partial O~ is stored in the output's precision (bf16 for a bf16 output,
+// which halves the split traffic; fp32 for an fp32 output); m and l are fp32.
+// With up to kU splits every load of a thread is issued in one round; more
+// splits take two passes (the maxima, then the sums) of kU splits at a time.
+template <int kU>
+__device__ __forceinline__ void merge_load(const float *__restrict__ part_o, const float *__restrict__ part_ml,
+                                           int64_t rows_total, int D, int splits, int s0, int64_t row, int c,
+                                           int out_dtype, float *ms, float *ls, float (*v)[8]) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+        ms[u] = kNegInf;
+        ls[u] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[u][e] = 0.f;
+        if (s0 + u < splits) {
+            const int64_t pr = (int64_t)(s0 + u) * rows_total + row;
+            const float2 ml = *reinterpret_cast<const float2 *>(part_ml + pr * 2);
+            ms[u] = ml.x;
+            ls[u] = ml.y;
+            if (out_dtype == DLLM_F32) {
+                const float4 a = *reinterpret_cast<const float4 *>(part_o + pr * D + c);
+                const float4 b = *reinterpret_cast<const float4 *>(part_o + pr * D + c + 4);
+                v[u][0] = a.x; v[u][1] = a.y; v[u][2] = a.z; v[u][3] = a.w;
+                v[u][4] = b.x; v[u][5] = b.y; v[u][6] = b.z; v[u][7] = b.w;
+            } else {
+                const uint4 h = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(part_o) + pr * D + c);
+                v[u][0] = bf16lo(h.x); v[u][1] = bf16hi(h.x); v[u][2] = bf16lo(h.y); v[u][3] = bf16hi(h.y);
+                v[u][4] = bf16lo(h.z); v[u][5] = bf16hi(h.z); v[u][6] = bf16lo(h.w); v[u][7] = bf16hi(h.w);
+            }
+        }
+    }
+}
+
 __global__ __launch_bounds__(256) void attn_merge_kernel(
     const float *__restrict__ part_o, const float *__restrict__ part_ml, int64_t rows_total, int D,
     int splits, void *__restrict__ out, int out_dtype, float *__restrict__ lse) {
     constexpr int kU = 8;                  // splits whose loads are in flight together
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int q4 = D / 4;
-    if (t >= rows_total * q4) return;
-    const int64_t row = t / q4;
-    const int c = (int)(t - row * q4) * 4;
+    const int q8 = D / 8;
+    if (t >= rows_total * q8) return;
+    const int64_t row = t / q8;
+    const int c = (int)(t - row * q8) * 8;
+    float ms[kU], ls[kU], v[kU][8];
     float mm = kNegInf;
-    for (int s0 = 0; s0 < splits; s0 += kU) {
-        float mv[kU];
+    if (splits <= kU) {
+        merge_load<kU>(part_o, part_ml, rows_total, D, splits, 0, row, c, out_dtype, ms, ls, v);
 #pragma unroll
-        for (int u = 0; u < kU; ++u)
-            mv[u] = s0 + u < splits ? part_ml[((int64_t)(s0 + u) * rows_total + row) * 2] : kNegInf;
+        for (int u = 0; u < kU; ++u) mm = fmaxf(mm, ms[u]);
+    } else {
+        for (int s0 = 0; s0 < splits; s0 += kU) {
 #pragma unroll
-        for (int u = 0; u < kU; ++u) mm = fmaxf(mm, mv[u]);
+            for (int u = 0; u < kU; ++u)
+                ms[u] = s0 + u < splits ? part_ml[((int64_t)(s0 + u) * rows_total + row) * 2] : kNegInf;
+#pragma unroll
+            for (int u = 0; u < kU; ++u) mm = fmaxf(mm, ms[u]);
+        }
     }
     float lt = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
     if (mm != kNegInf) {
         for (int s0 = 0; s0 < splits; s0 += kU) {
-            float ms[kU], ls[kU];
-            float4 v[kU];
-#pragma unroll
-            for (int u = 0; u < kU; ++u) {
-                ms[u] = kNegInf;
-                ls[u] = 0.f;
-                v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (s0 + u < splits) {
-                    const int64_t pr = (int64_t)(s0 + u) * rows_total + row;
-                    ms[u] = part_ml[pr * 2];
-                    ls[u] = part_ml[pr * 2 + 1];
-                    if (out_dtype == DLLM_F32) {
-                        v[u] = *reinterpret_cast<const float4 *>(part_o + pr * D + c);
-                    } else {
-                        const uint2 h = *reinterpret_cast<const uint2 *>(
-                            reinterpret_cast<const uint16_t *>(part_o) + pr * D + c);
-                        v[u] = make_float4(bf16lo(h.x), bf16hi(h.x), bf16lo(h.y), bf16hi(h.y));
-                    }
-                }
-            }
+            if (splits > kU) merge_load<kU>(part_o, part_ml, rows_total, D, splits, s0, row, c, out_dtype, ms, ls, v);
             // in split order
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
                 if (ms[u] == kNegInf) continue;
                 const float f = __builtin_amdgcn_exp2f(ms[u] - mm);
                 lt += ls[u] * f;
-                acc.x += v[u].x * f; acc.y += v[u].y * f; acc.z += v[u].z * f; acc.w += v[u].w * f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += v[u][e] * f;
             }
         }
     }
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
     const int64_t off = row * D + c;
     if (out_dtype == DLLM_F32) {
-        *reinterpret_cast<float4 *>(static_cast<float *>(out) + off) =
-            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+        float *o = static_cast<float *>(out) + off;
+        *reinterpret_cast<float4 *>(o) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+        *reinterpret_cast<float4 *>(o + 4) = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
     } else {
-        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + off) =
-            make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
+        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(out) + off) =
+            make_uint4(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                       pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv));
     }
     if (lse && c == 0) lse[row] = lt > 0.f ? mm * kLn2 + logf(lt) : kNegInf;
 }
@@ -658,7 +680,7 @@ int launch_mfma(const dllm_kv_cache &c, const AttnPlan &p, const void *q, int Hq
 
 int launch_attn_merge(const float *part_o, const float *part_ml, int64_t rows_total, int D,
                       int splits, void *out, int out_dtype, float *lse, hipStream_t s) {
-    const int64_t threads = rows_total * (D / 4);
+    const int64_t threads = rows_total * (D / 8);
     attn_merge_kernel<<<dim3((unsigned)cdiv64(threads, 256)), dim3(256), 0, s>>>(
         part_o, part_ml, rows_total, D, splits, out, out_dtype, lse);
     return launch_status();

@@ -107,7 +107,13 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
     auto vswz_r = [&](int r) { return CONV ? vswz_e4m3(r) : vswz_b(r); };
     constexpr int CSTAGE = CONV ? 2 * CTB + 3 * 128 + 16 : 0;   // + per-key kfac, bias, vfac; full flag
     constexpr int TAB = MAP ? kTableKeys * 4 : 0;
-    constexpr int SMEM = kNS * STAGE + 2 * CSTAGE + TAB;
+    // the two converted stages first, so that both lie within the 64 KB
+    // immediate offset of an LDS read from one base register: with the tile
+    // loop unrolled by two, every operand read of a converted stage is a
+    // loop-invariant register plus a constant
+    constexpr int OFF_RING = 2 * CSTAGE;
+    constexpr int OFF_TAB = OFF_RING + kNS * STAGE;
+    constexpr int SMEM = OFF_TAB + TAB;
     static_assert(TB % 1024 == 0 && CPR <= 16, "tile layout");
     static_assert(SMEM <= kLdsBytes, "LDS of one workgroup");
     static_assert((kNS - 2) * LW < 64, "vmcnt range");
@@ -136,7 +142,7 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
 
     // this split's key indices (with a map; nt * 32 <= kTableKeys), then the
     // index of tile-local key kappa is one LDS read, or arithmetic without one
-    int *tab = reinterpret_cast<int *>(smem + kNS * STAGE + 2 * CSTAGE);
+    int *tab = reinterpret_cast<int *>(smem + OFF_TAB);
     if (MAP) {
         const int32_t *kmap = key_idx + (int64_t)bi * n_keys;
         for (int j = threadIdx.x; j < nt * 32; j += NRG * kWave)
@@ -168,7 +174,7 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
         tk.s = E4 ? key_of(kt, lane & 31) : 0;
     };
     auto issue = [&](const TileKeys &tk, int slot) {
-        unsigned char *st = smem + slot * STAGE;
+        unsigned char *st = smem + OFF_RING + slot * STAGE;
 #pragma unroll
         for (int u = 0; u < NK / NRG; ++u) {
             // chunk position p of the tile: row p / CPR, stored slot p % CPR
@@ -226,7 +232,7 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
     };
     auto convert_read = [&](int kt, int slot, ConvIn &ci_) {
         if constexpr (CONV) {
-            const unsigned char *st = smem + slot * STAGE;
+            const unsigned char *st = smem + OFF_RING + slot * STAGE;
 #pragma unroll
             for (int it = 0; it < PER; ++it) {
                 const int idx = threadIdx.x + it * NRG * kWave;
@@ -244,7 +250,7 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
     };
     auto convert_write = [&](int cslot, const ConvIn &ci_) {
         if constexpr (CONV) {
-            unsigned char *cs = smem + kNS * STAGE + cslot * CSTAGE;
+            unsigned char *cs = smem + cslot * CSTAGE;
 #pragma unroll
             for (int it = 0; it < PER; ++it) {
                 const int idx = threadIdx.x + it * NRG * kWave;
@@ -320,19 +326,6 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
             for (int c = 0; c < NC; ++c)
                 ka[t][c] = *reinterpret_cast<const uint4 *>(krow + ((c * 4 + g) ^ kswz_b(kappa)) * 16);
         }
-        // V^T operands, read transposed from the row-major bf16 tile now, so
-        // the reads are in flight during the first product: local lane j
-        // reads row 8g + 4h + j/4, dims dt*16 + 4(j%4) .. +3; lane i then
-        // holds keys 8g+4h .. +3 at dim dt*16 + i
-        uint4 vop[NDT];
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            const int r0 = 8 * g + (l16 >> 2), r1 = r0 + 4;
-            const int cl = 2 * dt + ((l16 & 3) >> 1);
-            const uint2 lo = lds_tr16(vb + r0 * BROW + (cl ^ vswz_b(r0)) * 16 + 8 * (l16 & 1));
-            const uint2 hi = lds_tr16(vb + r1 * BROW + (cl ^ vswz_b(r1)) * 16 + 8 * (l16 & 1));
-            vop[dt] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        }
         f32x4_t sacc[RT][2];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) sacc[rt][0] = sacc[rt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -347,6 +340,21 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
                         sacc[rt][t], 0, 0, 0);
 
         side();      // independent work (the next tile's widening) under the products
+
+        // V^T operands, read transposed from the row-major bf16 tile once the
+        // score products are issued (they take the K operands' registers), in
+        // flight during the softmax: local lane j reads row 8g + 4h + j/4,
+        // dims dt*16 + 4(j%4) .. +3; lane i then holds keys 8g+4h .. +3 at
+        // dim dt*16 + i
+        uint4 vop[NDT];
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const int r0 = 8 * g + (l16 >> 2), r1 = r0 + 4;
+            const int cl = 2 * dt + ((l16 & 3) >> 1);
+            const uint2 lo = lds_tr16(vb + r0 * BROW + (cl ^ vswz_b(r0)) * 16 + 8 * (l16 & 1));
+            const uint2 hi = lds_tr16(vb + r1 * BROW + (cl ^ vswz_b(r1)) * 16 + 8 * (l16 & 1));
+            vop[dt] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
 
         // scores in base 2 relative to the running max, y = x - m, and their
         // row maxima for both row tiles first, so the rare rescale is one
@@ -445,8 +453,8 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
                 o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vop[dt]),
                                                                     pf[rt].v, o[dt][rt], 0, 0, 0);
     };
-    auto ring = [&](int slot) { return smem + slot * STAGE; };
-    auto cstage = [&](int cslot) { return smem + kNS * STAGE + cslot * CSTAGE; };
+    auto ring = [&](int slot) { return smem + OFF_RING + slot * STAGE; };
+    auto cstage = [&](int cslot) { return smem + cslot * CSTAGE; };
 
     // ---- the pipeline.  bf16: kNS - 1 tiles in flight; per tile, wait for
     // this wave's loads of it, one barrier (the tile is complete, every wave
@@ -518,8 +526,11 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
 
     // one e4m3 step: wait for the next tile's loads, one barrier, refill the
     // stage this tile used, read the next tile for widening, compute this
-    // one and write the next one back under its first product (slot = i % kNS)
-    auto conv_step = [&](int i, int slot, auto wait) {
+    // one and write the next one back under its first product (slot = i % kNS).
+    // The converted stage of tile i is i % 2, a compile-time constant `par`.
+    auto conv_step = [&](int i, auto par, auto wait) {
+        constexpr int P = decltype(par)::value;
+        const int slot = i % kNS;
         __builtin_amdgcn_sched_barrier(0);
         wait();
         ring_barrier();
@@ -533,19 +544,28 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
         const bool next = i + 1 < nt;
         ConvIn cn;
         if (next) convert_read(t_begin + i + 1, (slot + 1) % kNS, cn);
-        const unsigned char *cs = cstage(slot & 1);
+        const unsigned char *cs = cstage(P);
         compute(t_begin + i, cs, cs + CTB, reinterpret_cast<const float *>(cs + 2 * CTB), [&] {
             if (refill) issue(tk, slot);
-            if (next) convert_write((slot + 1) & 1, cn);
+            if (next) convert_write(P ^ 1, cn);
         });
     };
+    // tiles issued after the next one
+    auto conv_wait = [&](int i) {
+        return [=] { vm_wait_upto<(kNS - 2) * LW>(max(0, min(kNS - 2, nt - 2 - i)) * LW); };
+    };
     int i = 0;
-    for (; i < nt; ++i) {
-        if (CONV) {
-            // tiles issued after the next one
-            const int ahead = max(0, min(kNS - 2, nt - 2 - i));
-            conv_step(i, i % kNS, [&] { vm_wait_upto<(kNS - 2) * LW>(ahead * LW); });
-        } else {
+    if (CONV) {
+        using P0 = std::integral_constant<int, 0>;
+        using P1 = std::integral_constant<int, 1>;
+        for (; i + 1 < nt; i += 2) {
+            conv_step(i, P0{}, conv_wait(i));
+            conv_step(i + 1, P1{}, conv_wait(i + 1));
+        }
+        if (i < nt) conv_step(i, P0{}, conv_wait(i));
+    }
+    for (; !CONV && i < nt; ++i) {
+        {
             // tiles issued after this one
             const int ahead = min(kNS - 2, nt - 1 - i);
             __builtin_amdgcn_sched_barrier(0);
