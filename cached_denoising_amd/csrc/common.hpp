@@ -64,6 +64,21 @@ __device__ __forceinline__ uint32_t e4m3_rne(float q) {
     return sign | r;
 }
 
+// bits 0..3 of x as the low bits of four bytes (four 0/1 flags in one word)
+__device__ __forceinline__ uint32_t spread4(uint32_t x) {
+    return (x & 1u) | ((x & 2u) << 7) | ((x & 4u) << 14) | ((x & 8u) << 21);
+}
+
+// Four consecutive byte flags at p (p 4-aligned when `aligned`): one 32-bit
+// store when all four lie below `limit` positions from p, else byte stores.
+__device__ __forceinline__ void store_flags4(uint8_t *p, uint32_t bits4, int left, bool aligned) {
+    if (left >= 4 && aligned) {
+        *reinterpret_cast<uint32_t *>(p) = spread4(bits4);
+    } else {
+        for (int k = 0; k < 4 && k < left; ++k) p[k] = (uint8_t)((bits4 >> k) & 1u);
+    }
+}
+
 // cross-lane helpers on a 64-wide wavefront
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
 __device__ __forceinline__ int shfl_xor_i(int v, int m) { return __shfl_xor(v, m, kWave); }

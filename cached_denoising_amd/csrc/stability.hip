@@ -51,6 +51,33 @@ __global__ __launch_bounds__(256) void stability_reset_kernel(
     }
 }
 
+// The confidence and seed bit of one position, from its entropy, the step
+// its K/V were written and its stable flag.
+__device__ __forceinline__ bool seed_of(double alpha, double beta, const double *__restrict__ decay,
+                                        int n_decay, double hmax, double conf_thresh, int step, float en,
+                                        int tw, bool st, float *conf_out) {
+    // with the gate off (alpha = beta = 0) the score is +0 whatever the
+    // entropy and age; a zero beta drops the age term, which would add +0
+    // (the table is then not read)
+    double cf = 0.0;
+    if (alpha != 0.0 || beta != 0.0) {
+        const double h = (double)en;
+        double age = 0.0;
+        if (beta != 0.0) {
+            const int dt = step - tw;
+            age = beta * decay[dt < 0 ? 0 : min(dt, n_decay - 1)];
+        }
+        cf = alpha * (1.0 - h / hmax) + age;
+    }
+    if (conf_out) *conf_out = (float)cf;
+    return !st || cf < conf_thresh;
+}
+
+// ALL: every position recomputed in list order (pos == NULL, n == L <= 2
+// kThreads), so thread t holds the new state of positions t and t + kThreads
+// and takes their confidence and seed bits in the same pass, without reading
+// the state back.
+template <bool ALL>
 __global__ __launch_bounds__(kThreads) void stability_kernel(
     int B, int L, int step_arg, int32_t *__restrict__ step_dev, int advance, const int32_t *__restrict__ pos, int n,
     const int32_t *__restrict__ argmax, const float *__restrict__ maxprob,
@@ -83,6 +110,7 @@ __global__ __launch_bounds__(kThreads) void stability_kernel(
     // 1-2: record this step, then test the recomputed positions.  Every load
     // of a position is independent of the others, so they are all in flight
     // together; K is small.
+    bool fused_seed[2] = {false, false};
     for (int j = tid; j < n; j += kThreads) {
         const int p = pos ? pos[(int64_t)b * n + j] : j;
         if (p < 0 || p >= L) continue;
@@ -111,31 +139,28 @@ __global__ __launch_bounds__(kThreads) void stability_kernel(
         ring_step[ri] = step;
         entropy_latest[rowoff + p] = en;
         t_write[rowoff + p] = step;
-        if (test && same && sum / (double)K > tau) stable[rowoff + p] = 1;
+        const bool now_stable = was_stable || (test && same && sum / (double)K > tau);
+        if (!was_stable && now_stable) stable[rowoff + p] = 1;
+        if (ALL) {
+            float cf;
+            fused_seed[j / kThreads] = seed_of(alpha, beta, decay, n_decay, hmax, conf_thresh, step, en, step,
+                                               now_stable, &cf);
+            if (conf) conf[rowoff + p] = cf;
+        }
     }
-    __syncthreads();
+    __syncthreads();                                   // also orders any_seed's reset before its sets
 
     // 3-4a: confidence and the seed bit of every position (one per thread)
     for (int i0 = 0; i0 < L; i0 += kThreads) {
         const int i = i0 + tid;
         bool seed = false;
-        if (i < L) {
-            const bool st = stable[rowoff + i] != 0;
-            // with the gate off (alpha = beta = 0) the score is +0 whatever the
-            // entropy and age; a zero beta drops the age term, which would add
-            // +0 (the table is then not read)
-            double cf = 0.0;
-            if (alpha != 0.0 || beta != 0.0) {
-                const double h = (double)entropy_latest[rowoff + i];
-                double age = 0.0;
-                if (beta != 0.0) {
-                    const int dt = step - t_write[rowoff + i];
-                    age = beta * decay[dt < 0 ? 0 : min(dt, n_decay - 1)];
-                }
-                cf = alpha * (1.0 - h / hmax) + age;
-            }
-            if (conf) conf[rowoff + i] = (float)cf;
-            seed = !st || cf < conf_thresh;
+        if (ALL) {
+            seed = i < L && fused_seed[i0 / kThreads];
+        } else if (i < L) {
+            float cf;
+            seed = seed_of(alpha, beta, decay, n_decay, hmax, conf_thresh, step, entropy_latest[rowoff + i],
+                           t_write[rowoff + i], stable[rowoff + i] != 0, &cf);
+            if (conf) conf[rowoff + i] = cf;
         }
         const uint64_t bal = __ballot(seed);
         if (lane == 0) {
@@ -455,15 +480,21 @@ __global__ __launch_bounds__(kThreads) void evict_kernel(
     }
     __syncthreads();
 
-    // store pass: flags and the compacted mask, position-strided
-#pragma unroll 8
-    for (int i = tid; i < L; i += kThreads) {
-        const int w = i >> 5, bit = i & 31;
+    // store pass: flags and the compacted mask, four consecutive positions
+    // per thread, so a wave's flag stores cover 256 contiguous bytes (whole
+    // lines) instead of 64
+    const bool al_c = (((uintptr_t)(cached + rowoff)) & 3u) == 0;
+    const bool al_m = (((uintptr_t)(mask + rowoff)) & 3u) == 0;
+#pragma unroll 2
+    for (int i = 4 * tid; i < L; i += 4 * kThreads) {
+        const int w = i >> 5, sh = i & 31;             // the four positions share word w
         const uint32_t mw = mbits[w];
-        const bool on = (mw >> bit) & 1u;
-        cached[rowoff + i] = (uint8_t)((cbits[w] >> bit) & 1u);
-        mask[rowoff + i] = on ? 1 : 0;
-        if (on) next_pos[rowoff + wpref[w] + __popc(mw & ((1u << bit) - 1u))] = i;
+        const uint32_t m4 = (mw >> sh) & 0xFu;
+        store_flags4(cached + rowoff + i, (cbits[w] >> sh) & 0xFu, L - i, al_c);
+        store_flags4(mask + rowoff + i, m4, L - i, al_m);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if ((m4 >> k) & 1u) next_pos[rowoff + wpref[w] + __popc(mw & ((1u << (sh + k)) - 1u))] = i + k;
     }
     for (int i = n_total + tid; i < L; i += kThreads) next_pos[rowoff + i] = -1;
     if (tid == 0) {
@@ -509,11 +540,15 @@ int launch_stability(int B, int L, int step, int32_t *step_dev, const int32_t *p
     if (L > kMaxL) return DLLM_ERANGE;
     const int words = cdiv(L, kThreads) * (kThreads / 32);   // whole 1024-position chunks
     const size_t shmem = sizeof(uint32_t) * (size_t)words;
-    stability_kernel<<<dim3((unsigned)B), dim3(kThreads), shmem, s>>>(
-        B, L, step, step_dev, prm.advance_step, pos, n, argmax, maxprob, entropy, ring_argmax, ring_maxprob, ring_step,
-        entropy_latest, t_write, stable, prm.K, prm.D, prm.R, prm.R_early, prm.T_steps,
-        prm.refresh_every, prm.tau, prm.alpha, prm.beta,
-        prm.decay, prm.n_decay, prm.conf_thresh, hmax, mask, conf, next_pos, count, all_stable);
+    auto go = [&](auto all) {
+        stability_kernel<decltype(all)::value><<<dim3((unsigned)B), dim3(kThreads), shmem, s>>>(
+            B, L, step, step_dev, prm.advance_step, pos, n, argmax, maxprob, entropy, ring_argmax, ring_maxprob,
+            ring_step, entropy_latest, t_write, stable, prm.K, prm.D, prm.R, prm.R_early, prm.T_steps,
+            prm.refresh_every, prm.tau, prm.alpha, prm.beta,
+            prm.decay, prm.n_decay, prm.conf_thresh, hmax, mask, conf, next_pos, count, all_stable);
+    };
+    if (!pos && n == L && L <= 2 * kThreads) go(std::true_type{});
+    else go(std::false_type{});
     return launch_status();
 }
 

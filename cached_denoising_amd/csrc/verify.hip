@@ -155,19 +155,25 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(
         on_off += __popc(mbits[w]);
     }
     __syncthreads();
-    // store pass, position-strided
-#pragma unroll 4
-    for (int i = tid; i < L; i += kVThreads) {
-        const int w = i >> 5, bit = i & 31;
-        const bool rb = (rbits[w] >> bit) & 1u;
+    // store pass: four consecutive positions per thread, so a wave's
+    // withdrawal flags cover 256 contiguous bytes (whole lines); the flags of
+    // the few withdrawn positions are written one by one
+    const bool al_r = (((uintptr_t)(rollback + rowoff)) & 3u) == 0;
+#pragma unroll 2
+    for (int i = 4 * tid; i < L; i += 4 * kVThreads) {
+        const int w = i >> 5, sh = i & 31;             // the four positions share word w
+        const uint32_t r4 = (rbits[w] >> sh) & 0xFu;
         const uint32_t mw = mbits[w];
-        rollback[rowoff + i] = rb ? 1 : 0;
-        if (rb) {
-            mask[rowoff + i] = 1;
-            if (stable) stable[rowoff + i] = 0;
-            if (cached) cached[rowoff + i] = 0;
+        store_flags4(rollback + rowoff + i, r4, L - i, al_r);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if ((r4 >> k) & 1u) {
+                mask[rowoff + i + k] = 1;
+                if (stable) stable[rowoff + i + k] = 0;
+                if (cached) cached[rowoff + i + k] = 0;
+            }
+            if ((mw >> (sh + k)) & 1u) next_pos[rowoff + wpref[w] + __popc(mw & ((1u << (sh + k)) - 1u))] = i + k;
         }
-        if ((mw >> bit) & 1u) next_pos[rowoff + wpref[w] + __popc(mw & ((1u << bit) - 1u))] = i;
     }
     for (int i = base + tid; i < L; i += kVThreads) next_pos[rowoff + i] = -1;
 
