@@ -37,11 +37,22 @@ tau 0.5, seeded marginals and pair joints with planted conflicts.  The same
 kernel is also timed at the long-context shape (4 x 32768, its 64-position
 block decoded at once).
 
+Timing.  The K timed steps are one captured HIP graph, replayed behind
+untimed replays so that the host's launch of the graph (reported apart) is
+not inside the event pair.  Per call, HIP events on the launch stream give
+three figures: hot (an event pair around each call of 100 eager steps), cold
+(the same after a 1 GiB device read that evicts the caches) and b2b (back-to-
+back launches of the call alone from a graph, one event pair around them).
+The events are created without the system-scope fence a default event
+performs at record.  The roofline takes the cold figure for a call whose
+bytes fit the 256 MB last-level cache and the hot figure otherwise.
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config gpt2]
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -69,6 +80,49 @@ KERNEL_SRC = {"vocab_stats": ["vocab_stats.hip"],
               "verify": ["verify.hip"]}
 
 
+class Event:
+    """A HIP timing event created without the system-scope fence that a
+    default event performs when it is recorded (a write-back and invalidate
+    of the caches, which adds microseconds to every timed call and slows the
+    work after it).  It comes from the HIP runtime torch has loaded, so it
+    records on torch's streams."""
+    _hip = None
+
+    @classmethod
+    def hip(cls):
+        if cls._hip is None:
+            import torch
+            path = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+            L = ctypes.CDLL(path if os.path.exists(path) else "libamdhip64.so.7")
+            L.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = L
+        return cls._hip
+
+    def __init__(self):
+        self.ev = ctypes.c_void_p()
+        if self.hip().hipEventCreateWithFlags(ctypes.byref(self.ev), 0x20000000) != 0:   # hipEventDisableSystemFence
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self):
+        import torch
+        if self.hip().hipEventRecord(self.ev, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end) -> float:
+        """milliseconds from this event to `end` (both complete)"""
+        ms = ctypes.c_float()
+        if self.hip().hipEventElapsedTime(ctypes.byref(ms), self.ev, end.ev) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        if self.ev and self._hip is not None:
+            self._hip.hipEventDestroy(self.ev)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -79,8 +133,6 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from Python instead of replaying a captured graph")
-    ap.add_argument("--overlap", action="store_true",
-                    help="run the attention on a second stream beside the vocab pass (measured: no gain)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (HBM counter calibration)")
     return ap.parse_args()
@@ -123,7 +175,7 @@ def measured_traffic(kernel, config):
 class Step:
     """All device buffers of one workload and the kernels of one step."""
 
-    def __init__(self, D, W, cfg, dev, facache=False, overlap=False):
+    def __init__(self, D, W, cfg, dev, facache=False):
         import torch
         self.D, self.W, self.cfg, self.dev = D, W, cfg, dev
         B, L, H, d = cfg.B, cfg.L, cfg.Hkv, cfg.d
@@ -190,73 +242,29 @@ class Step:
         # stability kernel advances them, so a captured graph of several steps
         # replays successive steps
         self.step_t = torch.zeros(B, dtype=torch.int32, device=dev)
-        # the block's scatter + attention and the vocab pass share no data:
-        # in the captured step the attention runs on a second stream (default
-        # priority) beside the vocab pass, forked from and joined back into
-        # the main stream within each step
-        self.overlap = overlap and self.has_attn and self.has_vocab
-        if self.overlap:
-            self.side = torch.cuda.Stream(device=dev)
-            self.ev_fork, self.ev_join = torch.cuda.Event(), torch.cuda.Event()
-
-    def kernels(self):
-        ks = []
-        if self.has_attn:
-            ks.append("scatter_attention")
-        if self.facache:
-            ks.append("facache_merge")
-        if self.has_vocab:
-            ks.append("vocab_stats")
-        if self.has_stab:
-            ks.append("stability")
-        return ks
-
-    def run(self, events=None, flush=None):
+    def calls(self):
+        """the step's calls in order, as (name, function) pairs"""
         D, cfg = self.D, self.cfg
-
-        def mark(name, i):
-            if events is not None:
-                if i == 0 and flush is not None:
-                    flush()
-                events[name][i].record()
-
-        # per-kernel event passes run every call in order on one stream
-        overlap = self.overlap and events is None
+        out = []
         if self.has_attn:
             # the block's fresh K/V rows into the cache, then its queries over
             # the keys, in one call
-            mark("scatter_attention", 0)
-            if overlap:
-                import torch
-                self.ev_fork.record()
-                self.side.wait_event(self.ev_fork)
-                with torch.cuda.stream(self.side):
-                    D.dllm_scatter_attention(self.cache, self.kn, self.vn, self.pos, self.q, key_idx=self.key_idx,
-                                             out=self.out, workspace=self.attn_ws)
-                self.ev_join.record(self.side)
-            else:
-                D.dllm_scatter_attention(self.cache, self.kn, self.vn, self.pos, self.q, key_idx=self.key_idx,
-                                         out=self.out, workspace=self.attn_ws)
-            mark("scatter_attention", 1)
+            out.append(("scatter_attention", lambda: D.dllm_scatter_attention(
+                self.cache, self.kn, self.vn, self.pos, self.q, key_idx=self.key_idx, out=self.out,
+                workspace=self.attn_ws)))
         if self.facache:
-            mark("facache_merge", 0)
-            D.dllm_facache_merge(self.cache, self.qu, self.memo_o, self.memo_lse, key_idx=self.blk,
-                                 out=self.out_u, workspace=self.fa_ws)
-            mark("facache_merge", 1)
+            out.append(("facache_merge", lambda: D.dllm_facache_merge(
+                self.cache, self.qu, self.memo_o, self.memo_lse, key_idx=self.blk, out=self.out_u,
+                workspace=self.fa_ws)))
         if self.has_vocab:
-            mark("vocab_stats", 0)
-            D.dllm_vocab_stats(self.logits, V=cfg.V, argmax=self.am, maxprob=self.mp,
-                               entropy=self.en, workspace=self.vocab_ws)
-            mark("vocab_stats", 1)
-        if overlap:
-            import torch
-            torch.cuda.current_stream().wait_event(self.ev_join)
+            out.append(("vocab_stats", lambda: D.dllm_vocab_stats(
+                self.logits, V=cfg.V, argmax=self.am, maxprob=self.mp, entropy=self.en, workspace=self.vocab_ws)))
         if self.has_stab:
-            mark("stability", 0)
             B, L = cfg.B, cfg.L
-            D.dllm_stability_mask(self.st, self.step_t, None, self.am.view(B, L), self.mp.view(B, L),
-                                  self.en.view(B, L), advance_step=True, **self.kw)
-            mark("stability", 1)
+            out.append(("stability", lambda: D.dllm_stability_mask(
+                self.st, self.step_t, None, self.am.view(B, L), self.mp.view(B, L), self.en.view(B, L),
+                advance_step=True, **self.kw)))
+        return out
 
     def algorithmic_bytes(self):
         """bytes each kernel must move (reads + writes), per launch"""
@@ -310,7 +318,7 @@ class Step:
         run = lambda: self.D.dllm_block_attention(self.cache, qall, out=out)
         run()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = Event(), Event()
         e0.record()
         for _ in range(reps):
             run()
@@ -338,28 +346,15 @@ class FfnStep:
         self.out = torch.empty((M, self.K), dtype=torch.bfloat16, device=dev)
         self.facache = False
 
-    def kernels(self):
-        return ["fp8_addnorm", "fp8_gateup", "fp8_ffout"]
-
-    def run(self, events=None, flush=None):
+    def calls(self):
         D = self.D
-
-        def mark(name, i):
-            if events is not None:
-                if i == 0 and flush is not None:
-                    flush()
-                events[name][i].record()
-
-        mark("fp8_addnorm", 0)
-        D.dllm_fp8_addnorm_quant(self.x, self.res, self.gamma, eps=1e-6, residual_out=self.r_out,
-                                 codes=self.ca, scales=self.sa)
-        mark("fp8_addnorm", 1)
-        mark("fp8_gateup", 0)
-        D.dllm_fp8_gemm_swiglu(self.ca, self.sa, self.cgu, self.sgu, out_codes=self.ch, out_scales=self.sh)
-        mark("fp8_gateup", 1)
-        mark("fp8_ffout", 0)
-        D.dllm_fp8_gemm(self.ch, self.sh, self.cout, self.sout, out=self.out)
-        mark("fp8_ffout", 1)
+        return [
+            ("fp8_addnorm", lambda: D.dllm_fp8_addnorm_quant(self.x, self.res, self.gamma, eps=1e-6,
+                                                             residual_out=self.r_out, codes=self.ca, scales=self.sa)),
+            ("fp8_gateup", lambda: D.dllm_fp8_gemm_swiglu(self.ca, self.sa, self.cgu, self.sgu, out_codes=self.ch,
+                                                          out_scales=self.sh)),
+            ("fp8_ffout", lambda: D.dllm_fp8_gemm(self.ch, self.sh, self.cout, self.sout, out=self.out)),
+        ]
 
     def algorithmic_bytes(self):
         M, K, I = self.M, self.K, self.I
@@ -402,25 +397,13 @@ class PolicyStep:
         self.facache = False
         self.attn_split = False
 
-    def kernels(self):
-        return ["stability", "evict"]
-
-    def run(self, events=None, flush=None):
+    def calls(self):
         D = self.D
-
-        def mark(name, i):
-            if events is not None:
-                if i == 0 and flush is not None:
-                    flush()
-                events[name][i].record()
-
-        mark("stability", 0)
-        D.dllm_stability_mask(self.st, self.step_t, None, self.am, self.mp, self.en, advance_step=True,
-                              **self.kw)
-        mark("stability", 1)
-        mark("evict", 0)
-        D.dllm_evict_by_confidence(self.st, self.quota, None, self.evicted)
-        mark("evict", 1)
+        return [
+            ("stability", lambda: D.dllm_stability_mask(self.st, self.step_t, None, self.am, self.mp, self.en,
+                                                        advance_step=True, **self.kw)),
+            ("evict", lambda: D.dllm_evict_by_confidence(self.st, self.quota, None, self.evicted)),
+        ]
 
     def algorithmic_bytes(self):
         BL, K = self.B * self.L, self.cfg.K
@@ -450,13 +433,26 @@ class PolicyStep:
         run = lambda: self.D.dllm_evict_by_confidence(st, quota, None)
         run()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = Event(), Event()
         e0.record()
         for _ in range(reps):
             run()
         e1.record()
         torch.cuda.synchronize()
         return 1000.0 * e0.elapsed_time(e1) / reps
+
+
+def run_step(step, events=None, flush=None):
+    """one step: every call in order on the current stream; with events, an
+    event pair around each call (after `flush`, when given)"""
+    for name, fn in step.calls():
+        if events is not None:
+            if flush is not None:
+                flush()
+            events[name][0].record()
+        fn()
+        if events is not None:
+            events[name][1].record()
 
 
 def verify_inputs(B, L, n, Wn, seed, dev, block_at_end=False):
@@ -496,18 +492,10 @@ class VerifyStep:
         self.facache = False
         self.attn_split = False
 
-    def kernels(self):
-        return ["verify"]
-
-    def run(self, events=None, flush=None):
-        if events is not None:
-            if flush is not None:
-                flush()
-            events["verify"][0].record()
-        self.D.dllm_self_verify(self.st, self.dec, self.pm, self.pj, self.Wn, self.tau, rollback=self.rollback,
-                                n_rollback=self.nrb, rb_pos=self.rbp)
-        if events is not None:
-            events["verify"][1].record()
+    def calls(self):
+        return [("verify", lambda: self.D.dllm_self_verify(self.st, self.dec, self.pm, self.pj, self.Wn, self.tau,
+                                                           rollback=self.rollback, n_rollback=self.nrb,
+                                                           rb_pos=self.rbp))]
 
     def algorithmic_bytes(self):
         B, L, n, Wn = self.B, self.L, self.n, self.Wn
@@ -530,7 +518,7 @@ class VerifyStep:
         run = lambda: self.D.dllm_self_verify(st, dec, pm, pj, self.Wn, self.tau, rollback=rb)
         run()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = Event(), Event()
         e0.record()
         for _ in range(reps):
             run()
@@ -724,14 +712,14 @@ def main():
     elif args.config == "verify":
         step = VerifyStep(D, W, cfg, dev)
     else:
-        step = Step(D, W, cfg, dev, facache=args.config == "facache", overlap=args.overlap)
+        step = Step(D, W, cfg, dev, facache=args.config == "facache")
     for _ in range(args.warmup):
-        step.run()
+        run_step(step)
     torch.cuda.synchronize()
 
-    names = step.kernels()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    names = [n for n, _ in step.calls()]
+    start = Event()
+    end = Event()
     graph = None
     launch = {}
     if not args.eager:
@@ -740,7 +728,7 @@ def main():
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             for i in range(args.steps):
-                step.run()
+                run_step(step)
         torch.cuda.synchronize()
         graph.replay()                      # one untimed replay
         torch.cuda.synchronize()
@@ -773,50 +761,83 @@ def main():
         t_wall = time.perf_counter()
         start.record()
         for i in range(args.steps):
-            step.run()
+            run_step(step)
         end.record()
         torch.cuda.synchronize()
         t_wall = time.perf_counter() - t_wall
         ms = start.elapsed_time(end) / args.steps
 
-    # per-kernel times: HIP event pairs on the launch stream around each call,
-    # in eager passes of at least 100 steps, queued behind graph replays (or
-    # a flush) so that the host's launch gaps fall outside the event pairs.
-    # "hot": back to back, as in the step; "cold": a 1 GiB device write before
-    # every call, which evicts the 256 MB last-level cache and the L2s
+    # Per-call times, HIP event pairs on the launch stream:
+    #   hot   an event pair around each call of 100 eager steps, queued behind
+    #         GPU work so that no host launch gap falls inside a pair;
+    #   cold  the same with a 1 GiB device read before every call, which
+    #         leaves the 256 MB last-level cache and the L2s holding other,
+    #         clean data (a write would leave them dirty, and the call would
+    #         pay the write-back of someone else's data);
+    #   b2b   one event pair around R back-to-back launches of the call alone,
+    #         replayed from a captured graph behind 5 ms of queued GPU work:
+    #         the kernel's own duration, free of the few microseconds an event
+    #         pair adds to every call.
     iters = max(100, args.steps)
-    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    flush = lambda: flush_buf.fill_(1)
+    flush_buf = torch.ones(1 << 28, dtype=torch.int32, device=dev)      # 1 GiB
+    flush = lambda: flush_buf.amax()                                     # a read of every byte
 
-    def kernel_pass(cold):
-        ev = {n: [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(iters)]
-              for n in names}
-        # keep the GPU busy while the host queues the pass (about 150 us of
-        # host time per call): replays of the timed graph, which also keep
-        # the clocks where the timed region had them
-        busy_ms = max(20.0, 0.15 * iters * len(names))
+    def busy(ms_target):
+        # queued GPU work while the host enqueues a pass: replays of the
+        # timed graph (which keep the clocks where the timed region had
+        # them), else reads of the flush buffer
         if graph is not None:
-            for _ in range(min(200, max(1, int(busy_ms / max(ms * args.steps, 1e-3)) + 1))):
+            for _ in range(min(200, max(1, int(ms_target / max(ms * args.steps, 1e-3)) + 1))):
                 graph.replay()
         else:
-            for _ in range(max(1, int(busy_ms / 0.2))):
-                flush_buf.fill_(0)              # about 0.2 ms of GPU work each
+            for _ in range(max(1, int(ms_target / 0.25))):
+                flush()
+
+    def pct_stats(t):
+        t = sorted(t)
+        pct = lambda q: t[min(len(t) - 1, int(round(q * (len(t) - 1))))]
+        return {"mean": sum(t) / len(t), "p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)}
+
+    def kernel_pass(cold):
+        ev = {n: [[Event() for _ in range(2)] for _ in range(iters)]
+              for n in names}
+        busy(max(20.0, 0.15 * iters * len(names)))       # about 150 us of host time per call
         for i in range(iters):
-            step.run({n: ev[n][i] for n in names}, flush=flush if cold else None)
+            run_step(step, {n: ev[n][i] for n in names}, flush=flush if cold else None)
         torch.cuda.synchronize()
-        stats = {}
-        for n in names:
-            t = sorted(1000.0 * e[0].elapsed_time(e[1]) for e in ev[n])
-            pct = lambda q: t[min(len(t) - 1, int(round(q * (len(t) - 1))))]
-            stats[n] = {"mean": sum(t) / len(t), "p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)}
-        return stats
+        return {n: pct_stats([1000.0 * e[0].elapsed_time(e[1]) for e in ev[n]]) for n in names}
 
     hot = kernel_pass(False)
     cold = kernel_pass(True)
+
+    def b2b_pass(rounds=5):
+        out = {}
+        for n, fn in step.calls():
+            reps = int(min(400, max(20, 1000.0 / max(hot[n]["mean"], 1e-3))))   # about 1 ms per replay
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(reps):
+                    fn()
+            g.replay()
+            torch.cuda.synchronize()
+            for _ in range(20):
+                flush()                                  # about 5 ms of queued GPU work
+            e0, e1 = Event(), Event()
+            e0.record()
+            for _ in range(rounds):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            out[n] = {"mean": 1000.0 * e0.elapsed_time(e1) / (reps * rounds), "launches": reps * rounds,
+                      "reps": reps}
+            del g
+        return out
+
+    b2b = b2b_pass()
     del flush_buf
-    kernel_timing = ("HIP events on the launch stream around each call, eager passes of %d steps queued "
-                     "behind GPU work so that no host launch gap falls inside an event pair; cold = a "
-                     "1 GiB device write before every call" % iters)
+    kernel_timing = ("HIP events without the system-scope fence, on the launch stream: hot/cold = an event pair "
+                     "around each call of %d eager steps (cold: after a 1 GiB device read), b2b = one event pair "
+                     "around back-to-back launches of the call alone from a captured graph" % iters)
     per_kernel_us = {n: hot[n]["mean"] for n in names}
     alg = step.algorithmic_bytes()
     flops = step.algorithmic_flops()
@@ -825,6 +846,9 @@ def main():
     dom = max(per_kernel_us, key=per_kernel_us.get)
     # a working set that fits the 256 MB last-level cache is timed cold for
     # the roofline: the hot figure would be a cache rate, not an HBM one
+    # a larger one never stays in the cache between calls, and takes the hot
+    # figure of the call as it runs in the step (back to back, the memory-bound
+    # calls run slower: b2b is reported beside)
     mall_resident = alg[dom] < 256 * 2 ** 20
     dom_us = cold[dom]["mean"] if mall_resident else hot[dom]["mean"]
     traffic = measured_traffic(dom, args.config)
@@ -918,12 +942,11 @@ def main():
                    if args.config == "ffn" else
                    {"workload": desc, "name": cfg.name, "B": cfg.B, "L": cfg.L, "heads": cfg.Hq,
                     "kv_heads": cfg.Hkv, "d_head": cfg.d, "block": cfg.b, "vocab": cfg.V})
-                  | {"launch": ("eager" if graph is None else "hip graph of the timed steps")
-                     + ("; scatter + attention on a second stream beside vocab_stats"
-                        if getattr(step, "overlap", False) else "")},
+                  | {"launch": "eager" if graph is None else "hip graph of the timed steps"},
         "kernels_us": {n: round(v, 2) for n, v in per_kernel_us.items()},
         "kernels_us_pct": {n: {"hot": {k: round(v, 2) for k, v in hot[n].items()},
-                               "cold": {k: round(v, 2) for k, v in cold[n].items()}} for n in names},
+                               "cold": {k: round(v, 2) for k, v in cold[n].items()},
+                               "b2b": {k: round(v, 2) for k, v in b2b[n].items()}} for n in names},
         **launch,
         "roofline": roofline,
         **extra,
