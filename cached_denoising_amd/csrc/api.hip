@@ -55,6 +55,8 @@ int check_cache(const dllm_kv_cache *c) {
     const int esz = dtype_size(c->dtype);
     if (!esz) return DLLM_EDTYPE;
     if ((c->d_head * esz) % 16 != 0) return DLLM_EALIGN;
+    // the rows of one (sequence, KV head) are addressed with 32-bit offsets
+    if ((uint64_t)c->L * c->d_head * esz > 0xFFFFFFFFull) return DLLM_ERANGE;
     if (!aligned16(c->k) || !aligned16(c->v)) return DLLM_EALIGN;
     if (c->dtype == DLLM_E4M3) {
         if (c->d_head % 128 != 0) return DLLM_ESHAPE;

@@ -7,17 +7,25 @@
 // A workgroup of NRG (2 or 4) waves owns one (sequence, KV head, row chunk,
 // key split); wave w owns 32 rows of the chunk, and every wave walks the same
 // key tiles.  Each 32-key tile's K rows, V rows and (e4m3) per-key scales are
-// loaded once per workgroup, straight from HBM into a ring of kNS LDS stages
+// loaded once per workgroup, straight from HBM into a ring of LDS stages
 // (global_load_lds, no registers), the loads of one tile spread over the
 // waves.  Per tile a wave waits for its own loads, then one workgroup
 // barrier makes the whole tile visible and frees the stage the previous tile
-// used, which the next tile's loads then fill.  Each wave then reads
-//     A = K rows (16-byte chunks XOR-swizzled so that a read phase hits
-//         distinct banks), widened e4m3 -> bf16 exactly,
-//     B = its queries, held in registers for the whole walk,
-// for S^T = K Q^T on v_mfma_f32_16x16x32_bf16, runs the base-2 online
-// softmax with the lazy max, and accumulates O^T += V^T P^T with V^T read
-// transposed from the row-major V tile.  Compared with one wave per key run,
+// used, which the next tile's loads then fill.  Each wave then forms
+// S^T = K Q^T with its queries held in registers for the whole walk:
+//   bf16 cache: A = K rows (16-byte chunks XOR-swizzled so that a read phase
+//     hits distinct banks) and B = the queries on v_mfma_f32_16x16x32_bf16;
+//   e4m3 cache: A = the K codes as they landed in the ring and B = the
+//     queries split exactly into two e4m3 parts, hi + lo, each with a power-
+//     of-two scale per 32 dimensions, on the block-scaled
+//     v_mfma_scale_f32_16x16x128_f8f6f4 (two products per 16x16 tile, at
+//     twice the rate of bf16, so the product costs what the bf16 one does
+//     and the K tile is never widened); the per-key K scale then multiplies
+//     the scores.
+// It runs the base-2 online softmax with the lazy max, and accumulates
+// O^T += V^T P^T with V^T read transposed from a row-major bf16 V tile (an
+// e4m3 V tile is widened exactly to bf16 once per workgroup, and its per-key
+// scale multiplies P).  Compared with one wave per key run,
 // the K/V bytes cross L2 once per workgroup instead of once per row group,
 // and the query rows are loaded once.  Key splits write (m, l, O~) partials
 // for the merge kernel of the per-wave path.  With a memoized state per row
@@ -34,7 +42,10 @@ namespace {
 
 using namespace attn;
 
-constexpr int kNS = 4;                 // LDS ring stages: three tiles in flight while one is used
+constexpr int kNS = 4;                 // LDS ring stages (bf16): three tiles in flight while one is used
+constexpr int kNS8 = 4;                // LDS ring stages (e4m3): K of one tile is read from the ring
+                                       // while the next is widened and one more is in flight (a fifth
+                                       // or sixth stage measured no faster)
 constexpr int kTableKeys = 2048;       // key indices of one split held in LDS (with a key map)
 
 // XOR swizzle of the 16-byte chunks of K row kappa in LDS.  One 8-lane phase
@@ -46,6 +57,12 @@ __device__ __forceinline__ int kswz(int kappa) { return (kappa & 3) | ((kappa >>
 // 64 banks: a phase touches rows {0..3, 8..11, 16..19, 24..27} + 4t at one
 // logical chunk, and these 16 rows go to 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int kswz16(int kappa) { return (kappa & 3) | ((kappa >> 1) & 12); }
+// The same for 128-byte e4m3 K rows read as the A operand of the 16x16x128
+// product: a 16-lane phase reads rows {0..3, 8..11, 16..19, 24..27} + 4t at
+// one logical chunk; the row parity picks the 128-byte half of the 256-byte
+// bank line and this swizzle the 16-byte bank group within it, so the 16 rows
+// hit 16 distinct bank groups.
+__device__ __forceinline__ int kswz8(int kappa) { return ((kappa >> 1) & 1) | ((kappa >> 2) & 6); }
 // V rows of 256 bytes: a 32-lane phase of the transposed reads touches rows
 // {0..3, 8..11} (+4) at logical chunks {2dt, 2dt+1}; bits 1..3 separate those
 // 8 rows, bit 0 separates neighbouring rows for the widening's writes.
@@ -61,6 +78,76 @@ __device__ __forceinline__ void vm_wait_upto(int n) {
     } else {
         if (n >= MAXN) vm_wait<MAXN>();
         else vm_wait_upto<MAXN - 1>(n);
+    }
+}
+
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
+constexpr int kE8M0One = 127;          // E8M0 code of the scale 1.0
+
+// Block exponent of a 32-value query block with largest magnitude a: the
+// block divided by 2^e lies in [128, 256) at its largest (e4m3 holds up to
+// 448), clamped so that e and e - 4 are E8M0 scales; 0 for an all-zero block.
+__device__ __forceinline__ int query_block_exp(float a) {
+    if (!(a > 0.f)) return 0;
+    const int ex = (int)((__float_as_uint(a) >> 23) & 0xff) - 127;   // floor(log2 a); -127 if subnormal
+    return min(max(ex - 7, -123), 127);
+}
+
+// The queries as the B operand of the block-scaled 16x16x128 e4m3 product.
+// Lane (l16, g) holds dims 32g .. 32g+31 of row l16 (w: 32 bf16 values); its
+// bytes 0..15 belong to scale block g/2 and bytes 16..31 to block 2 + g/2,
+// and it supplies the scale of block g of its row (the operand's scale
+// layout: a block's scale sits in the lane of its row plus 16 times the block
+// index).  Each value x of a block with exponent e is split exactly into
+// x = hi * 2^e + lo * 2^(e-4): hi = x / 2^e rounded to e4m3, lo = the rest
+// times 16, which has at most 4 significant bits when x has bf16's 8 (values
+// more than 13 binades below the block's largest lose bits of lo, an error
+// below 2^-17 of the block's largest).  p[0] / p[1] hold hi / lo, sc[0] /
+// sc[1] their E8M0 scales.
+__device__ __forceinline__ void split_query(const uint4 (&w)[4], int g, i32x8_t (&p)[2], int (&sc)[2]) {
+    float x[32];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const uint32_t u[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            x[8 * c + 2 * k] = __uint_as_float(u[k] << 16);
+            x[8 * c + 2 * k + 1] = __uint_as_float(u[k] & 0xffff0000u);
+        }
+    }
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        a0 = fmaxf(a0, fabsf(x[j]));
+        a1 = fmaxf(a1, fabsf(x[16 + j]));
+    }
+    // lanes g and g^1 hold the two halves of blocks g/2 and 2 + g/2
+    a0 = fmaxf(a0, __shfl_xor(a0, 16));
+    a1 = fmaxf(a1, __shfl_xor(a1, 16));
+    const int e0 = query_block_exp(a0), e1 = query_block_exp(a1);
+    // block g's largest value: first halves of lane groups 2g, 2g+1 (g < 2)
+    // or second halves of groups 2(g-2), 2(g-2)+1
+    const int src = (threadIdx.x & 15) + 32 * (g & 1);
+    const float b0 = __shfl(a0, src), b1 = __shfl(a1, src);
+    const int es = query_block_exp(g < 2 ? b0 : b1);
+    sc[0] = es + 127;
+    sc[1] = es - 4 + 127;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+        const int e = d < 4 ? e0 : e1;
+        float xs[4], lo[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) xs[k] = ldexpf(x[4 * d + k], -e);
+        int hw = __builtin_amdgcn_cvt_pk_fp8_f32(xs[0], xs[1], 0, false);
+        hw = __builtin_amdgcn_cvt_pk_fp8_f32(xs[2], xs[3], hw, true);
+        lo[0] = (xs[0] - __builtin_amdgcn_cvt_f32_fp8(hw, 0)) * 16.f;
+        lo[1] = (xs[1] - __builtin_amdgcn_cvt_f32_fp8(hw, 1)) * 16.f;
+        lo[2] = (xs[2] - __builtin_amdgcn_cvt_f32_fp8(hw, 2)) * 16.f;
+        lo[3] = (xs[3] - __builtin_amdgcn_cvt_f32_fp8(hw, 3)) * 16.f;
+        int lw = __builtin_amdgcn_cvt_pk_fp8_f32(lo[0], lo[1], 0, false);
+        lw = __builtin_amdgcn_cvt_pk_fp8_f32(lo[2], lo[3], lw, true);
+        p[0][d] = hw;
+        p[1][d] = lw;
     }
 }
 
@@ -85,9 +172,11 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
     constexpr int NC = D / 32;             // k-chunks of the first product
     constexpr int NDT = D / 16;            // dim tiles of the second product
     constexpr bool E4 = KVDT == DLLM_E4M3;
-    // e4m3 tiles are widened to bf16 once per workgroup, into one of two
-    // converted stages; bf16 tiles are read where they landed
+    // e4m3 V tiles are widened to bf16 once per workgroup, into one of two
+    // converted stages, and e4m3 K tiles are read where they landed; bf16
+    // tiles are read where they landed
     constexpr bool CONV = E4;
+    constexpr int NS = E4 ? kNS8 : kNS;    // ring stages
     constexpr int ESZ = E4 ? 1 : 2;
     constexpr int ROWB = D * ESZ;          // bytes of one cached row
     constexpr int CPR = ROWB / 16;         // 16-byte chunks per cached row
@@ -95,28 +184,30 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
     constexpr int TB = 32 * ROWB;          // bytes of one K (or V) tile as cached
     constexpr int NK = TB / 1024;          // loads per K tile (as many for V)
     static_assert(NK % NRG == 0, "every wave issues the same loads");
+    static_assert(!E4 || D == 128, "e4m3 rows are one 128-element scale group");
     constexpr int LW = 2 * NK / NRG + (E4 ? 1 : 0);    // loads each wave issues per tile
     constexpr int STAGE = 2 * TB + (E4 ? 256 : 0);
     constexpr int BROW = D * 2;            // bytes of one bf16 row
     constexpr int CTB = 32 * BROW;         // one bf16 K (or V) tile
     // swizzles of the bf16 operand tiles, and of the ring stages as loaded
-    // (the operand tiles themselves for bf16; read linearly for widening)
+    // (the operand tiles themselves for bf16; e4m3 K read as the fp8 operand,
+    // e4m3 V read linearly for widening)
     auto kswz_b = [](int r) { return BROW == 256 ? kswz16(r) : kswz(r); };
     auto vswz_b = [](int r) { return BROW == 256 ? vswz16(r) : vswz_bf16(r); };
-    auto kswz_r = [&](int r) { return CONV ? kswz(r) : kswz_b(r); };
+    auto kswz_r = [&](int r) { return E4 ? kswz8(r) : kswz_b(r); };
     auto vswz_r = [&](int r) { return CONV ? vswz_e4m3(r) : vswz_b(r); };
-    constexpr int CSTAGE = CONV ? 2 * CTB + 3 * 128 + 16 : 0;   // + per-key kfac, bias, vfac; full flag
+    constexpr int CSTAGE = CONV ? CTB + 3 * 128 : 0;   // V + per-key kfac, bias, vfac
     constexpr int TAB = MAP ? kTableKeys * 4 : 0;
     // the two converted stages first, so that both lie within the 64 KB
     // immediate offset of an LDS read from one base register: with the tile
     // loop unrolled by two, every operand read of a converted stage is a
     // loop-invariant register plus a constant
     constexpr int OFF_RING = 2 * CSTAGE;
-    constexpr int OFF_TAB = OFF_RING + kNS * STAGE;
+    constexpr int OFF_TAB = OFF_RING + NS * STAGE;
     constexpr int SMEM = OFF_TAB + TAB;
     static_assert(TB % 1024 == 0 && CPR <= 16, "tile layout");
     static_assert(SMEM <= kLdsBytes, "LDS of one workgroup");
-    static_assert((kNS - 2) * LW < 64, "vmcnt range");
+    static_assert((NS - 2) * LW < 64, "vmcnt range");
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
 
@@ -154,7 +245,11 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
         return kt * 32 + kappa < n_keys ? kt * 32 + kappa : -1;
     };
 
-    uint4 qreg[RT][NC];                    // this wave's queries (loaded after the first tiles)
+    // this wave's queries (loaded after the first tiles): bf16 rows in the
+    // bf16 product's layout, or (e4m3) their two e4m3 parts and scales
+    uint4 qreg[RT][NC];
+    i32x8_t q8[RT][2];
+    int qsc[RT][2];
 
     // ---- loads of tile kt into ring stage `slot`: every wave issues NK/NRG
     // of the K tile's 1 KB loads, as many of the V tile's, and (e4m3) the
@@ -173,6 +268,11 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
         }
         tk.s = E4 ? key_of(kt, lane & 31) : 0;
     };
+    // wave-uniform bases of this (sequence, KV head)'s rows; a lane's load is
+    // one 32-bit byte offset from them (the rows of one (sequence, KV head)
+    // span less than 4 GiB)
+    const unsigned char *kbase = static_cast<const unsigned char *>(ck) + kv_base * ROWB;
+    const unsigned char *vbase = static_cast<const unsigned char *>(cv) + kv_base * ROWB;
     auto issue = [&](const TileKeys &tk, int slot) {
         unsigned char *st = smem + OFF_RING + slot * STAGE;
 #pragma unroll
@@ -183,9 +283,8 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
             const int p = j * 64 + lane;
             const int r = p / CPR, sl = p % CPR;
             const int kk = tk.k[u];
-            const unsigned char *src = static_cast<const unsigned char *>(ck) +
-                                       (kv_base + (kk < 0 ? 0 : kk)) * ROWB + (sl ^ kswz_r(r)) * 16;
-            lds_dma16<NT>(src, st + j * 1024);
+            const uint32_t off = (uint32_t)(kk < 0 ? 0 : kk) * ROWB + (uint32_t)(sl ^ kswz_r(r)) * 16;
+            lds_dma16s<NT>(kbase, off, st + j * 1024);
         }
 #pragma unroll
         for (int u = 0; u < NK / NRG; ++u) {
@@ -194,18 +293,18 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
             const int rho = RPI * jv + lane / CPR;
             const int chunk = (lane % CPR) ^ vswz_r(rho);
             const int kk = tk.v[u];
-            const unsigned char *src = static_cast<const unsigned char *>(cv) +
-                                       (kv_base + (kk < 0 ? 0 : kk)) * ROWB + chunk * 16;
-            lds_dma16<NT>(src, st + TB + jv * 1024);
+            const uint32_t off = (uint32_t)(kk < 0 ? 0 : kk) * ROWB + (uint32_t)chunk * 16;
+            lds_dma16s<NT>(vbase, off, st + TB + jv * 1024);
         }
         if (E4) {
             // lanes 0..31: K scales of keys 0..31; lanes 32..63: V scales;
-            // this wave writes lanes [64 w / NRG, 64 (w + 1) / NRG)
+            // this wave writes lanes [64 w / NRG, 64 (w + 1) / NRG), all of
+            // one kind
             const int lo = wave * (64 / NRG);
             if (lane >= lo && lane < lo + 64 / NRG) {
                 const int kk = tk.s;
-                const float *src = (lane < 32 ? ksc : vsc) + kv_base + (kk < 0 ? 0 : kk);
-                lds_dma4(src, st + 2 * TB);
+                const float *sbase = (lo < 32 ? ksc : vsc) + kv_base;
+                lds_dma4s(sbase, (uint32_t)(kk < 0 ? 0 : kk) * 4, st + 2 * TB);
             }
         }
     };
@@ -215,16 +314,15 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
         issue(tk, slot);
     };
 
-    // ---- e4m3: widen tile kt (ring stage `slot`) into converted stage
-    // `cslot`, the whole workgroup sharing the work: each 16-code chunk
-    // becomes two bf16 chunks in the bf16 layouts the reads expect (K chunks
-    // swizzled by kswz, V chunks by the bf16 vswz).  Threads 0..31 also
-    // write the per-key factors: kfac = K scale * scale * log2(e), the mask
-    // bias (0, or -inf for a missing key) and vfac = V scale, and wave 0
-    // whether all 32 keys are present.  Split in a read half and a write
+    // ---- e4m3: widen the V rows of tile kt (ring stage `slot`) into
+    // converted stage `cslot`, the whole workgroup sharing the work: each
+    // 16-code chunk becomes two bf16 chunks in the layout the transposed
+    // reads expect (the bf16 vswz).  Threads 0..31 also write the per-key
+    // factors: kfac = K scale * scale * log2(e), the mask bias (0, or -inf for
+    // a missing key) and vfac = V scale.  Split in a read half and a write
     // half, so the reads can be issued early.
-    constexpr int NCH = 32 * CPR;          // 16-code chunks per K (or V) tile
-    constexpr int PER = CONV ? (2 * NCH + NRG * kWave - 1) / (NRG * kWave) : 1;
+    constexpr int NCH = 32 * CPR;          // 16-code chunks per V tile
+    constexpr int PER = CONV ? (NCH + NRG * kWave - 1) / (NRG * kWave) : 1;
     struct ConvIn {
         uint4 w[PER];
         float ks, vs;
@@ -236,8 +334,8 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
 #pragma unroll
             for (int it = 0; it < PER; ++it) {
                 const int idx = threadIdx.x + it * NRG * kWave;
-                if (PER * NRG * kWave == 2 * NCH || idx < 2 * NCH)
-                    ci_.w[it] = *reinterpret_cast<const uint4 *>(st + idx * 16);   // K chunks, then V chunks
+                if (PER * NRG * kWave == NCH || idx < NCH)
+                    ci_.w[it] = *reinterpret_cast<const uint4 *>(st + TB + idx * 16);
             }
             const int kap = threadIdx.x & 31;
             const float *sc = reinterpret_cast<const float *>(st + 2 * TB);
@@ -254,27 +352,20 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
 #pragma unroll
             for (int it = 0; it < PER; ++it) {
                 const int idx = threadIdx.x + it * NRG * kWave;
-                if (PER * NRG * kWave != 2 * NCH && idx >= 2 * NCH) break;
-                const bool isv = idx >= NCH;
-                const int ci = isv ? idx - NCH : idx;
-                const int r = ci / CPR, sl = ci % CPR;
-                const int gc = sl ^ (isv ? vswz_r(r) : kswz_r(r));   // the row's chunk in slot sl
-                const int sw = isv ? vswz_b(r) : kswz_b(r);
-                unsigned char *row = cs + (isv ? CTB : 0) + r * BROW;
+                if (PER * NRG * kWave != NCH && idx >= NCH) break;
+                const int r = idx / CPR, sl = idx % CPR;
+                const int gc = sl ^ vswz_r(r);         // the row's chunk in slot sl
+                const int sw = vswz_b(r);
+                unsigned char *row = cs + r * BROW;
                 const uint4 w = ci_.w[it];
                 *reinterpret_cast<uint4 *>(row + ((2 * gc) ^ sw) * 16) = e4m3x8_to_bf16(w.x, w.y);
                 *reinterpret_cast<uint4 *>(row + ((2 * gc + 1) ^ sw) * 16) = e4m3x8_to_bf16(w.z, w.w);
             }
-            float *fac = reinterpret_cast<float *>(cs + 2 * CTB);
+            float *fac = reinterpret_cast<float *>(cs + CTB);
             if (threadIdx.x < 32) {
                 fac[threadIdx.x] = ci_.ks * scale_log2;
                 fac[32 + threadIdx.x] = ci_.present ? 0.f : kNegInf;
                 fac[64 + threadIdx.x] = ci_.vs;
-            }
-            if (wave == 0) {
-                // lanes 32..63 repeat keys 0..31
-                const bool all = __ballot(ci_.present) == ~0ull;
-                if (lane == 0) reinterpret_cast<int *>(fac)[96] = all ? 1 : 0;
             }
         } else {
             (void)cslot; (void)ci_;
@@ -290,26 +381,48 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) { m[rt] = kMinit; l[rt] = 0.f; }
 
-    // ---- one tile: kb / vb are its bf16 K and V rows (chunk-swizzled), fac
-    // its per-key factors (converted tiles only)
+    // e4m3 K operands of the tile being computed (loaded one step ahead):
+    // lane (l16, g) holds dims 32g .. 32g+31 of key 8(l16/4) + 4t + l16%4 of
+    // half t, the codes as cached, with the queries' parts on the same dims
+    uint4 k8[2][2];
+    auto load_k8 = [&](const unsigned char *kb) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int kappa = 8 * (l16 >> 2) + 4 * t + (l16 & 3);
+            const unsigned char *krow = kb + kappa * ROWB;
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                k8[t][c] = *reinterpret_cast<const uint4 *>(krow + ((2 * g + c) ^ kswz8(kappa)) * 16);
+        }
+    };
+
+    // ---- one tile: kb / vb are its bf16 K and V rows (chunk-swizzled; e4m3:
+    // K in k8, V widened), fac its per-key factors and tile_full whether all
+    // its keys are present (converted tiles only)
     auto compute = [&](int kt, const unsigned char *kb, const unsigned char *vb, const float *fac,
-                       auto &&side) {
+                       bool tile_full, auto &&side) {
         // factors of the keys 8g .. 8g+7 this lane holds in S^T
         float kfac[8], kbias[8], vfac[8];
         bool full = true;
         uint32_t present = ~0u;
         if (CONV) {
-            full = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int *>(fac)[96]) != 0;
+            full = tile_full;
             const float4 *f4 = reinterpret_cast<const float4 *>(fac);
             const float4 a0 = f4[2 * g], a1 = f4[2 * g + 1];
-            const float4 b0 = f4[8 + 2 * g], b1 = f4[8 + 2 * g + 1];
             const float4 c0 = f4[16 + 2 * g], c1 = f4[16 + 2 * g + 1];
             kfac[0] = a0.x; kfac[1] = a0.y; kfac[2] = a0.z; kfac[3] = a0.w;
             kfac[4] = a1.x; kfac[5] = a1.y; kfac[6] = a1.z; kfac[7] = a1.w;
-            kbias[0] = b0.x; kbias[1] = b0.y; kbias[2] = b0.z; kbias[3] = b0.w;
-            kbias[4] = b1.x; kbias[5] = b1.y; kbias[6] = b1.z; kbias[7] = b1.w;
             vfac[0] = c0.x; vfac[1] = c0.y; vfac[2] = c0.z; vfac[3] = c0.w;
             vfac[4] = c1.x; vfac[5] = c1.y; vfac[6] = c1.z; vfac[7] = c1.w;
+            if (full) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) kbias[e] = 0.f;
+            } else {
+                // the mask bias of missing keys, read only for tiles that have some
+                const float4 b0 = f4[8 + 2 * g], b1 = f4[8 + 2 * g + 1];
+                kbias[0] = b0.x; kbias[1] = b0.y; kbias[2] = b0.z; kbias[3] = b0.w;
+                kbias[4] = b1.x; kbias[5] = b1.y; kbias[6] = b1.z; kbias[7] = b1.w;
+            }
         } else {
             // keys present in the tile (bit kappa; lanes 32..63 repeat 0..31)
             present = (uint32_t)__ballot(key_of(kt, lane & 31) >= 0);
@@ -317,27 +430,44 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
         }
         // K operands of both 16-key halves: slot l16 of half t is key
         // 8(l16/4) + 4t + l16%4, so S^T leaves keys 8g .. 8g+7 of one row in a lane
-        uint4 ka[2][NC];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int kappa = 8 * (l16 >> 2) + 4 * t + (l16 & 3);
-            const unsigned char *krow = kb + kappa * BROW;
-#pragma unroll
-            for (int c = 0; c < NC; ++c)
-                ka[t][c] = *reinterpret_cast<const uint4 *>(krow + ((c * 4 + g) ^ kswz_b(kappa)) * 16);
-        }
         f32x4_t sacc[RT][2];
+        if constexpr (E4) {
+            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) sacc[rt][0] = sacc[rt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < 2; ++t) {
+                const i32x8_t a = {(int)k8[t][0].x, (int)k8[t][0].y, (int)k8[t][0].z, (int)k8[t][0].w,
+                                   (int)k8[t][1].x, (int)k8[t][1].y, (int)k8[t][1].z, (int)k8[t][1].w};
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
-                    sacc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, ka[t][c]), __builtin_bit_cast(bf16x8_t, qreg[rt][c]),
-                        sacc[rt][t], 0, 0, 0);
+                    sacc[rt][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        a, q8[rt][0], z, 0, 0, 0, kE8M0One, 0, qsc[rt][0]);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    sacc[rt][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        a, q8[rt][1], sacc[rt][t], 0, 0, 0, kE8M0One, 0, qsc[rt][1]);
+            }
+        } else {
+            uint4 ka[2][NC];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int kappa = 8 * (l16 >> 2) + 4 * t + (l16 & 3);
+                const unsigned char *krow = kb + kappa * BROW;
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    ka[t][c] = *reinterpret_cast<const uint4 *>(krow + ((c * 4 + g) ^ kswz_b(kappa)) * 16);
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) sacc[rt][0] = sacc[rt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+                        sacc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, ka[t][c]), __builtin_bit_cast(bf16x8_t, qreg[rt][c]),
+                            sacc[rt][t], 0, 0, 0);
+        }
 
         side();      // independent work (the next tile's widening) under the products
 
@@ -359,9 +489,10 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
         // scores in base 2 relative to the running max, y = x - m, and their
         // row maxima for both row tiles first, so the rare rescale is one
         // branch per tile and the rest of the tile is one straight block for
-        // the scheduler.  A tile with every key present folds the subtraction
-        // into the scaling FMA; one with missing keys adds their -inf bias.
+        // the scheduler.  The subtraction is folded into the scaling FMA, and
+        // a tile with missing keys sets theirs to -inf afterwards.
         float y[RT][8], ymx[RT];
+        bool lgrow = false;
         auto scores = [&](int rt, float *xo) {
             const f32x4_t s0 = sacc[rt][0], s1 = sacc[rt][1];
             const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
@@ -380,34 +511,39 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
         };
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            if (full) {
-                const f32x4_t s0 = sacc[rt][0], s1 = sacc[rt][1];
-                const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+            const f32x4_t s0 = sacc[rt][0], s1 = sacc[rt][1];
+            const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
 #pragma unroll
-                for (int e = 0; e < 8; ++e) y[rt][e] = fmaf(sv[e], CONV ? kfac[e] : scale_log2, -m[rt]);
-            } else {
-                float x[8];
-                scores(rt, x);
+            for (int e = 0; e < 8; ++e) y[rt][e] = fmaf(sv[e], CONV ? kfac[e] : scale_log2, -m[rt]);
+        }
+        if (!full) {
+            // missing keys (wave-uniform test): -inf
 #pragma unroll
-                for (int e = 0; e < 8; ++e) y[rt][e] = x[e] - m[rt];
-            }
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const bool miss = CONV ? kbias[e] != 0.f : !((present >> (8 * g + e)) & 1u);
+                    if (miss) y[rt][e] = kNegInf;
+                }
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
             float v = fmaxf(fmaxf(y[rt][0], y[rt][1]), y[rt][2]);
             v = fmaxf(fmaxf(v, y[rt][3]), y[rt][4]);
             v = fmaxf(fmaxf(v, y[rt][5]), y[rt][6]);
-            v = fmaxf(v, y[rt][7]);
-            ymx[rt] = group4_max(v);
+            ymx[rt] = fmaxf(v, y[rt][7]);      // this lane's 8 keys of the row
+            lgrow = lgrow || ymx[rt] > kLazy;
         }
         // the reference max moves only when a tile's max exceeds it by more
-        // than kLazy, so the O rescale is rare.  The rescale recomputes the
-        // scores from the products: y is relative to the old max, which is
-        // still the finite start value before a row's first key.
-        bool grow[RT], any = false;
+        // than kLazy, so the O rescale is rare.  A row's max exceeds it only
+        // if one of its four lanes' maxima does, so the row maxima are formed
+        // only when some lane of the wave sees such a key.  The rescale
+        // recomputes the scores from the products: y is relative to the old
+        // max, which is still the finite start value before a row's first key.
+        if (__ballot(lgrow)) {
+            bool grow[RT];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            grow[rt] = ymx[rt] > kLazy;
-            any = any || grow[rt];
-        }
-        if (__ballot(any)) {
+            for (int rt = 0; rt < RT; ++rt) grow[rt] = group4_max(ymx[rt]) > kLazy;
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
                 if (grow[rt]) {
@@ -456,26 +592,35 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
     auto ring = [&](int slot) { return smem + OFF_RING + slot * STAGE; };
     auto cstage = [&](int cslot) { return smem + cslot * CSTAGE; };
 
-    // ---- the pipeline.  bf16: kNS - 1 tiles in flight; per tile, wait for
+    // ---- the pipeline: NS - 1 tiles in flight.  bf16: per tile, wait for
     // this wave's loads of it, one barrier (the tile is complete, every wave
-    // is done with the stage the next load refills), refill, compute.
-    // e4m3: kNS tiles in flight; per tile, wait for the next tile's loads,
-    // one barrier, refill the stage the (already widened) tile used, widen
-    // the next tile, compute this one from its converted stage.
-    const int pro = CONV ? kNS : kNS - 1;
+    // is done with the stage the next load refills), refill, compute from the
+    // ring.  e4m3: per tile, wait for the next tile's loads, one barrier,
+    // refill the stage the previous tile used, read the next tile's V rows
+    // for widening, compute this one (K from the ring, V from its converted
+    // stage) and write the next one's widened V under the score products.
 #pragma unroll
-    for (int i = 0; i < kNS; ++i)
-        if (i < pro && i < nt) issue_tile(t_begin + i, i);
+    for (int i = 0; i < NS - 1; ++i)
+        if (i < nt) issue_tile(t_begin + i, i);
 
+    uint4 qraw[RT][4];                     // e4m3: dims 32g .. 32g+31 of each row
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const int r = row0 + rt * 16 + l16;
         const int gq = r / b, i = r - gq * b;
         const uint16_t *qrow = q + (((int64_t)bi * Hq + kvh * G + gq) * b + i) * D;
+        if constexpr (E4) {
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            qreg[rt][c] = make_uint4(0, 0, 0, 0);
-            if (r < M) qreg[rt][c] = *reinterpret_cast<const uint4 *>(qrow + chunk_dim<DLLM_BF16>(c, g));
+            for (int c = 0; c < 4; ++c) {
+                qraw[rt][c] = make_uint4(0, 0, 0, 0);
+                if (r < M) qraw[rt][c] = *reinterpret_cast<const uint4 *>(qrow + 32 * g + 8 * c);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                qreg[rt][c] = make_uint4(0, 0, 0, 0);
+                if (r < M) qreg[rt][c] = *reinterpret_cast<const uint4 *>(qrow + chunk_dim<DLLM_BF16>(c, g));
+            }
         }
     }
     // A memoized state (FACache) starts the rows of split 0: O~ = memo_o,
@@ -517,6 +662,10 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
             }
         }
     }
+    if constexpr (E4) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) split_query(qraw[rt], g, q8[rt], qsc[rt]);
+    }
     if (CONV && nt > 0) {
         ring_barrier();
         ConvIn c0;
@@ -524,38 +673,65 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
         convert_write(0, c0);
     }
 
-    // one e4m3 step: wait for the next tile's loads, one barrier, refill the
-    // stage this tile used, read the next tile for widening, compute this
-    // one and write the next one back under its first product (slot = i % kNS).
+    // Which tiles of the split have all 32 keys: arithmetic without a map;
+    // with one (at most 64 tiles), lane j checks tile j's table entries once.
+    uint64_t fullmask = 0;
+    if (CONV && MAP) {
+        bool f = true;
+        if (lane < nt) {
+            const int4 *t4 = reinterpret_cast<const int4 *>(tab + lane * 32);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int4 v = t4[j];
+                f = f && v.x >= 0 && v.y >= 0 && v.z >= 0 && v.w >= 0;
+            }
+        }
+        fullmask = __ballot(f);
+    }
+    auto tile_full = [&](int i) -> bool {
+        if (MAP) return (fullmask >> i) & 1ull;
+        return (t_begin + i + 1) * 32 <= n_keys;
+    };
+
+    // one e4m3 step (slot = i % NS): wait for the next tile's loads, one
+    // barrier (every wave is done with the previous tile's ring stage and
+    // with the converted stage the next tile is widened into), read the next
+    // tile's V rows, compute this tile (its K operands and the refill's key
+    // indices were read during the previous step) and issue the refill and
+    // write the widened rows under its score products; then read the next
+    // tile's K operands (its loads are complete and visible since this
+    // step's barrier) and the next refill's key indices (the table does not
+    // change), so neither is waited for after the next barrier.
     // The converted stage of tile i is i % 2, a compile-time constant `par`.
+    TileKeys tk;
     auto conv_step = [&](int i, auto par, auto wait) {
         constexpr int P = decltype(par)::value;
-        const int slot = i % kNS;
+        const int slot = i % NS;
         __builtin_amdgcn_sched_barrier(0);
         wait();
         ring_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        // the refill's key indices and the next tile's raw chunks are read
-        // now; the refill is issued and the widening written back under this
-        // tile's first product
-        const bool refill = i + kNS < nt;
-        TileKeys tk;
-        if (refill) keys_of(t_begin + i + kNS, tk);
+        const bool refill = i + NS - 1 < nt;
         const bool next = i + 1 < nt;
+        const int nslot = slot + 1 == NS ? 0 : slot + 1;
         ConvIn cn;
-        if (next) convert_read(t_begin + i + 1, (slot + 1) % kNS, cn);
+        if (next) convert_read(t_begin + i + 1, nslot, cn);
         const unsigned char *cs = cstage(P);
-        compute(t_begin + i, cs, cs + CTB, reinterpret_cast<const float *>(cs + 2 * CTB), [&] {
-            if (refill) issue(tk, slot);
+        compute(t_begin + i, nullptr, cs, reinterpret_cast<const float *>(cs + CTB), tile_full(i), [&] {
+            if (refill) issue(tk, slot == 0 ? NS - 1 : slot - 1);
             if (next) convert_write(P ^ 1, cn);
         });
+        if (next) load_k8(ring(nslot));
+        if (i + NS < nt) keys_of(t_begin + i + NS, tk);
     };
     // tiles issued after the next one
     auto conv_wait = [&](int i) {
-        return [=] { vm_wait_upto<(kNS - 2) * LW>(max(0, min(kNS - 2, nt - 2 - i)) * LW); };
+        return [=] { vm_wait_upto<(NS - 3) * LW>(max(0, min(NS - 3, nt - 2 - i)) * LW); };
     };
     int i = 0;
     if (CONV) {
+        if (nt > 0) load_k8(ring(0));
+        if (NS - 1 < nt) keys_of(t_begin + NS - 1, tk);
         using P0 = std::integral_constant<int, 0>;
         using P1 = std::integral_constant<int, 1>;
         for (; i + 1 < nt; i += 2) {
@@ -567,14 +743,14 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
     for (; !CONV && i < nt; ++i) {
         {
             // tiles issued after this one
-            const int ahead = min(kNS - 2, nt - 1 - i);
+            const int ahead = min(NS - 2, nt - 1 - i);
             __builtin_amdgcn_sched_barrier(0);
-            vm_wait_upto<(kNS - 2) * LW>(ahead * LW);
+            vm_wait_upto<(NS - 2) * LW>(ahead * LW);
             ring_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            if (i + kNS - 1 < nt) issue_tile(t_begin + i + kNS - 1, (i + kNS - 1) % kNS);
-            const unsigned char *st = ring(i % kNS);
-            compute(t_begin + i, st, st + TB, nullptr, [] {});
+            if (i + NS - 1 < nt) issue_tile(t_begin + i + NS - 1, (i + NS - 1) % NS);
+            const unsigned char *st = ring(i % NS);
+            compute(t_begin + i, st, st + TB, nullptr, true, [] {});
         }
     }
 

@@ -107,6 +107,37 @@ __device__ __forceinline__ void lds_dma4(const void *src, void *lds_base) {
 #endif
 }
 
+// The same two loads from a wave-uniform base plus a 32-bit per-lane byte
+// offset (the scalar-base form: no 64-bit address per lane)
+template <bool NT>
+__device__ __forceinline__ void lds_dma16s(const void *sbase, uint32_t voff, void *lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
+    if (NT)
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                     : : "v"(voff), "s"(sbase), "s"(m0) : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                     : : "v"(voff), "s"(sbase), "s"(m0) : "memory", "m0");
+#else
+    (void)sbase;
+    (void)voff;
+    (void)lds_base;
+#endif
+}
+
+__device__ __forceinline__ void lds_dma4s(const void *sbase, uint32_t voff, void *lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                 : : "v"(voff), "s"(sbase), "s"(m0) : "memory", "m0");
+#else
+    (void)sbase;
+    (void)voff;
+    (void)lds_base;
+#endif
+}
+
 // s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left at their maxima)
 template <int N>
 __device__ __forceinline__ void vm_wait() {

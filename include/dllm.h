@@ -147,7 +147,9 @@ int dllm_version(void);
  *   dtype     DLLM_F32, DLLM_BF16 or DLLM_E4M3 (E4M3 needs d % 128 == 0 and
  *             non-NULL scale arrays)
  *   k, v      device, 16-byte aligned, B*n_kv_heads*L*d elements each
- * Limits: B, L, n_kv_heads >= 1; d in 16..256 with d*size(dtype) % 16 == 0.
+ * Limits: B, L, n_kv_heads >= 1; d in 16..256 with d*size(dtype) % 16 == 0;
+ * L*d*size(dtype) < 2^32 bytes (the rows of one sequence and KV head),
+ * else DLLM_ERANGE.  Every call that takes a cache checks the same.
  * Returns DLLM_OK or a negative dllm_status.
  * ------------------------------------------------------------------------- */
 int dllm_cache_init(dllm_kv_cache *cache, int B, int L, int n_kv_heads, int d_head,

@@ -57,6 +57,8 @@ def test_host_validation_without_gpu(dl):
     assert L.dllm_cache_init(ctypes.byref(desc), 1, 8, 1, 16, 7, 16, 16, None, None, None) == -2
     assert L.dllm_cache_init(ctypes.byref(desc), 1, 8, 1, 24, 2, 16, 16, 16, 16, None) in (-3, -4)
     assert L.dllm_cache_init(None, 1, 8, 1, 16, 0, 16, 16, None, None, None) == -1
+    # one (sequence, KV head)'s rows must span less than 4 GiB: 2^24 bf16 rows of 128 do not
+    assert L.dllm_cache_init(ctypes.byref(desc), 1, 1 << 24, 1, 128, 1, 16, 16, None, None, None) == -5
     assert L.dllm_vocab_stats(None, 1, 4, 10, 5, None, None, None, None, 0, None) == -3   # stride < V
     assert L.dllm_vocab_stats(None, 5, 4, 10, 10, None, None, None, None, 0, None) == -2  # dtype
     assert L.dllm_vocab_stats(None, 1, 0, 10, 10, None, None, None, None, 0, None) == 0   # N = 0: no-op
