@@ -754,12 +754,16 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
         }
     }
 
-    // ---- row sums over the 4 lane groups, then this wave's rows out
+    // ---- row sums over the 4 lane groups, then this wave's rows out.  The
+    // rows' offsets are formed again here from an opaque copy of the lane
+    // index, so the compiler does not keep the prologue's across the loop.
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) l[rt] = group4_sum(l[rt]);
+    int l16e = l16;
+    asm volatile("" : "+v"(l16e));
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        const int r = row0 + rt * 16 + l16;
+        const int r = row0 + rt * 16 + l16e;
         if (r >= M) continue;
         const int gq = r / b, i = r - gq * b;
         const int64_t orow = ((int64_t)bi * Hq + kvh * G + gq) * b + i;
