@@ -244,10 +244,15 @@ __global__ __launch_bounds__(256) void fp8_quant_weight_kernel(const void *__res
 //
 // EPI 0 writes C in bf16.  EPI 1 is SwiGLU with the 1 x 128 quantisation of
 // its output: B's rows come in pairs of 128-row blocks (gate block j, then
-// up block j), so the wave of tile columns 0..127 holds gate features
-// 128 j .. +127 and its neighbour the matching up features; the neighbour
-// hands its accumulators over through LDS and the gate wave writes
-// silu(gate) * up as codes of [M, N/2] with scales [N/256, M].
+// up block j).  Wave wn takes gate features 64 wn .. +63 of the block and
+// the matching up features, so silu(gate) * up is formed in its own
+// registers, and it computes C^T (A operand = the weight rows, B operand =
+// the token rows): lane l then holds token l % 32 of each token tile and, in
+// register i, feature 8 (i / 4) + 4 (l / 32) + i % 4 of each feature tile, so
+// a token's 64 values of the wave are in two lanes (one swap gives their
+// maximum), four neighbouring features pack into one word of codes, and the
+// two waves of a block exchange one partial maximum per token.  It writes
+// codes of [M, N/2] with scales [N/256, M].
 constexpr int kBM = 256, kBN = 256, kBK = 128;
 constexpr int kTileBytes = kBM * kBK;                  // one operand tile of one stage
 constexpr int kGemmLds = 2 * 2 * kTileBytes;           // two stages of A and B: 128 KB
@@ -264,6 +269,17 @@ __device__ __forceinline__ f32x16_t mfma_scaled(const i32x8_t &a, const i32x8_t 
     case 1: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 1, sa, 0, sb);
     case 2: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 2, sa, 0, sb);
     default: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 3, sa, 0, sb);
+    }
+}
+
+// the block-scaled product with byte `sel` (0..3) of sb as B's scale
+__device__ __forceinline__ f32x16_t mfma_scaled_b(const i32x8_t &a, const i32x8_t &b, const f32x16_t &c,
+                                                  int sa, int sb, int sel) {
+    switch (sel) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 1, sb);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 2, sb);
+    default: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 3, sb);
     }
 }
 
@@ -378,9 +394,15 @@ __global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(
         __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
         asm volatile("s_barrier" ::: "memory");
         const int sav = *reinterpret_cast<const int *>(ssa + ks * 256 + wm * 128 + l32 * 4);
-        const int sbv = ssb[wn * ksteps + ks];
+        // EPI 0: the scale of the wave's 128 B rows; EPI 1: of the gate
+        // block (sbv) and of the up block (sbu)
+        const int sbv = ssb[(EPI == 1 ? 0 : wn) * ksteps + ks];
+        const int sbu = EPI == 1 ? (int)ssb[ksteps + ks] : 0;
         const unsigned char *at = smem + stage * 2 * kTileBytes + wm * 128 * kBK;
-        const unsigned char *bt = smem + stage * 2 * kTileBytes + kTileBytes + wn * 128 * kBK;
+        const unsigned char *bt = smem + stage * 2 * kTileBytes + kTileBytes;
+        // B tile row of operand tile t: EPI 0 the wave's 128 rows; EPI 1 its
+        // gate rows 64 wn .. +63 (t = 0, 1) and up rows 128 + 64 wn .. +63
+        auto brow = [&](int t) { return EPI == 1 ? (t < 2 ? 64 * wn + 32 * t : 64 + 64 * wn + 32 * t) : 128 * wn + 32 * t; };
         auto read_ops = [&](int kh, i32x8_t *av, i32x8_t *bv) {
             const int c0 = kh * 4 + lh * 2;
 #pragma unroll
@@ -390,8 +412,9 @@ __global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(
                 const uint4 x1 = *reinterpret_cast<const uint4 *>(at + swz(r, c0 + 1));
                 av[t] = i32x8_t{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
                                 (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-                const uint4 y0 = *reinterpret_cast<const uint4 *>(bt + swz(r, c0));
-                const uint4 y1 = *reinterpret_cast<const uint4 *>(bt + swz(r, c0 + 1));
+                const int rb = brow(t) + l32;
+                const uint4 y0 = *reinterpret_cast<const uint4 *>(bt + swz(rb, c0));
+                const uint4 y1 = *reinterpret_cast<const uint4 *>(bt + swz(rb, c0 + 1));
                 bv[t] = i32x8_t{(int)y0.x, (int)y0.y, (int)y0.z, (int)y0.w,
                                 (int)y1.x, (int)y1.y, (int)y1.z, (int)y1.w};
             }
@@ -404,13 +427,24 @@ __global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(
         read_ops(1, av[1], bv[1]);
         if (ks + 1 < ksteps) issue(ks + 1, stage ^ 1);
         if (ks + kPFD < ksteps) prefetch(ks + kPFD);
+        if (EPI == 1) {
+            // C^T: acc[ft][tt], feature tile ft (gate 0, 1; up 2, 3) by token tile tt
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
+            for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
+                for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct)
-                    acc[rt][ct] = mfma_scaled(av[kh][rt], bv[kh][ct], acc[rt][ct], sav, rt, sbv);
+                    for (int ft = 0; ft < 4; ++ft)
+                        acc[ft][tt] = mfma_scaled_b(bv[kh][ft], av[kh][tt], acc[ft][tt], ft < 2 ? sbv : sbu, sav, tt);
+        } else {
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < 4; ++ct)
+                        acc[rt][ct] = mfma_scaled(av[kh][rt], bv[kh][ct], acc[rt][ct], sav, rt, sbv);
+        }
     }
 
     // ---- epilogues: the tile leaves through LDS (the stages are free once
@@ -443,71 +477,70 @@ __global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(
                 *reinterpret_cast<uint4 *>(c + (int64_t)row * N + n0 + wn * 128 + ch * 8) = v;
         }
     } else {
-        // gate (wave wn = 0) and up (wn = 1) of one 128 x 128 block: each of
-        // the pair takes half the rows (row tiles 2 wn, 2 wn + 1) and hands
-        // the other half to its partner, one row tile per phase.  Straight-line
-        // code with selects, so the register allocator sees one path for both
-        // waves.  Per row (r2, i): the max over its 4 registers and the 32 lanes
-        // of this half (16-lane rows by DPP rotations, then lanes l and
-        // l ^ 16), its exponent and codes; the codes wait in LDS (16-byte
-        // chunks XOR-swizzled) clear of the exchange.
-        const bool gate_wave = wn == 0;
-        float *xch = reinterpret_cast<float *>(smem) + wm * 8192;    // [giver wn][4 ct][16 i][64]
-        auto xidx = [&](int giver, int ct, int i) { return ((giver * 4 + ct) * 16 + i) * 64 + lane; };
-        unsigned char *qb = smem + 65536 + wave * 8192;               // [64 rows][128 codes]
-        uint8_t *qsb = smem + 65536 + 4 * 8192 + wave * 64;           // the rows' E8M0 codes
+        // silu(gate) * up of this wave's 64 features (ft = 0, 1; up in
+        // ft + 2) of its 128 tokens, each token's partial maximum over them
+        // (a lane's 32 values, then lanes l and l ^ 32), the partner wave's
+        // partial maximum through LDS, the exponent and the codes.  Lane
+        // (l32, lh) holds token 32 tt + l32, features 32 ft + 8 q + 4 lh + j
+        // in register 4 q + j: four neighbouring features make one word.
+        float h[2][4][16];
+        float pm[4];
 #pragma unroll
-        for (int r2 = 0; r2 < 2; ++r2) {
+        for (int tt = 0; tt < 4; ++tt) {
+            float v = 0.f;
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    xch[xidx(wn, ct, i)] = gate_wave ? acc[2 + r2][ct][i] : acc[r2][ct][i];
-            __syncthreads();
-            float h[4][16];                             // silu(gate) * up of row tile 2 wn + r2
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct)
+            for (int ft = 0; ft < 2; ++ft)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const float mine = gate_wave ? acc[r2][ct][i] : acc[2 + r2][ct][i];
-                    const float other = xch[xidx(wn ^ 1, ct, i)];
-                    const float g = gate_wave ? mine : other, u = gate_wave ? other : mine;
-                    h[ct][i] = __fdividef(g, 1.0f + __expf(-g)) * u;
+                    const float g = acc[ft][tt][i], u = acc[ft + 2][tt][i];
+                    h[ft][tt][i] = __fdividef(g, 1.0f + __expf(-g)) * u;
+                    v = fmaxf(v, fabsf(h[ft][tt][i]));
                 }
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+            pm[tt] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        float *xm = reinterpret_cast<float *>(smem) + wm * 256;       // [wn][128 tokens]
+        if (lh == 0) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float v = fmaxf(fmaxf(fabsf(h[0][i]), fabsf(h[1][i])), fmaxf(fabsf(h[2][i]), fabsf(h[3][i])));
-                v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false)));
-                v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false)));
-                v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xf, 0xf, false)));
-                v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xf, 0xf, false)));
-                const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-                const int e = e8m0_exponent(fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
-                const float sc = inv_scale(e);
-                const int r = r2 * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);        // row of this wave's 64
+            for (int tt = 0; tt < 4; ++tt) xm[wn * 128 + 32 * tt + l32] = pm[tt];
+        }
+        __syncthreads();
+        // the codes wait in LDS: [128 tokens][64 codes] per wave, the four
+        // 16-byte chunks of a token's row XOR-swizzled by (row / 4) % 4
+        unsigned char *qb = smem + 4096 + wave * 8192;
+        int ex[4];
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct) {
-                    const int col = ct * 32 + l32;
-                    const uint32_t code =
-                        (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(h[ct][i] * sc, 0.f, 0, false) & 0xffu;
-                    qb[r * 128 + ((((col >> 4) ^ (r & 7)) << 4) | (col & 15))] = (uint8_t)code;
+        for (int tt = 0; tt < 4; ++tt) {
+            const float full = fmaxf(pm[tt], xm[(wn ^ 1) * 128 + 32 * tt + l32]);
+            ex[tt] = e8m0_exponent(full);
+            const float sc = inv_scale(ex[tt]);
+            const int r = 32 * tt + l32;
+#pragma unroll
+            for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t w = cvt4(h[ft][tt][4 * q] * sc, h[ft][tt][4 * q + 1] * sc,
+                                            h[ft][tt][4 * q + 2] * sc, h[ft][tt][4 * q + 3] * sc);
+                    const int col = 32 * ft + 8 * q + 4 * lh;             // byte of the token's 64
+                    *reinterpret_cast<uint32_t *>(qb + r * 64 + ((((col >> 4) ^ ((r >> 2) & 3))) << 4) + (col & 15)) = w;
                 }
-                if (l32 == 0) qsb[r] = (uint8_t)(e + 127);
-            }
-            __syncthreads();                            // the exchange is read before it is reused
         }
         __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));   // this wave's writes
-        // rows 64 wn .. +63 of the pair's block: 8 lanes per row, 8 rows per pass
+        // the wave's 128 tokens x 64 codes: 4 lanes per token, 16 tokens per pass
         const int half_n = N >> 1;
-        const int rbase = m0 + wm * 128 + wn * 64;
+        const int tbase = m0 + wm * 128;
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
-            const int r = p * 8 + (lane >> 3), ch = lane & 7;
-            const uint4 v = *reinterpret_cast<const uint4 *>(qb + r * 128 + ((ch ^ (r & 7)) << 4));
-            if (rbase + r < M)
-                *reinterpret_cast<uint4 *>(qc + (int64_t)(rbase + r) * half_n + (n0 >> 1) + ch * 16) = v;
+            const int r = p * 16 + (lane >> 2), ch = lane & 3;
+            const uint4 v = *reinterpret_cast<const uint4 *>(qb + r * 64 + ((ch ^ ((r >> 2) & 3)) << 4));
+            if (tbase + r < M)
+                *reinterpret_cast<uint4 *>(qc + (int64_t)(tbase + r) * half_n + (n0 >> 1) + 64 * wn + ch * 16) = v;
         }
-        if (rbase + lane < M) qs[(int64_t)(n0 >> 8) * M + rbase + lane] = qsb[lane];
+        if (wn == 0 && lh == 0) {
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+                if (tbase + 32 * tt + l32 < M) qs[(int64_t)(n0 >> 8) * M + tbase + 32 * tt + l32] = (uint8_t)(ex[tt] + 127);
+        }
     }
 }
 
