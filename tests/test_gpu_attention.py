@@ -160,6 +160,28 @@ def test_attention_e4m3_gqa(orc):
     _check(orc, D, cache, q, key_idx=kid, label="e4m3 gqa sink map")
 
 
+@pytest.mark.parametrize("B,Hkv,G,b,L", [(1, 3, 3, 40, 333), (2, 1, 1, 48, 200), (1, 2, 4, 20, 1000)])
+def test_attention_e4m3_ragged_rows_and_gaps(orc, B, Hkv, G, b, L):
+    """the grouped layout's e4m3 path (scores on the block-scaled fp8
+    product) at shapes whose row groups are partly empty (G b = 120, 48 and
+    80 rows: 4- and 2-wave workgroups with rows past the last), ragged key
+    counts, and key lists with padding inside tiles (every third slot -1),
+    so that tiles with missing keys sit between full ones"""
+    D = need_gpu()
+    d = 128
+    Hq = Hkv * G
+    cache = _fill(D, B, Hkv, L, d, W.E4M3, seed=B * 31 + L, std=1 / np.sqrt(d))
+    g = torch.Generator().manual_seed(L + 7)
+    q = (torch.randn((B, Hq, b, d), generator=g) / np.sqrt(d)).bfloat16().cuda()
+    _check(orc, D, cache, q, label=f"e4m3 ragged rows G{G} b{b} L{L}")
+    _check(orc, D, cache, (q.float() * 200).bfloat16(), label=f"e4m3 ragged rows sharp G{G} b{b} L{L}")
+    n_keys = L - L // 5
+    kid = torch.randperm(L, generator=g)[:n_keys].sort().values.to(torch.int32)
+    kid[::3] = -1
+    kid = kid.repeat(B, 1).cuda()
+    _check(orc, D, cache, q, key_idx=kid, label=f"e4m3 gaps G{G} b{b} L{L}")
+
+
 def test_attention_gpt2_full(orc):
     D = need_gpu()
     cfg = W.CONFIGS["gpt2"]
