@@ -47,6 +47,8 @@ def _case(D, B, Hkv, Hq, L, d, b, n, dtype, seed, with_map=False, bad=False):
     (2, 2, 2, 700, 128, 32, 32, W.BF16, True, False),     # key map: the two kernels in sequence
     (2, 1, 4, 600, 128, 64, 64, W.BF16, False, False),    # grouped rows: the two kernels in sequence
     (1, 2, 2, 300, 128, 32, 16, W.E4M3, False, False),    # e4m3: quantising scatter, then attention
+    (2, 2, 8, 700, 128, 64, 64, W.E4M3, True, True),      # e4m3, grouped rows, key map, padding and a bad position
+    (2, 1, 1, 500, 128, 48, 48, W.E4M3, True, False),     # the same with 2-wave workgroups, rows past the last
 ])
 def test_scatter_attention_equals_two_calls(orc, B, Hkv, Hq, L, d, b, n, dtype, with_map, bad):
     D = need_gpu()
@@ -78,6 +80,42 @@ def test_scatter_attention_equals_two_calls(orc, B, Hkv, Hq, L, d, b, n, dtype, 
                                  key_idx=kid.cpu().numpy() if kid is not None else None)
     e_abs, e_norm = attn_errors(o2, ref)
     assert e_abs <= (6e-2 if dtype == W.E4M3 else 2e-2) and e_norm <= 1e-2, (e_abs, e_norm)
+
+
+def test_scatter_attention_e4m3_sink_map_splits(orc):
+    """the long-context form at a small size: e4m3 cache, sinks + a rolling
+    window of 8188 keys ending at the sequence's end, 8 key splits, the block
+    at the newest positions (in the last split's keys) with padding, an
+    out-of-range position and two rows outside the map: bit for bit as the
+    scatter then the attention"""
+    D = need_gpu()
+    B, Hkv, Hq, L, d, b, n = 1, 1, 4, 9000, 128, 64, 64
+    (c1, c2), kn, vn, _, q, _ = _case(D, B, Hkv, Hq, L, d, b, n, W.E4M3, seed=9000)
+    pos = torch.arange(L - n, L, dtype=torch.int32, device="cuda").view(1, n).clone()
+    pos[0, 3] = -1                      # padding
+    pos[0, 7] = L + 1                   # out of range: skipped and counted
+    pos[0, 10] = 100                    # outside the map (between the sinks and the window)
+    pos[0, 11] = 2                      # a sink
+    kid = torch.empty((B, 4 + 8188), dtype=torch.int32, device="cuda")
+    D.dllm_sink_rolling_map(L, 4, 8188, torch.tensor([L], dtype=torch.int32, device="cuda"), kid)
+    say("scatter_attention e4m3 sink map splits")
+    ws = D.dllm_block_attention_workspace(c1, W.BF16, Hq, b, kid.shape[1])
+    assert ws > 0                       # key splits
+    bad1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bad2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    D.dllm_scatter_kv(c1, kn, vn, pos, bad_count=bad1)
+    o1 = D.dllm_block_attention(c1, q, key_idx=kid)
+    o2 = D.dllm_scatter_attention(c2, kn, vn, pos, q, key_idx=kid, bad_count=bad2)
+    torch.cuda.synchronize()
+    assert torch.equal(c1.k.view(torch.uint8), c2.k.view(torch.uint8))
+    assert torch.equal(c1.v.view(torch.uint8), c2.v.view(torch.uint8))
+    assert torch.equal(c1.k_scale, c2.k_scale) and torch.equal(c1.v_scale, c2.v_scale)
+    assert torch.equal(o1, o2)
+    assert int(bad1.item()) == int(bad2.item()) == 1
+    ck, cv, ks, vs = cache_np(c2)
+    ref, _ = orc.block_attention(ck, cv, ks, vs, W.E4M3, bits(q), W.BF16, key_idx=kid.cpu().numpy())
+    e_abs, e_norm = attn_errors(o2, ref)
+    assert e_abs <= 6e-2 and e_norm <= 1e-2, (e_abs, e_norm)
 
 
 def test_scatter_attention_rows_land_where_the_oracle_puts_them(orc):
