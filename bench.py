@@ -669,6 +669,56 @@ def cpu_baseline(step, D, W, cfg, frac=1.0):
     return t_total, "; ".join(parts) + "; times scaled linearly to the whole step"
 
 
+# the seeded inputs of each workload's step, by attribute name (the cache as
+# the timed steps leave it: every step writes the same fresh rows)
+INPUT_NAMES = ("logits", "q", "kn", "vn", "pos", "key_idx", "qu", "memo_o", "memo_lse",
+               "x", "res", "gamma", "w_gu_bf16", "w_out_bf16", "am", "mp", "en", "dec", "pm", "pj")
+
+
+def inputs_sha256(step):
+    """SHA-256 of the bytes of every input of the step (and of the cache)"""
+    import torch
+    names = [n for n in INPUT_NAMES
+             if not (n in ("am", "mp", "en") and getattr(step, "has_vocab", False))]   # outputs there
+    tensors = {n: getattr(step, n) for n in names if isinstance(getattr(step, n, None), torch.Tensor)}
+    cache = getattr(step, "cache", None)
+    if cache is not None:
+        for n in ("k", "v", "k_scale", "v_scale"):
+            if getattr(cache, n, None) is not None:
+                tensors["cache." + n] = getattr(cache, n)
+    out = {}
+    for n, t in tensors.items():
+        h = hashlib.sha256()
+        flat = t.contiguous().view(-1).view(torch.uint8)
+        for i in range(0, flat.numel(), 1 << 28):             # 256 MiB at a time through host memory
+            h.update(flat[i:i + (1 << 28)].cpu().numpy().tobytes())
+        out[n] = h.hexdigest()
+    return out
+
+
+def padded_stride_vocab_us(step, W, reps=50):
+    """vocab_stats on the same logits in rows padded to a 16-byte multiple
+    (the other stride the GPT-2-shaped rows are tested at), back to back"""
+    import torch
+    N, V = step.logits.shape
+    stride = (V + 7) // 8 * 8
+    padded = torch.zeros((N, stride), dtype=step.logits.dtype, device=step.logits.device)
+    padded[:, :V] = step.logits
+    run = lambda: step.D.dllm_vocab_stats(padded[:, :V], V=V, argmax=step.am, maxprob=step.mp,
+                                          entropy=step.en, workspace=step.vocab_ws)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = Event(), Event()
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1000.0 * e0.elapsed_time(e1) / reps
+    del padded
+    return stride, us
+
+
 def cpu_baseline_line(fn):
     """fn(frac) -> (seconds per step, sample): the oracle on every host core
     this process may use, then on one thread on a quarter of the sample"""
@@ -891,6 +941,9 @@ def main():
     if args.config == "verify":
         extra = {"verify_longctx_us": round(step.longctx_us(dev), 2),
                  "withdrawn_per_step": int(step.nrb.sum().item())}
+    if args.config == "gpt2":
+        stride, us = padded_stride_vocab_us(step, W)
+        extra = {"vocab_stats_padded_stride": stride, "vocab_stats_padded_stride_b2b_us": round(us, 2)}
     if args.no_cpu_baseline:
         cpu = None
     elif args.config == "ffn":
@@ -951,6 +1004,7 @@ def main():
         "roofline": roofline,
         **extra,
         "cpu_baseline": cpu,
+        "inputs_sha256": inputs_sha256(step),
         "wall_s": round(t_wall, 3),
     }
     print(json.dumps(line), flush=True)
