@@ -227,12 +227,15 @@ __global__ __launch_bounds__(256) void fp8_quant_weight_kernel(const void *__res
 // ---- the product: C = dequant(A) dequant(B)^T -------------------------------
 // A [M, K] codes with scales [K/128, M]; B [N, K] codes with scales
 // [N/128, K/128]; fp32 accumulation.  A workgroup of 4 waves owns a 256 x 256
-// tile, each wave 128 x 128 (4 x 4 tiles of 32 x 32), and walks K in steps
-// of 128 (one scale group): per step the A and B tiles (32 KB each) land in
-// one of two LDS stages by direct-to-LDS loads while the other stage is
-// read.  In LDS a 128-byte row keeps its eight 16-byte chunks XOR-swizzled
-// (swz) so that a read phase of 16 rows at one logical chunk hits all 64
-// banks once.
+// tile, each wave 128 x 128 (4 x 4 tiles of 32 x 32), and walks K in slices
+// of 64 through a ring of four LDS stages (A and B, 16 KB each per stage),
+// filled by direct-to-LDS loads four slices ahead of use.  The operands of
+// slice h + 1 are read into registers while the products of slice h run on
+// the registers read one slice earlier, so the matrix cores never wait for
+// an LDS read, and the one barrier per slice only confirms that slice h + 1
+// has landed and that slice h's stage is free for its refill.  In LDS a
+// 64-byte row keeps its four 16-byte chunks XOR-swizzled (swz) so that a
+// read phase of 16 rows at one logical chunk hits all 64 banks once.
 //
 // Operands of v_mfma_scale_f32_32x32x64_f8f6f4: lane l holds 32 bytes of
 // row l % 32 (A) or of column l % 32 (B), K bytes 32 (l / 32) .. +31 of the
@@ -253,12 +256,13 @@ __global__ __launch_bounds__(256) void fp8_quant_weight_kernel(const void *__res
 // maximum), four neighbouring features pack into one word of codes, and the
 // two waves of a block exchange one partial maximum per token.  It writes
 // codes of [M, N/2] with scales [N/256, M].
-constexpr int kBM = 256, kBN = 256, kBK = 128;
-constexpr int kTileBytes = kBM * kBK;                  // one operand tile of one stage
-constexpr int kGemmLds = 2 * 2 * kTileBytes;           // two stages of A and B: 128 KB
-constexpr int kGemmMaxK = 12288;                       // the scales of 96 k-steps fit beside them
-constexpr int kGemmSmem = kGemmLds + (kGemmMaxK / kBK) * (256 + 2) + 256;
-constexpr int kPFD = 2;                                // k-steps of L2 prefetch ahead of use
+constexpr int kBM = 256, kBN = 256, kBK = 128;         // kBK: one scale group
+constexpr int kHK = 64;                                // K width of one LDS stage
+constexpr int kStages = 4;
+constexpr int kSliceBytes = kBM * kHK;                 // one operand tile of one stage: 16 KB
+constexpr int kGemmLds = kStages * 2 * kSliceBytes;    // 128 KB
+constexpr int kGemmMaxK = 12288;                       // the scales of 96 groups fit beside them
+constexpr int kGemmSmem = kGemmLds + (kGemmMaxK / kBK) * (256 + 2);
 static_assert(kGemmSmem <= attn::kLdsBytes, "LDS of one workgroup");
 
 // the block-scaled product with byte `sel` (0..3) of sa as A's scale
@@ -283,12 +287,18 @@ __device__ __forceinline__ f32x16_t mfma_scaled_b(const i32x8_t &a, const i32x8_
     }
 }
 
-// LDS byte offset of 16-byte chunk c of tile row r.  A read phase of 16
-// lanes takes rows r .. r + 15 at one logical chunk and the 64 banks span 256
-// bytes, i.e. two 128-byte rows: the even rows of the phase share one half of
-// the bank window and the odd rows the other, so the swizzle must give the 8
-// rows of each parity distinct chunks: c ^ ((r >> 1) & 7).
-__device__ __forceinline__ int swz(int r, int c) { return r * kBK + ((c ^ ((r >> 1) & 7)) << 4); }
+// LDS byte offset of 16-byte chunk c (0..3) of stage row r.  A read phase of
+// 16 lanes takes rows r .. r + 15 at one logical chunk, and the 64 banks span
+// 256 bytes, i.e. four 64-byte rows: rows of equal r % 4 share a quarter of
+// the bank window, so the four rows of each residue need distinct chunks:
+// c ^ ((r >> 2) & 3).
+__device__ __forceinline__ int swz(int r, int c) { return r * kHK + ((c ^ ((r >> 2) & 3)) << 4); }
+
+// one slice's operands of one wave, and the E8M0 scales of its group
+struct GemmOps {
+    i32x8_t a[4], b[4];
+    int sa, sb, su;
+};
 
 template <int EPI>
 __global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(
@@ -313,52 +323,45 @@ __global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(
     const int m0 = tm * kBM, n0 = tn * kBN;
     const int ksteps = K / kBK;
 
-    // direct-to-LDS loads: wave w issues 1 KB loads u = 0..7 of each tile;
-    // load u covers tile rows 8 (8 w + u) .. +7, lane i row r = 8 (8 w + u) +
-    // i / 8, stored slot i % 8, which holds logical chunk (i % 8) ^ ((r >> 1) & 7)
-    // = (i % 8) ^ ((4 (u & 1) + i / 16) & 7)
-    const int lrow = lane >> 3;
-    const int lchunk0 = (lane & 7) ^ ((lane >> 4) & 7);
-    const int lchunk1 = (lane & 7) ^ ((4 + (lane >> 4)) & 7);
-    auto issue = [&](int ks, int stage) {
-        unsigned char *sa_lds = smem + stage * 2 * kTileBytes;
-        unsigned char *sb_lds = sa_lds + kTileBytes;
+    // direct-to-LDS loads of slice h: wave w issues 1 KB loads u = 0..3 of
+    // each tile; load u covers stage rows 16 (4 w + u) .. +15, lane i row
+    // r = 16 (4 w + u) + i / 4, stored slot i % 4, which holds logical chunk
+    // (i % 4) ^ ((r >> 2) & 3) = (i % 4) ^ ((i / 16) & 3).  Each lane's byte
+    // offset from the slice's wave-uniform base is fixed for the whole loop.
+    const int H = K / kHK;
+    const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
+    uint32_t offa[4], offb[4];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int r = 8 * (8 * wave + u) + lrow;
-            const int64_t k0 = (int64_t)ks * kBK + ((u & 1) ? lchunk1 : lchunk0) * 16;
-            const int ra = min(m0 + r, M - 1);          // rows past M read row M - 1, never stored
-            lds_dma16<false>(a + (int64_t)ra * K + k0, sa_lds + (8 * wave + u) * 1024);
-            lds_dma16<false>(b + (int64_t)(n0 + r) * K + k0, sb_lds + (8 * wave + u) * 1024);
+    for (int u = 0; u < 4; ++u) {
+        const int r = 16 * (4 * wave + u) + (lane >> 2);
+        offa[u] = (uint32_t)(min(r, M - 1 - m0) * K + lchunk * 16);   // rows past M read row M - 1, never stored
+        offb[u] = (uint32_t)(r * K + lchunk * 16);
+    }
+    const uint8_t *abase = a + (int64_t)m0 * K, *bbase = b + (int64_t)n0 * K;
+    const uint32_t smem_lds = attn::lds_addr(smem);
+    auto issue = [&](int h) {
+        const uint32_t st = smem_lds + (uint32_t)((h & (kStages - 1)) * 2 * kSliceBytes);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            attn::lds_dma16sm(abase + h * kHK, offa[u], st + (4 * wave + u) * 1024);
+            attn::lds_dma16sm(bbase + h * kHK, offb[u], st + kSliceBytes + (4 * wave + u) * 1024);
         }
     };
     // All E8M0 scales of the tile wait in LDS, read once in a prologue: the A
-    // scales of step ks at ssa + 256 ks, packed so that the word at
+    // scales of group g at ssa + 256 g, packed so that the word at
     // 128 wm + 4 l32 holds the scales of this lane's row in row tiles 0..3
     // (the MFMA's op_sel picks the byte), the B scales of the wave's 128
-    // columns at ssb[ksteps wn + ks].  The loop then issues no global load
+    // columns at ssb[ksteps wn + g].  The loop then issues no global load
     // the compiler sees, so it places no wait of its own (one would also wait
     // for the direct-to-LDS loads in flight, which it cannot see).
     unsigned char *ssa = smem + kGemmLds;
     unsigned char *ssb = ssa + ksteps * 256;
-    // L2 prefetch of step ks, kPFD steps before its use: one dword of every
-    // row's 128-byte chunk of A and B (wave w: rows 64 w .. 64 w + 63) into a
-    // dummy LDS slot, so that the step's refill, issued one step ahead, finds
-    // its lines in L2 (3.71 -> 3.59 ms on the Gate-Up product, same box)
-    unsigned char *pf_lds = smem + kGemmSmem - 256;
-    auto prefetch = [&](int ks) {
-        const int r = 64 * wave + lane;
-        const int64_t k0 = (int64_t)ks * kBK;
-        attn::lds_dma4(a + (int64_t)min(m0 + r, M - 1) * K + k0, pf_lds);
-        attn::lds_dma4(b + (int64_t)(n0 + r) * K + k0, pf_lds);
-    };
-    issue(0, 0);                                       // the first tiles load under the prologue
 #pragma unroll
-    for (int j = 1; j <= kPFD - 1; ++j)
-        if (j < ksteps) prefetch(j);
+    for (int h = 0; h < kStages - 1; ++h)               // the first slices load under the prologue
+        if (h < H) issue(h);
     {
-        // thread t reads row m0 + t of every step (256 threads read one step's
-        // 256 contiguous bytes together), 16 steps' loads in flight at a time
+        // thread t reads row m0 + t of every group (256 threads read one
+        // group's 256 contiguous bytes together), 16 groups' loads in flight
         const int wq = tid >> 7, rq = (tid >> 5) & 3, lq = tid & 31;   // tid = 128 wm + 32 rt + l32
         const uint8_t *src = sa + min(m0 + tid, M - 1);
         unsigned char *dst = ssa + wq * 128 + lq * 4 + rq;
@@ -383,69 +386,90 @@ __global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    for (int ks = 0; ks < ksteps; ++ks) {
-        const int stage = ks & 1;
-        // this wave's loads of step ks have landed; the barrier makes every
-        // wave's loads (and, the first time, the scales) visible and tells
-        // that every wave is done with the stage the next loads refill
-        // (the prefetch issued after them may still be in flight)
-        if (ks - 1 + kPFD < ksteps && ks > 0) vm_wait<2>();
-        else vm_wait<0>();
-        __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
-        asm volatile("s_barrier" ::: "memory");
-        const int sav = *reinterpret_cast<const int *>(ssa + ks * 256 + wm * 128 + l32 * 4);
-        // EPI 0: the scale of the wave's 128 B rows; EPI 1: of the gate
-        // block (sbv) and of the up block (sbu)
-        const int sbv = ssb[(EPI == 1 ? 0 : wn) * ksteps + ks];
-        const int sbu = EPI == 1 ? (int)ssb[ksteps + ks] : 0;
-        const unsigned char *at = smem + stage * 2 * kTileBytes + wm * 128 * kBK;
-        const unsigned char *bt = smem + stage * 2 * kTileBytes + kTileBytes;
-        // B tile row of operand tile t: EPI 0 the wave's 128 rows; EPI 1 its
-        // gate rows 64 wn .. +63 (t = 0, 1) and up rows 128 + 64 wn .. +63
-        auto brow = [&](int t) { return EPI == 1 ? (t < 2 ? 64 * wn + 32 * t : 64 + 64 * wn + 32 * t) : 128 * wn + 32 * t; };
-        auto read_ops = [&](int kh, i32x8_t *av, i32x8_t *bv) {
-            const int c0 = kh * 4 + lh * 2;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int r = t * 32 + l32;
-                const uint4 x0 = *reinterpret_cast<const uint4 *>(at + swz(r, c0));
-                const uint4 x1 = *reinterpret_cast<const uint4 *>(at + swz(r, c0 + 1));
-                av[t] = i32x8_t{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                                (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-                const int rb = brow(t) + l32;
-                const uint4 y0 = *reinterpret_cast<const uint4 *>(bt + swz(rb, c0));
-                const uint4 y1 = *reinterpret_cast<const uint4 *>(bt + swz(rb, c0 + 1));
-                bv[t] = i32x8_t{(int)y0.x, (int)y0.y, (int)y0.z, (int)y0.w,
-                                (int)y1.x, (int)y1.y, (int)y1.z, (int)y1.w};
-            }
-        };
-        // the step's operand reads are issued before the refill (the loads'
-        // inline assembly orders every memory access around it), so the
-        // products start as soon as the first operands land
-        i32x8_t av[2][4], bv[2][4];
-        read_ops(0, av[0], bv[0]);
-        read_ops(1, av[1], bv[1]);
-        if (ks + 1 < ksteps) issue(ks + 1, stage ^ 1);
-        if (ks + kPFD < ksteps) prefetch(ks + kPFD);
+    // B tile row of operand tile t: EPI 0 the wave's 128 rows; EPI 1 its
+    // gate rows 64 wn .. +63 (t = 0, 1) and up rows 128 + 64 wn .. +63
+    auto brow = [&](int t) { return EPI == 1 ? (t < 2 ? 64 * wn + 32 * t : 64 + 64 * wn + 32 * t) : 128 * wn + 32 * t; };
+    // operand pair t of slice h (t = 0..3: A tile t; 4..7: B tile t - 4)
+    auto read_pair = [&](int h, int t, GemmOps &o) {
+        const unsigned char *st = smem + (h & (kStages - 1)) * 2 * kSliceBytes;
+        const int tt = t & 3;
+        const int r = t < 4 ? wm * 128 + tt * 32 + l32 : brow(tt) + l32;
+        const unsigned char *base = t < 4 ? st : st + kSliceBytes;
+        const uint4 x0 = *reinterpret_cast<const uint4 *>(base + swz(r, 2 * lh));
+        const uint4 x1 = *reinterpret_cast<const uint4 *>(base + swz(r, 2 * lh + 1));
+        const i32x8_t v = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        if (t < 4) o.a[tt] = v;
+        else o.b[tt] = v;
+    };
+    // EPI 0: the scale of the wave's 128 B rows; EPI 1: of the gate block
+    // (sb) and of the up block (su)
+    auto read_scales = [&](int h, GemmOps &o) {
+        const int g = h >> 1;
+        o.sa = *reinterpret_cast<const int *>(ssa + g * 256 + wm * 128 + l32 * 4);
+        o.sb = ssb[(EPI == 1 ? 0 : wn) * ksteps + g];
+        o.su = EPI == 1 ? (int)ssb[ksteps + g] : 0;
+    };
+    auto product = [&](int i, const GemmOps &o) {
         if (EPI == 1) {
             // C^T: acc[ft][tt], feature tile ft (gate 0, 1; up 2, 3) by token tile tt
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-                    for (int ft = 0; ft < 4; ++ft)
-                        acc[ft][tt] = mfma_scaled_b(bv[kh][ft], av[kh][tt], acc[ft][tt], ft < 2 ? sbv : sbu, sav, tt);
+            const int tt = i >> 2, ft = i & 3;
+            acc[ft][tt] = mfma_scaled_b(o.b[ft], o.a[tt], acc[ft][tt], ft < 2 ? o.sb : o.su, o.sa, tt);
         } else {
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-                    for (int ct = 0; ct < 4; ++ct)
-                        acc[rt][ct] = mfma_scaled(av[kh][rt], bv[kh][ct], acc[rt][ct], sav, rt, sbv);
+            const int rt = i >> 2, ct = i & 3;
+            acc[rt][ct] = mfma_scaled(o.a[rt], o.b[ct], acc[rt][ct], o.sa, rt, o.sb);
         }
+    };
+    // one slice: confirm slice h + 1 and free slice h's stage (a barrier
+    // after this wave's own loads of h + 1 and its reads of h), then the 16
+    // products of slice h with the reads of slice h + 1 and the refill of
+    // slice h + 4 interleaved between them.  MORE: a slice h + 1 exists;
+    // REFILL: a slice h + 4 exists; `ahead`: slices loaded after h + 1.
+    auto slice = [&](auto more_t, auto refill_t, int h, int ahead, const GemmOps &cur, GemmOps &nxt) {
+        constexpr bool MORE = decltype(more_t)::value, REFILL = decltype(refill_t)::value;
+        if (MORE) {
+            if (ahead >= 2) vm_wait<16>();
+            else if (ahead == 1) vm_wait<8>();
+            else vm_wait<0>();
+            __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+            asm volatile("s_barrier" ::: "memory");
+            read_scales(h + 1, nxt);
+        }
+        const uint32_t st = smem_lds + (uint32_t)((h & (kStages - 1)) * 2 * kSliceBytes);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            product(i, cur);
+            if (MORE && i < 8) read_pair(h + 1, i, nxt);
+            if (REFILL && i >= 8 && i < 12) {
+                const int u = i - 8;
+                attn::lds_dma16sm(abase + (h + kStages) * kHK, offa[u], st + (4 * wave + u) * 1024);
+                attn::lds_dma16sm(bbase + (h + kStages) * kHK, offb[u], st + kSliceBytes + (4 * wave + u) * 1024);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+
+    GemmOps o0, o1;
+    vm_wait<0>();
+    __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+    asm volatile("s_barrier" ::: "memory");
+    read_scales(0, o0);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) read_pair(0, t, o0);
+    if (kStages - 1 < H) issue(kStages - 1);
+    // H is even (K is a multiple of 128), so slice h reads o0 for even h
+    int h = 0;
+    for (; h < H - kStages; h += 2) {
+        slice(T{}, T{}, h, 2, o0, o1);
+        slice(T{}, T{}, h + 1, 2, o1, o0);
     }
+    for (; h < H - 2; h += 2) {                        // at most once: slices H - 4, H - 3
+        slice(T{}, F{}, h, min(H - 1, h + 3) - (h + 1), o0, o1);
+        slice(T{}, F{}, h + 1, min(H - 1, h + 4) - (h + 2), o1, o0);
+    }
+    slice(T{}, F{}, h, 0, o0, o1);                     // h = H - 2
+    slice(F{}, F{}, h + 1, 0, o1, o0);
 
     // ---- epilogues: the tile leaves through LDS (the stages are free once
     // every wave is past its last step) so that global stores are 16 bytes
