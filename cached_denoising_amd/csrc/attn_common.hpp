@@ -126,21 +126,6 @@ __device__ __forceinline__ void lds_dma16s(const void *sbase, uint32_t voff, voi
 #endif
 }
 
-// The scalar-base 16-byte load with the LDS byte address given as an integer
-// (no generic-to-LDS pointer conversion, whose null check costs scalar
-// instructions at every load)
-__device__ __forceinline__ void lds_dma16sm(const void *sbase, uint32_t voff, uint32_t lds) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                 : : "v"(voff), "s"(sbase), "s"(m0) : "memory", "m0");
-#else
-    (void)sbase;
-    (void)voff;
-    (void)lds;
-#endif
-}
-
 __device__ __forceinline__ void lds_dma4s(const void *sbase, uint32_t voff, void *lds_base) {
 #if defined(__HIP_DEVICE_COMPILE__)
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));

@@ -142,8 +142,10 @@ def _gemm_check(c, ref, sabs, label, narrow=False):
 
 
 @pytest.mark.parametrize("exps", [WIDE, NARROW], ids=["wide", "narrow"])
-@pytest.mark.parametrize("M,N,K", [(1, 256, 128), (300, 512, 384), (256, 768, 4096), (513, 256, 12288),
-                                   (2048, 1024, 1024)])
+# K = 128, 256, 384, 640 and longer: the 64-wide slices of the product's
+# LDS ring run through each of its start and end paths (2, 4, 6, 10 slices)
+@pytest.mark.parametrize("M,N,K", [(1, 256, 128), (70, 256, 256), (300, 512, 384), (200, 768, 640),
+                                   (256, 768, 4096), (513, 256, 12288), (2048, 1024, 1024)])
 def test_fp8_gemm_parity(orc, M, N, K, exps):
     D = need_gpu()
     a, sa, w, sw = _gemm_case(D, M, N, K, seed=M + N + K, exps=exps)
@@ -178,7 +180,7 @@ def _swiglu_ref(orc, a, sa, w, sw, rows):
     return orc.swiglu(gate, up).reshape(len(rows), n // 2)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 256, 128), (300, 512, 384), (257, 1024, 4096)])
+@pytest.mark.parametrize("M,N,K", [(1, 256, 128), (65, 512, 256), (300, 512, 384), (257, 1024, 4096)])
 def test_fp8_gemm_swiglu(orc, M, N, K):
     """on products within 2^6 of each other, where the fp8 MFMA loses
     nothing, so gate and up carry only fp32 error"""
