@@ -228,6 +228,15 @@ def test_fp8_ffn_block_llada_sampled(orc):
     got = out[torch.from_numpy(rows).cuda()].double().cpu().numpy()
     e = np.abs(got - ref).max() / np.abs(ref).max()
     assert e <= 2e-2, e
+    # row by row as well, so that one wrong row cannot hide behind the
+    # largest output.  The chains differ by the bf16 output's rounding (up to
+    # 2^-9 relative per element), by the fp8 products' alignment window
+    # (under 2^-8 of each 32-product group's largest term) and by the rare
+    # fp8 code that float32 puts on the other side of a rounding boundary
+    # than float64; measured: relative L2 error 2.1e-3 per row on average,
+    # 4.2e-3 at most, over these 24 rows
+    rel = np.linalg.norm(got - ref, axis=1) / np.linalg.norm(ref, axis=1)
+    assert rel.max() <= 1e-2, rel.max()
 
 
 def test_fp8_gemm_deterministic():
