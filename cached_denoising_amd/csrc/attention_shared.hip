@@ -581,13 +581,18 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
                                   pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
         }
 
-        // ---- O^T += V^T P^T
+        // ---- O^T += V^T P^T.  The wave raises its issue priority over its
+        // products, so that the other wave of the SIMD, in its vector phase,
+        // fills the matrix cores' gaps instead of delaying the products
+        // (about 1 % on the long-context step, same box, interleaved)
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
                 o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vop[dt]),
                                                                     pf[rt].v, o[dt][rt], 0, 0, 0);
+        __builtin_amdgcn_s_setprio(0);
     };
     auto ring = [&](int slot) { return smem + OFF_RING + slot * STAGE; };
     auto cstage = [&](int cslot) { return smem + cslot * CSTAGE; };
