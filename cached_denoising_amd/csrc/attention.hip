@@ -283,14 +283,14 @@ __global__ __launch_bounds__(NW * kWave, 2) void attn_mfma_kernel(
                 }
                 mx = x[0];
 #pragma unroll
-                for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+                for (int e = 1; e < 8; ++e) mx = vmax(mx, x[e]);
             } else {
                 // one positive scale for every key: take the max of the raw scores
 #pragma unroll
                 for (int e = 0; e < 8; ++e) x[e] = kval[e] ? sv[e] : kNegInf;
                 mx = x[0];
 #pragma unroll
-                for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+                for (int e = 1; e < 8; ++e) mx = vmax(mx, x[e]);
                 mx *= scale_log2;
             }
             mx = group4_max(mx);

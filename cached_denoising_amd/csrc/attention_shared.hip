@@ -528,10 +528,10 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
         }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            float v = fmaxf(fmaxf(y[rt][0], y[rt][1]), y[rt][2]);
-            v = fmaxf(fmaxf(v, y[rt][3]), y[rt][4]);
-            v = fmaxf(fmaxf(v, y[rt][5]), y[rt][6]);
-            ymx[rt] = fmaxf(v, y[rt][7]);      // this lane's 8 keys of the row
+            float v = vmax(vmax(y[rt][0], y[rt][1]), y[rt][2]);
+            v = vmax(vmax(v, y[rt][3]), y[rt][4]);
+            v = vmax(vmax(v, y[rt][5]), y[rt][6]);
+            ymx[rt] = vmax(v, y[rt][7]);       // this lane's 8 keys of the row
             lgrow = lgrow || ymx[rt] > kLazy;
         }
         // the reference max moves only when a tile's max exceeds it by more
@@ -551,7 +551,7 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
                     scores(rt, x);
                     float v = x[0];
 #pragma unroll
-                    for (int e = 1; e < 8; ++e) v = fmaxf(v, x[e]);
+                    for (int e = 1; e < 8; ++e) v = vmax(v, x[e]);
                     const float mx = group4_max(v);
                     const float corr = __builtin_amdgcn_exp2f(m[rt] - mx);
                     l[rt] *= corr;

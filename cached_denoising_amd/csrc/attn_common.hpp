@@ -170,6 +170,11 @@ __device__ __forceinline__ int chunk_dim(int c, int g) {
     return (c * 4 + g) * 8;
 }
 
+// IEEE maximum (NaN-propagating).  For scores, which are finite or -inf, it
+// equals fmaxf; on gfx950 it becomes v_maximum3_f32 chains, without the
+// canonicalising moves that fmaxf's NaN rule adds before every input.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Max and sum over the four 16-lane groups (lanes l, l^16, l^32, l^48), the
 // result in every lane: two gfx950 lane swaps (v_permlane32_swap, then
 // v_permlane16_swap) on the VALU instead of cross-lane LDS permutes.  With
@@ -177,9 +182,9 @@ __device__ __forceinline__ int chunk_dim(int c, int g) {
 // and its partner's in the other.
 __device__ __forceinline__ float group4_max(float v) {
     const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    v = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float group4_sum(float v) {
     const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);

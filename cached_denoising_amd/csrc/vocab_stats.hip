@@ -67,9 +67,12 @@ __device__ __forceinline__ void acc_merge(Acc &a, const Acc &b) {
 // gives element e's column; columns increase with e.
 template <int NE, typename IdxFn>
 __device__ __forceinline__ void consume(Acc &st, const float (&x)[NE], IdxFn gidx) {
+    // IEEE maximum: a NaN logit would propagate, but logits are finite or
+    // -inf, where it equals fmaxf; on gfx950 it is a v_maximum3_f32 chain
+    // without fmaxf's canonicalising moves
     float cm = x[0];
 #pragma unroll
-    for (int e = 1; e < NE; ++e) cm = fmaxf(cm, x[e]);
+    for (int e = 1; e < NE; ++e) cm = __builtin_elementwise_maximum(cm, x[e]);
     if (cm >= st.m && cm != kNegInf) {
         int first = NE - 1;
 #pragma unroll
