@@ -414,11 +414,9 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
             kfac[4] = a1.x; kfac[5] = a1.y; kfac[6] = a1.z; kfac[7] = a1.w;
             vfac[0] = c0.x; vfac[1] = c0.y; vfac[2] = c0.z; vfac[3] = c0.w;
             vfac[4] = c1.x; vfac[5] = c1.y; vfac[6] = c1.z; vfac[7] = c1.w;
-            if (full) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) kbias[e] = 0.f;
-            } else {
-                // the mask bias of missing keys, read only for tiles that have some
+            if (!full) {
+                // the mask bias of missing keys, read only for tiles that have
+                // some (a full tile never reads kbias, so no zeros are kept)
                 const float4 b0 = f4[8 + 2 * g], b1 = f4[8 + 2 * g + 1];
                 kbias[0] = b0.x; kbias[1] = b0.y; kbias[2] = b0.z; kbias[3] = b0.w;
                 kbias[4] = b1.x; kbias[5] = b1.y; kbias[6] = b1.z; kbias[7] = b1.w;
@@ -497,8 +495,14 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
             const f32x4_t s0 = sacc[rt][0], s1 = sacc[rt][1];
             const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
             if (CONV) {
+                // the key biases again from the tile's factors (written for
+                // every tile, 0 for a present key), so that a full tile keeps
+                // none in registers for this rare path
+                const float4 *f4 = reinterpret_cast<const float4 *>(fac);
+                const float4 b0 = f4[8 + 2 * g], b1 = f4[8 + 2 * g + 1];
+                const float kb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
-                for (int e = 0; e < 8; ++e) xo[e] = fmaf(sv[e], kfac[e], kbias[e]);
+                for (int e = 0; e < 8; ++e) xo[e] = fmaf(sv[e], kfac[e], kb[e]);
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) xo[e] = sv[e] * scale_log2;
