@@ -194,6 +194,7 @@ __global__ __launch_bounds__(NW * kWave, 2) void attn_mfma_kernel(
         if (MAP) return ktab[(kt - t_begin) * 32 + kappa];
         return kt * 32 + kappa < n_keys ? kt * 32 + kappa : -1;
     };
+    const unsigned char *cvrows = static_cast<const unsigned char *>(cv) + kv_base * ROWB;
     auto issue = [&](int kt, Tile &T, unsigned char *vbuf) {
         T.kl = key_of(kt, lane & 31);
 #pragma unroll
@@ -213,9 +214,10 @@ __global__ __launch_bounds__(NW * kWave, 2) void attn_mfma_kernel(
             const int rho = RPI * u + lane / CPR;
             const int chunk = (lane % CPR) ^ vswz<KVDT>(rho);
             const int kk = key_of(kt, rho);
-            const unsigned char *src = static_cast<const unsigned char *>(cv) +
-                                       (kv_base + (kk < 0 ? 0 : kk)) * ROWB + chunk * 16;
-            lds_dma16<NT>(src, vbuf + u * 1024);
+            // a 32-bit byte offset from the wave-uniform base of this
+            // (sequence, KV head)'s rows, which span less than 4 GiB
+            const uint32_t off = (uint32_t)(kk < 0 ? 0 : kk) * ROWB + (uint32_t)chunk * 16;
+            lds_dma16<NT>(cvrows, off, lds_addr(vbuf) + u * 1024);
         }
         T.kfl = scale_log2;
         T.vsl = 1.f;

@@ -273,8 +273,9 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
     // span less than 4 GiB)
     const unsigned char *kbase = static_cast<const unsigned char *>(ck) + kv_base * ROWB;
     const unsigned char *vbase = static_cast<const unsigned char *>(cv) + kv_base * ROWB;
+    const uint32_t smem_lds = lds_addr(smem);
     auto issue = [&](const TileKeys &tk, int slot) {
-        unsigned char *st = smem + OFF_RING + slot * STAGE;
+        const uint32_t st = smem_lds + (uint32_t)(OFF_RING + slot * STAGE);
 #pragma unroll
         for (int u = 0; u < NK / NRG; ++u) {
             // chunk position p of the tile: row p / CPR, stored slot p % CPR
@@ -284,7 +285,7 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
             const int r = p / CPR, sl = p % CPR;
             const int kk = tk.k[u];
             const uint32_t off = (uint32_t)(kk < 0 ? 0 : kk) * ROWB + (uint32_t)(sl ^ kswz_r(r)) * 16;
-            lds_dma16s<NT>(kbase, off, st + j * 1024);
+            lds_dma16<NT>(kbase, off, st + j * 1024);
         }
 #pragma unroll
         for (int u = 0; u < NK / NRG; ++u) {
@@ -294,7 +295,7 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
             const int chunk = (lane % CPR) ^ vswz_r(rho);
             const int kk = tk.v[u];
             const uint32_t off = (uint32_t)(kk < 0 ? 0 : kk) * ROWB + (uint32_t)chunk * 16;
-            lds_dma16s<NT>(vbase, off, st + TB + jv * 1024);
+            lds_dma16<NT>(vbase, off, st + TB + jv * 1024);
         }
         if (E4) {
             // lanes 0..31: K scales of keys 0..31; lanes 32..63: V scales;
@@ -304,7 +305,7 @@ __global__ __launch_bounds__(NRG * kWave, 2) void attn_shared_kernel(
             if (lane >= lo && lane < lo + 64 / NRG) {
                 const int kk = tk.s;
                 const float *sbase = (lo < 32 ? ksc : vsc) + kv_base;
-                lds_dma4s(sbase, (uint32_t)(kk < 0 ? 0 : kk) * 4, st + 2 * TB);
+                lds_dma4(sbase, (uint32_t)(kk < 0 ? 0 : kk) * 4, st + 2 * TB);
             }
         }
     };

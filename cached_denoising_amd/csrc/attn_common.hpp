@@ -63,15 +63,19 @@ __device__ __forceinline__ uint2 lds_tr8(const unsigned char *p) {
 #endif
 }
 
-// Direct-to-LDS loads (global_load_lds): lane i of the wave writes lds_base +
-// size * i, lds_base wave-uniform.  They are issued from inline assembly, so
+// Direct-to-LDS loads (global_load_lds): lane i of the wave reads sbase +
+// voff_i and writes LDS byte lds + size * i, sbase and lds wave-uniform (the
+// scalar-base form: one 32-bit offset per lane, no 64-bit address).  The LDS
+// address is an integer, as lds_addr gives it once for a buffer: a generic
+// pointer converted to the LDS address space carries a null check (a scalar
+// compare and select) at every use.  They are issued from inline assembly, so
 // the compiler's wait-count pass does not see an LDS write in flight: seen,
 // it makes every later LDS read of the kernel wait for all outstanding loads
 // (vmcnt 0), which empties the load pipeline at each tile.  The kernels wait
-// for these loads themselves (vm_wait) before the data is read.  NT marks
-// the load non-temporal: right when the rows are read once, wrong when other
-// workgroups re-read them through L2.  M0 holds the LDS address; the s_nop
-// is the wait state an M0 write needs before an LDS-DMA instruction.
+// for these loads themselves (vm_wait) before the data is read.  NT marks the
+// load non-temporal: right when the rows are read once, wrong when other
+// workgroups re-read them through L2.  M0 holds the LDS address; the s_nop is
+// the wait state an M0 write needs before an LDS-DMA instruction.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 #if defined(__HIP_DEVICE_COMPILE__)
     return (uint32_t)(uintptr_t)(lds_u8 *)(const_cast<void *>(p));
@@ -81,38 +85,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 }
 
 template <bool NT>
-__device__ __forceinline__ void lds_dma16(const void *src, void *lds_base) {
+__device__ __forceinline__ void lds_dma16(const void *sbase, uint32_t voff, uint32_t lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
-    if (NT)
-        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
-                     : : "v"(src), "s"(m0) : "memory", "m0");
-    else
-        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                     : : "v"(src), "s"(m0) : "memory", "m0");
-#else
-    (void)src;
-    (void)lds_base;
-#endif
-}
-
-__device__ __forceinline__ void lds_dma4(const void *src, void *lds_base) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-                 : : "v"(src), "s"(m0) : "memory", "m0");
-#else
-    (void)src;
-    (void)lds_base;
-#endif
-}
-
-// The same two loads from a wave-uniform base plus a 32-bit per-lane byte
-// offset (the scalar-base form: no 64-bit address per lane)
-template <bool NT>
-__device__ __forceinline__ void lds_dma16s(const void *sbase, uint32_t voff, void *lds_base) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
     if (NT)
         asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                      : : "v"(voff), "s"(sbase), "s"(m0) : "memory", "m0");
@@ -122,19 +97,19 @@ __device__ __forceinline__ void lds_dma16s(const void *sbase, uint32_t voff, voi
 #else
     (void)sbase;
     (void)voff;
-    (void)lds_base;
+    (void)lds;
 #endif
 }
 
-__device__ __forceinline__ void lds_dma4s(const void *sbase, uint32_t voff, void *lds_base) {
+__device__ __forceinline__ void lds_dma4(const void *sbase, uint32_t voff, uint32_t lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
                  : : "v"(voff), "s"(sbase), "s"(m0) : "memory", "m0");
 #else
     (void)sbase;
     (void)voff;
-    (void)lds_base;
+    (void)lds;
 #endif
 }
 

@@ -287,25 +287,6 @@ __device__ __forceinline__ f32x16_t mfma_scaled_b(const i32x8_t &a, const i32x8_
     }
 }
 
-// Direct-to-LDS 16-byte load per lane (global_load_lds_dwordx4) from a
-// wave-uniform base plus a 32-bit per-lane byte offset, lane i writing LDS
-// byte lds + 16 i; the LDS address comes as an integer, so no generic-to-LDS
-// pointer conversion (and its null check) is paid per load.  Issued from
-// inline assembly, so the compiler's wait counts do not see it: the loop
-// waits for these loads itself.  The s_nop is the wait state an M0 write
-// needs before an LDS-DMA instruction.
-__device__ __forceinline__ void lds_load16(const void *sbase, uint32_t voff, uint32_t lds) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                 : : "v"(voff), "s"(sbase), "s"(m0) : "memory", "m0");
-#else
-    (void)sbase;
-    (void)voff;
-    (void)lds;
-#endif
-}
-
 // LDS byte offset of 16-byte chunk c (0..3) of stage row r.  A read phase of
 // 16 lanes takes rows r .. r + 15 at one logical chunk, and the 64 banks span
 // 256 bytes, i.e. four 64-byte rows: rows of equal r % 4 share a quarter of
@@ -362,8 +343,8 @@ __global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(
         const uint32_t st = smem_lds + (uint32_t)((h & (kStages - 1)) * 2 * kSliceBytes);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            lds_load16(abase + h * kHK, offa[u], st + (4 * wave + u) * 1024);
-            lds_load16(bbase + h * kHK, offb[u], st + kSliceBytes + (4 * wave + u) * 1024);
+            lds_dma16<false>(abase + h * kHK, offa[u], st + (4 * wave + u) * 1024);
+            lds_dma16<false>(bbase + h * kHK, offb[u], st + kSliceBytes + (4 * wave + u) * 1024);
         }
     };
     // All E8M0 scales of the tile wait in LDS, read once in a prologue: the A
@@ -460,8 +441,8 @@ __global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(
             if (MORE && i < 8) read_pair(h + 1, i, nxt);
             if (REFILL && i >= 8 && i < 12) {
                 const int u = i - 8;
-                lds_load16(abase + (h + kStages) * kHK, offa[u], st + (4 * wave + u) * 1024);
-                lds_load16(bbase + (h + kStages) * kHK, offb[u], st + kSliceBytes + (4 * wave + u) * 1024);
+                lds_dma16<false>(abase + (h + kStages) * kHK, offa[u], st + (4 * wave + u) * 1024);
+                lds_dma16<false>(bbase + (h + kStages) * kHK, offb[u], st + kSliceBytes + (4 * wave + u) * 1024);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
