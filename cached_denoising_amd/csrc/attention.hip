@@ -194,18 +194,27 @@ __global__ __launch_bounds__(NW * kWave, 2) void attn_mfma_kernel(
         if (MAP) return ktab[(kt - t_begin) * 32 + kappa];
         return kt * 32 + kappa < n_keys ? kt * 32 + kappa : -1;
     };
+    // the key whose rows tile-local key kappa loads: itself, or for a missing
+    // key (past the selection, -1 in the map) an in-range one, whose score
+    // is masked
+    auto key_ld = [&](int kt, int kappa) -> uint32_t {
+        if (MAP) return (uint32_t)max(ktab[(kt - t_begin) * 32 + kappa], 0);
+        return (uint32_t)min(kt * 32 + kappa, n_keys - 1);
+    };
+    // 32-bit byte offsets from the wave-uniform bases of this (sequence, KV
+    // head)'s rows, which span less than 4 GiB
+    const unsigned char *ckrows = static_cast<const unsigned char *>(ck) + kv_base * ROWB;
     const unsigned char *cvrows = static_cast<const unsigned char *>(cv) + kv_base * ROWB;
     auto issue = [&](int kt, Tile &T, unsigned char *vbuf) {
         T.kl = key_of(kt, lane & 31);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             // slot l16 of half t is key 8(l16/4) + 4t + l16%4
-            const int kk = key_of(kt, 8 * (l16 >> 2) + 4 * t + (l16 & 3));
-            const unsigned char *kp = static_cast<const unsigned char *>(ck) + (kv_base + (kk < 0 ? 0 : kk)) * ROWB;
+            const uint32_t koff = key_ld(kt, 8 * (l16 >> 2) + 4 * t + (l16 & 3)) * ROWB;
 #pragma unroll
             for (int cc = 0; cc < KR; ++cc) {
                 const int cd = KVDT == DLLM_E4M3 ? 2 * cc : cc;
-                T.kr[t][cc] = *reinterpret_cast<const uint4 *>(kp + chunk_dim<KVDT>(cd, g) * ESZ);
+                T.kr[t][cc] = *reinterpret_cast<const uint4 *>(ckrows + koff + chunk_dim<KVDT>(cd, g) * ESZ);
             }
         }
 #pragma unroll
@@ -213,16 +222,13 @@ __global__ __launch_bounds__(NW * kWave, 2) void attn_mfma_kernel(
             // this lane fills chunk slot lane % CPR of row RPI*u + lane / CPR
             const int rho = RPI * u + lane / CPR;
             const int chunk = (lane % CPR) ^ vswz<KVDT>(rho);
-            const int kk = key_of(kt, rho);
-            // a 32-bit byte offset from the wave-uniform base of this
-            // (sequence, KV head)'s rows, which span less than 4 GiB
-            const uint32_t off = (uint32_t)(kk < 0 ? 0 : kk) * ROWB + (uint32_t)chunk * 16;
+            const uint32_t off = key_ld(kt, rho) * ROWB + (uint32_t)chunk * 16;
             lds_dma16<NT>(cvrows, off, lds_addr(vbuf) + u * 1024);
         }
         T.kfl = scale_log2;
         T.vsl = 1.f;
         if (KVDT == DLLM_E4M3) {
-            const int64_t rr = kv_base + (T.kl < 0 ? 0 : T.kl);
+            const int64_t rr = kv_base + key_ld(kt, lane & 31);
             T.kfl = scale_log2 * ksc[rr];
             T.vsl = vsc[rr];
         }
