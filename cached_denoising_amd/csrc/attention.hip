@@ -83,7 +83,7 @@ __global__ __launch_bounds__(NW * kWave, 2) void attn_mfma_kernel(
     __shared__ float sm_ml[NW][ROWS][2];
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
     const int l16 = lane & 15;
     const int g = lane >> 4;
 
