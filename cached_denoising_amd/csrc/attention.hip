@@ -283,28 +283,30 @@ __global__ __launch_bounds__(NW * kWave, 2) void attn_mfma_kernel(
             const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
             float x[8];
             float mx;
+            // a full tile (wave-uniform) masks nothing
             if (KVDT == DLLM_E4M3) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float v = sv[e] * kfac[e];
-                    x[e] = kval[e] ? v : kNegInf;
-                }
-                mx = x[0];
-#pragma unroll
-                for (int e = 1; e < 8; ++e) mx = vmax(mx, x[e]);
+                for (int e = 0; e < 8; ++e) x[e] = sv[e] * kfac[e];
             } else {
-                // one positive scale for every key: take the max of the raw scores
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = kval[e] ? sv[e] : kNegInf;
-                mx = x[0];
-#pragma unroll
-                for (int e = 1; e < 8; ++e) mx = vmax(mx, x[e]);
-                mx *= scale_log2;
+                for (int e = 0; e < 8; ++e) x[e] = sv[e];
             }
-            mx = group4_max(mx);
-            const bool grow = mx > m[rt] + kLazy;
-            if (__ballot(grow)) {
-                if (grow) {
+            if (!full) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (!kval[e]) x[e] = kNegInf;
+            }
+            mx = x[0];
+#pragma unroll
+            for (int e = 1; e < 8; ++e) mx = vmax(mx, x[e]);
+            // one positive scale for every key (bf16): the max of the raw scores
+            if (KVDT != DLLM_E4M3) mx *= scale_log2;
+            // the row's max exceeds m + kLazy only if one of its four lanes'
+            // does, so the lane maxima are tested first and the row maxima
+            // formed only when some lane of the wave sees such a key
+            if (__ballot(mx > m[rt] + kLazy)) {
+                mx = group4_max(mx);
+                if (mx > m[rt] + kLazy) {
                     const float corr = __builtin_amdgcn_exp2f(m[rt] - mx);
                     l[rt] *= corr;
 #pragma unroll
