@@ -234,6 +234,8 @@ __global__ __launch_bounds__(NW * kWave, 2) void attn_mfma_kernel(
         }
     };
 
+    // the B operands of S^T, the same for every tile: read once from LDS
+    uint4 qreg[RT][NC];
     auto compute = [&](int kt, const Tile &T, const unsigned char *vt) {
         // per-key factors of the keys this lane holds in S^T (8g .. 8g+7), and
         // whether every key of the tile is present (then nothing is masked)
@@ -276,7 +278,7 @@ __global__ __launch_bounds__(NW * kWave, 2) void attn_mfma_kernel(
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 Frag qf;
-                qf.u = *reinterpret_cast<const uint4 *>(qs + (rt * 16 + l16) * QSTR + chunk_dim<KVDT>(c, g) * 2);
+                qf.u = qreg[rt][c];
                 s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop(0, c), qf.v, s0, 0, 0, 0);
                 s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop(1, c), qf.v, s1, 0, 0, 0);
             }
@@ -380,6 +382,11 @@ __global__ __launch_bounds__(NW * kWave, 2) void attn_mfma_kernel(
         if (idx < QN) *reinterpret_cast<uint4 *>(qs + (idx / (D / 8)) * QSTR + (idx % (D / 8)) * 16) = qv[it];
     }
     __syncthreads();
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            qreg[rt][c] = *reinterpret_cast<const uint4 *>(qs + (rt * 16 + l16) * QSTR + chunk_dim<KVDT>(c, g) * 2);
     for (int kt = t_begin; kt < t_end; kt += S) {
 #pragma unroll
         for (int j = 0; j < S; ++j) {
