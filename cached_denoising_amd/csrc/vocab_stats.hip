@@ -191,9 +191,13 @@ __global__ __launch_bounds__(kThreads) void vocab_stats_kernel(
         const uint4 *vp = reinterpret_cast<const uint4 *>(rp + a0);
         constexpr unsigned kStep = kUnroll * kThreads;       // vectors per step
         const int steps = (int)(nvec / kStep);               // full steps, uniform
+        // loads at 32-bit byte offsets from the row's wave-uniform base (a row
+        // spans less than 4 GiB): no 64-bit address per lane and load
+        const unsigned char *vb = reinterpret_cast<const unsigned char *>(vp);
         auto issue = [&](uint4 (&w)[kUnroll], unsigned o) {
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) w[u] = load_stream(vp + o + u * kThreads);
+            for (int u = 0; u < kUnroll; ++u)
+                w[u] = load_stream(reinterpret_cast<const uint4 *>(vb + (o + u * kThreads) * 16u));
         };
         auto fold = [&](const uint4 (&w)[kUnroll], unsigned o) {
             float x[kUnroll * kVec];
