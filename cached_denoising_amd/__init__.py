@@ -25,10 +25,12 @@ __all__ = [
     "dllm_vocab_stats_workspace", "dllm_stability_reset", "dllm_stability_mask",
     "dllm_refresh_interval", "dllm_cache_quotas", "dllm_evict_by_confidence",
     "dllm_parallel_width", "dllm_self_verify", "dllm_confidence_decay", "dllm_check_positions",
-    "dllm_scatter_attention_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "dllm_scatter_attention_noalloc", "NOALLOC_SCRATCH_BYTES", "dllm_workspace_size",
+    "WS_BLOCK_ATTENTION", "WS_FACACHE_MERGE", "WS_VOCAB_STATS",
 ]
 
 F32, BF16, E4M3 = 0, 1, 2
+WS_BLOCK_ATTENTION, WS_FACACHE_MERGE, WS_VOCAB_STATS = 0, 1, 2   # dllm_workspace_kind
 NOALLOC_SCRATCH_BYTES = 64 << 20      # DLLM_NOALLOC_SCRATCH_BYTES of include/dllm.h
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdllm.so")
 
@@ -51,6 +53,12 @@ class _StabParams(ctypes.Structure):
                 ("decay", ctypes.c_void_p), ("vocab", ctypes.c_int64),
                 ("R_early", ctypes.c_int32), ("T_steps", ctypes.c_int32),
                 ("refresh_every", ctypes.c_int32), ("n_decay", ctypes.c_int32)]
+
+
+class _WsArgs(ctypes.Structure):
+    _fields_ = [("cache", ctypes.POINTER(_KVCache)), ("q_dtype", ctypes.c_int32),
+                ("Hq", ctypes.c_int32), ("n_q", ctypes.c_int32), ("n_keys", ctypes.c_int32),
+                ("N", ctypes.c_int64), ("V", ctypes.c_int64)]
 
 
 EXPORTS = {
@@ -117,6 +125,7 @@ EXPORTS = {
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_size_t, ctypes.c_void_p]),
     "dllm_vocab_stats_workspace": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64]),
+    "dllm_workspace_size": (ctypes.c_size_t, [ctypes.c_int, ctypes.POINTER(_WsArgs)]),
     "dllm_stability_reset": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -567,6 +576,15 @@ def dllm_fp8_gemm_swiglu(a: torch.Tensor, a_scale: torch.Tensor, w: torch.Tensor
 
 def dllm_vocab_stats_workspace(N: int, V: int) -> int:
     return lib().dllm_vocab_stats_workspace(N, V)
+
+
+def dllm_workspace_size(which: int, cache: Optional[Cache] = None, q_dtype: int = BF16, Hq: int = 0,
+                        n_q: int = 0, n_keys: int = 0, N: int = 0, V: int = 0) -> int:
+    """Workspace bytes of the call `which` names (WS_*), from the shape fields
+    that kind reads; 0 for an unknown kind or rejected shapes."""
+    args = _WsArgs(cache=ctypes.pointer(cache.desc) if cache is not None else None,
+                   q_dtype=q_dtype, Hq=Hq, n_q=n_q, n_keys=n_keys, N=N, V=V)
+    return lib().dllm_workspace_size(which, ctypes.byref(args))
 
 
 def dllm_vocab_stats(logits: torch.Tensor, V: Optional[int] = None,

@@ -372,6 +372,20 @@ size_t dllm_vocab_stats_workspace(int64_t N, int64_t V) {
     return plan_vocab(N, V).ws_bytes;
 }
 
+size_t dllm_workspace_size(int which, const dllm_workspace_args *a) {
+    if (a == nullptr) return 0;
+    switch (which) {
+    case DLLM_WS_BLOCK_ATTENTION:
+        return dllm_block_attention_workspace(a->cache, a->q_dtype, a->Hq, a->n_q, a->n_keys);
+    case DLLM_WS_FACACHE_MERGE:
+        return dllm_facache_merge_workspace(a->cache, a->q_dtype, a->Hq, a->n_q, a->n_keys);
+    case DLLM_WS_VOCAB_STATS:
+        return dllm_vocab_stats_workspace(a->N, a->V);
+    default:
+        return 0;
+    }
+}
+
 int dllm_vocab_stats(const void *logits, int dtype, int64_t N, int64_t V, int64_t row_stride,
                      int32_t *argmax, float *maxprob, float *entropy, void *workspace,
                      size_t ws_bytes, void *stream) {

@@ -16,6 +16,8 @@
  *   dllm_fp8_*             per-group FP8 FFN: quantisers, add & norm + quant,
  *                          block-scaled GEMM, GEMM + SwiGLU + quant
  *   dllm_vocab_stats       argmax token, max-probability, entropy per row
+ *   dllm_*_workspace, dllm_workspace_size
+ *                          scratch bytes a call needs for its shapes
  *   dllm_stability_reset   clear the per-position decode state
  *   dllm_stability_mask    history ring, stability test, confidence score and
  *                          window expansion -> next step's compute mask
@@ -38,7 +40,9 @@
  * Conventions shared by every call
  *   - Every array argument is a DEVICE pointer to memory the caller owns
  *     (the library allocates no device memory and keeps no state between
- *     calls).  Scalars and parameter structs are host values.
+ *     calls, apart from the fixed per-GPU array that
+ *     dllm_scatter_attention_noalloc works in).  Scalars and parameter
+ *     structs are host values.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls enqueue work on it and return without synchronising.
  *   - Shapes are row-major (C order), innermost dimension last.
@@ -408,6 +412,36 @@ int dllm_vocab_stats(const void *logits, int dtype, int64_t N, int64_t V, int64_
                      void *workspace, size_t ws_bytes, void *stream);
 
 size_t dllm_vocab_stats_workspace(int64_t N, int64_t V);
+
+/* ---------------------------------------------------------------------------
+ * dllm_workspace_size -- the three workspace queries above behind one call,
+ * for a caller that sizes every workspace through a single entry point.
+ *   which       a dllm_workspace_kind
+ *   shape_args  host pointer to a dllm_workspace_args.  The block-attention
+ *               and FACache kinds read cache, q_dtype, Hq, n_q (the block's
+ *               b for block attention) and n_keys; the vocab kind reads N and
+ *               V.  Other fields are ignored.
+ * Returns what the matching query returns for those shapes, and 0 for an
+ * unknown kind or a NULL shape_args (as the queries do for shapes they
+ * reject: the call itself then reports the error).
+ * ------------------------------------------------------------------------- */
+typedef enum {
+    DLLM_WS_BLOCK_ATTENTION = 0,  /* dllm_block_attention, dllm_scatter_attention */
+    DLLM_WS_FACACHE_MERGE = 1,    /* dllm_facache_merge                          */
+    DLLM_WS_VOCAB_STATS = 2       /* dllm_vocab_stats                            */
+} dllm_workspace_kind;
+
+typedef struct {
+    const dllm_kv_cache *cache;
+    int q_dtype;
+    int Hq;
+    int n_q;
+    int n_keys;
+    int64_t N;
+    int64_t V;
+} dllm_workspace_args;
+
+size_t dllm_workspace_size(int which, const dllm_workspace_args *shape_args);
 
 /* ---------------------------------------------------------------------------
  * dllm_stability_reset -- empty the history ring (ring_step = -1) and clear

@@ -188,3 +188,26 @@ def test_noalloc_scratch_limit(dl):
                                             131072, 0.0, 16, 1, None, None) == -2
     assert L.dllm_scatter_attention_noalloc(ctypes.byref(desc), 16, 16, 1, 16, 64, None, None, 1, 32, 64, 16,
                                             131072, 0.0, 16, 1, None, None) == -1
+
+
+def test_workspace_size_dispatches_to_each_query(dl):
+    L = dl.lib()
+    gqa = dl._KVCache(B=4, L=32768, n_kv_heads=8, d_head=128, dtype=2, k=16, v=16, k_scale=16,
+                      v_scale=16)
+    mha = dl._KVCache(B=16, L=2048, n_kv_heads=32, d_head=128, dtype=1, k=16, v=16)
+    ref = dl.Cache(gqa, None, None, None, None)
+    for desc, Hq, n_q, n_keys in [(gqa, 32, 64, 8192), (gqa, 32, 7, 100), (mha, 32, 32, 2048),
+                                  (mha, 32, 2016, 32), (mha, 30, 32, 2048), (mha, 32, 0, 2048)]:
+        c = dl.Cache(desc, None, None, None, None)
+        want = L.dllm_block_attention_workspace(ctypes.byref(desc), 1, Hq, n_q, n_keys)
+        assert dl.dllm_workspace_size(dl.WS_BLOCK_ATTENTION, c, dl.BF16, Hq, n_q, n_keys) == want
+        want = L.dllm_facache_merge_workspace(ctypes.byref(desc), 1, Hq, n_q, n_keys)
+        assert dl.dllm_workspace_size(dl.WS_FACACHE_MERGE, c, dl.BF16, Hq, n_q, n_keys) == want
+    assert dl.dllm_workspace_size(dl.WS_BLOCK_ATTENTION, ref, dl.BF16, 32, 64, 8192) > 0
+    for N, V in [(64, 126464), (512, 126464), (8192, 50257), (0, 7), (3, 0)]:
+        assert dl.dllm_workspace_size(dl.WS_VOCAB_STATS, N=N, V=V) == L.dllm_vocab_stats_workspace(N, V)
+    assert dl.dllm_workspace_size(dl.WS_VOCAB_STATS, N=64, V=126464) > 0
+    # an unknown kind, a missing cache and a NULL argument block answer 0
+    assert dl.dllm_workspace_size(3, ref, dl.BF16, 32, 64, 8192) == 0
+    assert dl.dllm_workspace_size(dl.WS_BLOCK_ATTENTION, None, dl.BF16, 32, 64, 8192) == 0
+    assert L.dllm_workspace_size(dl.WS_VOCAB_STATS, None) == 0
