@@ -72,6 +72,45 @@ def test_attention_tiny_f32(orc):
     _check(orc, D, cache, q * W.sharp_query_scale(cfg) ** 0.5, label="tiny f32 sharp")
 
 
+# Shapes the MFMA layouts do not take (float32 queries or cache, head sizes
+# other than 64 and 128) run on the float32 path, one wave per query row over
+# 64-key tiles: several tiles with a ragged tail, GQA, every cache dtype, two
+# e4m3 scale groups per row, and a key map with padding.  An index outside
+# [0, L) is skipped like padding (the library's convention; the oracle takes
+# only valid maps), so that case is checked against the padded map's output.
+VALU_CASES = [
+    ("f32 cache, f32 q, d32", W.F32, torch.float32, 32, 4, 2, 5, 200, False),
+    ("bf16 cache, f32 q, d64", W.BF16, torch.float32, 64, 2, 1, 7, 130, False),
+    ("bf16 cache, bf16 q, d96", W.BF16, torch.bfloat16, 96, 6, 3, 9, 257, False),
+    ("e4m3 cache, bf16 q, d256", W.E4M3, torch.bfloat16, 256, 2, 2, 3, 150, False),
+    ("f32 cache, f32 q, d48, map", W.F32, torch.float32, 48, 3, 1, 4, 300, True),
+]
+
+
+@pytest.mark.parametrize("label,kv,qt,d,Hq,Hkv,b,L,with_map", VALU_CASES)
+def test_attention_valu_path(orc, label, kv, qt, d, Hq, Hkv, b, L, with_map):
+    D = need_gpu()
+    B = 2
+    cache = _fill(D, B, Hkv, L, d, kv, seed=31 + d, std=1 / np.sqrt(d))
+    g = torch.Generator().manual_seed(32 + d)
+    q = (torch.randn((B, Hq, b, d), generator=g) / np.sqrt(d)).to(qt).cuda()
+    kid = None
+    if with_map:
+        rng = np.random.default_rng(33)
+        m = np.stack([rng.permutation(L)[:150] for _ in range(B)]).astype(np.int32)
+        m[rng.random(m.shape) < 0.2] = -1
+        m[0, 7] = m[1, 3] = -1
+        kid = torch.from_numpy(m).cuda()
+    out, _ = _check(orc, D, cache, q, key_idx=kid, label=label)
+    _check(orc, D, cache, (q.float() * 8 * np.sqrt(d)).to(qt), key_idx=kid, label=label + " sharp")
+    if with_map:
+        m[0, 7] = L + 5
+        m[1, 3] = -7
+        out2 = D.dllm_block_attention(cache, q, key_idx=torch.from_numpy(m).cuda())
+        torch.cuda.synchronize()
+        assert torch.equal(out2, out), label
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("Hq,Hkv,b,L", [(2, 2, 32, 200), (4, 1, 32, 77), (8, 2, 64, 333),
                                         (3, 3, 5, 40), (2, 1, 48, 1000)])
