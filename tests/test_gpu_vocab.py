@@ -77,6 +77,27 @@ def test_vocab_strides_and_splits(orc, V, stride, N):
         _compare(orc, x.to(tdt).cuda(), dt, V, label=f"V{V} stride{stride} N{N} dt{dt}")
 
 
+def test_vocab_edge_sizes(orc):
+    """no rows; one logit per row (max-prob exactly 1, entropy exactly 0);
+    rows shorter than one 16-byte vector; a view whose rows all start off
+    the 16-byte grid (the head and tail of every row peeled)"""
+    D = need_gpu()
+    for dt, tdt in ((W.F32, torch.float32), (W.BF16, torch.bfloat16)):
+        am, mp, en = D.dllm_vocab_stats(torch.zeros((0, 10), dtype=tdt, device="cuda"))
+        assert am.numel() == mp.numel() == en.numel() == 0
+        x = torch.randn((37, 3), generator=torch.Generator().manual_seed(5)) * 4
+        am, mp, en = _compare(orc, x.to(tdt).cuda(), dt, 1, label=f"V1 dt{dt}")
+        # the exponent argument is x log2(e) minus the rounded m log2(e), so
+        # the one probability is 1 within the rounding of that product
+        assert np.all(am == 0)
+        assert np.all(np.abs(mp - 1.0) <= 4e-7) and np.all(np.abs(en) <= 1e-6), (mp.min(), mp.max(), en)
+        for V in (2, 3, 7, 8, 9):
+            _compare(orc, x.repeat(1, 3).to(tdt).cuda(), dt, V, label=f"V{V} dt{dt}")
+        big = torch.randn((50, 1100), generator=torch.Generator().manual_seed(6)).to(tdt).cuda()
+        view = big[:, 5:5 + 1000]                            # row stride 1100, start off the grid
+        _compare(orc, view, dt, 1000, label=f"offset view dt{dt}")
+
+
 def test_vocab_gpt2_full_sampled(orc):
     cfg = W.CONFIGS["gpt2"]
     x = W.logits(cfg, device="cuda")
