@@ -11,10 +11,13 @@
 // elements before the first 16-byte boundary and after the last are peeled
 // off.  Each thread keeps an online state over base-2 exponents
 // a_j = (x_j - m) log2(e):
-//     m = running max,  s = sum 2^a_j,  t = sum 2^a_j a_j,  idx = argmax
-// so that  maxprob = 1/s  and  entropy = ln s - ln2 * t / s.  States merge in
-// a fixed order (wave butterfly, then the waves in order, then splits), so
-// the result is bitwise reproducible.  The probabilities never touch memory.
+//     m = max,  s = sum 2^a_j,  t = sum 2^a_j a_j,  idx = argmax
+// so that  maxprob = 1/s  and  entropy = ln s - ln2 * t / s.  In the main
+// loop m is a reference up to 8 below the max (terms up to e^8), and the
+// state is taken to the max once at the end; the entropy does not depend on
+// the reference, 1/s does.  States merge in a fixed order (wave butterfly,
+// then the waves in order, then splits), so the result is bitwise
+// reproducible.  The probabilities never touch memory.
 #include "common.hpp"
 
 #include <climits>
@@ -24,6 +27,11 @@ namespace {
 
 constexpr int kUnroll = 2;      // 16-byte loads per thread per step (two steps in flight)
 constexpr float kNegInf = -__builtin_inff();
+// In the main loop the exponents are taken against a reference max that moves
+// only when a step's max exceeds it by more than this (natural units): terms
+// then stay below e^8, and the rescale is rare instead of taken by some lane
+// of the wave on almost every step
+constexpr float kLazyRef = 8.0f;
 
 struct Acc {
     float m, s, t;
@@ -63,6 +71,45 @@ __device__ __forceinline__ void acc_merge(Acc &a, const Acc &b) {
     a = Acc{m, s, t, idx};
 }
 
+// Add the terms 2^a and 2^a a of NE logits, a = (x - m) log2(e), to s and t
+// (m finite).  A -inf logit gives 0 * -inf = NaN in t; such terms add
+// nothing, so the logits are then summed again without them.
+template <int NE>
+__device__ __forceinline__ void fold_sums(const float (&x)[NE], float m, float &s, float &t) {
+    const float mL = m * kLog2e;
+    float s0 = 0.f, s1 = 0.f, t0 = 0.f, t1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < NE; e += 2) {
+        const float a0 = fmaf(x[e], kLog2e, -mL);
+        const float p0 = __builtin_amdgcn_exp2f(a0);
+        s0 += p0;
+        t0 = fmaf(p0, a0, t0);
+        if (e + 1 < NE) {
+            const float a1 = fmaf(x[e + 1], kLog2e, -mL);
+            const float p1 = __builtin_amdgcn_exp2f(a1);
+            s1 += p1;
+            t1 = fmaf(p1, a1, t1);
+        }
+    }
+    float cs = s0 + s1, ct = t0 + t1;
+    if (ct != ct) {
+        // a -inf logit gave 0 * -inf; such terms add nothing, drop them
+        cs = 0.f;
+        ct = 0.f;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            if (x[e] != kNegInf) {
+                const float a = fmaf(x[e], kLog2e, -mL);
+                const float p = __builtin_amdgcn_exp2f(a);
+                cs += p;
+                ct = fmaf(p, a, ct);
+            }
+        }
+    }
+    s += cs;
+    t += ct;
+}
+
 // Fold NE consecutive-in-thread-order elements into the state.  gidx(e)
 // gives element e's column; columns increase with e.
 template <int NE, typename IdxFn>
@@ -93,38 +140,7 @@ __device__ __forceinline__ void consume(Acc &st, const float (&x)[NE], IdxFn gid
         }
     }
     if (st.m == kNegInf) return;                 // nothing finite seen yet
-    const float mL = st.m * kLog2e;
-    float s0 = 0.f, s1 = 0.f, t0 = 0.f, t1 = 0.f;
-#pragma unroll
-    for (int e = 0; e < NE; e += 2) {
-        const float a0 = fmaf(x[e], kLog2e, -mL);
-        const float p0 = __builtin_amdgcn_exp2f(a0);
-        s0 += p0;
-        t0 = fmaf(p0, a0, t0);
-        if (e + 1 < NE) {
-            const float a1 = fmaf(x[e + 1], kLog2e, -mL);
-            const float p1 = __builtin_amdgcn_exp2f(a1);
-            s1 += p1;
-            t1 = fmaf(p1, a1, t1);
-        }
-    }
-    float cs = s0 + s1, ct = t0 + t1;
-    if (ct != ct) {
-        // a -inf logit gave 0 * -inf; such terms add nothing, drop them
-        cs = 0.f;
-        ct = 0.f;
-#pragma unroll
-        for (int e = 0; e < NE; ++e) {
-            if (x[e] != kNegInf) {
-                const float a = fmaf(x[e], kLog2e, -mL);
-                const float p = __builtin_amdgcn_exp2f(a);
-                cs += p;
-                ct = fmaf(p, a, ct);
-            }
-        }
-    }
-    st.s += cs;
-    st.t += ct;
+    fold_sums<NE>(x, st.m, st.s, st.t);
 }
 
 template <int DT> struct Elem;
@@ -199,13 +215,45 @@ __global__ __launch_bounds__(kThreads) void vocab_stats_kernel(
             for (int u = 0; u < kUnroll; ++u)
                 w[u] = load_stream(reinterpret_cast<const uint4 *>(vb + (o + u * kThreads) * 16u));
         };
+        // The main loop keeps a lazy state: sums lm_s, lm_t against the
+        // reference lm, and the step with the first maximum so far (its max
+        // bm and offset bo by selects, its raw vectors in this thread's LDS
+        // slot, stored under the lanes' record mask).  The position of the
+        // maximum within that step is found once after the loop, and the sums
+        // are then taken to bm: the state the per-step form keeps, without
+        // its position scan and rescale, which some lane of the wave needed on
+        // almost every step.
+        constexpr int NE = kUnroll * kVec;
+        float lm = kNegInf, lm_s = 0.f, lm_t = 0.f, bm = kNegInf;
+        unsigned bo = 0;
+        __shared__ uint4 s_bw[kUnroll][kThreads];     // the recorded step's raw vectors, per thread
         auto fold = [&](const uint4 (&w)[kUnroll], unsigned o) {
-            float x[kUnroll * kVec];
+            float x[NE];
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) E::unpack(w[u], x + u * kVec);
-            consume<kUnroll * kVec>(st, x, [&](int e) {
-                return (int)(a0 + (int64_t)(o + (e / kVec) * kThreads) * kVec + (e % kVec));
-            });
+            // IEEE maximum (v_maximum3_f32, no canonicalising moves): logits
+            // are finite or -inf, where it equals fmaxf
+            float cm = x[0];
+#pragma unroll
+            for (int e = 1; e < NE; ++e) cm = __builtin_elementwise_maximum(cm, x[e]);
+            // a later step with an equal max keeps the earlier one (lower positions)
+            const bool rec = cm > bm;
+            bm = rec ? cm : bm;
+            bo = rec ? o : bo;
+            if (rec) {
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) s_bw[u][tid] = w[u];
+            }
+            if (cm > lm + kLazyRef) {                    // also the first finite step (lm = -inf)
+                if (lm_s > 0.f) {
+                    const float d = (lm - cm) * kLog2e;
+                    const float f = __builtin_amdgcn_exp2f(d);
+                    lm_t = f * (lm_t + lm_s * d);
+                    lm_s *= f;
+                }
+                lm = cm;
+            }
+            if (lm != kNegInf) fold_sums<NE>(x, lm, lm_s, lm_t);
         };
         // two register buffers: step i+1 is in flight while step i is folded
         uint4 wa[kUnroll], wb[kUnroll];
@@ -222,6 +270,21 @@ __global__ __launch_bounds__(kThreads) void vocab_stats_kernel(
         if (i < steps) {
             fold(wa, off);
             off += kStep;
+        }
+        if (bm != kNegInf) {
+            // the first position of the maximum in the recorded step, and the
+            // sums relative to the maximum (the max term alone gives lm_s >= 1)
+            float x[NE];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) E::unpack(s_bw[u][tid], x + u * kVec);
+            int first = NE - 1;
+#pragma unroll
+            for (int e = NE - 1; e >= 0; --e)
+                if (x[e] == bm) first = e;
+            const int gi = (int)(a0 + (int64_t)(bo + (first / kVec) * kThreads) * kVec + (first % kVec));
+            const float d = (lm - bm) * kLog2e;
+            const float f = __builtin_amdgcn_exp2f(d);
+            st = Acc{bm, lm_s * f, f * (lm_t + lm_s * d), gi};
         }
         if (peel) consume<1>(st, xp, [&](int) { return (int)jp; });
         // the rest: fewer than kStep vectors
