@@ -143,8 +143,16 @@ def test_attention_key_splits(orc, d, Hq, Hkv, b, L, dtype):
     assert D.dllm_block_attention_workspace(cache, W.BF16, Hq, b, L) > 0
     g = torch.Generator().manual_seed(L + 1)
     q = (torch.randn((B, Hq, b, d), generator=g) / np.sqrt(d)).bfloat16().cuda()
-    _check(orc, D, cache, q, label=f"split d{d} L{L}")
+    out, _ = _check(orc, D, cache, q, label=f"split d{d} L{L}")
     _check(orc, D, cache, (q.float() * 12 * np.sqrt(d)).bfloat16(), label=f"split d{d} L{L} sharp")
+    # a workspace of exactly the size the single workspace query gives
+    # (uninitialised: the partials are written before they are read)
+    need = D.dllm_workspace_size(D.WS_BLOCK_ATTENTION, cache, D.BF16, Hq, b, L)
+    assert need == D.dllm_block_attention_workspace(cache, W.BF16, Hq, b, L)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out2 = D.dllm_block_attention(cache, q, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out)
 
 
 def test_attention_e4m3_map_key_splits(orc):
