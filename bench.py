@@ -57,6 +57,7 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -719,19 +720,39 @@ def padded_stride_vocab_us(step, W, reps=50):
     return stride, us
 
 
+CPU_BUDGET_S = 12.0     # seconds of oracle runs on every core; half that on one thread
+
+
+def repeat_timed(call, budget):
+    """call() -> (seconds per step, sample), repeated until `budget` seconds
+    have passed (at least once): the median, the sample, the repeats and the
+    seconds spent"""
+    t0 = time.perf_counter()
+    dts, sample = [], ""
+    while True:
+        dt, sample = call()
+        dts.append(dt)
+        if time.perf_counter() - t0 >= budget:
+            break
+    return statistics.median(dts), sample, len(dts), time.perf_counter() - t0
+
+
 def cpu_baseline_line(fn):
     """fn(frac) -> (seconds per step, sample): the oracle on every host core
-    this process may use, then on one thread on a quarter of the sample"""
+    this process may use, then on one thread on a quarter of the sample, each
+    repeated for a bounded time (median of the repeats)"""
     import oracle
     model, nproc = cpu_info()
     threads = oracle.set_threads(host_threads())
-    dt, sample = fn(1.0)
+    dt, sample, reps, spent = repeat_timed(lambda: fn(1.0), CPU_BUDGET_S)
     oracle.set_threads(1)
-    dt1, sample1 = fn(0.25)
+    dt1, sample1, reps1, spent1 = repeat_timed(lambda: fn(0.25), CPU_BUDGET_S / 2)
     oracle.set_threads(threads)
-    return {"value": round(1.0 / dt, 4), "unit": "steps/s", "cores": threads, "kind": "oracle",
-            "sample": sample, "cpu_model": model, "nproc": nproc,
-            "value_1thread": round(1.0 / dt1, 4), "sample_1thread": sample1}
+    sig = lambda x: float(f"{x:.4g}")                     # four significant figures
+    return {"value": sig(1.0 / dt), "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "repeats": reps, "seconds": round(spent, 1), "cpu_model": model,
+            "nproc": nproc, "value_1thread": sig(1.0 / dt1), "sample_1thread": sample1,
+            "repeats_1thread": reps1, "seconds_1thread": round(spent1, 1)}
 
 
 def main():
