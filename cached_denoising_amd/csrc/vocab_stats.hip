@@ -300,12 +300,28 @@ __global__ __launch_bounds__(kThreads) void vocab_stats_kernel(
         }
     }
 
-    // wave butterfly, then the waves in order
+    // the wave: its max, every lane's sums taken to it (one exponential per
+    // lane), then butterfly sums and the lowest index among the lanes at the
+    // max (every lane ends with the same values); then the waves in order
+    {
+        float wm = st.m;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        Acc other{shfl_xor_f(st.m, o), shfl_xor_f(st.s, o), shfl_xor_f(st.t, o),
-                  shfl_xor_i(st.idx, o)};
-        acc_merge(st, other);
+        for (int o = 32; o >= 1; o >>= 1) wm = fmaxf(wm, shfl_xor_f(wm, o));
+        float ws = 0.f, wt = 0.f;
+        if (st.s > 0.f) {
+            const float d = (st.m - wm) * kLog2e;
+            const float f = exp2f(d);
+            ws = st.s * f;
+            wt = f * (st.t + st.s * d);
+        }
+        int wi = st.m == wm ? st.idx : INT_MAX;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            ws += shfl_xor_f(ws, o);
+            wt += shfl_xor_f(wt, o);
+            wi = min(wi, shfl_xor_i(wi, o));
+        }
+        st = Acc{wm, ws, wt, wi};
     }
     __shared__ Acc waves[kThreads / kWave];
     if ((tid & (kWave - 1)) == 0) waves[tid / kWave] = st;
