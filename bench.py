@@ -912,7 +912,7 @@ def main():
                      "around each call of %d eager steps (cold: after a 1 GiB device read), b2b = one event pair "
                      "around back-to-back launches of the call alone from a captured graph; a cold roofline figure "
                      "is the mean of the cold launches between their 10th and 90th percentiles" % iters)
-    per_kernel_us = {n: hot[n]["mean"] for n in names}
+    per_kernel_us = {n: hot[n]["tmean"] for n in names}
     alg = step.algorithmic_bytes()
     flops = step.algorithmic_flops()
     # the dominant kernel is the one the step spends the most time in; it is
