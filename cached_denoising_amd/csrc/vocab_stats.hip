@@ -6,8 +6,9 @@
 // One workgroup of 256 threads (512 when there are too few rows to fill the
 // chip) streams one row, or one contiguous split of a row when there are very
 // few rows, with non-temporal 16-byte loads.  The loop is software-pipelined:
-// each thread keeps the next step's two loads in flight while it folds the
-// current two, so a wave never waits on memory with nothing issued.  The few
+// each thread keeps the next step's loads (three or two 16-byte vectors) in
+// flight while it folds the current ones, so a wave never waits on memory
+// with nothing issued.  The few
 // elements before the first 16-byte boundary and after the last are peeled
 // off.  Each thread keeps an online state over base-2 exponents
 // a_j = (x_j - m) log2(e):
