@@ -56,7 +56,7 @@ def _evict_case(orc, D, B, L, conf, cached, mask, quota, pos, label):
 def test_evict_small_ragged(orc, kind):
     D = need_gpu()
     rng = np.random.default_rng({"ties": 11, "wide": 12, "grid": 13}[kind])
-    for L in (1, 7, 63, 64, 65, 1000, 1024, 1025, 3001):
+    for L in (1, 7, 63, 64, 65, 1000, 1024, 1025, 2048, 2049, 3001):
         B = int(rng.integers(1, 5))
         conf = _conf(rng, B, L, kind)
         cached = (rng.random((B, L)) < 0.6).astype(np.uint8)
